@@ -1,0 +1,361 @@
+"""CPU oracle for the Mixture-of-Experts layer forward.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, obviously correct
+statement of what the layer computes.  Only the test suite, the package's
+smoke check and the benchmark's CPU-baseline leg may import it; the library
+and its binding never do, and this module never imports them.
+
+Precision.  Every floating-point step runs in float64 (NumPy).  The one place
+the pages fix a precision that decides an integer is the router: the gate
+output is taken in float32 before the softmax and the top-k (MindSpore
+hyper-parallel ``moe.py``, ``TokenChoiceTopKRouter.forward``: the gate is
+evaluated "in float32 for numerical stability"; Qwen3-Omni issue #115,
+``SpeedupMoeSparseMoeBlock.forward``: ``softmax(..., dtype=float)``).  So the
+router logits are rounded once to float32 and the top-k decision is taken on
+those float32 values; everything after that is float64 again.
+
+Pages and sections cited below:
+
+* [QO] Qwen3-Omni issue #115, "Training: Extremely Slow Deepspeed Engine
+  initialization ...": ``SpeedupMoeExperts`` (concatenated experts
+  ``gate_up_proj [E, H, 2I]``, ``down_proj [E, I, H]``; per-expert training
+  loop and all-expert ``bmm`` eval path) and ``SpeedupMoeSparseMoeBlock.forward``
+  (gate -> fp32 softmax -> top-k -> optional renormalisation).
+* [HP] MindSpore hyper-parallel coverage page for ``moe.py``:
+  ``TokenChoiceTopKRouter.forward``, ``_run_experts_for_loop``,
+  ``MoE.permutation``, ``MoE.unpermutation``, ``MoE.forward``.
+* [TP] transformers PR "Qwen3 moe": ``Ep2DpParallel._token_dispatch`` (layout of
+  the rows one expert-parallel rank receives) and ``_token_combine``.
+* [ED] transformers "Expert parallelism" docs, section "Token dispatch"
+  (contiguous expert blocks per rank; combine with routing weights on the
+  source rank).
+
+Readings where the pages leave a step open (each also listed in the design
+notes): logits stay float32 (not bf16) before the softmax; the top-k ranks the
+float32 logits (softmax is monotone, so the selected set is the same) with
+ties going to the lower expert id and ``-0.0 == +0.0``; slots of one token are
+ordered by that key; the routing weight multiplies the expert output in the
+combine (as [QO] does), not the expert input; no epsilon in the
+renormalisation.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "router_logits", "select_topk", "routing_weights", "route",
+    "expert_counts", "expert_offsets", "permutation", "gather_rows",
+    "silu", "swiglu_expert", "grouped_swiglu", "combine", "unpermute",
+    "moe_layer_forward", "moe_layer_forward_brute", "moe_layer_forward_tokens",
+    "dispatch_rank_major", "reshuffle_rank_to_expert", "ep_rank_forward",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Router  ([QO] SpeedupMoeSparseMoeBlock.forward; [HP] TokenChoiceTopKRouter.forward)
+# ---------------------------------------------------------------------------
+
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """Router logits ``L[t, e] = sum_h x[t, h] * Wr[e, h] (+ b[e])``.
+
+    ``Wr`` has the ``nn.Linear(H, E)`` layout ``[E, H]`` ([QO] ``self.gate``;
+    [HP] ``self.gate = nn.Linear(dim, num_experts)``).  The optional per-expert
+    bias is added to the logit (it is the skewed workload's popularity knob).
+    Computed in float64, rounded once to float32 (the gate is taken in float32
+    on both pages)."""
+    L = _f64(x) @ _f64(w_router).T
+    if bias is not None:
+        L = L + _f64(bias)[None, :]
+    L32 = L.astype(np.float32)
+    if not np.all(np.isfinite(L32)):
+        raise ValueError("router logits must be finite")
+    return L32
+
+
+def select_topk(logits32: np.ndarray, k: int) -> np.ndarray:
+    """Top-k experts per token ([QO] ``torch.topk(routing_weights, top_k)``;
+    [HP] ``scores_with_bias.topk``).
+
+    Experts are ranked by the key (-logit, expert id): larger float32 logit
+    first, equal logits (float equality, so -0.0 equals +0.0) go to the lower
+    id.  Returns ``ids[T, k]`` int32 in that order."""
+    L = np.asarray(logits32, dtype=np.float32)
+    T, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("top_k must be in [1, E]")
+    eid = np.broadcast_to(np.arange(E, dtype=np.int64), L.shape)
+    # np.lexsort sorts by the last key first; -L compares -0.0 == +0.0.
+    order = np.lexsort((eid, -L.astype(np.float64)), axis=-1)
+    return order[:, :k].astype(np.int32)
+
+
+def routing_weights(logits32: np.ndarray, ids: np.ndarray, norm_topk_prob: bool) -> np.ndarray:
+    """Routing weights of the selected experts ([QO] forward: fp32 softmax
+    over all experts, keep the top-k probabilities, divide by their sum when
+    ``norm_topk_prob``).  Softmax uses the max-subtracted form; float64."""
+    L = _f64(logits32)
+    m = L.max(axis=1, keepdims=True)
+    p = np.exp(L - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    if norm_topk_prob:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w
+
+
+def route(x, w_router, bias, top_k: int, norm_topk_prob: bool):
+    """Router logits, top-k ids and routing weights for every token."""
+    L = router_logits(x, w_router, bias)
+    ids = select_topk(L, top_k)
+    w = routing_weights(L, ids, norm_topk_prob)
+    return L, ids, w
+
+
+# ---------------------------------------------------------------------------
+# Histogram and permutation  ([HP] MoE.permutation, TokenChoiceTopKRouter.forward)
+# ---------------------------------------------------------------------------
+
+def expert_counts(ids: np.ndarray, E: int) -> np.ndarray:
+    """Tokens per expert ([HP] ``torch.bincount(selected_experts.flatten(),
+    minlength=num_experts)``): count each (token, slot) pair once."""
+    c = np.zeros(E, dtype=np.int64)
+    for e in np.asarray(ids).reshape(-1):
+        c[int(e)] += 1
+    return c.astype(np.int32)
+
+
+def expert_offsets(counts: np.ndarray) -> np.ndarray:
+    """Start row of each expert's group in expert-major order, plus the end:
+    ``o[0] = 0, o[e + 1] = o[e] + c[e]``."""
+    o = np.zeros(len(counts) + 1, dtype=np.int64)
+    for e, c in enumerate(counts):
+        o[e + 1] = o[e] + int(c)
+    return o.astype(np.int32)
+
+
+def permutation(ids: np.ndarray, E: int):
+    """Token-major -> expert-major order ([HP] ``MoE.permutation``: a stable
+    argsort of the flattened expert ids; ``token_indices = flat // top_k``).
+
+    Written out directly: for each expert in ascending id, the flat slots
+    ``t * k + j`` that chose it, in ascending slot order (so ascending token,
+    since a token never picks one expert twice).
+
+    Returns ``(sorted_slot[N], sorted_token[N], slot_pos[N])``:
+    ``sorted_slot[p]`` is the flat slot at expert-major position ``p``,
+    ``sorted_token[p] = sorted_slot[p] // k`` its token, and ``slot_pos`` the
+    inverse (``slot_pos[sorted_slot[p]] = p``)."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    order: List[int] = []
+    for e in range(E):
+        order.extend(int(i) for i in np.flatnonzero(flat == e))
+    sorted_slot = np.asarray(order, dtype=np.int64)
+    slot_pos = np.empty(T * k, dtype=np.int64)
+    slot_pos[sorted_slot] = np.arange(T * k)
+    return (sorted_slot.astype(np.int32), (sorted_slot // k).astype(np.int32),
+            slot_pos.astype(np.int32))
+
+
+def gather_rows(x, index) -> np.ndarray:
+    """``x[index]`` ([HP] ``routed_x = x_flat[token_indices]``)."""
+    return np.asarray(x)[np.asarray(index, dtype=np.int64)]
+
+
+# ---------------------------------------------------------------------------
+# Experts  ([QO] SpeedupMoeExperts; [HP] _run_experts_for_loop)
+# ---------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU, ``z * sigmoid(z) = z / (1 + exp(-z))``."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(x_rows, gate_up_e, down_e) -> np.ndarray:
+    """One expert on its rows ([QO] training path: ``gate_up = state @
+    gate_up_proj[e]``; ``gate, up = gate_up.chunk(2)``; ``up * act(gate)``;
+    ``@ down_proj[e]``).  Gate is the first I columns of ``gate_up``."""
+    gu = _f64(gate_up_e)
+    I2 = gu.shape[1]
+    I = I2 // 2
+    G = _f64(x_rows) @ gu
+    g, u = G[:, :I], G[:, I:]
+    h = silu(g) * u
+    return h @ _f64(down_e)
+
+
+def grouped_swiglu(x_rows_expert_major, counts, gate_up, down) -> np.ndarray:
+    """Per-expert SwiGLU over rows already in expert-major order, split by
+    ``counts`` ([HP] ``_run_experts_for_loop``; empty experts are skipped)."""
+    X = np.asarray(x_rows_expert_major)
+    N = X.shape[0]
+    H = np.asarray(down).shape[2]
+    Y = np.zeros((N, H), dtype=np.float64)
+    start = 0
+    for e, n in enumerate(np.asarray(counts).tolist()):
+        if n == 0:
+            continue
+        Y[start:start + n] = swiglu_expert(X[start:start + n], gate_up[e], down[e])
+        start += n
+    return Y
+
+
+def combine(y_slot_major, weights) -> np.ndarray:
+    """Weighted sum of each token's k expert outputs in slot order:
+    ``out[t] = sum_j w[t, j] * y[t * k + j]`` ([QO] ``expert_out * routing_weights``
+    then ``index_add_`` into the token rows; [HP] ``MoE.unpermutation``)."""
+    w = _f64(weights)
+    T, k = w.shape
+    Y = _f64(y_slot_major).reshape(T, k, -1)
+    out = np.zeros((T, Y.shape[2]), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * Y[:, j, :]
+    return out
+
+
+def unpermute(y_expert_major, slot_pos) -> np.ndarray:
+    """Expert-major rows back to flat-slot order: ``y_slot[i] = y[slot_pos[i]]``."""
+    return _f64(y_expert_major)[np.asarray(slot_pos, dtype=np.int64)]
+
+
+# ---------------------------------------------------------------------------
+# The layer  ([QO] SpeedupMoeSparseMoeBlock.forward + SpeedupMoeExperts training
+# path; [HP] MoE.forward)
+# ---------------------------------------------------------------------------
+
+def moe_layer_forward(x, w_router, bias, gate_up, down, top_k: int,
+                      norm_topk_prob: bool) -> dict:
+    """Full layer: route, permute, per-expert SwiGLU loop, combine.
+
+    Returns a dict with ``logits`` (float32 [T, E]), ``ids`` ([T, k]),
+    ``weights`` ([T, k] float64), ``counts``, ``offsets``, ``sorted_slot``,
+    ``sorted_token``, ``slot_pos``, ``y`` (expert-major expert outputs, float64
+    [N, H]) and ``out`` (float64 [T, H])."""
+    x = np.asarray(x)
+    E = np.asarray(w_router).shape[0]
+    L, ids, w = route(x, w_router, bias, top_k, norm_topk_prob)
+    counts = expert_counts(ids, E)
+    offsets = expert_offsets(counts)
+    sorted_slot, sorted_token, slot_pos = permutation(ids, E)
+    y = np.zeros((ids.size, np.asarray(down).shape[2]), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        y[lo:hi] = swiglu_expert(gather_rows(x, sorted_token[lo:hi]), gate_up[e], down[e])
+    out = combine(unpermute(y, slot_pos), w)
+    return dict(logits=L, ids=ids, weights=w, counts=counts, offsets=offsets,
+                sorted_slot=sorted_slot, sorted_token=sorted_token,
+                slot_pos=slot_pos, y=y, out=out)
+
+
+def moe_layer_forward_brute(x, w_router, bias, gate_up, down, top_k: int,
+                            norm_topk_prob: bool) -> np.ndarray:
+    """Every expert applied to every token, then masked by the selection and
+    weighted ([QO] ``SpeedupMoeExperts`` eval path: ``bmm`` over all experts,
+    one-hot mask times routing weights, sum over experts).  Small inputs only."""
+    L, ids, w = route(x, w_router, bias, top_k, norm_topk_prob)
+    E = np.asarray(w_router).shape[0]
+    T = np.asarray(x).shape[0]
+    out = np.zeros((T, np.asarray(down).shape[2]), dtype=np.float64)
+    for e in range(E):
+        y_all = swiglu_expert(x, gate_up[e], down[e])          # [T, H]
+        mask_w = np.where(ids == e, w, 0.0).sum(axis=1)        # [T]
+        out += mask_w[:, None] * y_all
+    return out
+
+
+def moe_layer_forward_tokens(x, w_router, bias, gate_up, down, top_k: int,
+                             norm_topk_prob: bool, tokens: Sequence[int]) -> dict:
+    """The layer output for a chosen subset of tokens only.  Each token is
+    routed and combined on its own, so its row equals the full layer's row
+    ([QO] per-token reading of the forward).  Used to spot-check large
+    workloads."""
+    xs = np.asarray(x)[np.asarray(tokens, dtype=np.int64)]
+    L, ids, w = route(xs, w_router, bias, top_k, norm_topk_prob)
+    out = np.zeros((xs.shape[0], np.asarray(down).shape[2]), dtype=np.float64)
+    for j in range(top_k):
+        for e in np.unique(ids[:, j]):
+            rows = np.flatnonzero(ids[:, j] == e)
+            out[rows] += w[rows, j:j + 1] * swiglu_expert(xs[rows], gate_up[int(e)], down[int(e)])
+    return dict(logits=L, ids=ids, weights=w, out=out)
+
+
+# ---------------------------------------------------------------------------
+# One expert-parallel rank  ([TP] Ep2DpParallel; [ED] "Token dispatch")
+# ---------------------------------------------------------------------------
+
+def dispatch_rank_major(source_hidden: Sequence, w_router, top_k: int,
+                        norm_topk_prob: bool, local_lo: int, E_local: int):
+    """Rows one EP rank receives, laid out rank-major.
+
+    Each source rank routes its own tokens with the shared router, keeps the
+    (token, expert) pairs whose expert lies in this rank's contiguous block
+    ``[local_lo, local_lo + E_local)`` ([ED]: experts are cut into contiguous
+    blocks), orders them by (local expert, token) and sends them; the receiver
+    concatenates by source rank ([TP] ``_token_dispatch``: the all-to-all
+    returns rows grouped by source rank, each block ordered by local expert).
+
+    Returns ``(rows[N, H] float32, counts_rm[R, E_local] int32, meta)`` with
+    ``meta[i] = (source rank, token, slot j)`` of received row ``i``."""
+    rows, meta = [], []
+    R = len(source_hidden)
+    C = np.zeros((R, E_local), dtype=np.int64)
+    for r, xr in enumerate(source_hidden):
+        xr = np.asarray(xr)
+        L, ids, _ = route(xr, w_router, None, top_k, norm_topk_prob)
+        for el in range(E_local):
+            e = local_lo + el
+            tok, slot = np.nonzero(ids == e)       # row-major: ascending token
+            C[r, el] = len(tok)
+            rows.append(xr[tok])
+            meta.extend((r, int(t), int(j)) for t, j in zip(tok, slot))
+    H = np.asarray(source_hidden[0]).shape[1]
+    R_rm = np.concatenate(rows, axis=0) if rows else np.zeros((0, H), np.float32)
+    return R_rm, C.astype(np.int32), meta
+
+
+def reshuffle_rank_to_expert(counts_rm: np.ndarray) -> np.ndarray:
+    """Index map from expert-major position to rank-major row.
+
+    Received rows are blocks ``(source rank r, local expert e)`` in rank-major
+    order; the experts need blocks ``(e, r)``.  Block order within a block is
+    kept.  Returns ``src[p]``: the rank-major row placed at expert-major
+    position ``p`` ([TP] ``_reshuffle_indices`` / the comment that the
+    received rows "need to be reshuffled")."""
+    C = np.asarray(counts_rm, dtype=np.int64)
+    R, El = C.shape
+    start = np.zeros((R, El), dtype=np.int64)
+    pos = 0
+    for r in range(R):
+        for e in range(El):
+            start[r, e] = pos
+            pos += C[r, e]
+    src: List[int] = []
+    for e in range(El):
+        for r in range(R):
+            src.extend(range(int(start[r, e]), int(start[r, e] + C[r, e])))
+    return np.asarray(src, dtype=np.int32)
+
+
+def ep_rank_forward(rows_rm, counts_rm, gate_up_local, down_local) -> dict:
+    """Reshuffle received rows to expert-major, run the local experts, and put
+    the outputs back in rank-major order.  No routing weight is applied here:
+    the source rank combines ([ED] "Token dispatch"; [TP] ``_token_combine``
+    returns the raw expert outputs)."""
+    src = reshuffle_rank_to_expert(counts_rm)
+    counts_em = np.asarray(counts_rm, dtype=np.int64).sum(axis=0)
+    X = gather_rows(rows_rm, src)
+    Y_em = grouped_swiglu(X, counts_em, gate_up_local, down_local)
+    Y_rm = np.zeros_like(Y_em)
+    Y_rm[src.astype(np.int64)] = Y_em
+    return dict(src=src, counts=counts_em.astype(np.int32), y_em=Y_em, y_rm=Y_rm)

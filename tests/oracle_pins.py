@@ -1,0 +1,385 @@
+"""Pins for the CPU oracle: checks against facts fixed by the pages and by
+mathematics, not against the oracle's own formulas.
+
+Each ``pin_*`` function raises ``AssertionError`` when the oracle is wrong.
+They are plain functions so that a test can also plant a mistake in the
+oracle and confirm that some pin catches it.
+
+What pins what:
+
+* router logits: one-hot tokens (closed form), zero weights (logit = bias),
+  small-integer inputs (exact integer dot products by brute force);
+* top-k: all-equal logits (closed form of the lower-id tie rule), large bias
+  on a chosen set, -0.0 vs +0.0, brute force over all k-subsets;
+* routing weights: renormalised weights sum to one, k = 1 gives 1, uniform
+  logits give 1/k and 1/E exactly, the two-expert sigmoid closed form, the
+  full softmax against scipy's;
+* counts / permutation: sum invariant, numpy's bincount and stable argsort,
+  bijection, gather-then-inverse identity;
+* expert FFN / combine: the all-expert masked path of the Qwen3-Omni issue
+  (brute force), identical experts (dense SwiGLU via torch), E = 1, k = E soft
+  mixture, zero token, the scalar closed form at H = I = 1, permute + combine
+  with an identity expert;
+* expert-parallel rank: a hand-worked reshuffle, and equality with the
+  token-choice layer when one rank owns every expert.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def _layer(T, H, I, E, seed=0, std=0.3):
+    r = _rng(seed)
+    x = r.standard_normal((T, H)).astype(np.float32)
+    wr = (r.standard_normal((E, H)) * std).astype(np.float32)
+    gu = (r.standard_normal((E, H, 2 * I)) * std).astype(np.float32)
+    dn = (r.standard_normal((E, I, H)) * std).astype(np.float32)
+    return x, wr, gu, dn
+
+
+def _torch_swiglu(x, gu, dn):
+    """Dense SwiGLU with torch's own SiLU (an independent implementation)."""
+    xt = torch.as_tensor(np.asarray(x, np.float64))
+    gut = torch.as_tensor(np.asarray(gu, np.float64))
+    dnt = torch.as_tensor(np.asarray(dn, np.float64))
+    I = gut.shape[1] // 2
+    G = xt @ gut
+    h = torch.nn.functional.silu(G[:, :I]) * G[:, I:]
+    return (h @ dnt).numpy()
+
+
+# --------------------------------------------------------------------- logits
+
+def pin_logits_onehot():
+    """A one-hot token selects one column of the router weight:
+    ``L[t, e] = Wr[e, h_t] + b[e]`` with a single product, so exact."""
+    r = _rng(1)
+    T, H, E = 12, 16, 8
+    hs = r.integers(0, H, T)
+    x = np.zeros((T, H), np.float32)
+    x[np.arange(T), hs] = 1.0
+    wr = r.standard_normal((E, H)).astype(np.float32)
+    b = r.standard_normal(E).astype(np.float32)
+    L = O.router_logits(x, wr, b)
+    expect = (wr[:, hs].T.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+    assert L.dtype == np.float32
+    assert np.array_equal(L, expect), "one-hot logits"
+
+
+def pin_logits_zero_weight():
+    b = np.array([0.5, -1.25, 3.0, 0.0], np.float32)
+    L = O.router_logits(np.ones((3, 8), np.float32), np.zeros((4, 8), np.float32), b)
+    assert np.array_equal(L, np.tile(b, (3, 1))), "zero router weight gives the bias"
+
+
+def pin_logits_integer_exact():
+    """Small integers: the exact dot product by brute force in Python ints."""
+    r = _rng(2)
+    T, H, E = 5, 7, 4
+    x = r.integers(-3, 4, (T, H))
+    wr = r.integers(-3, 4, (E, H))
+    L = O.router_logits(x.astype(np.float32), wr.astype(np.float32))
+    for t in range(T):
+        for e in range(E):
+            s = 0
+            for h in range(H):
+                s += int(x[t, h]) * int(wr[e, h])
+            assert L[t, e] == s, "integer logits"
+
+
+# --------------------------------------------------------------------- top-k
+
+def pin_topk_all_ties():
+    """All logits equal: the lower-id rule gives experts 0..k-1 for every
+    token, and counts ``[T]*k + [0]*(E-k)``."""
+    T, E, k = 6, 8, 3
+    L = np.zeros((T, E), np.float32)
+    ids = O.select_topk(L, k)
+    assert np.array_equal(ids, np.tile(np.arange(k), (T, 1))), "tie rule"
+    c = O.expert_counts(ids, E)
+    assert np.array_equal(c, np.array([T] * k + [0] * (E - k))), "tie counts"
+
+
+def pin_topk_bias_set():
+    """A +100 bias on a chosen set S routes every token to S, in order of
+    decreasing bias (ties to the lower id)."""
+    r = _rng(3)
+    T, H, E, k = 10, 8, 8, 3
+    x = r.standard_normal((T, H)).astype(np.float32)
+    wr = (0.01 * r.standard_normal((E, H))).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    b[6], b[1], b[4] = 100.0, 100.0, 101.0
+    L = O.router_logits(x, wr, b)
+    ids = O.select_topk(L, k)
+    assert set(map(tuple, np.sort(ids, axis=1))) == {(1, 4, 6)}, "bias set"
+    assert np.all(ids[:, 0] == 4), "largest bias first"
+
+
+def pin_topk_negzero():
+    """-0.0 and +0.0 are equal logits: the lower id wins either way."""
+    L = np.array([[-1.0, 0.0, -0.0, -2.0], [-1.0, -0.0, 0.0, -2.0]], np.float32)
+    ids = O.select_topk(L, 2)
+    assert np.array_equal(ids, [[1, 2], [1, 2]]), "signed zero tie"
+
+
+def pin_topk_bruteforce():
+    """Distinct logits: the top-k set maximises the sum over all k-subsets;
+    order is decreasing logit."""
+    r = _rng(4)
+    T, E, k = 20, 6, 3
+    L = r.standard_normal((T, E)).astype(np.float32)
+    ids = O.select_topk(L, k)
+    for t in range(T):
+        best = max(itertools.combinations(range(E), k),
+                   key=lambda s: sum(float(L[t, e]) for e in s))
+        assert set(ids[t].tolist()) == set(best), "top-k set"
+        vals = [float(L[t, e]) for e in ids[t]]
+        assert all(vals[i] > vals[i + 1] for i in range(k - 1)), "top-k order"
+
+
+# ------------------------------------------------------------------- weights
+
+def pin_weights_sum_to_one():
+    x, wr, _, _ = _layer(32, 16, 4, 8, seed=5)
+    L, ids, w = O.route(x, wr, None, 3, True)
+    assert np.all(np.abs(w.sum(axis=1) - 1.0) < 1e-12), "renormalised sum"
+    assert np.all((w > 0) & (w <= 1)), "weights in (0, 1]"
+
+
+def pin_weights_k1_norm():
+    x, wr, _, _ = _layer(16, 8, 4, 4, seed=6)
+    _, _, w = O.route(x, wr, None, 1, True)
+    assert np.all(w == 1.0), "k=1 renormalised weight is exactly 1"
+
+
+def pin_weights_uniform():
+    """Equal logits: softmax is 1/E; renormalised top-k is 1/k (powers of 2,
+    so exact)."""
+    L = np.zeros((4, 8), np.float32)
+    ids = O.select_topk(L, 2)
+    assert np.all(O.routing_weights(L, ids, True) == 0.5)
+    assert np.all(O.routing_weights(L, ids, False) == 0.125)
+
+
+def pin_weights_two_expert_closed_form():
+    """E = 2, k = 1, no renormalisation: the selected weight is
+    ``1 / (1 + exp(-(L_max - L_min)))``."""
+    L = np.array([[0.3, -1.2], [2.0, 2.5], [-0.7, -0.7]], np.float32)
+    ids = O.select_topk(L, 1)
+    w = O.routing_weights(L, ids, False)
+    for t in range(3):
+        a, b = float(L[t].max()), float(L[t].min())
+        assert abs(w[t, 0] - 1.0 / (1.0 + math.exp(-(a - b)))) < 1e-15
+
+
+def pin_weights_full_softmax():
+    r = _rng(7)
+    L = r.standard_normal((9, 5)).astype(np.float32) * 4
+    ids = O.select_topk(L, 5)
+    w = O.routing_weights(L, ids, False)
+    sm = scipy.special.softmax(L.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(sm, ids.astype(np.int64), 1), rtol=1e-13, atol=0)
+
+
+# ----------------------------------------------------- counts / permutation
+
+def pin_counts_and_permutation():
+    r = _rng(8)
+    T, E, k = 50, 7, 3
+    ids = np.stack([r.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    c = O.expert_counts(ids, E)
+    assert c.sum() == T * k and np.all(c <= T)
+    assert np.array_equal(c, np.bincount(ids.ravel(), minlength=E))
+    o = O.expert_offsets(c)
+    assert o[0] == 0 and o[-1] == T * k and np.array_equal(np.diff(o), c)
+    ss, st, sp = O.permutation(ids, E)
+    ref = np.argsort(ids.ravel(), kind="stable")
+    assert np.array_equal(ss, ref), "stable expert-major order"
+    assert np.array_equal(st, ref // k)
+    assert np.array_equal(np.sort(sp), np.arange(T * k)), "bijection"
+    flat_t = np.repeat(np.arange(T), k)
+    assert np.array_equal(st[sp], flat_t), "sorted_token[slot_pos[t*k+j]] == t"
+    x = r.standard_normal((T, 4))
+    back = O.unpermute(O.gather_rows(x, st), sp).reshape(T, k, 4)
+    for j in range(k):
+        assert np.array_equal(back[:, j], x), "gather then inverse is identity"
+
+
+# ------------------------------------------------------------ experts/layer
+
+def pin_brute_vs_loop():
+    """Per-expert loop with index-add equals the all-expert masked path
+    (the two forward paths of ``SpeedupMoeExperts``)."""
+    x, wr, gu, dn = _layer(24, 16, 8, 6, seed=9)
+    for k, norm in ((2, True), (3, False), (6, True)):
+        a = O.moe_layer_forward(x, wr, None, gu, dn, k, norm)["out"]
+        b = O.moe_layer_forward_brute(x, wr, None, gu, dn, k, norm)
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12), "loop vs brute"
+
+
+def pin_identical_experts():
+    """Identical experts with renormalised weights: the output is the dense
+    SwiGLU of the token whatever the routing."""
+    x, wr, gu, dn = _layer(16, 12, 6, 5, seed=10)
+    gu[:] = gu[0]
+    dn[:] = dn[0]
+    out = O.moe_layer_forward(x, wr, None, gu, dn, 2, True)["out"]
+    assert np.allclose(out, _torch_swiglu(x, gu[0], dn[0]), rtol=1e-11, atol=1e-12)
+
+
+def pin_single_expert_dense():
+    x, wr, gu, dn = _layer(8, 10, 4, 1, seed=11)
+    out = O.moe_layer_forward(x, wr, None, gu, dn, 1, False)["out"]
+    assert np.allclose(out, _torch_swiglu(x, gu[0], dn[0]), rtol=1e-11, atol=1e-12)
+
+
+def pin_soft_mixture():
+    """k = E with renormalisation is the softmax-weighted sum of all experts."""
+    x, wr, gu, dn = _layer(8, 8, 4, 4, seed=12)
+    out = O.moe_layer_forward(x, wr, None, gu, dn, 4, True)["out"]
+    L = (x.astype(np.float64) @ wr.astype(np.float64).T).astype(np.float32)
+    p = scipy.special.softmax(L.astype(np.float64), axis=1)
+    ref = sum(p[:, e:e + 1] * _torch_swiglu(x, gu[e], dn[e]) for e in range(4))
+    assert np.allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_zero_token():
+    x, wr, gu, dn = _layer(6, 8, 4, 4, seed=13)
+    x[2] = 0.0
+    out = O.moe_layer_forward(x, wr, None, gu, dn, 2, True)["out"]
+    assert np.all(out[2] == 0.0), "silu(0) * 0 = 0"
+
+
+def pin_scalar_closed_form():
+    """H = I = 1, E = 2, k = 1: ``out = w * silu(x g) * (x u) * d`` with the
+    gate in column 0 of ``gate_up`` and the up projection in column 1."""
+    with open(os.path.join(GOLDEN, "scalar_layer.json")) as f:
+        case = json.load(f)
+    x = np.array(case["x"], np.float32).reshape(-1, 1)
+    wr = np.array(case["router_weight"], np.float32).reshape(2, 1)
+    gu = np.array(case["gate_up"], np.float32).reshape(2, 1, 2)
+    dn = np.array(case["down"], np.float32).reshape(2, 1, 1)
+    res = O.moe_layer_forward(x, wr, None, gu, dn, 1, case["norm_topk_prob"])
+    for t, xv in enumerate(x[:, 0].tolist()):
+        e = 0 if xv * float(wr[0, 0]) >= xv * float(wr[1, 0]) else 1
+        if xv * float(wr[0, 0]) == xv * float(wr[1, 0]):
+            e = 0
+        g, u, d = float(gu[e, 0, 0]), float(gu[e, 0, 1]), float(dn[e, 0, 0])
+        z = xv * g
+        ref = (z / (1.0 + math.exp(-z))) * (xv * u) * d
+        assert res["ids"][t, 0] == e
+        assert abs(res["out"][t, 0] - ref) <= 1e-15 * max(1.0, abs(ref)), "scalar closed form"
+    assert np.allclose(res["out"][:, 0], case["expected_out"], rtol=1e-12, atol=1e-15)
+
+
+def pin_identity_expert_roundtrip():
+    """Permute, apply an identity 'expert', combine with renormalised weights:
+    the tokens come back."""
+    r = _rng(14)
+    T, E, k, H = 30, 6, 3, 5
+    x = r.standard_normal((T, H))
+    L = r.standard_normal((T, E)).astype(np.float32)
+    ids = O.select_topk(L, k)
+    w = O.routing_weights(L, ids, True)
+    _, st, sp = O.permutation(ids, E)
+    y = O.gather_rows(x, st)
+    out = O.combine(O.unpermute(y, sp), w)
+    assert np.allclose(out, x, rtol=1e-13, atol=1e-13)
+
+
+def pin_token_subset():
+    x, wr, gu, dn = _layer(20, 8, 4, 5, seed=15)
+    full = O.moe_layer_forward(x, wr, None, gu, dn, 2, True)["out"]
+    toks = [0, 7, 19, 3]
+    sub = O.moe_layer_forward_tokens(x, wr, None, gu, dn, 2, True, toks)["out"]
+    assert np.allclose(sub, full[toks], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ EP rank
+
+def pin_reshuffle_worked_example():
+    """Hand-worked reshuffle: rank-major blocks (r0,e0)=[0], (r0,e1)=[1,2],
+    (r1,e0)=[3,4,5], (r1,e1)=[] become expert-major e0: 0,3,4,5; e1: 1,2."""
+    with open(os.path.join(GOLDEN, "reshuffle_example.json")) as f:
+        case = json.load(f)
+    src = O.reshuffle_rank_to_expert(np.array(case["counts_rank_major"]))
+    assert src.tolist() == case["expert_major_source_rows"]
+
+
+def pin_reshuffle_properties():
+    r = _rng(16)
+    C = r.integers(0, 5, (4, 3))
+    C[1, 2] = 0
+    src = O.reshuffle_rank_to_expert(C)
+    N = int(C.sum())
+    assert np.array_equal(np.sort(src), np.arange(N)), "bijection"
+    x = r.standard_normal((N, 2))
+    back = np.empty_like(x)
+    back[src] = x[src]
+    assert np.array_equal(back, x)
+
+
+def pin_ep_equals_token_choice():
+    """One rank owning every expert: the rank-major path, combined on the
+    source side with the routing weights, equals the token-choice layer."""
+    r = _rng(17)
+    R, T, H, I, E, k = 3, 10, 8, 4, 4, 2
+    xs = [r.standard_normal((T, H)).astype(np.float32) for _ in range(R)]
+    wr = (0.5 * r.standard_normal((E, H))).astype(np.float32)
+    gu = (0.3 * r.standard_normal((E, H, 2 * I))).astype(np.float32)
+    dn = (0.3 * r.standard_normal((E, I, H))).astype(np.float32)
+    rows, C, meta = O.dispatch_rank_major(xs, wr, k, True, 0, E)
+    res = O.ep_rank_forward(rows, C, gu, dn)
+    assert np.array_equal(res["counts"], C.sum(axis=0))
+    for rr in range(R):
+        ref = O.moe_layer_forward(xs[rr], wr, None, gu, dn, k, True)
+        out = np.zeros((T, H))
+        for i, (src_r, t, j) in enumerate(meta):
+            if src_r == rr:
+                out[t] += ref["weights"][t, j] * res["y_rm"][i]
+        assert np.allclose(out, ref["out"], rtol=1e-12, atol=1e-13)
+
+
+
+def pin_page_shape_examples():
+    """The shapes the moe.py page's docstring examples print."""
+    with open(os.path.join(GOLDEN, "page_shape_examples.json")) as f:
+        case = json.load(f)
+    g = case["grouped_experts"]
+    r = _rng(18)
+    x = r.standard_normal((g["tokens"], g["dim"]))
+    gu = r.standard_normal((g["num_experts"], g["dim"], 2 * g["hidden_dim"]))
+    dn = r.standard_normal((g["num_experts"], g["hidden_dim"], g["dim"]))
+    assert list(O.grouped_swiglu(x, g["counts"], gu, dn).shape) == g["out_shape"]
+    c = case["router"]
+    x = r.standard_normal((c["tokens"], c["dim"])).astype(np.float32)
+    wr = r.standard_normal((c["num_experts"], c["dim"])).astype(np.float32)
+    L, ids, w = O.route(x, wr, None, c["top_k"], False)
+    assert list(w.shape) == c["scores_shape"] and list(ids.shape) == c["indices_shape"]
+    assert list(O.expert_counts(ids, c["num_experts"]).shape) == c["counts_shape"]
+    m = case["moe"]
+    b, s, d = m["input_shape"]
+    x = r.standard_normal((b * s, d)).astype(np.float32)
+    wr = r.standard_normal((m["num_experts"], d)).astype(np.float32)
+    gu = r.standard_normal((m["num_experts"], d, 2 * m["hidden_dim"]))
+    dn = r.standard_normal((m["num_experts"], m["hidden_dim"], d))
+    out = O.moe_layer_forward(x, wr, None, gu, dn, m["top_k"], True)["out"]
+    assert list(out.reshape(b, s, d).shape) == m["out_shape"]
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

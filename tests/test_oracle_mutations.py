@@ -1,0 +1,103 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that some
+pin fails for each: the pins are sensitive enough to be trusted."""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from tests import oracle_pins as P
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _some_pin_fails():
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+def _swapped_gate_up(x_rows, gate_up_e, down_e):
+    gu = np.asarray(gate_up_e, np.float64)
+    I = gu.shape[1] // 2
+    G = np.asarray(x_rows, np.float64) @ gu
+    return (O.silu(G[:, I:]) * G[:, :I]) @ np.asarray(down_e, np.float64)
+
+
+def _sigmoid_not_silu(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))
+
+
+def _higher_id_ties(logits32, k):
+    L = np.asarray(logits32, np.float32)
+    eid = np.broadcast_to(np.arange(L.shape[1]), L.shape)
+    return np.lexsort((-eid, -L.astype(np.float64)), axis=-1)[:, :k].astype(np.int32)
+
+
+def _no_renorm(logits32, ids, norm):
+    return _orig["routing_weights"](logits32, ids, False)
+
+
+def _weights_twice(y, w):
+    return _orig["combine"](y, np.asarray(w) ** 2)
+
+
+def _unstable_perm(ids, E):
+    ss, st, sp = _orig["permutation"](ids, E)
+    k = ids.shape[1]
+    flat = np.asarray(ids).reshape(-1)
+    ss = ss.copy()
+    for e in range(E):
+        sel = np.flatnonzero(flat[ss] == e)
+        ss[sel] = ss[sel][::-1]
+    sp = np.empty_like(ss)
+    sp[ss] = np.arange(len(ss))
+    return ss, ss // k, sp
+
+
+def _bf16_logits(x, w_router, bias=None):
+    L = _orig["router_logits"](x, w_router, bias)
+    u = L.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _drop_bias(x, w_router, bias=None):
+    return _orig["router_logits"](x, w_router, None)
+
+
+def _off_by_one_offsets(counts):
+    o = _orig["expert_offsets"](counts)
+    o[1:] += 1
+    return o
+
+
+_orig = {n: getattr(O, n) for n in ("routing_weights", "combine", "permutation",
+                                     "router_logits", "expert_offsets")}
+
+MUTATIONS = {
+    "swiglu_expert": _swapped_gate_up,
+    "silu": _sigmoid_not_silu,
+    "select_topk": _higher_id_ties,
+    "routing_weights": _no_renorm,
+    "combine": _weights_twice,
+    "permutation": _unstable_perm,
+    "router_logits": _bf16_logits,
+    "expert_offsets": _off_by_one_offsets,
+}
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert not _some_pin_fails()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    monkeypatch.setattr(O, name, MUTATIONS[name])
+    assert _some_pin_fails(), f"no pin catches a mistake in {name}"
+
+
+def test_drop_bias_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "router_logits", _drop_bias)
+    assert _some_pin_fails()

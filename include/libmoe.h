@@ -1,0 +1,242 @@
+/*
+ * libmoe — Mixture-of-Experts layer forward on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the token-choice MoE block of the Qwen3 family as the pages
+ * state it:
+ *   - Qwen3-Omni issue #115 ("Training: Extremely Slow Deepspeed Engine
+ *     initialization ..."), SpeedupMoeSparseMoeBlock.forward: gate -> float32
+ *     softmax -> top-k -> optional renormalisation (norm_topk_prob); and
+ *     SpeedupMoeExperts: concatenated experts gate_up_proj [E, H, 2I] (gate in
+ *     columns [0, I), up in [I, 2I)) and down_proj [E, I, H], SwiGLU
+ *     up * silu(gate), outputs weighted by the routing weights and added into
+ *     the token rows;
+ *   - MindSpore hyper-parallel moe.py page: TokenChoiceTopKRouter.forward
+ *     (returns routing weights, expert ids, tokens per expert),
+ *     MoE.permutation (stable token-major -> expert-major order),
+ *     GroupedExperts / _run_experts_for_loop (per-expert SwiGLU over rows in
+ *     expert-major order split by counts), MoE.unpermutation (add back);
+ *   - transformers PR "Qwen3 moe", Ep2DpParallel._token_dispatch: the rows one
+ *     expert-parallel rank receives come grouped by source rank and must be
+ *     reshuffled to expert-major order before the grouped experts.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to row-major, contiguous
+ *     buffers, 16-byte aligned, allocated and owned by the caller.  The
+ *     library allocates nothing, frees nothing and never synchronises the
+ *     host; all work is enqueued on `stream` in order.
+ *   - Every argument is validated before anything is enqueued.  On error the
+ *     call returns a negative status (below) and enqueues nothing.  A status of
+ *     MOE_ERR_HIP means a launch failed after validation.
+ *   - T = 0 (or N = 0) is a valid no-op apart from zero-filling outputs that
+ *     are defined for every expert (counts, offsets).
+ *   - Device-side contents (expert ids, counts, offsets) cannot be validated
+ *     on the host; kernels clamp every index they derive from them, so
+ *     inconsistent contents give unspecified values but never out-of-bounds
+ *     accesses.
+ *   - dtype MOE_BF16: hidden states, weights, expert outputs and the layer
+ *     output are bfloat16; router logits and routing weights are float32;
+ *     all accumulation is float32.  dtype MOE_F32: everything float32.
+ *   - Shape limits: 1 <= top_k <= E <= 256; H a multiple of 128 and I a
+ *     multiple of 64 (the router alone needs only H a multiple of 64);
+ *     routed rows N <= 2^30; rank-major mode R * E <= 4096.
+ *   - Calls are stateless and may be made from several host threads on
+ *     different streams.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  MOE_ERR_DTYPE = -3,       /* unknown dtype */
+  MOE_ERR_WORKSPACE = -4,   /* workspace missing or smaller than moe_workspace_size() */
+  MOE_ERR_UNSUPPORTED = -5, /* valid request this build does not handle */
+  MOE_ERR_HIP = -6,         /* a HIP launch failed */
+  MOE_ERR_ALIGN = -7        /* a pointer is not 16-byte aligned */
+};
+
+/* Workspace queries: `op` names the entry point. */
+enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_GATE_UP = 2,
+  MOE_OP_DOWN = 3,
+  MOE_OP_GROUPED_SWIGLU = 4,
+  MOE_OP_LAYER = 5
+};
+
+/* Bytes of device workspace entry point `op` needs for these sizes.
+ * N is the number of routed rows (T * top_k for token choice; for the
+ * rank-major permutation and the grouped calls, the caller's row count).
+ * R is the number of source ranks (rank-major permutation only, else 0).
+ * Returns 0 if the op needs none, (size_t)-1 for invalid sizes. */
+size_t moe_workspace_size(int op, int T, int H, int I, int E, int top_k, int R,
+                          int N, moe_dtype dt);
+
+/* Human-readable text for a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* Library ABI version (increments on any signature change). */
+int moe_version(void);
+
+/*
+ * moe_route — router GEMM, float32 softmax, top-k, renormalisation.
+ * Qwen3-Omni issue #115, SpeedupMoeSparseMoeBlock.forward; MindSpore moe.py,
+ * TokenChoiceTopKRouter.forward (softmax scoring).
+ *
+ *   router_logits[t, e] = sum_h hidden_states[t, h] * router_weight[e, h]
+ *                         + router_bias[e]                      (float32)
+ *   topk_ids[t, 0..k-1]  = the k experts with the largest logits, in order of
+ *                          decreasing logit; equal logits (-0 == +0) go to the
+ *                          lower expert id.
+ *   topk_weights[t, j]   = softmax(router_logits[t, :])[topk_ids[t, j]],
+ *                          divided by the sum over j when norm_topk_prob != 0.
+ *   num_tokens_per_expert[e] = number of (t, j) with topk_ids[t, j] == e.
+ *
+ * hidden_states [T, H] dt; router_weight [E, H] dt (nn.Linear(H, E) layout);
+ * router_bias [E] float32 or NULL (no bias); router_logits [T, E] float32 or
+ * NULL (not written); topk_ids [T, k] int32; topk_weights [T, k] float32;
+ * num_tokens_per_expert [E] int32 or NULL.  No workspace.
+ */
+int moe_route(const void* hidden_states, const void* router_weight,
+              const float* router_bias, int T, int H, int E, int top_k,
+              int norm_topk_prob, moe_dtype dt, float* router_logits,
+              int32_t* topk_ids, float* topk_weights,
+              int32_t* num_tokens_per_expert, hipStream_t stream);
+
+/*
+ * moe_permute — expert histogram, offsets and the expert-major permutation.
+ * MindSpore moe.py, MoE.permutation (stable argsort of the flattened expert
+ * ids, token = flat index // top_k, bincount); transformers PR "Qwen3 moe",
+ * Ep2DpParallel._token_dispatch (rank-major received rows).
+ *
+ * Token-choice mode (topk_ids != NULL, rank_major_counts == NULL):
+ *   N = T * top_k flat slots i = t * top_k + j with expert topk_ids[t, j].
+ *   Expert-major order lists, for e = 0..E-1, the slots with expert e in
+ *   ascending i.  For expert-major position p:
+ *     sorted_slot_ids[p]  = i,   sorted_token_ids[p] = i / top_k,
+ *     slot_pos[i] = p.
+ * Rank-major mode (topk_ids == NULL, rank_major_counts != NULL):
+ *   N received rows laid out as blocks (source rank r = 0..R-1, local expert
+ *   e = 0..E-1) of rank_major_counts[r, e] rows (int32 [R, E], device).
+ *   Expert-major order lists blocks (e, r) with each block's order kept.
+ *     sorted_slot_ids[p] = sorted_token_ids[p] = received row i,
+ *     slot_pos[i] = p.   Sum of rank_major_counts must equal N.
+ * Both modes: num_tokens_per_expert [E] int32, expert_offsets [E + 1] int32
+ * (exclusive prefix sum, expert_offsets[E] = N); sorted_token_ids,
+ * sorted_slot_ids, slot_pos [N] int32.  sorted_slot_ids may be NULL.
+ * Workspace: moe_workspace_size(MOE_OP_PERMUTE, ...).  Deterministic.
+ */
+int moe_permute(const int32_t* topk_ids, int T, int top_k,
+                const int32_t* rank_major_counts, int R, int N, int E,
+                int32_t* num_tokens_per_expert, int32_t* expert_offsets,
+                int32_t* sorted_token_ids, int32_t* sorted_slot_ids,
+                int32_t* slot_pos, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
+ * moe_gather_rows — x_perm[p, :] = x[row_index[p], :] (MindSpore moe.py,
+ * MoE.forward: routed_x = x_flat[token_indices]).  Optional: the grouped
+ * GEMMs gather rows on load and never need x_perm.
+ * x [x_rows, H] dt; row_index [N] int32 (clamped to [0, x_rows)); x_perm
+ * [N, H] dt.
+ */
+int moe_gather_rows(const void* x, int x_rows, const int32_t* row_index, int N,
+                    int H, moe_dtype dt, void* x_perm, hipStream_t stream);
+
+/*
+ * moe_grouped_gate_up_swiglu — first grouped GEMM with the SwiGLU fused.
+ * Qwen3-Omni issue #115, SpeedupMoeExperts.forward (gate_up = state @
+ * gate_up_proj[e]; gate, up = chunk(2); up * silu(gate)); MindSpore moe.py,
+ * _run_experts_for_loop.
+ *   For each expert e and expert-major row p in [expert_offsets[e],
+ *   expert_offsets[e+1]):  g = x[row(p)] @ gate_up[e]  (float32 accumulate),
+ *   h[p, n] = silu(g[n]) * g[I + n]  for n < I, rounded to dt.
+ *   row(p) = row_index[p], or p when row_index is NULL.
+ * x [x_rows, H] dt (row indices are clamped to [0, x_rows)); expert_offsets
+ * [E + 1] int32 (device); gate_up [E, H, 2I] dt;
+ * h [N, I] dt.  Empty experts are skipped.  Workspace:
+ * moe_workspace_size(MOE_OP_GATE_UP, ...).
+ */
+int moe_grouped_gate_up_swiglu(const void* x, int x_rows, const int32_t* row_index,
+                               const int32_t* expert_offsets, int N, int H,
+                               int I, int E, const void* gate_up, moe_dtype dt,
+                               void* h, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * moe_grouped_down — second grouped GEMM (Qwen3-Omni issue #115,
+ * SpeedupMoeExperts.forward: expert_out = gated_output @ down_proj[e]).
+ *   y[dst(p), :] = h[p, :] @ down[e]   for p in expert e's rows,
+ *   dst(p) = out_index[p], or p when out_index is NULL (expert-major y).
+ * h [N, I] dt; down [E, I, H] dt; y [N, H] dt.  out_index must be a
+ * permutation of [0, N).  Workspace: moe_workspace_size(MOE_OP_DOWN, ...).
+ */
+int moe_grouped_down(const void* h, const int32_t* expert_offsets,
+                     const int32_t* out_index, int N, int H, int I, int E,
+                     const void* down, moe_dtype dt, void* y, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_swiglu — both grouped GEMMs: y[dst(p)] = SwiGLU_e(x[row(p)]).
+ * Intermediate h lives in the workspace
+ * (moe_workspace_size(MOE_OP_GROUPED_SWIGLU, ...)).  With row_index =
+ * out_index = the rank-major permutation's sorted_token_ids this is one
+ * expert-parallel rank's reshuffle -> experts -> reverse reshuffle, with the
+ * row moves fused into the GEMM loads and stores.
+ */
+int moe_grouped_swiglu(const void* x, int x_rows, const int32_t* row_index,
+                       const int32_t* out_index, const int32_t* expert_offsets,
+                       int N, int H, int I, int E, const void* gate_up,
+                       const void* down, moe_dtype dt, void* y, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_combine — weighted un-permute (Qwen3-Omni issue #115: expert_out *
+ * routing_weights, index_add_ into the token rows; MindSpore moe.py,
+ * MoE.unpermutation).
+ *   out[t, :] = sum_{j = 0..k-1} w[t, j] * y[src(t, j), :]
+ * accumulated in float32 in ascending j, rounded once to dt; no atomics, so
+ * bitwise deterministic.  src(t, j) = slot_pos[t * k + j], or t * k + j when
+ * slot_pos is NULL (y already in flat-slot order).  w = topk_weights [T, k]
+ * float32, or 1 when NULL (plain un-permute).  y [N, H] dt; out [T, H] dt.
+ */
+int moe_combine(const void* y, const int32_t* slot_pos,
+                const float* topk_weights, int T, int top_k, int H,
+                moe_dtype dt, void* out, hipStream_t stream);
+
+/*
+ * moe_layer_forward — the whole layer: moe_route, moe_permute (token
+ * choice), the two grouped GEMMs (rows gathered on load, outputs stored in
+ * flat-slot order) and moe_combine.  Qwen3-Omni issue #115,
+ * SpeedupMoeSparseMoeBlock.forward returns (out, router_logits).
+ * out [T, H] dt; router_logits [T, E] float32 or NULL; topk_ids [T, k] int32,
+ * topk_weights [T, k] float32 and num_tokens_per_expert [E] int32 are written
+ * (the latter two may be NULL).  Workspace:
+ * moe_workspace_size(MOE_OP_LAYER, ...).
+ */
+int moe_layer_forward(const void* hidden_states, const void* router_weight,
+                      const float* router_bias, const void* gate_up,
+                      const void* down, int T, int H, int I, int E, int top_k,
+                      int norm_topk_prob, moe_dtype dt, void* out,
+                      float* router_logits, int32_t* topk_ids,
+                      float* topk_weights, int32_t* num_tokens_per_expert,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

@@ -1,0 +1,263 @@
+"""libmoe: MI355X-native MoE layer forward (router -> permutation -> grouped
+SwiGLU experts -> combine) as hand-written HIP kernels behind a C ABI.
+
+This module is the thin Python binding: it checks tensors, allocates outputs
+and workspace with torch, and passes device pointers and torch's current
+stream to libmoe.so.  Every step of the computation runs in the library's
+kernels; importing fails if the library is missing.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+lib = _lib.load()
+
+__all__ = ["lib", "route", "permute", "permute_rank_major", "gather_rows",
+           "grouped_gate_up_swiglu", "grouped_down", "grouped_swiglu", "combine",
+           "layer_forward", "workspace_size", "MoEError"]
+
+MoEError = _lib.MoEError
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.MOE_BF16
+    if t.dtype == torch.float32:
+        return _lib.MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; bf16 or float32")
+
+
+def _chk(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _call(name: str, *args):
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise MoEError(name, st)
+
+
+def workspace_size(op: int, T=0, H=0, I=0, E=0, top_k=0, R=0, N=0, dtype=torch.bfloat16) -> int:
+    dt = _lib.MOE_BF16 if dtype == torch.bfloat16 else _lib.MOE_F32
+    n = lib.moe_workspace_size(op, T, H, I, E, top_k, R, N, dt)
+    if n == ctypes_size_max():
+        raise ValueError("invalid sizes for workspace query")
+    return n
+
+
+def ctypes_size_max() -> int:
+    import ctypes
+    return ctypes.c_size_t(-1).value
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Tuple[int, int, torch.Tensor]:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return ws.data_ptr(), ws.numel() * ws.element_size(), ws
+    t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return t.data_ptr(), nbytes, t
+
+
+def route(x: torch.Tensor, router_weight: torch.Tensor, top_k: int,
+          norm_topk_prob: bool = True, router_bias: Optional[torch.Tensor] = None,
+          with_logits: bool = True, with_counts: bool = True):
+    """Router logits, top-k ids and routing weights (and tokens per expert)."""
+    T, H = x.shape
+    E = router_weight.shape[0]
+    dev = x.device
+    _chk(x, "x")
+    _chk(router_weight, "router_weight", x.dtype, (E, H))
+    _chk(router_bias, "router_bias", torch.float32, (E,))
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev) if with_logits else None
+    ids = torch.empty(T, top_k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, top_k, dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if with_counts else None
+    _call("moe_route", x.data_ptr(), router_weight.data_ptr(), _chk(router_bias, "router_bias"),
+          T, H, E, top_k, int(norm_topk_prob), _dt(x), _chk(logits, "logits"), ids.data_ptr(),
+          w.data_ptr(), _chk(counts, "counts"), _stream(dev))
+    return logits, ids, w, counts
+
+
+def permute(topk_ids: torch.Tensor, num_experts: int, workspace=None) -> dict:
+    """Histogram, offsets and the stable expert-major permutation of the
+    (token, slot) pairs."""
+    T, k = topk_ids.shape
+    _chk(topk_ids, "topk_ids", torch.int32)
+    dev = topk_ids.device
+    N = T * k
+    E = num_experts
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               sorted_token=torch.empty(N, dtype=torch.int32, device=dev),
+               sorted_slot=torch.empty(N, dtype=torch.int32, device=dev),
+               slot_pos=torch.empty(N, dtype=torch.int32, device=dev))
+    nb = lib.moe_workspace_size(_lib.MOE_OP_PERMUTE, T, 0, 0, E, k, 0, N, _lib.MOE_BF16)
+    wp, wb, _keep = _workspace(nb, dev, workspace)
+    _call("moe_permute", topk_ids.data_ptr(), T, k, None, 0, N, E, out["counts"].data_ptr(),
+          out["offsets"].data_ptr(), out["sorted_token"].data_ptr(),
+          out["sorted_slot"].data_ptr(), out["slot_pos"].data_ptr(), wp, wb, _stream(dev))
+    return out
+
+
+def permute_rank_major(counts_rank_major: torch.Tensor, N: int, workspace=None) -> dict:
+    """Expert-major order of rows received rank-major (blocks (rank, expert))."""
+    R, E = counts_rank_major.shape
+    _chk(counts_rank_major, "counts_rank_major", torch.int32)
+    dev = counts_rank_major.device
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               sorted_token=torch.empty(N, dtype=torch.int32, device=dev),
+               sorted_slot=torch.empty(N, dtype=torch.int32, device=dev),
+               slot_pos=torch.empty(N, dtype=torch.int32, device=dev))
+    nb = lib.moe_workspace_size(_lib.MOE_OP_PERMUTE, 0, 0, 0, E, 1, R, N, _lib.MOE_BF16)
+    wp, wb, _keep = _workspace(nb, dev, workspace)
+    _call("moe_permute", None, 0, 1, counts_rank_major.data_ptr(), R, N, E,
+          out["counts"].data_ptr(), out["offsets"].data_ptr(), out["sorted_token"].data_ptr(),
+          out["sorted_slot"].data_ptr(), out["slot_pos"].data_ptr(), wp, wb, _stream(dev))
+    return out
+
+
+def gather_rows(x: torch.Tensor, row_index: torch.Tensor) -> torch.Tensor:
+    N = row_index.shape[0]
+    _chk(x, "x")
+    _chk(row_index, "row_index", torch.int32)
+    out = torch.empty(N, x.shape[1], dtype=x.dtype, device=x.device)
+    _call("moe_gather_rows", x.data_ptr(), x.shape[0], row_index.data_ptr(), N, x.shape[1],
+          _dt(x), out.data_ptr(), _stream(x.device))
+    return out
+
+
+def grouped_gate_up_swiglu(x: torch.Tensor, offsets: torch.Tensor, gate_up: torch.Tensor,
+                           N: int, row_index: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, workspace=None) -> torch.Tensor:
+    """h[p] = SwiGLU gate/up of x[row_index[p]] for expert-major rows p."""
+    E, H, I2 = gate_up.shape
+    I = I2 // 2
+    _chk(x, "x")
+    _chk(gate_up, "gate_up", x.dtype)
+    _chk(offsets, "offsets", torch.int32, (E + 1,))
+    _chk(row_index, "row_index", torch.int32)
+    dev = x.device
+    h = out if out is not None else torch.empty(N, I, dtype=x.dtype, device=dev)
+    _chk(h, "h", x.dtype, (N, I))
+    nb = lib.moe_workspace_size(_lib.MOE_OP_GATE_UP, 0, H, I, E, 1, 0, N, _dt(x))
+    wp, wb, _keep = _workspace(nb, dev, workspace)
+    _call("moe_grouped_gate_up_swiglu", x.data_ptr(), x.shape[0], _chk(row_index, "row_index"),
+          offsets.data_ptr(), N, H, I, E, gate_up.data_ptr(), _dt(x), h.data_ptr(), wp, wb,
+          _stream(dev))
+    return h
+
+
+def grouped_down(h: torch.Tensor, offsets: torch.Tensor, down: torch.Tensor,
+                 out_index: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 workspace=None) -> torch.Tensor:
+    """y[out_index[p]] = h[p] @ down[expert of p]."""
+    E, I, H = down.shape
+    N = h.shape[0]
+    _chk(h, "h")
+    _chk(down, "down", h.dtype)
+    _chk(offsets, "offsets", torch.int32, (E + 1,))
+    _chk(out_index, "out_index", torch.int32)
+    dev = h.device
+    y = out if out is not None else torch.empty(N, H, dtype=h.dtype, device=dev)
+    _chk(y, "y", h.dtype, (N, H))
+    nb = lib.moe_workspace_size(_lib.MOE_OP_DOWN, 0, H, I, E, 1, 0, N, _dt(h))
+    wp, wb, _keep = _workspace(nb, dev, workspace)
+    _call("moe_grouped_down", h.data_ptr(), offsets.data_ptr(), _chk(out_index, "out_index"), N,
+          H, I, E, down.data_ptr(), _dt(h), y.data_ptr(), wp, wb, _stream(dev))
+    return y
+
+
+def grouped_swiglu(x: torch.Tensor, offsets: torch.Tensor, gate_up: torch.Tensor,
+                   down: torch.Tensor, N: int, row_index: Optional[torch.Tensor] = None,
+                   out_index: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   workspace=None) -> torch.Tensor:
+    """Both grouped GEMMs: y[out_index[p]] = SwiGLU_e(x[row_index[p]])."""
+    E, H, I2 = gate_up.shape
+    I = I2 // 2
+    _chk(x, "x")
+    _chk(gate_up, "gate_up", x.dtype)
+    _chk(down, "down", x.dtype, (E, I, H))
+    _chk(offsets, "offsets", torch.int32, (E + 1,))
+    dev = x.device
+    y = out if out is not None else torch.empty(N, H, dtype=x.dtype, device=dev)
+    _chk(y, "y", x.dtype, (N, H))
+    nb = lib.moe_workspace_size(_lib.MOE_OP_GROUPED_SWIGLU, 0, H, I, E, 1, 0, N, _dt(x))
+    wp, wb, _keep = _workspace(nb, dev, workspace)
+    _call("moe_grouped_swiglu", x.data_ptr(), x.shape[0], _chk(row_index, "row_index"),
+          _chk(out_index, "out_index"), offsets.data_ptr(), N, H, I, E, gate_up.data_ptr(),
+          down.data_ptr(), _dt(x), y.data_ptr(), wp, wb, _stream(dev))
+    return y
+
+
+def combine(y: torch.Tensor, T: int, top_k: int, topk_weights: Optional[torch.Tensor] = None,
+            slot_pos: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = sum_j w[t, j] * y[src(t, j)] in float32, j ascending."""
+    H = y.shape[1]
+    _chk(y, "y")
+    _chk(topk_weights, "topk_weights", torch.float32, (T, top_k))
+    _chk(slot_pos, "slot_pos", torch.int32)
+    o = out if out is not None else torch.empty(T, H, dtype=y.dtype, device=y.device)
+    _chk(o, "out", y.dtype, (T, H))
+    _call("moe_combine", y.data_ptr(), _chk(slot_pos, "slot_pos"),
+          _chk(topk_weights, "topk_weights"), T, top_k, H, _dt(y), o.data_ptr(),
+          _stream(y.device))
+    return o
+
+
+class LayerBuffers:
+    """Preallocated outputs and workspace for repeated layer_forward calls."""
+
+    def __init__(self, T, H, I, E, top_k, dtype, device):
+        self.out = torch.empty(T, H, dtype=dtype, device=device)
+        self.logits = torch.empty(T, E, dtype=torch.float32, device=device)
+        self.ids = torch.empty(T, top_k, dtype=torch.int32, device=device)
+        self.weights = torch.empty(T, top_k, dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, dtype=torch.int32, device=device)
+        dt = _lib.MOE_BF16 if dtype == torch.bfloat16 else _lib.MOE_F32
+        nb = lib.moe_workspace_size(_lib.MOE_OP_LAYER, T, H, I, E, top_k, 0, T * top_k, dt)
+        self.workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
+        self.ws_bytes = nb
+
+
+def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
+                  down: torch.Tensor, top_k: int, norm_topk_prob: bool = True,
+                  router_bias: Optional[torch.Tensor] = None,
+                  buffers: Optional[LayerBuffers] = None):
+    """The whole MoE layer forward; returns (out, router_logits, topk_ids,
+    topk_weights, num_tokens_per_expert)."""
+    T, H = x.shape
+    E = router_weight.shape[0]
+    I = gate_up.shape[2] // 2
+    _chk(x, "x")
+    _chk(router_weight, "router_weight", x.dtype, (E, H))
+    _chk(gate_up, "gate_up", x.dtype, (E, H, 2 * I))
+    _chk(down, "down", x.dtype, (E, I, H))
+    _chk(router_bias, "router_bias", torch.float32, (E,))
+    b = buffers if buffers is not None else LayerBuffers(T, H, I, E, top_k, x.dtype, x.device)
+    _call("moe_layer_forward", x.data_ptr(), router_weight.data_ptr(),
+          _chk(router_bias, "router_bias"), gate_up.data_ptr(), down.data_ptr(), T, H, I, E,
+          top_k, int(norm_topk_prob), _dt(x), b.out.data_ptr(), b.logits.data_ptr(),
+          b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(), b.workspace.data_ptr(),
+          b.ws_bytes, _stream(x.device))
+    return b.out, b.logits, b.ids, b.weights, b.counts

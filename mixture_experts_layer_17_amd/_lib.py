@@ -1,0 +1,65 @@
+"""ctypes view of libmoe.so: the C ABI declared in include/libmoe.h.
+
+Raises ImportError when the shared library is missing; there is no other
+implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("LIBMOE_PATH", os.path.join(_HERE, "libmoe.so"))
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+MOE_OP_ROUTE = 0
+MOE_OP_PERMUTE = 1
+MOE_OP_GATE_UP = 2
+MOE_OP_DOWN = 3
+MOE_OP_GROUPED_SWIGLU = 4
+MOE_OP_LAYER = 5
+
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
+          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_UNSUPPORTED", -6: "MOE_ERR_HIP",
+          -7: "MOE_ERR_ALIGN"}
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); must match include/libmoe.h
+SIGNATURES = {
+    "moe_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "moe_status_string": (ctypes.c_char_p, [_i]),
+    "moe_version": (_i, []),
+    "moe_route": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
+    "moe_permute": (_i, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_gather_rows": (_i, [_p, _i, _p, _i, _i, _i, _p, _p]),
+    "moe_grouped_gate_up_swiglu": (_i, [_p, _i, _p, _p, _i, _i, _i, _i, _p, _i, _p, _p, _sz, _p]),
+    "moe_grouped_down": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p, _p, _sz, _p]),
+    "moe_grouped_swiglu": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]),
+    "moe_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p]),
+    "moe_layer_forward": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
+                               _p, _p, _sz, _p]),
+}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"libmoe.so not found at {path}; build it with "
+            "`python -m mixture_experts_layer_17_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib

@@ -1,0 +1,288 @@
+// libmoe C ABI: argument validation, workspace carve-up and launch sequencing.
+// Every entry point validates everything before it enqueues anything.
+#include <stdint.h>
+
+#include "../../include/libmoe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxE = 256;
+constexpr int kMaxRankMajorBlocks = 4096;
+constexpr int kVersion = 1;
+
+size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool dtype_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+int check_dims(int H, int I, int E, int k) {
+  if (E < 1 || E > kMaxE) return MOE_ERR_SHAPE;
+  if (k < 1 || k > E) return MOE_ERR_SHAPE;
+  if (H <= 0 || H % 128 != 0) return MOE_ERR_SHAPE;
+  if (I < 0 || I % 64 != 0) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// Row counts are int32 on the device; keep N * max(H, 2I) element offsets
+// inside 64-bit math and every row index inside int32.
+bool rows_ok(long long rows) { return rows >= 0 && rows <= (1ll << 30); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+struct LayerWs {
+  int32_t *ids, *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
+  float* weights;
+  void *perm, *h, *y, *tiles_up, *tiles_down;
+  size_t total;
+};
+
+LayerWs layer_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
+  LayerWs w{};
+  const size_t N = (size_t)T * k;
+  const bool bf16 = dt == MOE_BF16;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? base + off : nullptr;
+    off += al(bytes);
+    return p;
+  };
+  w.ids = (int32_t*)take(N * 4);
+  w.weights = (float*)take(N * 4);
+  w.counts = (int32_t*)take((size_t)E * 4);
+  w.offsets = (int32_t*)take((size_t)(E + 1) * 4);
+  w.sorted_token = (int32_t*)take(N * 4);
+  w.sorted_slot = (int32_t*)take(N * 4);
+  w.slot_pos = (int32_t*)take(N * 4);
+  w.perm = take(permute_ws_bytes((int)N, E, 0));
+  w.h = take(N * (size_t)I * esize(dt));
+  w.y = take(N * (size_t)H * esize(dt));
+  const GemmTileCfg cu = pick_gate_up_cfg(bf16, (int)N, H, I, E);
+  const GemmTileCfg cd = pick_down_cfg(bf16, (int)N, H, I, E);
+  w.tiles_up = take(tile_list_bytes((int)N, E, cu.BM));
+  w.tiles_down = take(tile_list_bytes((int)N, E, cd.BM));
+  w.total = off;
+  return w;
+}
+
+size_t swiglu_ws(int N, int H, int I, int E, moe_dtype dt, size_t* h_bytes,
+                 size_t* up_bytes) {
+  const bool bf16 = dt == MOE_BF16;
+  const GemmTileCfg cu = pick_gate_up_cfg(bf16, N, H, I, E);
+  const GemmTileCfg cd = pick_down_cfg(bf16, N, H, I, E);
+  *h_bytes = al((size_t)N * I * esize(dt));
+  *up_bytes = tile_list_bytes(N, E, cu.BM);
+  return *h_bytes + *up_bytes + tile_list_bytes(N, E, cd.BM);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return kVersion; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_DTYPE: return "unknown dtype";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_UNSUPPORTED: return "unsupported request";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_size(int op, int T, int H, int I, int E, int top_k, int R, int N,
+                          moe_dtype dt) {
+  const size_t bad = (size_t)-1;
+  if (!dtype_ok(dt)) return bad;
+  switch (op) {
+    case MOE_OP_ROUTE: return 0;
+    case MOE_OP_PERMUTE:
+      if (E < 1 || E > kMaxE) return bad;
+      if (R > 0) {
+        if ((long long)R * E > kMaxRankMajorBlocks || !rows_ok(N)) return bad;
+        return permute_ws_bytes(N, E, R);
+      }
+      if (T < 0 || top_k < 1 || top_k > E || !rows_ok((long long)T * top_k)) return bad;
+      return permute_ws_bytes(T * top_k, E, 0);
+    case MOE_OP_GATE_UP:
+    case MOE_OP_DOWN:
+    case MOE_OP_GROUPED_SWIGLU: {
+      if (check_dims(H, I, E, 1) != MOE_OK || !rows_ok(N)) return bad;
+      const bool bf16 = dt == MOE_BF16;
+      if (op == MOE_OP_GATE_UP) return tile_list_bytes(N, E, pick_gate_up_cfg(bf16, N, H, I, E).BM);
+      if (op == MOE_OP_DOWN) return tile_list_bytes(N, E, pick_down_cfg(bf16, N, H, I, E).BM);
+      size_t hb, ub;
+      return swiglu_ws(N, H, I, E, dt, &hb, &ub);
+    }
+    case MOE_OP_LAYER:
+      if (check_dims(H, I, E, top_k) != MOE_OK || T < 0 || !rows_ok((long long)T * top_k))
+        return bad;
+      return layer_ws(nullptr, T, H, I, E, top_k, dt).total;
+    default: return bad;
+  }
+}
+
+int moe_route(const void* x, const void* wr, const float* bias, int T, int H, int E, int k,
+              int norm, moe_dtype dt, float* logits, int32_t* ids, float* w, int32_t* counts,
+              hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (T < 0 || !rows_ok(T) || E < 1 || E > kMaxE || k < 1 || k > E || H <= 0 || H % 64 != 0)
+    return MOE_ERR_SHAPE;
+  if (T > 0 && (!x || !wr || !ids || !w)) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wr)) return MOE_ERR_ALIGN;
+  return hip_status(launch_route(dt == MOE_BF16, x, wr, bias, T, H, E, k, norm, logits, ids, w,
+                                 counts, s));
+}
+
+int moe_permute(const int32_t* ids, int T, int k, const int32_t* C, int R, int N, int E,
+                int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot,
+                int32_t* slot_pos, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (E < 1 || E > kMaxE) return MOE_ERR_SHAPE;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if ((ids == nullptr) == (C == nullptr)) return MOE_ERR_NULL;
+  if (ids) {
+    if (T < 0 || k < 1 || k > E || !rows_ok((long long)T * k)) return MOE_ERR_SHAPE;
+    const int n = T * k;
+    if (n > 0 && (!sorted_token || !slot_pos)) return MOE_ERR_NULL;
+    const size_t need = permute_ws_bytes(n, E, 0);
+    if (n > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_permute_topk(ids, T, k, E, counts, offsets, sorted_token,
+                                          sorted_slot, slot_pos, ws, s));
+  }
+  if (R < 1 || (long long)R * E > kMaxRankMajorBlocks || !rows_ok(N)) return MOE_ERR_SHAPE;
+  if (N > 0 && (!sorted_token || !slot_pos)) return MOE_ERR_NULL;
+  if (!ws || ws_bytes < permute_ws_bytes(N, E, R)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_permute_rank_major(C, R, N, E, counts, offsets, sorted_token,
+                                              sorted_slot, slot_pos, ws, s));
+}
+
+int moe_gather_rows(const void* x, int x_rows, const int32_t* idx, int N, int H, moe_dtype dt,
+                    void* out, hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (N < 0 || !rows_ok(N) || x_rows < 0 || H <= 0 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if (N > 0 && (!x || !idx || !out)) return MOE_ERR_NULL;
+  if (N > 0 && x_rows < 1) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+  return hip_status(launch_gather_rows(dt == MOE_BF16, x, x_rows, idx, N, H, out, s));
+}
+
+int moe_grouped_gate_up_swiglu(const void* x, int x_rows, const int32_t* row_index,
+                               const int32_t* offsets, int N, int H, int I, int E,
+                               const void* gate_up, moe_dtype dt, void* h, void* ws,
+                               size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (check_dims(H, I, E, 1) != MOE_OK || I == 0 || !rows_ok(N) || x_rows < 0)
+    return MOE_ERR_SHAPE;
+  if (N == 0) return MOE_OK;
+  if (x_rows < 1) return MOE_ERR_SHAPE;
+  if (!x || !offsets || !gate_up || !h) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(gate_up) || !aligned16(h)) return MOE_ERR_ALIGN;
+  const bool bf16 = dt == MOE_BF16;
+  const GemmTileCfg c = pick_gate_up_cfg(bf16, N, H, I, E);
+  if (!ws || ws_bytes < tile_list_bytes(N, E, c.BM)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_gate_up(bf16, c, x, x_rows, row_index, offsets, N, H, I, E, gate_up,
+                                   h, ws, s));
+}
+
+int moe_grouped_down(const void* h, const int32_t* offsets, const int32_t* out_index, int N,
+                     int H, int I, int E, const void* down, moe_dtype dt, void* y, void* ws,
+                     size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (check_dims(H, I, E, 1) != MOE_OK || I == 0 || !rows_ok(N)) return MOE_ERR_SHAPE;
+  if (N == 0) return MOE_OK;
+  if (!h || !offsets || !down || !y) return MOE_ERR_NULL;
+  if (!aligned16(h) || !aligned16(down) || !aligned16(y)) return MOE_ERR_ALIGN;
+  const bool bf16 = dt == MOE_BF16;
+  const GemmTileCfg c = pick_down_cfg(bf16, N, H, I, E);
+  if (!ws || ws_bytes < tile_list_bytes(N, E, c.BM)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_down(bf16, c, h, offsets, out_index, N, H, I, E, down, y, ws, s));
+}
+
+int moe_grouped_swiglu(const void* x, int x_rows, const int32_t* row_index,
+                       const int32_t* out_index, const int32_t* offsets, int N, int H, int I,
+                       int E, const void* gate_up, const void* down, moe_dtype dt, void* y,
+                       void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (check_dims(H, I, E, 1) != MOE_OK || I == 0 || !rows_ok(N) || x_rows < 0)
+    return MOE_ERR_SHAPE;
+  if (N == 0) return MOE_OK;
+  if (x_rows < 1) return MOE_ERR_SHAPE;
+  if (!x || !offsets || !gate_up || !down || !y) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(gate_up) || !aligned16(down) || !aligned16(y))
+    return MOE_ERR_ALIGN;
+  size_t hb, ub;
+  const size_t need = swiglu_ws(N, H, I, E, dt, &hb, &ub);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const bool bf16 = dt == MOE_BF16;
+  char* base = (char*)ws;
+  void* h = base;
+  const GemmTileCfg cu = pick_gate_up_cfg(bf16, N, H, I, E);
+  const GemmTileCfg cd = pick_down_cfg(bf16, N, H, I, E);
+  hipError_t e = launch_gate_up(bf16, cu, x, x_rows, row_index, offsets, N, H, I, E, gate_up, h,
+                                base + hb, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_down(bf16, cd, h, offsets, out_index, N, H, I, E, down, y,
+                                base + hb + ub, s));
+}
+
+int moe_combine(const void* y, const int32_t* slot_pos, const float* w, int T, int k, int H,
+                moe_dtype dt, void* out, hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (T < 0 || k < 1 || !rows_ok((long long)T * k) || H <= 0 || H % 8 != 0)
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!y || !out) return MOE_ERR_NULL;
+  if (!aligned16(y) || !aligned16(out)) return MOE_ERR_ALIGN;
+  return hip_status(launch_combine(dt == MOE_BF16, y, slot_pos, w, T, k, H, out, s));
+}
+
+int moe_layer_forward(const void* x, const void* wr, const float* bias, const void* gate_up,
+                      const void* down, int T, int H, int I, int E, int k, int norm,
+                      moe_dtype dt, void* out, float* logits, int32_t* ids, float* weights,
+                      int32_t* counts, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
+    return MOE_ERR_SHAPE;
+  if (T > 0 && (!x || !wr || !gate_up || !down || !out)) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wr) || !aligned16(gate_up) || !aligned16(down) ||
+      !aligned16(out))
+    return MOE_ERR_ALIGN;
+  const size_t need = layer_ws(nullptr, T, H, I, E, k, dt).total;
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  LayerWs w = layer_ws((char*)ws, T, H, I, E, k, dt);
+  if (!ids) ids = w.ids;
+  if (!weights) weights = w.weights;
+  if (!counts) counts = w.counts;
+  const bool bf16 = dt == MOE_BF16;
+  const int N = T * k;
+  // the histogram comes from the permutation pass, so the router skips it
+  hipError_t e = launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_permute_topk(ids, T, k, E, counts, w.offsets, w.sorted_token, w.sorted_slot,
+                          w.slot_pos, w.perm, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (N == 0) return MOE_OK;
+  const GemmTileCfg cu = pick_gate_up_cfg(bf16, N, H, I, E);
+  const GemmTileCfg cd = pick_down_cfg(bf16, N, H, I, E);
+  e = launch_gate_up(bf16, cu, x, T, w.sorted_token, w.offsets, N, H, I, E, gate_up, w.h,
+                     w.tiles_up, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // outputs land in flat-slot order (row t * k + j), so the combine reads each
+  // token's k rows contiguously.
+  e = launch_down(bf16, cd, w.h, w.offsets, w.sorted_slot, N, H, I, E, down, w.y, w.tiles_down,
+                  s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_combine(bf16, w.y, nullptr, weights, T, k, H, out, s));
+}
+
+}  // extern "C"

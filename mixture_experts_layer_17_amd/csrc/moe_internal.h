@@ -1,0 +1,55 @@
+// Host-side launchers shared between libmoe's translation units.  Every
+// launcher enqueues on `s` and returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct GemmTileCfg {
+  int BM;        // rows per tile
+  int BN;        // B columns per tile (SwiGLU: gate half + up half)
+  int id;        // which compiled instance
+};
+
+// Router: logits, top-k ids/weights, optional counts (counts must be zeroed
+// first; launch_fill_i32 does that).
+hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* bias,
+                        int T, int H, int E, int k, int norm, float* logits,
+                        int32_t* ids, float* w, int32_t* counts, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+
+// Token-choice permutation.  ws layout is given by permute_ws_bytes().
+size_t permute_ws_bytes(int N, int E, int R);
+hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                               int32_t* sorted_slot, int32_t* slot_pos, void* ws,
+                               hipStream_t s);
+hipError_t launch_permute_rank_major(const int32_t* counts_rm, int R, int N, int E,
+                                     int32_t* counts, int32_t* offsets,
+                                     int32_t* sorted_token, int32_t* sorted_slot,
+                                     int32_t* slot_pos, void* ws, hipStream_t s);
+
+hipError_t launch_gather_rows(bool bf16, const void* x, int x_rows, const int32_t* idx, int N,
+                              int H, void* out, hipStream_t s);
+
+hipError_t launch_combine(bool bf16, const void* y, const int32_t* slot_pos,
+                          const float* w, int T, int k, int H, void* out, hipStream_t s);
+
+// Grouped GEMMs.
+GemmTileCfg pick_gate_up_cfg(bool bf16, int N, int H, int I, int E);
+GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E);
+size_t tile_list_bytes(int N, int E, int BM);
+hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_rows,
+                          const int32_t* row_index, const int32_t* offsets, int N, int H,
+                          int I, int E, const void* gate_up, void* h, void* tile_ws,
+                          hipStream_t s);
+hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h,
+                       const int32_t* offsets, const int32_t* out_index, int N, int H,
+                       int I, int E, const void* down, void* y, void* tile_ws,
+                       hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,293 @@
+// Expert histogram, offsets and the stable expert-major permutation.
+//
+// Semantics: MindSpore moe.py, MoE.permutation (argsort(stable=True) of the
+// flattened expert ids; token index = flat index // top_k; bincount with
+// minlength = num_experts).  Rank-major mode: transformers PR "Qwen3 moe",
+// Ep2DpParallel._token_dispatch (received rows grouped by source rank, each
+// group ordered by local expert, to be reshuffled to expert-major order).
+//
+// Token-choice mode, deterministic and atomic-free on the ordering:
+//   1. chunk pass: the N flat slots are cut into chunks of 1024.  Each wave
+//      takes 64 consecutive slots at a time and finds, with 8 ballots over
+//      the expert id bits, the lanes holding the same expert; the lane's rank
+//      among equal lanes below it is a popcount.  Per-expert counts of the 16
+//      segments of a chunk are prefix-summed in LDS, giving each slot its
+//      stable rank inside the chunk and the chunk's histogram.
+//   2. scan pass (one workgroup): per expert, exclusive prefix over chunks;
+//      counts; exclusive prefix over experts -> offsets; chunk base =
+//      offset + prefix.
+//   3. scatter pass: position = chunk base[expert] + rank.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int PM_CHUNK = 1024;            // slots per chunk
+constexpr int PM_SEG = 64;                // slots per wave step
+constexpr int PM_NSEG = PM_CHUNK / PM_SEG;
+constexpr int PM_MAXE = 256;
+constexpr int PM_MAX_RE = 4096;           // rank-major: max R * E
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Pass 1: chunk histogram + stable rank of each slot inside its chunk.
+__global__ __launch_bounds__(256) void permute_chunk_kernel(
+    const int32_t* __restrict__ ids, int N, int E, int32_t* __restrict__ hist /*[nchunk][E]*/,
+    int32_t* __restrict__ rank /*[N]*/) {
+  __shared__ int s_cnt[PM_NSEG][PM_MAXE];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = blockIdx.x;
+  for (int i = threadIdx.x; i < PM_NSEG * PM_MAXE; i += 256) (&s_cnt[0][0])[i] = 0;
+  __syncthreads();
+
+  int my_e[4], my_rank[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int seg = q * 4 + wave;
+    const int i = c * PM_CHUNK + seg * PM_SEG + lane;
+    int e = (i < N) ? ids[i] : -1;
+    const bool valid = (e >= 0 && e < E);
+    if (!valid) e = -1;
+    unsigned long long match = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const unsigned long long bb = __ballot(bit);
+      match &= bit ? bb : ~bb;
+    }
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    my_e[q] = e;
+    my_rank[q] = valid ? __popcll(match & below) : 0;
+    // the lowest lane of each equal-expert group records the group size
+    if (valid && (match & below) == 0ull) s_cnt[seg][e] = __popcll(match);
+  }
+  __syncthreads();
+  // per-expert exclusive prefix over the 16 segments
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = 0;
+#pragma unroll
+    for (int sg = 0; sg < PM_NSEG; ++sg) {
+      const int v = s_cnt[sg][e];
+      s_cnt[sg][e] = run;
+      run += v;
+    }
+    hist[(size_t)c * E + e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int seg = q * 4 + wave;
+    const int i = c * PM_CHUNK + seg * PM_SEG + lane;
+    if (i < N) rank[i] = (my_e[q] >= 0) ? s_cnt[seg][my_e[q]] + my_rank[q] : -1;
+  }
+}
+
+// Pass 2: one workgroup of 1024 threads; thread (e, part) sums a quarter of
+// the chunks for expert e.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(
+    int32_t* __restrict__ hist_base /*[nchunk][E] in: hist, out: base*/, int nchunk, int E,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int s_part[4][PM_MAXE];
+  __shared__ int s_off[PM_MAXE + 1];
+  const int e = threadIdx.x & (PM_MAXE - 1);
+  const int part = threadIdx.x >> 8;
+  const int per = (nchunk + 3) / 4;
+  const int c0 = part * per, c1 = min(nchunk, c0 + per);
+  int run = 0;
+  if (e < E)
+    for (int c = c0; c < c1; ++c) run += hist_base[(size_t)c * E + e];
+  s_part[part][e] = run;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int x = 0; x < E; ++x) {
+      s_off[x] = acc;
+      acc += s_part[0][x] + s_part[1][x] + s_part[2][x] + s_part[3][x];
+    }
+    s_off[E] = acc;
+  }
+  __syncthreads();
+  if (e < E) {
+    int base = s_off[e];
+    for (int p = 0; p < part; ++p) base += s_part[p][e];
+    for (int c = c0; c < c1; ++c) {
+      const int v = hist_base[(size_t)c * E + e];
+      hist_base[(size_t)c * E + e] = base;
+      base += v;
+    }
+    if (part == 0) {
+      counts[e] = s_part[0][e] + s_part[1][e] + s_part[2][e] + s_part[3][e];
+      offsets[e] = s_off[e];
+    }
+  }
+  if (threadIdx.x == 0) offsets[E] = s_off[E];
+}
+
+// Pass 3: scatter.
+__global__ __launch_bounds__(256) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ base, int N, int E, int k, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  const int e = ids[i];
+  const int rk = rank[i];
+  if (e < 0 || e >= E || rk < 0) { slot_pos[i] = -1; return; }
+  const int c = i / PM_CHUNK;
+  const int p = base[(size_t)c * E + e] + rk;
+  if (p < 0 || p >= N) { slot_pos[i] = -1; return; }
+  sorted_token[p] = i / k;
+  if (sorted_slot) sorted_slot[p] = i;
+  slot_pos[i] = p;
+}
+
+// Rank-major mode, pass 1 (one workgroup): prefix tables of the count matrix.
+//   rm_start[r * E + e]: first received row of block (r, e) (rank-major order)
+//   em_start[r * E + e]: first expert-major position of block (r, e)
+__global__ __launch_bounds__(256) void rank_major_scan_kernel(
+    const int32_t* __restrict__ C, int R, int E, int N, int32_t* __restrict__ rm_start,
+    int32_t* __restrict__ em_start, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int s_cnt[PM_MAXE];
+  __shared__ int s_off[PM_MAXE + 1];
+  const int RE = R * E;
+  // rank-major prefix: serial over R*E (<= 4096) entries, small.
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int i = 0; i < RE; ++i) {
+      rm_start[i] = acc;
+      acc += max(0, C[i]);
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = 0;
+    for (int r = 0; r < R; ++r) run += max(0, C[r * E + e]);
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) { s_off[e] = acc; acc += s_cnt[e]; }
+    s_off[E] = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = s_off[e];
+    for (int r = 0; r < R; ++r) {
+      em_start[r * E + e] = run;
+      run += max(0, C[r * E + e]);
+    }
+    counts[e] = s_cnt[e];
+    offsets[e] = min(s_off[e], N);
+  }
+  if (threadIdx.x == 0) offsets[E] = min(s_off[E], N);
+}
+
+// Rank-major mode, pass 2: each received row finds its block by binary search
+// over the rank-major starts and moves to the block's expert-major start.
+__global__ __launch_bounds__(256) void rank_major_scatter_kernel(
+    const int32_t* __restrict__ C, const int32_t* __restrict__ rm_start,
+    const int32_t* __restrict__ em_start, int RE, int N, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+  __shared__ int s_rm[PM_MAX_RE];
+  for (int i = threadIdx.x; i < RE; i += 256) s_rm[i] = rm_start[i];
+  __syncthreads();
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  // largest block index b with s_rm[b] <= i (that block is non-empty)
+  int lo = 0, hi = RE - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_rm[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int within = i - s_rm[b];
+  if (within >= max(0, C[b])) { slot_pos[i] = -1; return; }   // rows beyond sum(C)
+  const int p = em_start[b] + within;
+  if (p < 0 || p >= N) { slot_pos[i] = -1; return; }
+  sorted_token[p] = i;
+  if (sorted_slot) sorted_slot[p] = i;
+  slot_pos[i] = p;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const T* __restrict__ x,
+                                                          const int32_t* __restrict__ idx,
+                                                          int N, int H, int nrows_x,
+                                                          T* __restrict__ out) {
+  const int per_row = H / 8;
+  const long long total = (long long)N * per_row;
+  for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (long long)gridDim.x * 256) {
+    const int p = (int)(q / per_row);
+    const int c = (int)(q % per_row);
+    const int src = clampi(idx[p], 0, nrows_x - 1);
+    const chunk8<T> v = load_chunk<T>(x + (size_t)src * H + 8 * c);
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<u32x4*>(out + (size_t)p * H + 8 * c) = v.v;
+    } else {
+      reinterpret_cast<u32x4*>(out + (size_t)p * H + 8 * c)[0] = v.lo;
+      reinterpret_cast<u32x4*>(out + (size_t)p * H + 8 * c)[1] = v.hi;
+    }
+  }
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t permute_ws_bytes(int N, int E, int R) {
+  if (R > 0) return 2 * align256((size_t)R * E * sizeof(int32_t));
+  const size_t nchunk = (size_t)(N + PM_CHUNK - 1) / PM_CHUNK;
+  return align256(nchunk * E * sizeof(int32_t)) + align256((size_t)N * sizeof(int32_t));
+}
+
+hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot,
+                               int32_t* slot_pos, void* ws, hipStream_t s) {
+  const int N = T * k;
+  if (N <= 0) {
+    hipError_t e = launch_fill_i32(counts, E, 0, s);
+    if (e != hipSuccess) return e;
+    return launch_fill_i32(offsets, E + 1, 0, s);
+  }
+  const int nchunk = (N + PM_CHUNK - 1) / PM_CHUNK;
+  int32_t* hist = (int32_t*)ws;
+  int32_t* rank = (int32_t*)((char*)ws + align256((size_t)nchunk * E * sizeof(int32_t)));
+  permute_chunk_kernel<<<nchunk, 256, 0, s>>>(ids, N, E, hist, rank);
+  permute_scan_kernel<<<1, 1024, 0, s>>>(hist, nchunk, E, counts, offsets);
+  permute_scatter_kernel<<<(N + 255) / 256, 256, 0, s>>>(ids, rank, hist, N, E, k, sorted_token,
+                                                         sorted_slot, slot_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_rank_major(const int32_t* C, int R, int N, int E, int32_t* counts,
+                                     int32_t* offsets, int32_t* sorted_token,
+                                     int32_t* sorted_slot, int32_t* slot_pos, void* ws,
+                                     hipStream_t s) {
+  int32_t* rm = (int32_t*)ws;
+  int32_t* em = (int32_t*)((char*)ws + align256((size_t)R * E * sizeof(int32_t)));
+  rank_major_scan_kernel<<<1, 256, 0, s>>>(C, R, E, N, rm, em, counts, offsets);
+  if (N > 0)
+    rank_major_scatter_kernel<<<(N + 255) / 256, 256, 0, s>>>(C, rm, em, R * E, N, sorted_token,
+                                                              sorted_slot, slot_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(bool bf16, const void* x, int x_rows, const int32_t* idx, int N,
+                              int H, void* out, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const long long total = (long long)N * (H / 8);
+  const int grid = (int)std::min<long long>((total + 255) / 256, 8192);
+  // source indices are clamped to [0, x_rows)
+  if (bf16)
+    gather_rows_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, idx, N, H, x_rows,
+                                                    (bf16_t*)out);
+  else
+    gather_rows_kernel<float><<<grid, 256, 0, s>>>((const float*)x, idx, N, H, x_rows,
+                                                   (float*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

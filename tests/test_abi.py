@@ -1,0 +1,66 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and its host-side logic (workspace sizing, argument
+validation) behaves.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_17_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmoe.h")
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), f"libmoe.so does not export {n}"
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_version() >= 1
+    assert lib.moe_status_string(0) == b"ok"
+    for s in range(-7, 0):
+        assert lib.moe_status_string(s) != b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    ws = lambda *a: lib.moe_workspace_size(*a)
+    assert ws(_lib.MOE_OP_ROUTE, 64, 128, 64, 8, 2, 0, 128, 0) == 0
+    small = ws(_lib.MOE_OP_LAYER, 64, 2048, 768, 128, 8, 0, 512, 1)
+    big = ws(_lib.MOE_OP_LAYER, 4096, 2048, 768, 128, 8, 0, 32768, 1)
+    assert 0 < small < big
+    # holds at least h [N, I] and y [N, H] in bf16
+    assert big >= 32768 * (768 + 2048) * 2
+    assert ws(_lib.MOE_OP_LAYER, 64, 100, 64, 8, 2, 0, 128, 1) == SIZE_MAX      # H % 128
+    assert ws(_lib.MOE_OP_LAYER, 64, 128, 64, 300, 2, 0, 128, 1) == SIZE_MAX    # E > 256
+    assert ws(_lib.MOE_OP_PERMUTE, 0, 0, 0, 16, 1, 8, 32768, 1) > 0
+    assert ws(_lib.MOE_OP_PERMUTE, 0, 0, 0, 16, 1, 1000, 32768, 1) == SIZE_MAX  # R * E
+    assert ws(99, 1, 128, 64, 8, 2, 0, 2, 1) == SIZE_MAX
+    assert ws(_lib.MOE_OP_GATE_UP, 0, 2048, 768, 128, 1, 0, 32768, 1) > 0
+
+
+def test_validation_happens_before_any_launch(lib):
+    fake = 4096  # never dereferenced: every call below fails validation
+    assert lib.moe_route(fake, fake, None, 4, 128, 0, 1, 1, 1, None, fake, fake, None, None) == -2
+    assert lib.moe_route(fake, fake, None, 4, 128, 8, 2, 1, 5, None, fake, fake, None, None) == -3
+    assert lib.moe_route(fake + 4, fake, None, 4, 128, 8, 2, 1, 1, None, fake, fake, None, None) == -7
+    assert lib.moe_combine(fake, None, None, 4, 0, 128, 1, fake, None) == -2
+    assert lib.moe_grouped_down(fake, fake, None, 8, 128, 64, 8, fake, 1, fake, fake, 8, None) == -4
+    assert lib.moe_gather_rows(None, 4, fake, 8, 128, 1, fake, None) == -1

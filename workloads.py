@@ -163,3 +163,14 @@ def make(name: str, seed: int = 0, **overrides):
     zipf_s = cfg.pop("zipf_s", None)
     bias = zipf_router_bias(cfg["E"], zipf_s) if zipf_s is not None else None
     return make_layer(name=name, seed=seed, router_bias=bias, **cfg)
+
+
+def random_topk_ids(T: int, E: int, k: int, seed: int = 0,
+                    popularity: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Random expert selections: for each token, k distinct experts drawn
+    without replacement (uniformly, or in proportion to ``popularity``).
+    A stand-in for a router's output when only the permutation is tested."""
+    g = torch.Generator().manual_seed(seed)
+    p = torch.ones(E) if popularity is None else popularity.float()
+    p = p.expand(T, E).contiguous()
+    return torch.multinomial(p, k, replacement=False, generator=g).to(torch.int32)

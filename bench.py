@@ -1,0 +1,301 @@
+"""Benchmark: MoE layer forward on one MI355X.
+
+A step is one pass of the whole layer (router -> permutation -> grouped
+gate_up + SwiGLU -> grouped down -> combine) over one batch of seeded
+synthetic input already resident in HBM.  The layer runs as its five C-ABI
+calls on torch's current stream, with HIP events between them so that each
+kernel's average duration is measured live over the timed steps.
+
+Prints one JSON line.  Default workload: the Qwen3-30B-A3B-shaped prefill
+layer, T = 4096 tokens, H = 2048, I = 768, E = 128, top_k = 8, bf16.
+
+Other modes:
+  --workload NAME        another named workload (decode, skewed, tiny)
+  --copy-calibration     only run a plain 1 GiB device copy (for scaling the
+                         rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s per MoE layer fwd (bf16); % MFMA peak; decode HBM GB/s"
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA (published)
+PEAK_F32_FLOPS = 157.3e12     # MI355X fp32 (published)
+PEAK_HBM = 8.0e12             # MI355X HBM3E bytes/s (published)
+KERNELS = ("route", "permute", "gate_up_swiglu", "down", "combine")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_a3b_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic(wl, counts):
+    """Per-kernel algorithmic FLOPs and HBM bytes for one layer pass.
+    Weights count once per expert that received rows; gathered rows count
+    once per token; intermediates count once written and once read."""
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.top_k
+    es = 2 if wl.dtype.itemsize == 2 else 4
+    N = T * k
+    hit = int((counts > 0).sum())
+    f = {
+        "route": 2.0 * T * H * E,
+        "permute": 0.0,
+        "gate_up_swiglu": 2.0 * N * H * 2 * I,
+        "down": 2.0 * N * I * H,
+        "combine": 2.0 * N * H,
+    }
+    b = {
+        "route": T * H * es + E * H * es + T * E * 4 + T * k * 8,
+        "permute": N * 4 * 5,
+        "gate_up_swiglu": hit * H * 2 * I * es + T * H * es + N * I * es,
+        "down": hit * I * H * es + N * I * es + N * H * es,
+        "combine": N * H * es + N * 4 + T * H * es,
+    }
+    return f, b, hit
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The CPU oracle, as it stands, on this host: the whole workload, run
+    until about budget_s seconds of work are done (at least once)."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    x = wl.hidden_states.float().numpy()
+    wr = wl.router_weight.float().numpy()
+    gu = wl.gate_up.float().numpy()
+    dn = wl.down.float().numpy()
+    bias = wl.router_bias.numpy() if wl.router_bias is not None else None
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        O.moe_layer_forward(x, wr, bias, gu, dn, wl.top_k, wl.norm_topk_prob)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 5:
+            break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": wl.T * wl.top_k * runs / el, "unit": "routed tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole {wl.name} workload ({wl.T} tokens, all experts), {runs} run(s), "
+                      f"{el:.1f} s, float64 NumPy per-expert loop on {cpu}, "
+                      f"affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def source_sha(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic of a kernel from committed rocprofv3 counter summaries,
+    only while the kernel source still matches the one measured."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    src = os.path.join(ROOT, t["source"])
+    if not os.path.exists(src) or source_sha(src) != t.get("source_sha256"):
+        return None
+    return t.get("traffic_bytes")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", args.gpus))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU only: the MoE layer forward here has no multi-GPU "
+              "path (no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_17_amd as moe
+    import workloads
+    from mixture_experts_layer_17_amd import _lib
+
+    wl = workloads.make(args.workload)
+    if not hasattr(wl, "T"):
+        print("bench.py times token-choice layers; the EP-rank workload is a parity case",
+              file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.top_k
+    N = T * k
+    bf16 = wl.dtype == torch.bfloat16
+    dt = _lib.MOE_BF16 if bf16 else _lib.MOE_F32
+    x, wr, gu, dn = (t.to(dev).contiguous() for t in (wl.hidden_states, wl.router_weight,
+                                                       wl.gate_up, wl.down))
+    bias = wl.router_bias.to(dev) if wl.router_bias is not None else None
+    f32, i32 = torch.float32, torch.int32
+    logits = torch.empty(T, E, dtype=f32, device=dev)
+    ids = torch.empty(T, k, dtype=i32, device=dev)
+    w = torch.empty(T, k, dtype=f32, device=dev)
+    counts = torch.empty(E, dtype=i32, device=dev)
+    offsets = torch.empty(E + 1, dtype=i32, device=dev)
+    sorted_token = torch.empty(N, dtype=i32, device=dev)
+    sorted_slot = torch.empty(N, dtype=i32, device=dev)
+    slot_pos = torch.empty(N, dtype=i32, device=dev)
+    h = torch.empty(N, I, dtype=wl.dtype, device=dev)
+    y = torch.empty(N, H, dtype=wl.dtype, device=dev)
+    out = torch.empty(T, H, dtype=wl.dtype, device=dev)
+    L = moe.lib
+
+    def ws(op):
+        n = L.moe_workspace_size(op, T, H, I, E, k, 0, N, dt)
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=dev), n
+
+    ws_perm, nperm = ws(_lib.MOE_OP_PERMUTE)
+    ws_up, nup = ws(_lib.MOE_OP_GATE_UP)
+    ws_dn, ndn = ws(_lib.MOE_OP_DOWN)
+    s = torch.cuda.current_stream(dev)
+    sp = s.cuda_stream
+    P = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+
+    calls = [
+        lambda: L.moe_route(P(x), P(wr), P(bias), T, H, E, k, int(wl.norm_topk_prob), dt,
+                            P(logits), P(ids), P(w), None, sp),
+        lambda: L.moe_permute(P(ids), T, k, None, 0, N, E, P(counts), P(offsets),
+                              P(sorted_token), P(sorted_slot), P(slot_pos), P(ws_perm), nperm,
+                              sp),
+        lambda: L.moe_grouped_gate_up_swiglu(P(x), T, P(sorted_token), P(offsets), N, H, I, E,
+                                             P(gu), dt, P(h), P(ws_up), nup, sp),
+        lambda: L.moe_grouped_down(P(h), P(offsets), P(sorted_slot), N, H, I, E, P(dn), dt,
+                                   P(y), P(ws_dn), ndn, sp),
+        lambda: L.moe_combine(P(y), None, P(w), T, k, H, dt, P(out), sp),
+    ]
+
+    def step(evs=None):
+        for i, c in enumerate(calls):
+            if evs is not None:
+                evs[i].record(s)
+            st = c()
+            if st != 0:
+                raise RuntimeError(f"{KERNELS[i]} failed with status {st}")
+        if evs is not None:
+            evs[len(calls)].record(s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(s)
+    for i in range(args.steps):
+        step(ev[i])
+    end.record(s)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    per_kernel_ms = {KERNELS[j]: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1])
+                                                for i in range(args.steps)]))
+                     for j in range(len(calls))}
+
+    c_np = counts.cpu().numpy()
+    flops, bytes_, hit = algorithmic(wl, c_np)
+    peak_f = PEAK_BF16_FLOPS if bf16 else PEAK_F32_FLOPS
+    kern = {}
+    for kname in KERNELS:
+        t_s = per_kernel_ms[kname] * 1e-3
+        kern[kname] = {
+            "avg_us": round(per_kernel_ms[kname] * 1e3, 2),
+            "tflops": round(flops[kname] / t_s / 1e12, 2),
+            "gbps": round(bytes_[kname] / t_s / 1e9, 1),
+            "mfma_frac": round(flops[kname] / t_s / peak_f, 4),
+            "hbm_frac": round(bytes_[kname] / t_s / PEAK_HBM, 4),
+        }
+    dom = max(KERNELS, key=lambda n: per_kernel_ms[n])
+    t_dom = per_kernel_ms[dom] * 1e-3
+    hbm_floor = bytes_[dom] / PEAK_HBM
+    mfma_floor = flops[dom] / peak_f
+    if hbm_floor >= mfma_floor:
+        roof = {"bound": "hbm", "achieved": round(bytes_[dom] / t_dom / 1e9, 1),
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops[dom] / t_dom / 1e12, 2),
+                "peak": peak_f / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = load_traffic(dom, wl.name)
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = int(bytes_[dom])
+    roof["algorithmic_flops"] = int(flops[dom])
+
+    layer_flops = sum(flops.values())
+    result = {
+        "metric": METRIC,
+        "value": round(N / (ms_per_step * 1e-3), 1),
+        "unit": "routed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic: seeded Gaussian inputs and random-init weights of the named layer shape",
+        "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "top_k": k,
+                   "norm_topk_prob": wl.norm_topk_prob, "routed_rows": N,
+                   "experts_hit": hit},
+        "layer_tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "layer_mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / peak_f, 4),
+        "roofline": roof,
+        "kernels": kern,
+        "wall_s_timed": round(t_wall, 3),
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

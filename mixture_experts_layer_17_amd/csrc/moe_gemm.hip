@@ -401,11 +401,19 @@ size_t tile_list_bytes(int N, int E, int BM) {
 
 GemmTileCfg pick_gate_up_cfg(bool bf16, int N, int H, int I, int E) {
   (void)H;
+  if (bf16) {
+    const GemmTileCfg c = pick_lds_cfg(N, E, I, true);
+    if (c.id >= 0) return c;
+  }
   return pick_cfg(bf16, N, E, I, true);
 }
 
 GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E) {
   (void)I;
+  if (bf16) {
+    const GemmTileCfg c = pick_lds_cfg(N, E, H, false);
+    if (c.id >= 0) return c;
+  }
   return pick_cfg(bf16, N, E, H, false);
 }
 
@@ -413,6 +421,9 @@ hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_
                           const int32_t* row_index, const int32_t* offsets, int N, int H, int I,
                           int E, const void* gate_up, void* h, void* tile_ws, hipStream_t s) {
   if (N <= 0) return hipSuccess;
+  if (lds_cfg_id(c.id))
+    return launch_lds_gemm(true, c, x, H, row_index, x_rows, gate_up, (long long)H * 2 * I, 2 * I,
+                           H, I, h, I, nullptr, N, offsets, N, E, I / (c.BN / 2), tile_ws, s);
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
   build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);
@@ -427,6 +438,9 @@ hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h, const int
                        const int32_t* out_index, int N, int H, int I, int E, const void* down,
                        void* y, void* tile_ws, hipStream_t s) {
   if (N <= 0) return hipSuccess;
+  if (lds_cfg_id(c.id))
+    return launch_lds_gemm(false, c, h, I, nullptr, N, down, (long long)I * H, H, I, 0, y, H,
+                           out_index, N, offsets, N, E, H / c.BN, tile_ws, s);
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
   build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);

@@ -1,0 +1,428 @@
+// Grouped expert GEMMs for bf16 on gfx950: asynchronous global->LDS loads
+// into a multi-stage ring, transposing LDS reads for the weights, MFMA
+// 16x16x32 bf16 with float32 accumulation.
+//
+// Semantics as the float path (moe_gemm.hip): Qwen3-Omni issue #115,
+// SpeedupMoeExperts.forward -- per expert e, gate_up = x_e @ gate_up_proj[e],
+// h = up * silu(gate), y_e = h @ down_proj[e]; MindSpore moe.py,
+// _run_experts_for_loop -- rows in expert-major order split by counts.
+//
+// Data path per K-block of 32:
+//   * activations: BM gathered rows x 64 bytes, loaded with
+//     global_load_lds_dwordx4 (lane i of a wave instruction lands at
+//     base + 16 i); each lane picks the global 16-byte chunk that belongs at
+//     its LDS slot, which realises an XOR swizzle of the 4 chunks of a row
+//     by f(row) = ((row >> 1) ^ (row >> 3)) & 3.  Reads are ds_read_b128.
+//   * weights: 32 rows (k) x BN columns in their natural [k][n] layout
+//     (n contiguous), loaded the same way with 32-byte segments of a row
+//     XOR-swizzled by h(row) = (row & 3) | ((row >> 1) & 4).  The MFMA
+//     operand needs 8 consecutive k of one column per lane; ds_read_b64_tr_b16
+//     delivers that: within each 16-lane group, lane s reads 4 consecutive
+//     columns of row (kbase + s / 4) and lane j receives column j of rows
+//     kbase .. kbase + 3.
+//   * MFMA operands are (weights, activations), so the accumulator tile is
+//     C^T: each lane holds 4 consecutive output columns of one row, stored
+//     with one 8-byte write.
+//   * STAGES K-blocks are in flight; a block's loads are issued STAGES - 1
+//     iterations before it is consumed, and one barrier per iteration both
+//     publishes the landed block and retires the slot being refilled.
+//   * m-tiles of 16 rows are dealt to the WM wave rows round-robin, so a
+//     ragged tile still splits its rows evenly; m-tiles beyond the tile's
+//     rows are skipped.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int NUM_XCD = 8;
+constexpr int BK = 32;   // k per stage
+
+typedef short i16x4_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_v lds_i16x4;
+
+__device__ __forceinline__ int fswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int hswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// One 16-byte-per-lane asynchronous copy global -> LDS: lane i's 16 bytes
+// land at lds + 16 i (lds is wave-uniform, passed in M0).  Issued from asm
+// so that the compiler's wait-count pass, which cannot tell the four stage
+// buffers apart across loop iterations, does not drain every copy in flight
+// before each LDS read; completion is tracked with explicit vmcnt waits
+// below.  The instruction writes no registers, so nothing the compiler
+// allocates can be overwritten while it is in flight.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* g, const unsigned char* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const lds_u8*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(a)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Waits until at most N of this wave's vector-memory loads are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU>
+struct lcfg {
+  static constexpr int NW = WM * WN;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int MT = BM / 16;                 // m-tiles per workgroup tile
+  static constexpr int TM = MT / WM;                 // m-tiles per wave
+  static constexpr int CW = SWIGLU ? (BN / 2) / WN : BN / WN;  // output cols per wave
+  static constexpr int TNO = CW / 16;
+  static constexpr int TN = SWIGLU ? 2 * TNO : TNO;
+  static constexpr int A_BYTES = BM * BK * 2;        // per stage
+  static constexpr int B_BYTES = BK * BN * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS = STAGES * STAGE_BYTES;
+  static constexpr int A_INST = A_BYTES / 1024;      // wave instructions per stage
+  static constexpr int B_INST = B_BYTES / 1024;
+  static constexpr int A_PER = (A_INST + NW - 1) / NW;
+  static constexpr int B_PER = B_INST / NW;
+  static constexpr int ROWB = BN * 2;                // bytes per weight row in LDS
+  static constexpr int SEGS = BN / 16;               // 32-byte segments per weight row
+  static_assert(MT % WM == 0 && TM >= 1, "m-tiles per wave");
+  static_assert(CW % 16 == 0 && TNO >= 1, "n-tiles per wave");
+  static_assert(B_INST % NW == 0, "weight loads split evenly");
+  static_assert(SEGS >= 8, "swizzle needs 8 segments per row");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
+    const bf16_t* __restrict__ X, int ldx, const int32_t* __restrict__ x_index, int x_rows,
+    const bf16_t* __restrict__ W, long long w_estride, int ldw, int K, int up_off,
+    bf16_t* __restrict__ C, int ldc, const int32_t* __restrict__ c_index, int c_rows,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count, int n_ntiles) {
+  using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU>;
+  static_assert(STAGES == 4, "the main loop is unrolled over four stage buffers");
+  // One array per stage: the compiler can then tell which buffer an
+  // asynchronous load writes and which one a read uses, and does not wait
+  // for every load in flight before each LDS read.
+  __shared__ __align__(16) unsigned char st0[G::STAGE_BYTES];
+  __shared__ __align__(16) unsigned char st1[G::STAGE_BYTES];
+  __shared__ __align__(16) unsigned char st2[G::STAGE_BYTES];
+  __shared__ __align__(16) unsigned char st3[G::STAGE_BYTES];
+
+  // ---- job (M-tile, N-tile), XCD-aware: consecutive jobs share an XCD
+  const int jobs = tiles_count[0] * n_ntiles;
+  const int per_xcd = (jobs + NUM_XCD - 1) / NUM_XCD;
+  const int xcd = blockIdx.x % NUM_XCD;
+  const int local = blockIdx.x / NUM_XCD;
+  if (local >= per_xcd) return;
+  const int job = xcd * per_xcd + local;
+  if (job >= jobs) return;
+  const int mt = job / n_ntiles;
+  const int nt = job - mt * n_ntiles;
+  const int4 tile = tiles[mt];
+  const int e = tile.x, row0 = tile.y, rows = tile.z;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int n0 = SWIGLU ? nt * (BN / 2) : nt * BN;
+  const bf16_t* We = W + (long long)e * w_estride;
+
+  // ---- load assignments: global source of this lane's 16 bytes in each of
+  // the wave's load instructions (advanced by one K-block per issue)
+  const bf16_t* a_src[G::A_PER];
+  int a_lds[G::A_PER];
+  bool a_on[G::A_PER];
+#pragma unroll
+  for (int u = 0; u < G::A_PER; ++u) {
+    const int inst = wave + u * G::NW;
+    a_on[u] = inst < G::A_INST;
+    const int q = (a_on[u] ? inst : 0) * 64 + lane;   // 16-byte slot in the A block
+    const int row = q >> 2;
+    const int c = (q & 3) ^ fswz(row);
+    int src = row0 + min(row, rows - 1);
+    if (x_index) src = x_index[src];
+    src = min(max(src, 0), x_rows - 1);
+    a_src[u] = X + (long long)src * ldx + 8 * c;
+    a_lds[u] = (a_on[u] ? inst : 0) * 1024;
+  }
+  const bf16_t* b_src[G::B_PER];
+  int b_lds[G::B_PER];
+#pragma unroll
+  for (int u = 0; u < G::B_PER; ++u) {
+    const int inst = wave + u * G::NW;
+    const int q = inst * 64 + lane;                   // 16-byte slot in the B block
+    const int row = q / (BN / 8);
+    const int p = q % (BN / 8);
+    const int seg = (p >> 1) ^ hswz(row);
+    int col = 16 * seg + 8 * (p & 1);                  // logical B-tile column
+    if constexpr (SWIGLU)
+      col = col < BN / 2 ? n0 + col : up_off + n0 + (col - BN / 2);
+    else
+      col = n0 + col;
+    b_src[u] = We + (long long)row * ldw + col;
+    b_lds[u] = G::A_BYTES + inst * 1024;
+  }
+
+  auto issue = [&](unsigned char* base) {
+#pragma unroll
+    for (int u = 0; u < G::A_PER; ++u) {
+      if (a_on[u]) copy16_to_lds(a_src[u], base + a_lds[u]);
+      a_src[u] += BK;
+    }
+#pragma unroll
+    for (int u = 0; u < G::B_PER; ++u) {
+      copy16_to_lds(b_src[u], base + b_lds[u]);
+      b_src[u] += (long long)BK * ldw;
+    }
+  };
+
+  // ---- per-lane LDS read offsets (bytes within a stage)
+  int xa_off[G::TM];
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i) {
+    const int row = 16 * (wm + WM * i) + r16;
+    xa_off[i] = row * 64 + 16 * (g ^ fswz(row));
+  }
+  // this wave's m-tiles wm, wm + WM, ... that hold rows (wave-uniform)
+  const int tm_on = __builtin_amdgcn_readfirstlane(
+      min(G::TM, max(0, ((rows + 15) / 16 - wm + WM - 1) / WM)));
+  int wb_off[G::TN][2];
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    int cb;  // logical column base of this 16-column tile
+    if constexpr (SWIGLU)
+      cb = j < G::TNO ? wn * G::CW + 16 * j : BN / 2 + wn * G::CW + 16 * (j - G::TNO);
+    else
+      cb = wn * G::CW + 16 * j;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 8 * g + 4 * hf + (r16 >> 2);
+      wb_off[j][hf] = G::A_BYTES + row * G::ROWB + 32 * ((cb >> 4) ^ hswz(row)) + 8 * (r16 & 3);
+    }
+  }
+
+  f32x4_v acc[G::TM][G::TN];
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = K / BK;
+  constexpr int PER_STAGE_MAX = G::A_PER + G::B_PER;
+  const bool a_full = (G::A_INST % G::NW == 0) || (wave < G::A_INST % G::NW);
+
+  auto compute = [&](const unsigned char* base) {
+    chunk8<bf16_t> wf[G::TN];
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) {
+      const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(base + wb_off[j][0]));
+      const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(base + wb_off[j][1]));
+      wf[j].v = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      if (i < tm_on) {
+        chunk8<bf16_t> xf;
+        xf.v = *reinterpret_cast<const u32x4*>(base + xa_off[i]);
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma_16x16x32(wf[j], xf, acc[i][j]);
+      }
+    }
+  };
+
+  // prologue: STAGES - 1 blocks in flight
+  if (0 < KT) issue(st0);
+  if (1 < KT) issue(st1);
+  if (2 < KT) issue(st2);
+
+  // Step for K-block kb held in CUR: wait for it (later blocks stay in
+  // flight), barrier, refill NXT (the buffer every wave finished reading in
+  // the previous step), then compute.
+#define MOE_STEP(CUR, NXT, S)                                                        \
+  {                                                                                 \
+    const int kb = kt + (S);                                                        \
+    if (kb < KT) {                                                                  \
+      if (KT - 1 - kb >= STAGES - 2) {                                              \
+        if (a_full) wait_vmcnt<(STAGES - 2) * PER_STAGE_MAX>();                     \
+        else wait_vmcnt<(STAGES - 2) * (PER_STAGE_MAX - 1)>();                      \
+      } else {                                                                      \
+        wait_vmcnt<0>();                                                            \
+      }                                                                             \
+      __builtin_amdgcn_s_barrier();                                                 \
+      asm volatile("" ::: "memory");                                                \
+      if (kb + STAGES - 1 < KT) issue(NXT);                                         \
+      compute(CUR);                                                                 \
+    }                                                                               \
+  }
+  for (int kt = 0; kt < KT; kt += STAGES) {
+    MOE_STEP(st0, st3, 0)
+    MOE_STEP(st1, st0, 1)
+    MOE_STEP(st2, st1, 2)
+    MOE_STEP(st3, st2, 3)
+  }
+#undef MOE_STEP
+
+  // ---- epilogue: acc[i][j][q] = C[row m][col cb_j + 4 g + q]
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i) {
+    const int m = 16 * (wm + WM * i) + r16;
+    if (i >= tm_on || m >= rows) continue;
+    const int p = row0 + m;
+    if constexpr (SWIGLU) {
+      bf16_t* crow = C + (long long)p * ldc + n0 + wn * G::CW + 4 * g;
+#pragma unroll
+      for (int j = 0; j < G::TNO; ++j) {
+        uint32_t d[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float h0 = silu_f32(acc[i][j][2 * q]) * acc[i][G::TNO + j][2 * q];
+          const float h1 = silu_f32(acc[i][j][2 * q + 1]) * acc[i][G::TNO + j][2 * q + 1];
+          d[q] = (uint32_t)f32_to_bf16_bits(h0) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
+        }
+        *reinterpret_cast<uint2*>(crow + 16 * j) = make_uint2(d[0], d[1]);
+      }
+    } else {
+      const int dst = c_index ? c_index[p] : p;
+      if (dst < 0 || dst >= c_rows) continue;
+      bf16_t* crow = C + (long long)dst * ldc + n0 + wn * G::CW + 4 * g;
+#pragma unroll
+      for (int j = 0; j < G::TNO; ++j) {
+        const uint32_t d0 = (uint32_t)f32_to_bf16_bits(acc[i][j][0]) |
+                            ((uint32_t)f32_to_bf16_bits(acc[i][j][1]) << 16);
+        const uint32_t d1 = (uint32_t)f32_to_bf16_bits(acc[i][j][2]) |
+                            ((uint32_t)f32_to_bf16_bits(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(crow + 16 * j) = make_uint2(d0, d1);
+      }
+    }
+  }
+}
+
+// Tile list with even splits: an expert with c rows gets nt = ceil(c / BM)
+// tiles of ceil(c / nt) rows rounded up to 16 (the last one shorter).
+__global__ __launch_bounds__(256) void build_tiles_even_kernel(
+    const int32_t* __restrict__ offsets, int E, int N, int BM, int4* __restrict__ tiles,
+    int32_t* __restrict__ tiles_count) {
+  __shared__ int s_nt[256];
+  __shared__ int s_start[257];
+  const int e = threadIdx.x;
+  int lo = 0, hi = 0, nt = 0;
+  if (e < E) {
+    lo = min(max(offsets[e], 0), N);
+    hi = min(max(offsets[e + 1], lo), N);
+    nt = (hi - lo + BM - 1) / BM;
+  }
+  s_nt[e] = nt;
+  __syncthreads();
+  // exclusive scan over 256 entries by wave 0 (4 values per lane)
+  if (e < 64) {
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { v[q] = s_nt[4 * e + q]; sum += v[q]; }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (e >= off) incl += o;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { s_start[4 * e + q] = run; run += v[q]; }
+    if (e == 63) { s_start[256] = incl; tiles_count[0] = incl; }
+  }
+  __syncthreads();
+  if (e < E && nt > 0) {
+    const int c = hi - lo;
+    const int per = ((c + nt - 1) / nt + 15) & ~15;
+    const int t0 = s_start[e];
+    for (int t = 0; t < nt; ++t) {
+      const int r0 = lo + t * per;
+      tiles[t0 + t] = make_int4(e, r0, max(0, min(per, hi - r0)), 0);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU>
+hipError_t launch_lds(const void* X, int ldx, const int32_t* x_index, int x_rows, const void* W,
+                      long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
+                      const int32_t* c_index, int c_rows, const int4* tiles,
+                      const int32_t* tiles_count, int n_ntiles, int grid, hipStream_t s) {
+  using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU>;
+  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU>), dim3(grid),
+                     dim3(G::THREADS), 0, s, (const bf16_t*)X, ldx, x_index, x_rows,
+                     (const bf16_t*)W, w_estride, ldw, K, up_off, (bf16_t*)C, ldc, c_index,
+                     c_rows, tiles, tiles_count, n_ntiles);
+  return hipGetLastError();
+}
+
+struct LdsCfg { int BM, BN; };
+// 10: 256 x 256, 4 x 2 waves (64 x 128 per wave)    large groups
+// 11: 128 x 256, 2 x 2 waves                          mid
+// 12:  64 x 256, 1 x 4 waves                          small groups
+// 13:  16 x 256, 1 x 4 waves                          decode
+constexpr LdsCfg kLds[] = {{256, 256}, {128, 256}, {64, 256}, {16, 256}};
+
+hipError_t launch_lds_cfg(bool swiglu, int id, const void* X, int ldx, const int32_t* x_index,
+                          int x_rows, const void* W, long long w_estride, int ldw, int K,
+                          int up_off, void* C, int ldc, const int32_t* c_index, int c_rows,
+                          const int4* tiles, const int32_t* tiles_count, int n_ntiles, int grid,
+                          hipStream_t s) {
+#define MOE_ARGS X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C, ldc, c_index, c_rows, \
+                 tiles, tiles_count, n_ntiles, grid, s
+#define MOE_CASE(ID, BM, BN, WM, WN, ST)                                    \
+  case ID:                                                                \
+    return swiglu ? launch_lds<BM, BN, WM, WN, ST, true>(MOE_ARGS)        \
+                  : launch_lds<BM, BN, WM, WN, ST, false>(MOE_ARGS);
+  switch (id) {
+    MOE_CASE(10, 256, 256, 4, 2, 4)
+    MOE_CASE(11, 128, 256, 2, 2, 4)
+    MOE_CASE(12, 64, 256, 1, 4, 4)
+    MOE_CASE(13, 16, 256, 1, 4, 4)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_CASE
+#undef MOE_ARGS
+}
+
+}  // namespace
+
+bool lds_cfg_id(int id) { return id >= 10 && id <= 13; }
+
+GemmTileCfg pick_lds_cfg(int N, int E, int cols, bool swiglu) {
+  // weight columns per tile: 256 (SwiGLU: 128 gate + 128 up)
+  const int need = swiglu ? 128 : 256;
+  if (cols % need != 0) return GemmTileCfg{0, 0, -1};
+  const double mean_rows = E > 0 ? (double)N / E : 0.0;
+  int id;
+  if (mean_rows >= 160.0) id = 10;
+  else if (mean_rows >= 64.0) id = 11;
+  else if (mean_rows >= 24.0) id = 12;
+  else id = 13;
+  return GemmTileCfg{kLds[id - 10].BM, kLds[id - 10].BN, id};
+}
+
+hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int ldx,
+                           const int32_t* x_index, int x_rows, const void* W,
+                           long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
+                           const int32_t* c_index, int c_rows, const int32_t* offsets, int N,
+                           int E, int n_ntiles, void* tile_ws, hipStream_t s) {
+  int32_t* count = (int32_t*)tile_ws;
+  int4* tiles = (int4*)((char*)tile_ws + 256);
+  build_tiles_even_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);
+  const long long max_tiles = (long long)N / c.BM + std::min(E, N);
+  long long jobs = max_tiles * n_ntiles;
+  jobs = (jobs + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+  const int grid = (int)std::max<long long>(jobs, NUM_XCD);
+  return launch_lds_cfg(swiglu, c.id, X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C,
+                        ldc, c_index, c_rows, tiles, count, n_ntiles, grid, s);
+}
+
+}  // namespace moe

@@ -39,7 +39,15 @@ hipError_t launch_gather_rows(bool bf16, const void* x, int x_rows, const int32_
 hipError_t launch_combine(bool bf16, const void* y, const int32_t* slot_pos,
                           const float* w, int T, int k, int H, void* out, hipStream_t s);
 
-// Grouped GEMMs.
+// Grouped GEMMs.  Configs with id >= 10 run the LDS-ring kernel
+// (moe_gemm_lds.hip); the others the register-transpose kernel.
+bool lds_cfg_id(int id);
+GemmTileCfg pick_lds_cfg(int N, int E, int cols, bool swiglu);
+hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int ldx,
+                           const int32_t* x_index, int x_rows, const void* W,
+                           long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
+                           const int32_t* c_index, int c_rows, const int32_t* offsets, int N,
+                           int E, int n_ntiles, void* tile_ws, hipStream_t s);
 GemmTileCfg pick_gate_up_cfg(bool bf16, int N, int H, int I, int E);
 GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E);
 size_t tile_list_bytes(int N, int E, int BM);

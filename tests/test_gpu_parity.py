@@ -76,6 +76,8 @@ def test_layer_tiny_fp32(moe):
     dict(T=200, H=384, I=192, E=8, top_k=2),      # narrow-tile fallback
     dict(T=129, H=512, I=64, E=6, top_k=6),       # k = E
     dict(T=70, H=256, I=128, E=1, top_k=1),       # one expert
+    dict(T=200, H=256, I=128, E=32, top_k=8),     # ~50 rows per expert
+    dict(T=150, H=512, I=192, E=8, top_k=2),      # K-blocks not a multiple of the stages
 ])
 def test_layer_small_bf16(moe, shape):
     wl = workloads.make_layer(f"small_{shape['T']}", norm_topk_prob=True, seed=1, **shape)

@@ -1,10 +1,10 @@
 """Benchmark: MoE layer forward on one MI355X.
 
-A step is one pass of the whole layer (router -> permutation -> grouped
+A step is one moe_layer_forward call (router -> permutation -> grouped
 gate_up + SwiGLU -> grouped down -> combine) over one batch of seeded
-synthetic input already resident in HBM.  The layer runs as its five C-ABI
-calls on torch's current stream, with HIP events between them so that each
-kernel's average duration is measured live over the timed steps.
+synthetic input already resident in HBM, on torch's current stream.  The
+library records caller-supplied HIP events between its stages, so each
+stage's average duration is measured live over the timed steps.
 
 Prints one JSON line.  Default workload: the Qwen3-30B-A3B-shaped prefill
 layer, T = 4096 tokens, H = 2048, I = 768, E = 128, top_k = 8, bf16.
@@ -32,7 +32,7 @@ METRIC = "routed tokens/s per MoE layer fwd (bf16); % MFMA peak; decode HBM GB/s
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA (published)
 PEAK_F32_FLOPS = 157.3e12     # MI355X fp32 (published)
 PEAK_HBM = 8.0e12             # MI355X HBM3E bytes/s (published)
-KERNELS = ("route", "permute", "gate_up_swiglu", "down", "combine")
+KERNELS = ("route", "permute", "gate_up_swiglu", "down", "combine")  # stage order
 
 
 def parse():
@@ -176,68 +176,67 @@ def main():
     ids = torch.empty(T, k, dtype=i32, device=dev)
     w = torch.empty(T, k, dtype=f32, device=dev)
     counts = torch.empty(E, dtype=i32, device=dev)
-    offsets = torch.empty(E + 1, dtype=i32, device=dev)
-    sorted_token = torch.empty(N, dtype=i32, device=dev)
-    sorted_slot = torch.empty(N, dtype=i32, device=dev)
-    slot_pos = torch.empty(N, dtype=i32, device=dev)
-    h = torch.empty(N, I, dtype=wl.dtype, device=dev)
-    y = torch.empty(N, H, dtype=wl.dtype, device=dev)
     out = torch.empty(T, H, dtype=wl.dtype, device=dev)
     L = moe.lib
 
-    def ws(op):
-        n = L.moe_workspace_size(op, T, H, I, E, k, 0, N, dt)
-        return torch.empty(max(n, 1), dtype=torch.uint8, device=dev), n
-
-    ws_perm, nperm = ws(_lib.MOE_OP_PERMUTE)
-    ws_up, nup = ws(_lib.MOE_OP_GATE_UP)
-    ws_dn, ndn = ws(_lib.MOE_OP_DOWN)
+    nws = L.moe_workspace_size(_lib.MOE_OP_LAYER, T, H, I, E, k, 0, N, dt)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     s = torch.cuda.current_stream(dev)
     sp = s.cuda_stream
     P = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
 
-    calls = [
-        lambda: L.moe_route(P(x), P(wr), P(bias), T, H, E, k, int(wl.norm_topk_prob), dt,
-                            P(logits), P(ids), P(w), None, sp),
-        lambda: L.moe_permute(P(ids), T, k, None, 0, N, E, P(counts), P(offsets),
-                              P(sorted_token), P(sorted_slot), P(slot_pos), P(ws_perm), nperm,
-                              sp),
-        lambda: L.moe_grouped_gate_up_swiglu(P(x), T, P(sorted_token), P(offsets), N, H, I, E,
-                                             P(gu), dt, P(h), P(ws_up), nup, sp),
-        lambda: L.moe_grouped_down(P(h), P(offsets), P(sorted_slot), N, H, I, E, P(dn), dt,
-                                   P(y), P(ws_dn), ndn, sp),
-        lambda: L.moe_combine(P(y), None, P(w), T, k, H, dt, P(out), sp),
-    ]
+    # HIP events for the per-stage split, recorded by the library between its
+    # kernels on the same stream (the layer is launched exactly as users do)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    nst = len(KERNELS) + 1
+
+    def new_event():
+        ev = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
 
     def step(evs=None):
-        for i, c in enumerate(calls):
-            if evs is not None:
-                evs[i].record(s)
-            st = c()
-            if st != 0:
-                raise RuntimeError(f"{KERNELS[i]} failed with status {st}")
-        if evs is not None:
-            evs[len(calls)].record(s)
+        st = L.moe_layer_forward(P(x), P(wr), P(bias), P(gu), P(dn), T, H, I, E, k,
+                                 int(wl.norm_topk_prob), dt, P(out), P(logits), P(ids), P(w),
+                                 P(counts), P(ws), nws, evs, sp)
+        if st != 0:
+            raise RuntimeError(f"moe_layer_forward failed with status {st}")
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-          for _ in range(args.steps)]
+    ev_arrays = []
+    for _ in range(args.steps):
+        arr = (ctypes.c_void_p * nst)(*[new_event() for _ in range(nst)])
+        ev_arrays.append(arr)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(s)
     for i in range(args.steps):
-        step(ev[i])
+        step(ev_arrays[i])
     end.record(s)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    per_kernel_ms = {KERNELS[j]: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1])
-                                                for i in range(args.steps)]))
-                     for j in range(len(calls))}
+    per_kernel_ms = {}
+    f = ctypes.c_float()
+    for j, kname in enumerate(KERNELS):
+        acc = []
+        for arr in ev_arrays:
+            if hip.hipEventElapsedTime(ctypes.byref(f), arr[j], arr[j + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            acc.append(f.value)
+        per_kernel_ms[kname] = float(np.mean(acc))
+    for arr in ev_arrays:
+        for j in range(nst):
+            hip.hipEventDestroy(arr[j])
 
     c_np = counts.cpu().numpy()
     flops, bytes_, hit = algorithmic(wl, c_np)

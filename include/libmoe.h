@@ -221,10 +221,14 @@ int moe_combine(const void* y, const int32_t* slot_pos,
  * choice), the two grouped GEMMs (rows gathered on load, outputs stored in
  * flat-slot order) and moe_combine.  Qwen3-Omni issue #115,
  * SpeedupMoeSparseMoeBlock.forward returns (out, router_logits).
- * out [T, H] dt; router_logits [T, E] float32 or NULL; topk_ids [T, k] int32,
+ * out [T, H] dt; router_logits [T, E] float32, topk_ids [T, k] int32,
  * topk_weights [T, k] float32 and num_tokens_per_expert [E] int32 are written
- * (the latter two may be NULL).  Workspace:
+ * when non-NULL (the workspace holds them otherwise).  Workspace:
  * moe_workspace_size(MOE_OP_LAYER, ...).
+ * stage_events: NULL, or an array of 6 caller-created HIP events recorded on
+ * `stream` before the router, the permutation, the first GEMM, the second
+ * GEMM and the combine, and after the combine (for per-stage timing; NULL
+ * entries are skipped).  The library neither creates nor destroys them.
  */
 int moe_layer_forward(const void* hidden_states, const void* router_weight,
                       const float* router_bias, const void* gate_up,
@@ -233,7 +237,7 @@ int moe_layer_forward(const void* hidden_states, const void* router_weight,
                       float* router_logits, int32_t* topk_ids,
                       float* topk_weights, int32_t* num_tokens_per_expert,
                       void* workspace, size_t workspace_bytes,
-                      hipStream_t stream);
+                      hipEvent_t* stage_events, hipStream_t stream);
 
 #ifdef __cplusplus
 }

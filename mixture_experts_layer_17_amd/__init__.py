@@ -259,5 +259,5 @@ def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.T
           _chk(router_bias, "router_bias"), gate_up.data_ptr(), down.data_ptr(), T, H, I, E,
           top_k, int(norm_topk_prob), _dt(x), b.out.data_ptr(), b.logits.data_ptr(),
           b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(), b.workspace.data_ptr(),
-          b.ws_bytes, _stream(x.device))
+          b.ws_bytes, None, _stream(x.device))
     return b.out, b.logits, b.ids, b.weights, b.counts

@@ -42,7 +42,7 @@ SIGNATURES = {
     "moe_grouped_swiglu": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]),
     "moe_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p]),
     "moe_layer_forward": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
-                               _p, _p, _sz, _p]),
+                               _p, _p, _sz, _p, _p]),
 }
 
 

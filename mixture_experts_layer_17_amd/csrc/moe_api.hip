@@ -191,7 +191,7 @@ int moe_grouped_gate_up_swiglu(const void* x, int x_rows, const int32_t* row_ind
   const GemmTileCfg c = pick_gate_up_cfg(bf16, N, H, I, E);
   if (!ws || ws_bytes < tile_list_bytes(N, E, c.BM)) return MOE_ERR_WORKSPACE;
   return hip_status(launch_gate_up(bf16, c, x, x_rows, row_index, offsets, N, H, I, E, gate_up,
-                                   h, ws, s));
+                                   h, ws, false, s));
 }
 
 int moe_grouped_down(const void* h, const int32_t* offsets, const int32_t* out_index, int N,
@@ -205,7 +205,7 @@ int moe_grouped_down(const void* h, const int32_t* offsets, const int32_t* out_i
   const bool bf16 = dt == MOE_BF16;
   const GemmTileCfg c = pick_down_cfg(bf16, N, H, I, E);
   if (!ws || ws_bytes < tile_list_bytes(N, E, c.BM)) return MOE_ERR_WORKSPACE;
-  return hip_status(launch_down(bf16, c, h, offsets, out_index, N, H, I, E, down, y, ws, s));
+  return hip_status(launch_down(bf16, c, h, offsets, out_index, N, H, I, E, down, y, ws, false, s));
 }
 
 int moe_grouped_swiglu(const void* x, int x_rows, const int32_t* row_index,
@@ -229,10 +229,10 @@ int moe_grouped_swiglu(const void* x, int x_rows, const int32_t* row_index,
   const GemmTileCfg cu = pick_gate_up_cfg(bf16, N, H, I, E);
   const GemmTileCfg cd = pick_down_cfg(bf16, N, H, I, E);
   hipError_t e = launch_gate_up(bf16, cu, x, x_rows, row_index, offsets, N, H, I, E, gate_up, h,
-                                base + hb, s);
+                                base + hb, false, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(launch_down(bf16, cd, h, offsets, out_index, N, H, I, E, down, y,
-                                base + hb + ub, s));
+                                base + hb + ub, false, s));
 }
 
 int moe_combine(const void* y, const int32_t* slot_pos, const float* w, int T, int k, int H,
@@ -249,7 +249,8 @@ int moe_combine(const void* y, const int32_t* slot_pos, const float* w, int T, i
 int moe_layer_forward(const void* x, const void* wr, const float* bias, const void* gate_up,
                       const void* down, int T, int H, int I, int E, int k, int norm,
                       moe_dtype dt, void* out, float* logits, int32_t* ids, float* weights,
-                      int32_t* counts, void* ws, size_t ws_bytes, hipStream_t s) {
+                      int32_t* counts, void* ws, size_t ws_bytes, hipEvent_t* stage_events,
+                      hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
     return MOE_ERR_SHAPE;
@@ -265,24 +266,38 @@ int moe_layer_forward(const void* x, const void* wr, const float* bias, const vo
   if (!counts) counts = w.counts;
   const bool bf16 = dt == MOE_BF16;
   const int N = T * k;
+  auto mark = [&](int i) {
+    if (stage_events && stage_events[i]) (void)hipEventRecord(stage_events[i], s);
+  };
+  mark(0);
   // the histogram comes from the permutation pass, so the router skips it
   hipError_t e = launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_permute_topk(ids, T, k, E, counts, w.offsets, w.sorted_token, w.sorted_slot,
-                          w.slot_pos, w.perm, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  if (N == 0) return MOE_OK;
+  mark(1);
   const GemmTileCfg cu = pick_gate_up_cfg(bf16, N, H, I, E);
   const GemmTileCfg cd = pick_down_cfg(bf16, N, H, I, E);
-  e = launch_gate_up(bf16, cu, x, T, w.sorted_token, w.offsets, N, H, I, E, gate_up, w.h,
-                     w.tiles_up, s);
+  // the permutation's scan pass also writes both GEMMs' tile lists
+  e = launch_permute_topk(ids, T, k, E, counts, w.offsets, w.sorted_token, w.sorted_slot,
+                          w.slot_pos, w.perm, s, w.tiles_up, cu.BM, w.tiles_down, cd.BM);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(2);
+  if (N > 0) {
+    e = launch_gate_up(bf16, cu, x, T, w.sorted_token, w.offsets, N, H, I, E, gate_up, w.h,
+                       w.tiles_up, true, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  mark(3);
   // outputs land in flat-slot order (row t * k + j), so the combine reads each
   // token's k rows contiguously.
-  e = launch_down(bf16, cd, w.h, w.offsets, w.sorted_slot, N, H, I, E, down, w.y, w.tiles_down,
-                  s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_combine(bf16, w.y, nullptr, weights, T, k, H, out, s));
+  if (N > 0) {
+    e = launch_down(bf16, cd, w.h, w.offsets, w.sorted_slot, N, H, I, E, down, w.y,
+                    w.tiles_down, true, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  mark(4);
+  e = launch_combine(bf16, w.y, nullptr, weights, T, k, H, out, s);
+  mark(5);
+  return hip_status(e);
 }
 
 }  // extern "C"

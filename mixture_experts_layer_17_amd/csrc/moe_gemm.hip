@@ -31,6 +31,7 @@
 //     have the same lane layout, so silu(g) * u is formed in registers.
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "moe_tiles.h"
 
 namespace moe {
 namespace {
@@ -39,8 +40,7 @@ constexpr int NUM_XCD = 8;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Builds the M-tile list from expert offsets (one workgroup, E <= 256).
-// tiles[t] = {expert, first row, rows, 0}; tiles_count[0] = number of tiles.
+// One block builds the M-tile list from the expert offsets.
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                           int E, int N, int BM,
                                                           int4* __restrict__ tiles,
@@ -48,28 +48,12 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
   __shared__ int s_nt[256];
   __shared__ int s_start[257];
   const int e = threadIdx.x;
-  int lo = 0, hi = 0, nt = 0;
+  int lo = 0, hi = 0;
   if (e < E) {
     lo = min(max(offsets[e], 0), N);
     hi = min(max(offsets[e + 1], lo), N);
-    nt = (hi - lo + BM - 1) / BM;
   }
-  s_nt[e] = nt;
-  __syncthreads();
-  if (e == 0) {
-    int acc = 0;
-    for (int x = 0; x < E; ++x) { s_start[x] = acc; acc += s_nt[x]; }
-    s_start[E] = acc;
-    tiles_count[0] = acc;
-  }
-  __syncthreads();
-  if (e < E) {
-    const int t0 = s_start[e];
-    for (int t = 0; t < nt; ++t) {
-      const int r0 = lo + t * BM;
-      tiles[t0 + t] = make_int4(e, r0, min(BM, hi - r0), 0);
-    }
-  }
+  build_tile_list(E, lo, hi, BM, tiles, tiles_count, s_nt, s_start);
 }
 
 // Bytes of 16-byte slots per LDS row: BK elements.
@@ -394,6 +378,13 @@ int grid_for(int N, int E, int BM, int n_ntiles) {
 
 }  // namespace
 
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int N, int BM, void* tile_ws,
+                              hipStream_t s) {
+  build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, BM, (int4*)((char*)tile_ws + 256),
+                                       (int32_t*)tile_ws);
+  return hipGetLastError();
+}
+
 size_t tile_list_bytes(int N, int E, int BM) {
   const size_t max_tiles = (size_t)N / BM + (size_t)E + 1;
   return 256 + ((max_tiles * sizeof(int4) + 255) & ~(size_t)255);
@@ -419,14 +410,16 @@ GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E) {
 
 hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_rows,
                           const int32_t* row_index, const int32_t* offsets, int N, int H, int I,
-                          int E, const void* gate_up, void* h, void* tile_ws, hipStream_t s) {
+                          int E, const void* gate_up, void* h, void* tile_ws, bool tiles_ready,
+                          hipStream_t s) {
   if (N <= 0) return hipSuccess;
   if (lds_cfg_id(c.id))
     return launch_lds_gemm(true, c, x, H, row_index, x_rows, gate_up, (long long)H * 2 * I, 2 * I,
-                           H, I, h, I, nullptr, N, offsets, N, E, I / (c.BN / 2), tile_ws, s);
+                           H, I, h, I, nullptr, N, offsets, N, E, I / (c.BN / 2), tile_ws,
+                           tiles_ready, s);
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
-  build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);
+  if (!tiles_ready) build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);
   const int n_ntiles = I / (c.BN / 2);
   const int grid = grid_for(N, E, c.BM, n_ntiles);
   (void)bf16;
@@ -436,14 +429,14 @@ hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_
 
 hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h, const int32_t* offsets,
                        const int32_t* out_index, int N, int H, int I, int E, const void* down,
-                       void* y, void* tile_ws, hipStream_t s) {
+                       void* y, void* tile_ws, bool tiles_ready, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   if (lds_cfg_id(c.id))
     return launch_lds_gemm(false, c, h, I, nullptr, N, down, (long long)I * H, H, I, 0, y, H,
-                           out_index, N, offsets, N, E, H / c.BN, tile_ws, s);
+                           out_index, N, offsets, N, E, H / c.BN, tile_ws, tiles_ready, s);
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
-  build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);
+  if (!tiles_ready) build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);
   const int n_ntiles = H / c.BN;
   const int grid = grid_for(N, E, c.BM, n_ntiles);
   (void)bf16;

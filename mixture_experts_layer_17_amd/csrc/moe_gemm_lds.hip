@@ -39,6 +39,7 @@ constexpr int NUM_XCD = 8;
 constexpr int BK = 32;   // k per stage
 
 typedef short i16x4_v __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_v;
 typedef __attribute__((address_space(3))) i16x4_v lds_i16x4;
 
 __device__ __forceinline__ int fswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
@@ -75,11 +76,11 @@ template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU>
 struct lcfg {
   static constexpr int NW = WM * WN;
   static constexpr int THREADS = NW * 64;
-  static constexpr int MT = BM / 16;                 // m-tiles per workgroup tile
+  static constexpr int MT = BM / 32;                 // 32-row m-tiles per workgroup tile
   static constexpr int TM = MT / WM;                 // m-tiles per wave
   static constexpr int CW = SWIGLU ? (BN / 2) / WN : BN / WN;  // output cols per wave
-  static constexpr int TNO = CW / 16;
-  static constexpr int TN = SWIGLU ? 2 * TNO : TNO;
+  static constexpr int TNO = CW / 32;                // 32-col output tiles per wave
+  static constexpr int TN = SWIGLU ? 2 * TNO : TNO;  // weight tiles per wave
   static constexpr int A_BYTES = BM * BK * 2;        // per stage
   static constexpr int B_BYTES = BK * BN * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -90,8 +91,8 @@ struct lcfg {
   static constexpr int B_PER = B_INST / NW;
   static constexpr int ROWB = BN * 2;                // bytes per weight row in LDS
   static constexpr int SEGS = BN / 16;               // 32-byte segments per weight row
-  static_assert(MT % WM == 0 && TM >= 1, "m-tiles per wave");
-  static_assert(CW % 16 == 0 && TNO >= 1, "n-tiles per wave");
+  static_assert(BM % 32 == 0 && MT % WM == 0 && TM >= 1, "m-tiles per wave");
+  static_assert(CW % 32 == 0 && TNO >= 1, "n-tiles per wave");
   static_assert(B_INST % NW == 0, "weight loads split evenly");
   static_assert(SEGS >= 8, "swizzle needs 8 segments per row");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -104,14 +105,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     bf16_t* __restrict__ C, int ldc, const int32_t* __restrict__ c_index, int c_rows,
     const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count, int n_ntiles) {
   using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU>;
-  static_assert(STAGES == 4, "the main loop is unrolled over four stage buffers");
-  // One array per stage: the compiler can then tell which buffer an
-  // asynchronous load writes and which one a read uses, and does not wait
-  // for every load in flight before each LDS read.
-  __shared__ __align__(16) unsigned char st0[G::STAGE_BYTES];
-  __shared__ __align__(16) unsigned char st1[G::STAGE_BYTES];
-  __shared__ __align__(16) unsigned char st2[G::STAGE_BYTES];
-  __shared__ __align__(16) unsigned char st3[G::STAGE_BYTES];
+  static_assert(STAGES >= 2, "at least double buffering");
+  // STAGES ring slots of STAGE_BYTES.  The copies are invisible to the
+  // compiler (asm), so it inserts no waits for them; the explicit vmcnt
+  // waits plus the barrier order each slot's fill before its reads, and the
+  // asm memory clobbers keep the compiler from moving LDS reads across them.
+  extern __shared__ __align__(16) unsigned char smem[];
 
   // ---- job (M-tile, N-tile), XCD-aware: consecutive jobs share an XCD
   const int jobs = tiles_count[0] * n_ntiles;
@@ -183,169 +182,159 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     }
   };
 
-  // ---- per-lane LDS read offsets (bytes within a stage)
-  int xa_off[G::TM];
+  // ---- per-lane LDS read offsets (bytes within a stage) for the 32x32x16
+  // MFMA operands.  Activations ("B" operand): lane l needs row
+  // 32 * mtile + l % 32, k = 8 (l / 32) .. + 7 of the k-step, i.e. chunk
+  // 2 kk + l / 32 of the row.  Weights ("A" operand): lane l needs column
+  // n = l % 32 of the tile and the same k values; 16-lane group q reads
+  // columns 16 (q & 1) .. + 15 and k 8 (q >> 1) .. + 7 with two transposing
+  // reads of 4 rows each.
+  const int l32 = lane & 31, hl = lane >> 5;
+  int xa_off[G::TM][2];
 #pragma unroll
   for (int i = 0; i < G::TM; ++i) {
-    const int row = 16 * (wm + WM * i) + r16;
-    xa_off[i] = row * 64 + 16 * (g ^ fswz(row));
+    const int row = 32 * (wm + WM * i) + l32;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) xa_off[i][kk] = row * 64 + 16 * ((2 * kk + hl) ^ fswz(row));
   }
   // this wave's m-tiles wm, wm + WM, ... that hold rows (wave-uniform)
   const int tm_on = __builtin_amdgcn_readfirstlane(
-      min(G::TM, max(0, ((rows + 15) / 16 - wm + WM - 1) / WM)));
-  int wb_off[G::TN][2];
+      min(G::TM, max(0, ((rows + 31) / 32 - wm + WM - 1) / WM)));
+  const int gq = lane >> 4, s16 = lane & 15;
+  int wb_off[G::TN][2][2];   // [tile][k-step][half]
 #pragma unroll
   for (int j = 0; j < G::TN; ++j) {
-    int cb;  // logical column base of this 16-column tile
+    int cb;  // logical column base of this 32-column tile
     if constexpr (SWIGLU)
-      cb = j < G::TNO ? wn * G::CW + 16 * j : BN / 2 + wn * G::CW + 16 * (j - G::TNO);
+      cb = j < G::TNO ? wn * G::CW + 32 * j : BN / 2 + wn * G::CW + 32 * (j - G::TNO);
     else
-      cb = wn * G::CW + 16 * j;
+      cb = wn * G::CW + 32 * j;
+    const int col = cb + 16 * (gq & 1) + 4 * (s16 & 3);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int row = 8 * g + 4 * hf + (r16 >> 2);
-      wb_off[j][hf] = G::A_BYTES + row * G::ROWB + 32 * ((cb >> 4) ^ hswz(row)) + 8 * (r16 & 3);
-    }
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = 16 * kk + 8 * (gq >> 1) + 4 * hf + (s16 >> 2);
+        wb_off[j][kk][hf] =
+            G::A_BYTES + row * G::ROWB + 32 * ((col >> 4) ^ hswz(row)) + 2 * (col & 15);
+      }
   }
 
-  f32x4_v acc[G::TM][G::TN];
+  f32x16_v acc[G::TM][G::TN];
 #pragma unroll
   for (int i = 0; i < G::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // All fragment reads of a k-step are issued before its MFMAs (rows past
+  // the tile's end read in-bounds stale LDS and are never stored); only the
+  // MFMAs of m-tiles without rows are skipped, on a wave-uniform condition.
+  auto compute = [&](const unsigned char* base) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_v wf[G::TN];
+      bf16x8_v xf[G::TM];
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) {
+        const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(base + wb_off[j][kk][0]));
+        const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(base + wb_off[j][kk][1]));
+        wf[j] = __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+        xf[i] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(base + xa_off[i][kk]));
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i) {
+        if (i < tm_on) {
+#pragma unroll
+          for (int j = 0; j < G::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
 
   const int KT = K / BK;
   constexpr int PER_STAGE_MAX = G::A_PER + G::B_PER;
   const bool a_full = (G::A_INST % G::NW == 0) || (wave < G::A_INST % G::NW);
 
-  auto compute = [&](const unsigned char* base) {
-    chunk8<bf16_t> wf[G::TN];
-#pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(base + wb_off[j][0]));
-      const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(base + wb_off[j][1]));
-      wf[j].v = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int i = 0; i < G::TM; ++i) {
-      if (i < tm_on) {
-        chunk8<bf16_t> xf;
-        xf.v = *reinterpret_cast<const u32x4*>(base + xa_off[i]);
-#pragma unroll
-        for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma_16x16x32(wf[j], xf, acc[i][j]);
-      }
-    }
-  };
-
   // prologue: STAGES - 1 blocks in flight
-  if (0 < KT) issue(st0);
-  if (1 < KT) issue(st1);
-  if (2 < KT) issue(st2);
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < KT) issue(smem + p * G::STAGE_BYTES);
 
-  // Step for K-block kb held in CUR: wait for it (later blocks stay in
-  // flight), barrier, refill NXT (the buffer every wave finished reading in
-  // the previous step), then compute.
-#define MOE_STEP(CUR, NXT, S)                                                        \
-  {                                                                                 \
-    const int kb = kt + (S);                                                        \
-    if (kb < KT) {                                                                  \
-      if (KT - 1 - kb >= STAGES - 2) {                                              \
-        if (a_full) wait_vmcnt<(STAGES - 2) * PER_STAGE_MAX>();                     \
-        else wait_vmcnt<(STAGES - 2) * (PER_STAGE_MAX - 1)>();                      \
-      } else {                                                                      \
-        wait_vmcnt<0>();                                                            \
-      }                                                                             \
-      __builtin_amdgcn_s_barrier();                                                 \
-      asm volatile("" ::: "memory");                                                \
-      if (kb + STAGES - 1 < KT) issue(NXT);                                         \
-      compute(CUR);                                                                 \
-    }                                                                               \
+  // Step for K-block kb: wait for it (later blocks stay in flight), barrier,
+  // refill the slot every wave finished reading in the previous step, compute.
+  int slot = 0;                       // kb % STAGES
+  int fill = STAGES - 1;              // (kb + STAGES - 1) % STAGES
+  for (int kb = 0; kb < KT; ++kb) {
+    if (KT - 1 - kb >= STAGES - 2) {
+      if (a_full) wait_vmcnt<(STAGES - 2) * PER_STAGE_MAX>();
+      else wait_vmcnt<(STAGES - 2) * (PER_STAGE_MAX - 1)>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kb + STAGES - 1 < KT) issue(smem + fill * G::STAGE_BYTES);
+    compute(smem + slot * G::STAGE_BYTES);
+    slot = (slot + 1 == STAGES) ? 0 : slot + 1;
+    fill = (fill + 1 == STAGES) ? 0 : fill + 1;
   }
-  for (int kt = 0; kt < KT; kt += STAGES) {
-    MOE_STEP(st0, st3, 0)
-    MOE_STEP(st1, st0, 1)
-    MOE_STEP(st2, st1, 2)
-    MOE_STEP(st3, st2, 3)
-  }
-#undef MOE_STEP
 
-  // ---- epilogue: acc[i][j][q] = C[row m][col cb_j + 4 g + q]
+  // ---- epilogue.  acc[i][j][q] = C[row m][col cb_j + 8 (q / 4) + 4 hl + q % 4]
+  // with m = 32 * mtile + l % 32.  Each wave stages one 32-row m-tile of its
+  // output (32 x CW bf16) in a private LDS area, then writes whole row
+  // segments of 2 * CW bytes with 16-byte stores.
+  constexpr int OB = G::CW * 2;              // bytes per staged output row
+  constexpr int LPR = OB / 16;               // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;              // rows per store instruction
+  static_assert(32 * OB * G::NW <= G::LDS, "output staging fits in the ring");
+  __builtin_amdgcn_s_barrier();              // every wave is done with the ring
+  asm volatile("" ::: "memory");
+  unsigned char* stg = smem + wave * 32 * OB;
 #pragma unroll
   for (int i = 0; i < G::TM; ++i) {
-    const int m = 16 * (wm + WM * i) + r16;
-    if (i >= tm_on || m >= rows) continue;
-    const int p = row0 + m;
-    if constexpr (SWIGLU) {
-      bf16_t* crow = C + (long long)p * ldc + n0 + wn * G::CW + 4 * g;
+    if (i >= tm_on) continue;
 #pragma unroll
-      for (int j = 0; j < G::TNO; ++j) {
-        uint32_t d[2];
+    for (int j = 0; j < G::TNO; ++j)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float h0 = silu_f32(acc[i][j][2 * q]) * acc[i][G::TNO + j][2 * q];
-          const float h1 = silu_f32(acc[i][j][2 * q + 1]) * acc[i][G::TNO + j][2 * q + 1];
-          d[q] = (uint32_t)f32_to_bf16_bits(h0) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
+      for (int a = 0; a < 4; ++a) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float g = acc[i][j][4 * a + q];
+          if constexpr (SWIGLU) {
+            // silu(g) * u in float32; rounded to bf16 on store
+            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+            v[q] = sg * acc[i][G::TNO + j][4 * a + q];
+          } else {
+            v[q] = g;
+          }
         }
-        *reinterpret_cast<uint2*>(crow + 16 * j) = make_uint2(d[0], d[1]);
+        const uint32_t d0 = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        const uint32_t d1 = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2*>(stg + l32 * OB + 2 * (32 * j + 8 * a + 4 * hl)) = make_uint2(d0, d1);
       }
-    } else {
-      const int dst = c_index ? c_index[p] : p;
-      if (dst < 0 || dst >= c_rows) continue;
-      bf16_t* crow = C + (long long)dst * ldc + n0 + wn * G::CW + 4 * g;
+    // LDS writes above and reads below are this wave's own: program order
+    // plus the compiler's lgkmcnt waits order them.
+    const int mrow0 = 32 * (wm + WM * i);
 #pragma unroll
-      for (int j = 0; j < G::TNO; ++j) {
-        const uint32_t d0 = (uint32_t)f32_to_bf16_bits(acc[i][j][0]) |
-                            ((uint32_t)f32_to_bf16_bits(acc[i][j][1]) << 16);
-        const uint32_t d1 = (uint32_t)f32_to_bf16_bits(acc[i][j][2]) |
-                            ((uint32_t)f32_to_bf16_bits(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(crow + 16 * j) = make_uint2(d0, d1);
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int r = r0 + lane / LPR;
+      const int m = mrow0 + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * OB + 16 * (lane % LPR));
+      if (m < rows) {
+        const int p = row0 + m;
+        int dst = p;
+        if constexpr (!SWIGLU) dst = c_index ? c_index[p] : p;
+        if (dst >= 0 && dst < c_rows)
+          *reinterpret_cast<u32x4*>(C + (long long)dst * ldc + n0 + wn * G::CW + 8 * (lane % LPR)) = v;
       }
-    }
-  }
-}
-
-// Tile list with even splits: an expert with c rows gets nt = ceil(c / BM)
-// tiles of ceil(c / nt) rows rounded up to 16 (the last one shorter).
-__global__ __launch_bounds__(256) void build_tiles_even_kernel(
-    const int32_t* __restrict__ offsets, int E, int N, int BM, int4* __restrict__ tiles,
-    int32_t* __restrict__ tiles_count) {
-  __shared__ int s_nt[256];
-  __shared__ int s_start[257];
-  const int e = threadIdx.x;
-  int lo = 0, hi = 0, nt = 0;
-  if (e < E) {
-    lo = min(max(offsets[e], 0), N);
-    hi = min(max(offsets[e + 1], lo), N);
-    nt = (hi - lo + BM - 1) / BM;
-  }
-  s_nt[e] = nt;
-  __syncthreads();
-  // exclusive scan over 256 entries by wave 0 (4 values per lane)
-  if (e < 64) {
-    int v[4], sum = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { v[q] = s_nt[4 * e + q]; sum += v[q]; }
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (e >= off) incl += o;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { s_start[4 * e + q] = run; run += v[q]; }
-    if (e == 63) { s_start[256] = incl; tiles_count[0] = incl; }
-  }
-  __syncthreads();
-  if (e < E && nt > 0) {
-    const int c = hi - lo;
-    const int per = ((c + nt - 1) / nt + 15) & ~15;
-    const int t0 = s_start[e];
-    for (int t = 0; t < nt; ++t) {
-      const int r0 = lo + t * per;
-      tiles[t0 + t] = make_int4(e, r0, max(0, min(per, hi - r0)), 0);
     }
   }
 }
@@ -356,19 +345,26 @@ hipError_t launch_lds(const void* X, int ldx, const int32_t* x_index, int x_rows
                       const int32_t* c_index, int c_rows, const int4* tiles,
                       const int32_t* tiles_count, int n_ntiles, int grid, hipStream_t s) {
   using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU>), dim3(grid),
-                     dim3(G::THREADS), 0, s, (const bf16_t*)X, ldx, x_index, x_rows,
+                     dim3(G::THREADS), G::LDS, s, (const bf16_t*)X, ldx, x_index, x_rows,
                      (const bf16_t*)W, w_estride, ldw, K, up_off, (bf16_t*)C, ldc, c_index,
                      c_rows, tiles, tiles_count, n_ntiles);
   return hipGetLastError();
 }
 
 struct LdsCfg { int BM, BN; };
-// 10: 256 x 256, 4 x 2 waves (64 x 128 per wave)    large groups
-// 11: 128 x 256, 2 x 2 waves                          mid
-// 12:  64 x 256, 1 x 4 waves                          small groups
-// 13:  16 x 256, 1 x 4 waves                          decode
-constexpr LdsCfg kLds[] = {{256, 256}, {128, 256}, {64, 256}, {16, 256}};
+// id: tile, waves (M x N), wave tile
+// 10: 256 x 256, 2 x 2 waves, 128 x 128   (1 wave per SIMD)
+// 11: 128 x 256, 2 x 2 waves,  64 x 128
+// 12:  64 x 256, 1 x 4 waves,  64 x  64
+// 13:  32 x 256, 1 x 4 waves,  32 x  64   (decode)
+// 14: 320 x 256, 2 x 4 waves, 160 x  64   (2 waves per SIMD; one tile per
+//     expert when groups hold up to 320 rows)
+constexpr LdsCfg kLds[] = {{256, 256}, {128, 256}, {64, 256}, {32, 256}, {320, 256}};
 
 hipError_t launch_lds_cfg(bool swiglu, int id, const void* X, int ldx, const int32_t* x_index,
                           int x_rows, const void* W, long long w_estride, int ldw, int K,
@@ -382,10 +378,11 @@ hipError_t launch_lds_cfg(bool swiglu, int id, const void* X, int ldx, const int
     return swiglu ? launch_lds<BM, BN, WM, WN, ST, true>(MOE_ARGS)        \
                   : launch_lds<BM, BN, WM, WN, ST, false>(MOE_ARGS);
   switch (id) {
-    MOE_CASE(10, 256, 256, 4, 2, 4)
+    MOE_CASE(10, 256, 256, 2, 2, 4)
     MOE_CASE(11, 128, 256, 2, 2, 4)
     MOE_CASE(12, 64, 256, 1, 4, 4)
-    MOE_CASE(13, 16, 256, 1, 4, 4)
+    MOE_CASE(13, 32, 256, 1, 4, 4)
+    MOE_CASE(14, 320, 256, 2, 4, 3)
     default: return hipErrorInvalidValue;
   }
 #undef MOE_CASE
@@ -394,7 +391,7 @@ hipError_t launch_lds_cfg(bool swiglu, int id, const void* X, int ldx, const int
 
 }  // namespace
 
-bool lds_cfg_id(int id) { return id >= 10 && id <= 13; }
+bool lds_cfg_id(int id) { return id >= 10 && id <= 14; }
 
 GemmTileCfg pick_lds_cfg(int N, int E, int cols, bool swiglu) {
   // weight columns per tile: 256 (SwiGLU: 128 gate + 128 up)
@@ -402,7 +399,7 @@ GemmTileCfg pick_lds_cfg(int N, int E, int cols, bool swiglu) {
   if (cols % need != 0) return GemmTileCfg{0, 0, -1};
   const double mean_rows = E > 0 ? (double)N / E : 0.0;
   int id;
-  if (mean_rows >= 160.0) id = 10;
+  if (mean_rows >= 160.0) id = 14;
   else if (mean_rows >= 64.0) id = 11;
   else if (mean_rows >= 24.0) id = 12;
   else id = 13;
@@ -413,10 +410,13 @@ hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int
                            const int32_t* x_index, int x_rows, const void* W,
                            long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                            const int32_t* c_index, int c_rows, const int32_t* offsets, int N,
-                           int E, int n_ntiles, void* tile_ws, hipStream_t s) {
+                           int E, int n_ntiles, void* tile_ws, bool tiles_ready, hipStream_t s) {
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
-  build_tiles_even_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);
+  if (!tiles_ready) {
+    const hipError_t err = launch_build_tiles(offsets, E, N, c.BM, tile_ws, s);
+    if (err != hipSuccess) return err;
+  }
   const long long max_tiles = (long long)N / c.BM + std::min(E, N);
   long long jobs = max_tiles * n_ntiles;
   jobs = (jobs + NUM_XCD - 1) / NUM_XCD * NUM_XCD;

@@ -24,10 +24,13 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 
 // Token-choice permutation.  ws layout is given by permute_ws_bytes().
 size_t permute_ws_bytes(int N, int E, int R);
+// Optionally also writes the GEMMs' tile lists (tile_ws_a / tile_ws_b for
+// row-tile heights BM_a / BM_b; NULL to skip).
 hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E,
                                int32_t* counts, int32_t* offsets, int32_t* sorted_token,
                                int32_t* sorted_slot, int32_t* slot_pos, void* ws,
-                               hipStream_t s);
+                               hipStream_t s, void* tile_ws_a = nullptr, int BM_a = 0,
+                               void* tile_ws_b = nullptr, int BM_b = 0);
 hipError_t launch_permute_rank_major(const int32_t* counts_rm, int R, int N, int E,
                                      int32_t* counts, int32_t* offsets,
                                      int32_t* sorted_token, int32_t* sorted_slot,
@@ -47,17 +50,20 @@ hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int
                            const int32_t* x_index, int x_rows, const void* W,
                            long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                            const int32_t* c_index, int c_rows, const int32_t* offsets, int N,
-                           int E, int n_ntiles, void* tile_ws, hipStream_t s);
+                           int E, int n_ntiles, void* tile_ws, bool tiles_ready, hipStream_t s);
+// Builds the tile list of row-tile height BM into tile_ws (one block).
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int N, int BM, void* tile_ws,
+                              hipStream_t s);
 GemmTileCfg pick_gate_up_cfg(bool bf16, int N, int H, int I, int E);
 GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E);
 size_t tile_list_bytes(int N, int E, int BM);
 hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_rows,
                           const int32_t* row_index, const int32_t* offsets, int N, int H,
                           int I, int E, const void* gate_up, void* h, void* tile_ws,
-                          hipStream_t s);
+                          bool tiles_ready, hipStream_t s);
 hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h,
                        const int32_t* offsets, const int32_t* out_index, int N, int H,
                        int I, int E, const void* down, void* y, void* tile_ws,
-                       hipStream_t s);
+                       bool tiles_ready, hipStream_t s);
 
 }  // namespace moe

@@ -19,6 +19,7 @@
 //   3. scatter pass: position = chunk base[expert] + rank.
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "moe_tiles.h"
 
 namespace moe {
 namespace {
@@ -84,13 +85,20 @@ __global__ __launch_bounds__(256) void permute_chunk_kernel(
   }
 }
 
-// Pass 2: one workgroup of 1024 threads; thread (e, part) sums a quarter of
-// the chunks for expert e.
+// Pass 2: one workgroup.  Thread (e, part) of 1024 sums a quarter of the
+// chunks for expert e; the experts' totals are scanned by one wave; each
+// part then turns its chunk histograms into chunk bases.  Optionally the
+// first 256 threads also write the grouped GEMMs' tile lists.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
     int32_t* __restrict__ hist_base /*[nchunk][E] in: hist, out: base*/, int nchunk, int E,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+    int N, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int4* __restrict__ tiles_a, int32_t* __restrict__ count_a, int BM_a,
+    int4* __restrict__ tiles_b, int32_t* __restrict__ count_b, int BM_b) {
   __shared__ int s_part[4][PM_MAXE];
+  __shared__ int s_tot[PM_MAXE];
   __shared__ int s_off[PM_MAXE + 1];
+  __shared__ int s_nt[PM_MAXE];
+  __shared__ int s_start[PM_MAXE + 1];
   const int e = threadIdx.x & (PM_MAXE - 1);
   const int part = threadIdx.x >> 8;
   const int per = (nchunk + 3) / 4;
@@ -100,15 +108,9 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
     for (int c = c0; c < c1; ++c) run += hist_base[(size_t)c * E + e];
   s_part[part][e] = run;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int x = 0; x < E; ++x) {
-      s_off[x] = acc;
-      acc += s_part[0][x] + s_part[1][x] + s_part[2][x] + s_part[3][x];
-    }
-    s_off[E] = acc;
-  }
+  if (part == 0) s_tot[e] = s_part[0][e] + s_part[1][e] + s_part[2][e] + s_part[3][e];
   __syncthreads();
+  block_scan256(s_tot, s_off);
   if (e < E) {
     int base = s_off[e];
     for (int p = 0; p < part; ++p) base += s_part[p][e];
@@ -118,11 +120,16 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
       base += v;
     }
     if (part == 0) {
-      counts[e] = s_part[0][e] + s_part[1][e] + s_part[2][e] + s_part[3][e];
+      counts[e] = s_tot[e];
       offsets[e] = s_off[e];
     }
   }
   if (threadIdx.x == 0) offsets[E] = s_off[E];
+  if (tiles_a == nullptr && tiles_b == nullptr) return;   // uniform over the block
+  __syncthreads();
+  const int lo = min(s_off[e], N), hi = min(s_off[e] + s_tot[e], N);
+  if (tiles_a) build_tile_list(E, lo, hi, BM_a, tiles_a, count_a, s_nt, s_start);
+  if (tiles_b) build_tile_list(E, lo, hi, BM_b, tiles_b, count_b, s_nt, s_start);
 }
 
 // Pass 3: scatter.
@@ -143,45 +150,47 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   slot_pos[i] = p;
 }
 
-// Rank-major mode, pass 1 (one workgroup): prefix tables of the count matrix.
+// Rank-major mode, pass 1 (one workgroup of 256 threads): prefix tables of
+// the count matrix.
 //   rm_start[r * E + e]: first received row of block (r, e) (rank-major order)
 //   em_start[r * E + e]: first expert-major position of block (r, e)
 __global__ __launch_bounds__(256) void rank_major_scan_kernel(
     const int32_t* __restrict__ C, int R, int E, int N, int32_t* __restrict__ rm_start,
     int32_t* __restrict__ em_start, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  __shared__ int s_cnt[PM_MAXE];
-  __shared__ int s_off[PM_MAXE + 1];
+  __shared__ int s_v[256];
+  __shared__ int s_x[257];
+  const int t = threadIdx.x;
   const int RE = R * E;
-  // rank-major prefix: serial over R*E (<= 4096) entries, small.
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < RE; ++i) {
-      rm_start[i] = acc;
-      acc += max(0, C[i]);
-    }
-  }
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int run = 0;
-    for (int r = 0; r < R; ++r) run += max(0, C[r * E + e]);
-    s_cnt[e] = run;
-  }
+  // rank-major prefix: thread t owns blocks [t * per, (t + 1) * per)
+  const int per = (RE + 255) / 256;
+  int sum = 0;
+  for (int i = t * per; i < min(RE, (t + 1) * per); ++i) sum += max(0, C[i]);
+  s_v[t] = sum;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) { s_off[e] = acc; acc += s_cnt[e]; }
-    s_off[E] = acc;
+  block_scan256(s_v, s_x);
+  int run = s_x[t];
+  for (int i = t * per; i < min(RE, (t + 1) * per); ++i) {
+    rm_start[i] = run;
+    run += max(0, C[i]);
   }
+  // expert totals and expert-major starts
+  int tot = 0;
+  if (t < E)
+    for (int r = 0; r < R; ++r) tot += max(0, C[r * E + t]);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int run = s_off[e];
+  s_v[t] = tot;
+  __syncthreads();
+  block_scan256(s_v, s_x);
+  if (t < E) {
+    int acc = s_x[t];
     for (int r = 0; r < R; ++r) {
-      em_start[r * E + e] = run;
-      run += max(0, C[r * E + e]);
+      em_start[r * E + t] = acc;
+      acc += max(0, C[r * E + t]);
     }
-    counts[e] = s_cnt[e];
-    offsets[e] = min(s_off[e], N);
+    counts[t] = tot;
+    offsets[t] = min(s_x[t], N);
   }
-  if (threadIdx.x == 0) offsets[E] = min(s_off[E], N);
+  if (t == 0) offsets[E] = min(s_x[256], N);
 }
 
 // Rank-major mode, pass 2: each received row finds its block by binary search
@@ -245,7 +254,8 @@ size_t permute_ws_bytes(int N, int E, int R) {
 
 hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E, int32_t* counts,
                                int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot,
-                               int32_t* slot_pos, void* ws, hipStream_t s) {
+                               int32_t* slot_pos, void* ws, hipStream_t s, void* tile_ws_a,
+                               int BM_a, void* tile_ws_b, int BM_b) {
   const int N = T * k;
   if (N <= 0) {
     hipError_t e = launch_fill_i32(counts, E, 0, s);
@@ -256,7 +266,10 @@ hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E, int32_t*
   int32_t* hist = (int32_t*)ws;
   int32_t* rank = (int32_t*)((char*)ws + align256((size_t)nchunk * E * sizeof(int32_t)));
   permute_chunk_kernel<<<nchunk, 256, 0, s>>>(ids, N, E, hist, rank);
-  permute_scan_kernel<<<1, 1024, 0, s>>>(hist, nchunk, E, counts, offsets);
+  auto tl = [](void* w) { return w ? (int4*)((char*)w + 256) : (int4*)nullptr; };
+  permute_scan_kernel<<<1, 1024, 0, s>>>(hist, nchunk, E, N, counts, offsets, tl(tile_ws_a),
+                                         (int32_t*)tile_ws_a, BM_a, tl(tile_ws_b),
+                                         (int32_t*)tile_ws_b, BM_b);
   permute_scatter_kernel<<<(N + 255) / 256, 256, 0, s>>>(ids, rank, hist, N, E, k, sorted_token,
                                                          sorted_slot, slot_pos);
   return hipGetLastError();

@@ -9,10 +9,13 @@
 // softmax is monotone so the selected set equals the set ranked by
 // probability, and the selection depends on the logits alone.
 //
-// Layout: one workgroup (4 waves) per 16 tokens.  Both operands are
+// Layout: one workgroup of 8 waves per 16 tokens.  Both operands are
 // K-contiguous (x is [T, H], Wr is [E, H]), so each lane loads its MFMA
-// operand chunk straight from global memory; no LDS staging is needed for
-// the GEMM.  Wave w owns the 16-expert column tiles w, w + 4, ...
+// operand chunk straight from global memory.  The waves split K: wave w
+// takes the 32-wide k-chunks w, w + 8, ... for all E experts, so every wave
+// has many independent loads in flight.  The 8 partial logit tiles are then
+// added in a fixed tree through LDS (deterministic), and each wave runs the
+// softmax / top-k epilogue for 2 tokens.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -21,7 +24,9 @@ namespace {
 
 constexpr int RT_TOK = 16;     // tokens per workgroup
 constexpr int RT_MAXE = 256;   // max experts
-constexpr int RT_NTW = 4;      // max 16-wide expert tiles per wave (256 / 16 / 4)
+constexpr int RT_NT = RT_MAXE / 16;
+constexpr int RT_WAVES = 8;
+constexpr int RT_LD = RT_MAXE + 4;   // LDS row stride (floats)
 
 // Larger logit first; equal logits (IEEE equality, so -0 == +0) go to the
 // lower expert id.
@@ -29,64 +34,96 @@ __device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb)
   return va > vb || (va == vb && ea < eb);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void route_kernel(
+template <typename T, int NT>
+__global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias,
     int T_, int H, int E, int k, int norm, float* __restrict__ logits_out,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ counts) {
-  __shared__ float s_logit[RT_TOK][RT_MAXE + 1];
+  // partial-sum buffers for the reduction tree; buffer 0 finally holds the
+  // logits of the 16 tokens
+  __shared__ float s_red[RT_WAVES / 2][RT_TOK][RT_LD];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * RT_TOK;
   const int g = lane >> 4;      // k-chunk group
   const int r = lane & 15;      // row (token) / column (expert) within a tile
-  const int NT = (E + 15) >> 4;
 
-  // ---- GEMM: acc[j] = logits tile (16 tokens x 16 experts), tile = wave + 4 j
-  f32x4_v acc[RT_NTW];
+  f32x4_v acc[NT];
 #pragma unroll
-  for (int j = 0; j < RT_NTW; ++j) acc[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
   const int tok = min(t0 + r, T_ - 1);
   const T* xrow = x + (size_t)tok * H + 8 * g;
-  const T* wrow[RT_NTW];
-  bool wvalid[RT_NTW];
+  // experts beyond E read row E - 1 (valid memory); their columns are never
+  // stored as logits, so no branch is needed around the loads
+  const T* wrow[NT];
 #pragma unroll
-  for (int j = 0; j < RT_NTW; ++j) {
-    const int e = (wave + 4 * j) * 16 + r;
-    wvalid[j] = (wave + 4 * j) < NT && e < E;
-    wrow[j] = wr + (size_t)(wvalid[j] ? e : 0) * H + 8 * g;
-  }
-  const bool wave_active = wave < NT;
+  for (int j = 0; j < NT; ++j) wrow[j] = wr + (size_t)min(j * 16 + r, E - 1) * H + 8 * g;
 
-  if (wave_active) {
-    for (int k0 = 0; k0 < H; k0 += 32) {
-      chunk8<T> a = load_chunk<T>(xrow + k0);
+  // wave w takes blocks of CPB consecutive 32-wide k-chunks: w, w + 8, ...;
+  // all loads of a block are issued before its MFMAs
+  constexpr int CPB = 4;
+  const int nchunk = H / 32;
+  const int nfull = nchunk / CPB;           // full blocks
+  for (int blk = wave; blk < nfull; blk += RT_WAVES) {
+    chunk8<T> a[CPB];
+    chunk8<T> b[CPB][NT];
 #pragma unroll
-      for (int j = 0; j < RT_NTW; ++j) {
-        if (wave + 4 * j < NT) {
-          chunk8<T> b = wvalid[j] ? load_chunk<T>(wrow[j] + k0) : zero_chunk<T>();
-          acc[j] = mfma_16x16x32(a, b, acc[j]);
-        }
-      }
+    for (int u = 0; u < CPB; ++u) {
+      const int k0 = 32 * (blk * CPB + u);
+      a[u] = load_chunk<T>(xrow + k0);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b[u][j] = load_chunk<T>(wrow[j] + k0);
     }
 #pragma unroll
-    for (int j = 0; j < RT_NTW; ++j) {
-      const int e = (wave + 4 * j) * 16 + r;
-      if (wave + 4 * j < NT && e < E) {
+    for (int u = 0; u < CPB; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = mfma_16x16x32(a[u], b[u][j], acc[j]);
+  }
+  // leftover chunks (H / 32 not a multiple of CPB)
+  for (int c = nfull * CPB + wave; c < nchunk; c += RT_WAVES) {
+    const int k0 = 32 * c;
+    const chunk8<T> a = load_chunk<T>(xrow + k0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = mfma_16x16x32(a, load_chunk<T>(wrow[j] + k0), acc[j]);
+  }
+
+  // ---- fixed-order tree: 8 -> 4 -> 2 -> 1 partial tiles
+#pragma unroll
+  for (int half = RT_WAVES / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_red[wave - half][4 * g + i][16 * j + r] = acc[j][i];
+    }
+    __syncthreads();
+    if (wave < half) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] += s_red[wave][4 * g + i][16 * j + r];
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int e = 16 * j + r;
+      if (e < E) {
         const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_logit[4 * g + i][e] = acc[j][i] + b;
+        for (int i = 0; i < 4; ++i) s_red[0][4 * g + i][e] = acc[j][i] + b;
       }
     }
   }
   __syncthreads();
 
-  // ---- Epilogue: wave w handles tokens 4w .. 4w + 3 of this workgroup.
-  for (int q = 0; q < 4; ++q) {
-    const int row = 4 * wave + q;
+  // ---- Epilogue: wave w handles tokens 2w, 2w + 1 of this workgroup.
+  for (int q = 0; q < RT_TOK / RT_WAVES; ++q) {
+    const int row = (RT_TOK / RT_WAVES) * wave + q;
     const int t = t0 + row;
     if (t >= T_) break;
     // lane owns experts lane, lane + 64, lane + 128, lane + 192
@@ -96,7 +133,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     for (int c = 0; c < 4; ++c) {
       const int e = lane + 64 * c;
       if (e < E) {
-        v[c] = s_logit[row][e];
+        v[c] = s_red[0][row][e];
         avail |= 1u << c;
         if (logits_out) logits_out[(size_t)t * E + e] = v[c];
       } else {
@@ -177,12 +214,24 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
   }
   if (T <= 0) return hipSuccess;
   const dim3 grid((T + RT_TOK - 1) / RT_TOK);
-  if (bf16)
-    route_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, (const bf16_t*)wr, bias, T, H,
-                                              E, k, norm, logits, ids, w, counts);
-  else
-    route_kernel<float><<<grid, 256, 0, s>>>((const float*)x, (const float*)wr, bias, T, H, E,
-                                             k, norm, logits, ids, w, counts);
+  const dim3 block(RT_WAVES * 64);
+  const int nt = (E + 15) / 16;
+#define MOE_ROUTE(NT)                                                                          \
+  do {                                                                                         \
+    if (bf16)                                                                                  \
+      route_kernel<bf16_t, NT><<<grid, block, 0, s>>>((const bf16_t*)x, (const bf16_t*)wr,     \
+                                                      bias, T, H, E, k, norm, logits, ids, w, \
+                                                      counts);                                 \
+    else                                                                                       \
+      route_kernel<float, NT><<<grid, block, 0, s>>>((const float*)x, (const float*)wr, bias,  \
+                                                     T, H, E, k, norm, logits, ids, w, counts);\
+  } while (0)
+  if (nt <= 1) MOE_ROUTE(1);
+  else if (nt <= 2) MOE_ROUTE(2);
+  else if (nt <= 4) MOE_ROUTE(4);
+  else if (nt <= 8) MOE_ROUTE(8);
+  else MOE_ROUTE(16);
+#undef MOE_ROUTE
   return hipGetLastError();
 }
 

@@ -286,9 +286,9 @@ def test_invalid_arguments_rejected(moe):
     assert L.moe_route(p + 2, p, None, 4, 128, 8, 2, 1, 1, None, p, p, None, s) == -7
     assert L.moe_route(None, p, None, 4, 128, 8, 2, 1, 1, None, p, p, None, s) == -1
     assert L.moe_layer_forward(p, p, None, p, p, 4, 100, 64, 8, 2, 1, 1, p, None, None, None,
-                               None, p, 1 << 20, s) == -2                               # H % 128
+                               None, p, 1 << 20, None, s) == -2                         # H % 128
     assert L.moe_layer_forward(p, p, None, p, p, 4, 128, 64, 8, 2, 1, 1, p, None, None, None,
-                               None, p, 16, s) == -4                                    # workspace
+                               None, p, 16, None, s) == -4                              # workspace
     assert L.moe_permute(None, 4, 2, None, 0, 8, 8, p, p, p, p, p, p, 1 << 20, s) == -1
     assert L.moe_permute(None, 0, 1, p, 1000, 8, 8, p, p, p, p, p, p, 1 << 20, s) == -2  # R*E
     torch.cuda.synchronize()

@@ -1,13 +1,13 @@
 // Grouped expert GEMMs for bf16 on gfx950: asynchronous global->LDS loads
 // into a multi-stage ring, transposing LDS reads for the weights, MFMA
-// 16x16x32 bf16 with float32 accumulation.
+// 32x32x16 bf16 with float32 accumulation.
 //
 // Semantics as the float path (moe_gemm.hip): Qwen3-Omni issue #115,
 // SpeedupMoeExperts.forward -- per expert e, gate_up = x_e @ gate_up_proj[e],
 // h = up * silu(gate), y_e = h @ down_proj[e]; MindSpore moe.py,
 // _run_experts_for_loop -- rows in expert-major order split by counts.
 //
-// Data path per K-block of 32:
+// Data path per K-block of 32 (two MFMA k-steps of 16):
 //   * activations: BM gathered rows x 64 bytes, loaded with
 //     global_load_lds_dwordx4 (lane i of a wave instruction lands at
 //     base + 16 i); each lane picks the global 16-byte chunk that belongs at
@@ -16,19 +16,21 @@
 //   * weights: 32 rows (k) x BN columns in their natural [k][n] layout
 //     (n contiguous), loaded the same way with 32-byte segments of a row
 //     XOR-swizzled by h(row) = (row & 3) | ((row >> 1) & 4).  The MFMA
-//     operand needs 8 consecutive k of one column per lane; ds_read_b64_tr_b16
-//     delivers that: within each 16-lane group, lane s reads 4 consecutive
-//     columns of row (kbase + s / 4) and lane j receives column j of rows
-//     kbase .. kbase + 3.
+//     operand needs 8 consecutive k of one column per lane; two
+//     ds_read_b64_tr_b16 deliver that: within each 16-lane group, lane s
+//     reads 4 consecutive columns of row (kbase + s / 4) and lane j receives
+//     column j of rows kbase .. kbase + 3.
 //   * MFMA operands are (weights, activations), so the accumulator tile is
-//     C^T: each lane holds 4 consecutive output columns of one row, stored
-//     with one 8-byte write.
-//   * STAGES K-blocks are in flight; a block's loads are issued STAGES - 1
-//     iterations before it is consumed, and one barrier per iteration both
-//     publishes the landed block and retires the slot being refilled.
-//   * m-tiles of 16 rows are dealt to the WM wave rows round-robin, so a
-//     ragged tile still splits its rows evenly; m-tiles beyond the tile's
-//     rows are skipped.
+//     C^T: each lane holds 4 consecutive output columns of one row.
+//   * Software pipeline: the LDS fragments of the next k-step are read while
+//     the MFMAs of the current one run, so LDS traffic hides under the
+//     matrix pipe.  One barrier per K-block, between its two k-steps, both
+//     publishes the next landed block and retires the block just read, whose
+//     slot is refilled right away; STAGES - 2 further blocks stay in flight.
+//   * 32-row m-tiles are dealt to the WM wave rows round-robin; m-tiles
+//     beyond the tile's rows skip their MFMAs.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -84,7 +86,11 @@ struct lcfg {
   static constexpr int A_BYTES = BM * BK * 2;        // per stage
   static constexpr int B_BYTES = BK * BN * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS = STAGES * STAGE_BYTES;
+  static constexpr int RING = STAGES * STAGE_BYTES;
+  // 1 KB that absorbs the surplus activation copies of waves with a short
+  // share, so every wave issues the same number of copies per block
+  static constexpr int DUMP = (BM * BK * 2 / 1024) % NW ? 1024 : 0;
+  static constexpr int LDS = RING + DUMP;
   static constexpr int A_INST = A_BYTES / 1024;      // wave instructions per stage
   static constexpr int B_INST = B_BYTES / 1024;
   static constexpr int A_PER = (A_INST + NW - 1) / NW;
@@ -172,7 +178,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   auto issue = [&](unsigned char* base) {
 #pragma unroll
     for (int u = 0; u < G::A_PER; ++u) {
-      if (a_on[u]) copy16_to_lds(a_src[u], base + a_lds[u]);
+      // a copy past the A block re-reads row chunk 0 into the dump area
+      copy16_to_lds(a_src[u], a_on[u] ? base + a_lds[u] : smem + G::RING);
       a_src[u] += BK;
     }
 #pragma unroll
@@ -185,23 +192,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   // ---- per-lane LDS read offsets (bytes within a stage) for the 32x32x16
   // MFMA operands.  Activations ("B" operand): lane l needs row
   // 32 * mtile + l % 32, k = 8 (l / 32) .. + 7 of the k-step, i.e. chunk
-  // 2 kk + l / 32 of the row.  Weights ("A" operand): lane l needs column
-  // n = l % 32 of the tile and the same k values; 16-lane group q reads
-  // columns 16 (q & 1) .. + 15 and k 8 (q >> 1) .. + 7 with two transposing
-  // reads of 4 rows each.
+  // 2 kk + l / 32 of the row; the row swizzle f depends only on l % 32
+  // because m-tiles start at multiples of 32, so m-tiles differ by a
+  // constant offset.  Weights ("A" operand): lane l needs column n = l % 32
+  // of the tile and the same k values; 16-lane group q reads columns
+  // 16 (q & 1) .. + 15 and k 8 (q >> 1) .. + 7 with two transposing reads of
+  // 4 rows each.  Those rows are 16 kk + 8 (q >> 1) + 4 hf + s / 4, whose
+  // swizzle h = s / 4 | (q >> 1) << 2 does not depend on kk or hf, so kk and
+  // hf are constant offsets too.
   const int l32 = lane & 31, hl = lane >> 5;
-  int xa_off[G::TM][2];
+  constexpr int XI = 32 * WM * 64;                 // bytes between a wave's m-tiles
+  int xa_off[2];
 #pragma unroll
-  for (int i = 0; i < G::TM; ++i) {
-    const int row = 32 * (wm + WM * i) + l32;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) xa_off[i][kk] = row * 64 + 16 * ((2 * kk + hl) ^ fswz(row));
-  }
+  for (int kk = 0; kk < 2; ++kk)
+    xa_off[kk] = (32 * wm + l32) * 64 + 16 * ((2 * kk + hl) ^ fswz(l32));
   // this wave's m-tiles wm, wm + WM, ... that hold rows (wave-uniform)
   const int tm_on = __builtin_amdgcn_readfirstlane(
       min(G::TM, max(0, ((rows + 31) / 32 - wm + WM - 1) / WM)));
   const int gq = lane >> 4, s16 = lane & 15;
-  int wb_off[G::TN][2][2];   // [tile][k-step][half]
+  const int wrow = 8 * (gq >> 1) + (s16 >> 2);
+  const int wsw = (s16 >> 2) | ((gq >> 1) << 2);
+  int wb_off[G::TN];
 #pragma unroll
   for (int j = 0; j < G::TN; ++j) {
     int cb;  // logical column base of this 32-column tile
@@ -210,14 +221,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     else
       cb = wn * G::CW + 32 * j;
     const int col = cb + 16 * (gq & 1) + 4 * (s16 & 3);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int row = 16 * kk + 8 * (gq >> 1) + 4 * hf + (s16 >> 2);
-        wb_off[j][kk][hf] =
-            G::A_BYTES + row * G::ROWB + 32 * ((col >> 4) ^ hswz(row)) + 2 * (col & 15);
-      }
+    wb_off[j] = G::A_BYTES + wrow * G::ROWB + 32 * ((col >> 4) ^ wsw) + 2 * (col & 15);
   }
 
   f32x16_v acc[G::TM][G::TN];
@@ -228,62 +232,133 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // All fragment reads of a k-step are issued before its MFMAs (rows past
-  // the tile's end read in-bounds stale LDS and are never stored); only the
-  // MFMAs of m-tiles without rows are skipped, on a wave-uniform condition.
-  auto compute = [&](const unsigned char* base) {
+  // Fragment reads of k-step kk of the block at `base` (rows past the
+  // tile's end read in-bounds stale LDS and are never stored).
+  auto read_w = [&](const unsigned char* base, int kk, bf16x8_v (&wf)[G::TN]) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_v wf[G::TN];
-      bf16x8_v xf[G::TM];
-#pragma unroll
-      for (int j = 0; j < G::TN; ++j) {
-        const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(base + wb_off[j][kk][0]));
-        const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(base + wb_off[j][kk][1]));
-        wf[j] = __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int i = 0; i < G::TM; ++i)
-        xf[i] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(base + xa_off[i][kk]));
-#pragma unroll
-      for (int i = 0; i < G::TM; ++i) {
-        if (i < tm_on) {
-#pragma unroll
-          for (int j = 0; j < G::TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
-        }
-      }
+    for (int j = 0; j < G::TN; ++j) {
+      const unsigned char* p = base + wb_off[j] + 16 * kk * G::ROWB;
+      const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+      const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * G::ROWB));
+      wf[j] = __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto read_x = [&](const unsigned char* base, int kk, int i) {
+    return __builtin_bit_cast(bf16x8_v,
+                              *reinterpret_cast<const u32x4*>(base + xa_off[kk] + XI * i));
+  };
+  const int KT = K / BK;
+  constexpr int PER = G::A_PER + G::B_PER;   // copies per block, every wave
+  // Wait until at most `nb` of this wave's most recent blocks are in flight.
+  auto wait_blocks = [&](int nb) {
+    static_assert(STAGES <= 6 && 4 * PER < 64, "wait table");
+    switch (nb) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<PER>(); break;
+      case 2: wait_vmcnt<2 * PER>(); break;
+      case 3: wait_vmcnt<3 * PER>(); break;
+      default: wait_vmcnt<4 * PER>(); break;
     }
   };
 
-  const int KT = K / BK;
-  constexpr int PER_STAGE_MAX = G::A_PER + G::B_PER;
-  const bool a_full = (G::A_INST % G::NW == 0) || (wave < G::A_INST % G::NW);
-
-  // prologue: STAGES - 1 blocks in flight
+  // prologue: every slot gets a block
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
+  for (int p = 0; p < STAGES; ++p)
     if (p < KT) issue(smem + p * G::STAGE_BYTES);
 
-  // Step for K-block kb: wait for it (later blocks stay in flight), barrier,
-  // refill the slot every wave finished reading in the previous step, compute.
-  int slot = 0;                       // kb % STAGES
-  int fill = STAGES - 1;              // (kb + STAGES - 1) % STAGES
-  for (int kb = 0; kb < KT; ++kb) {
-    if (KT - 1 - kb >= STAGES - 2) {
-      if (a_full) wait_vmcnt<(STAGES - 2) * PER_STAGE_MAX>();
-      else wait_vmcnt<(STAGES - 2) * (PER_STAGE_MAX - 1)>();
-    } else {
-      wait_vmcnt<0>();
-    }
+  // block 0 landed (blocks 1 .. min(STAGES, KT) - 1 may stay in flight)
+  wait_blocks(min(STAGES, KT) - 1);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // The main loop, specialised on the number of this wave's m-tiles that
+  // hold rows (TA), so it is straight-line code: m-tiles past TA are neither
+  // read nor multiplied.
+  auto main_loop = [&](auto ta_c) {
+    constexpr int TA = decltype(ta_c)::value;
+    bf16x8_v w0[G::TN], w1[G::TN], xf[TA];
+    // MFMAs of one k-step, m-tile by m-tile; right after m-tile i's MFMAs
+    // are issued its activation register is refilled with the fragment of
+    // the next k-step (`nbase`, `nkk`), so the LDS read runs under the
+    // remaining MFMAs and one register set serves both k-steps.
+    auto mma_roll = [&](const bf16x8_v (&wf)[G::TN], const unsigned char* nbase, int nkk) {
+#pragma unroll
+      for (int i = 0; i < TA; ++i) {
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+        xf[i] = read_x(nbase, nkk, i);
+        // keep this order: the scheduler would otherwise gather the reads
+        // next to their first use and expose their latency
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Block b's first k-step is multiplied before the barrier that
+    // publishes block b + 1, its second k-step after it.  Between the two,
+    // every wave has finished reading slot b (LDS reads waited), so the
+    // barrier also retires slot b, which is refilled with block b + STAGES
+    // right after it.  The loop body starts after a barrier, where no LDS
+    // read is pending, so the wait-count state at the loop head is exact.
+    read_w(smem, 0, w0);
+#pragma unroll
+    for (int i = 0; i < TA; ++i) xf[i] = read_x(smem, 0, i);
+    read_w(smem, 1, w1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_roll(w0, smem, 1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (KT > 1) wait_blocks(min(STAGES - 2, KT - 2));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kb + STAGES - 1 < KT) issue(smem + fill * G::STAGE_BYTES);
-    compute(smem + slot * G::STAGE_BYTES);
-    slot = (slot + 1 == STAGES) ? 0 : slot + 1;
-    fill = (fill + 1 == STAGES) ? 0 : fill + 1;
+
+    int slot = 0;                                      // kb % STAGES
+    for (int kb = 0; kb + 1 < KT; ++kb) {
+      unsigned char* cur = smem + slot * G::STAGE_BYTES;
+      slot = (slot + 1 == STAGES) ? 0 : slot + 1;
+      unsigned char* nxt = smem + slot * G::STAGE_BYTES;
+      if (kb + STAGES < KT) issue(cur);
+      // second k-step of block kb, reading block kb + 1's first
+      read_w(nxt, 0, w0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_roll(w1, nxt, 0);
+      // first k-step of block kb + 1, reading its second
+      read_w(nxt, 1, w1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_roll(w0, nxt, 1);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (kb + 2 < KT) wait_blocks(min(STAGES - 2, KT - 3 - kb));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    // second k-step of the last block
+#pragma unroll
+    for (int i = 0; i < TA; ++i)
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[j], xf[i], acc[i][j], 0, 0, 0);
+  };
+  // Waves without rows issue the same copies and join the same barriers.
+  auto empty_loop = [&]() {
+    if (KT > 1) wait_blocks(min(STAGES - 2, KT - 2));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    for (int kb = 0; kb + 1 < KT; ++kb) {
+      if (kb + STAGES < KT) issue(smem + (kb % STAGES) * G::STAGE_BYTES);
+      if (kb + 2 < KT) wait_blocks(min(STAGES - 2, KT - 3 - kb));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+  };
+  static_assert(G::TM <= 8, "m-tiles per wave");
+  switch (tm_on) {
+    case 0: empty_loop(); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (G::TM >= 2) main_loop(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (G::TM >= 3) main_loop(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (G::TM >= 4) main_loop(std::integral_constant<int, 4>{}); break;
+    case 5: if constexpr (G::TM >= 5) main_loop(std::integral_constant<int, 5>{}); break;
+    case 6: if constexpr (G::TM >= 6) main_loop(std::integral_constant<int, 6>{}); break;
+    case 7: if constexpr (G::TM >= 7) main_loop(std::integral_constant<int, 7>{}); break;
+    default: if constexpr (G::TM >= 8) main_loop(std::integral_constant<int, 8>{}); break;
   }
 
   // ---- epilogue.  acc[i][j][q] = C[row m][col cb_j + 8 (q / 4) + 4 hl + q % 4]
@@ -382,7 +457,7 @@ hipError_t launch_lds_cfg(bool swiglu, int id, const void* X, int ldx, const int
     MOE_CASE(11, 128, 256, 2, 2, 4)
     MOE_CASE(12, 64, 256, 1, 4, 4)
     MOE_CASE(13, 32, 256, 1, 4, 4)
-    MOE_CASE(14, 320, 256, 2, 4, 3)
+    MOE_CASE(14, 320, 256, 2, 4, 4)
     default: return hipErrorInvalidValue;
   }
 #undef MOE_CASE

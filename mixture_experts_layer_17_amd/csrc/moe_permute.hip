@@ -13,10 +13,10 @@
 //      among equal lanes below it is a popcount.  Per-expert counts of the 16
 //      segments of a chunk are prefix-summed in LDS, giving each slot its
 //      stable rank inside the chunk and the chunk's histogram.
-//   2. scan pass (one workgroup): per expert, exclusive prefix over chunks;
-//      counts; exclusive prefix over experts -> offsets; chunk base =
-//      offset + prefix.
-//   3. scatter pass: position = chunk base[expert] + rank.
+//   2. place pass (one workgroup per chunk): every workgroup sums the chunk
+//      histograms per expert (all chunks -> counts, earlier chunks -> the
+//      chunk's base within the expert), scans the counts over experts into
+//      offsets, and places its slots at offset + base + rank.
 #include "moe_common.h"
 #include "moe_internal.h"
 #include "moe_tiles.h"
@@ -85,69 +85,75 @@ __global__ __launch_bounds__(256) void permute_chunk_kernel(
   }
 }
 
-// Pass 2: one workgroup.  Thread (e, part) of 1024 sums a quarter of the
-// chunks for expert e; the experts' totals are scanned by one wave; each
-// part then turns its chunk histograms into chunk bases.  Optionally the
-// first 256 threads also write the grouped GEMMs' tile lists.
-__global__ __launch_bounds__(1024) void permute_scan_kernel(
-    int32_t* __restrict__ hist_base /*[nchunk][E] in: hist, out: base*/, int nchunk, int E,
-    int N, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+// Pass 2, one workgroup per chunk c (1024 threads, one slot each).  Thread
+// (e, part) sums a quarter of the chunk histograms of expert e, both over
+// all chunks (the expert's total) and over the chunks before c; the totals
+// are scanned over experts into offsets; slot i of the chunk then goes to
+// offsets[e] + (expert e's slots in earlier chunks) + its rank in the chunk.
+// Every workgroup computes the same totals (integers, so identically), and
+// workgroup 0 also writes counts, offsets and the grouped GEMMs' tile lists.
+__global__ __launch_bounds__(1024) void permute_place_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ hist /*[nchunk][E]*/, int nchunk, int N, int E, int k,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int4* __restrict__ tiles_a, int32_t* __restrict__ count_a, int BM_a,
     int4* __restrict__ tiles_b, int32_t* __restrict__ count_b, int BM_b) {
-  __shared__ int s_part[4][PM_MAXE];
+  __shared__ int s_tot_p[4][PM_MAXE];
+  __shared__ int s_bef_p[4][PM_MAXE];
   __shared__ int s_tot[PM_MAXE];
   __shared__ int s_off[PM_MAXE + 1];
+  __shared__ int s_base[PM_MAXE];
   __shared__ int s_nt[PM_MAXE];
   __shared__ int s_start[PM_MAXE + 1];
+  const int c = blockIdx.x;
   const int e = threadIdx.x & (PM_MAXE - 1);
   const int part = threadIdx.x >> 8;
   const int per = (nchunk + 3) / 4;
   const int c0 = part * per, c1 = min(nchunk, c0 + per);
-  int run = 0;
+  int tot = 0, bef = 0;
   if (e < E)
-    for (int c = c0; c < c1; ++c) run += hist_base[(size_t)c * E + e];
-  s_part[part][e] = run;
+    for (int cc = c0; cc < c1; ++cc) {
+      const int v = hist[(size_t)cc * E + e];
+      tot += v;
+      bef += cc < c ? v : 0;
+    }
+  s_tot_p[part][e] = tot;
+  s_bef_p[part][e] = bef;
   __syncthreads();
-  if (part == 0) s_tot[e] = s_part[0][e] + s_part[1][e] + s_part[2][e] + s_part[3][e];
+  if (part == 0) s_tot[e] = s_tot_p[0][e] + s_tot_p[1][e] + s_tot_p[2][e] + s_tot_p[3][e];
   __syncthreads();
   block_scan256(s_tot, s_off);
-  if (e < E) {
-    int base = s_off[e];
-    for (int p = 0; p < part; ++p) base += s_part[p][e];
-    for (int c = c0; c < c1; ++c) {
-      const int v = hist_base[(size_t)c * E + e];
-      hist_base[(size_t)c * E + e] = base;
-      base += v;
+  if (part == 0)
+    s_base[e] = s_off[e] + s_bef_p[0][e] + s_bef_p[1][e] + s_bef_p[2][e] + s_bef_p[3][e];
+  __syncthreads();
+
+  const int i = c * PM_CHUNK + threadIdx.x;
+  if (i < N) {
+    const int ei = ids[i];
+    const int rk = rank[i];
+    int pos = -1;
+    if (ei >= 0 && ei < E && rk >= 0) {
+      pos = s_base[ei] + rk;
+      if (pos >= N) pos = -1;
     }
-    if (part == 0) {
-      counts[e] = s_tot[e];
-      offsets[e] = s_off[e];
+    if (pos >= 0) {
+      sorted_token[pos] = i / k;
+      if (sorted_slot) sorted_slot[pos] = i;
     }
+    slot_pos[i] = pos;
+  }
+
+  if (c != 0) return;   // uniform over the block
+  if (part == 0 && e < E) {
+    counts[e] = s_tot[e];
+    offsets[e] = s_off[e];
   }
   if (threadIdx.x == 0) offsets[E] = s_off[E];
   if (tiles_a == nullptr && tiles_b == nullptr) return;   // uniform over the block
-  __syncthreads();
   const int lo = min(s_off[e], N), hi = min(s_off[e] + s_tot[e], N);
   if (tiles_a) build_tile_list(E, lo, hi, BM_a, tiles_a, count_a, s_nt, s_start);
   if (tiles_b) build_tile_list(E, lo, hi, BM_b, tiles_b, count_b, s_nt, s_start);
-}
-
-// Pass 3: scatter.
-__global__ __launch_bounds__(256) void permute_scatter_kernel(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
-    const int32_t* __restrict__ base, int N, int E, int k, int32_t* __restrict__ sorted_token,
-    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= N) return;
-  const int e = ids[i];
-  const int rk = rank[i];
-  if (e < 0 || e >= E || rk < 0) { slot_pos[i] = -1; return; }
-  const int c = i / PM_CHUNK;
-  const int p = base[(size_t)c * E + e] + rk;
-  if (p < 0 || p >= N) { slot_pos[i] = -1; return; }
-  sorted_token[p] = i / k;
-  if (sorted_slot) sorted_slot[p] = i;
-  slot_pos[i] = p;
 }
 
 // Rank-major mode, pass 1 (one workgroup of 256 threads): prefix tables of
@@ -267,11 +273,10 @@ hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E, int32_t*
   int32_t* rank = (int32_t*)((char*)ws + align256((size_t)nchunk * E * sizeof(int32_t)));
   permute_chunk_kernel<<<nchunk, 256, 0, s>>>(ids, N, E, hist, rank);
   auto tl = [](void* w) { return w ? (int4*)((char*)w + 256) : (int4*)nullptr; };
-  permute_scan_kernel<<<1, 1024, 0, s>>>(hist, nchunk, E, N, counts, offsets, tl(tile_ws_a),
-                                         (int32_t*)tile_ws_a, BM_a, tl(tile_ws_b),
-                                         (int32_t*)tile_ws_b, BM_b);
-  permute_scatter_kernel<<<(N + 255) / 256, 256, 0, s>>>(ids, rank, hist, N, E, k, sorted_token,
-                                                         sorted_slot, slot_pos);
+  permute_place_kernel<<<nchunk, 1024, 0, s>>>(ids, rank, hist, nchunk, N, E, k, sorted_token,
+                                               sorted_slot, slot_pos, counts, offsets,
+                                               tl(tile_ws_a), (int32_t*)tile_ws_a, BM_a,
+                                               tl(tile_ws_b), (int32_t*)tile_ws_b, BM_b);
   return hipGetLastError();
 }
 

@@ -9,13 +9,19 @@
 // softmax is monotone so the selected set equals the set ranked by
 // probability, and the selection depends on the logits alone.
 //
-// Layout: one workgroup of 8 waves per 16 tokens.  Both operands are
-// K-contiguous (x is [T, H], Wr is [E, H]), so each lane loads its MFMA
-// operand chunk straight from global memory.  The waves split K: wave w
-// takes the 32-wide k-chunks w, w + 8, ... for all E experts, so every wave
-// has many independent loads in flight.  The 8 partial logit tiles are then
-// added in a fixed tree through LDS (deterministic), and each wave runs the
-// softmax / top-k epilogue for 2 tokens.
+// Layout: one workgroup of 8 waves per 16 tokens, each reading all of Wr.
+//   * Logits: K streams through an LDS ring in blocks of 128-byte rows (the
+//     16 x rows, then the E Wr rows).  Every copy instruction moves 8 whole
+//     rows of 128 bytes, which the load path serves at about twice the rate
+//     of MFMA-shaped loads (16 rows x 64 bytes per instruction).  Wave w
+//     owns expert tiles w, w + 8 over all of K, so no partial sums are
+//     combined across waves.
+//   * Epilogue: each wave takes 2 tokens, 32 lanes per token, each lane
+//     holding its experts as 64-bit keys (order-preserving float bits of the
+//     logit, then the complemented expert id, so a larger key is a larger
+//     logit or, on a tie, a lower id).  k rounds of a DPP max over the keys
+//     select the top-k in order; sums for the softmax use the same fixed
+//     DPP pattern, so every result is deterministic.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -23,16 +29,111 @@ namespace moe {
 namespace {
 
 constexpr int RT_TOK = 16;     // tokens per workgroup
-constexpr int RT_MAXE = 256;   // max experts
-constexpr int RT_NT = RT_MAXE / 16;
 constexpr int RT_WAVES = 8;
-constexpr int RT_LD = RT_MAXE + 4;   // LDS row stride (floats)
 
-// Larger logit first; equal logits (IEEE equality, so -0 == +0) go to the
-// lower expert id.
-__device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb) {
-  return va > vb || (va == vb && ea < eb);
+// Order-preserving key: larger key <=> larger logit, or equal logits
+// (IEEE equality, so -0 == +0) and a lower expert id.
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;                      // -0 ranks as +0
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
 }
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) {
+  return (int)(0xffffffffu - (uint32_t)k);
+}
+
+// DPP lane exchange within 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  return ((uint64_t)dpp32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL>((uint32_t)v);
+}
+constexpr int DPP_QUAD_1032 = 0xb1;   // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_2301 = 0x4e;   // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROR4 = 0x124;       // row_ror:4
+constexpr int DPP_ROR8 = 0x128;       // row_ror:8
+
+// Every lane of a 16-lane row gets the row's largest key.
+__device__ __forceinline__ uint64_t row_max(uint64_t k) {
+  uint64_t o = dpp64<DPP_QUAD_1032>(k); k = o > k ? o : k;
+  o = dpp64<DPP_QUAD_2301>(k); k = o > k ? o : k;
+  o = dpp64<DPP_ROR4>(k); k = o > k ? o : k;
+  o = dpp64<DPP_ROR8>(k); k = o > k ? o : k;
+  return k;
+}
+// Row sums in a fixed pattern; lane 0 of each row holds a deterministic sum.
+__device__ __forceinline__ float row_sum(float v) {
+  v += __uint_as_float(dpp32<DPP_QUAD_1032>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<DPP_QUAD_2301>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<DPP_ROR4>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<DPP_ROR8>(__float_as_uint(v)));
+  return v;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Sum over the 32 lanes of this lane's half-wave (rows 0-1 or 2-3).
+__device__ __forceinline__ float half_sum(float v, int half) {
+  v = row_sum(v);
+  const float a = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+  const float b = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 16));
+  const float c = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 32));
+  const float d = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 48));
+  return half ? c + d : a + b;
+}
+
+// One global->LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds + 16 i (lds is wave-uniform, passed in M0).  Issued from asm, with
+// explicit vmcnt waits below, so the compiler does not drain every copy in
+// flight before each LDS read.  It writes no registers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void rt_copy16(const void* g, const unsigned char* lds) {
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const uint32_t a = (uint32_t)(uintptr_t)(const lds_u8*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(a)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void rt_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Rows of a K block in LDS are 128 bytes (8 chunks of 16 bytes); chunk c of
+// row r sits at physical chunk c ^ f(r), which makes the 16 rows read by one
+// MFMA operand load hit 16 distinct bank groups.
+__device__ __forceinline__ int rt_swz(int row) { return (row >> 1) & 7; }
+
+template <typename T, int NT>
+struct rcfg {
+  static constexpr int KB = 128 / (int)sizeof(T);   // K elements per block (128-byte rows)
+  static constexpr int ROWS = RT_TOK + NT * 16;      // x rows, then Wr rows
+  static constexpr int STAGE = ROWS * 128;
+  static constexpr int Q = ROWS / 8;                 // copy instructions per block (8 rows each)
+  static constexpr int LDE = NT * 16 + 4;            // logits row stride (floats)
+  static constexpr int LOG_BYTES = RT_TOK * LDE * 4;
+  static constexpr int NS0 = (160 * 1024 - LOG_BYTES) / STAGE;
+  static constexpr int NS = NS0 > 8 ? 8 : NS0;       // ring stages
+  static constexpr int LDS = NS * STAGE + LOG_BYTES;
+  static constexpr int CPL = (NT * 16 + 31) / 32;    // experts per lane in the epilogue
+  static_assert(NS >= 2, "ring");
+  static_assert(ROWS % 8 == 0, "whole copy instructions");
+};
 
 template <typename T, int NT>
 __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(
@@ -40,153 +141,187 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(
     int T_, int H, int E, int k, int norm, float* __restrict__ logits_out,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ counts) {
-  // partial-sum buffers for the reduction tree; buffer 0 finally holds the
-  // logits of the 16 tokens
-  __shared__ float s_red[RT_WAVES / 2][RT_TOK][RT_LD];
+  using C = rcfg<T, NT>;
+  constexpr int NS = C::NS;
+  // NS ring stages of [x rows | Wr rows] x 128 bytes, then the logits
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* s_log = reinterpret_cast<float*>(smem + NS * C::STAGE);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * RT_TOK;
-  const int g = lane >> 4;      // k-chunk group
-  const int r = lane & 15;      // row (token) / column (expert) within a tile
+  const int g = lane >> 4;      // k group of the MFMA operands
+  const int r = lane & 15;      // token row / expert column within a tile
 
-  f32x4_v acc[NT];
+  // ---- copies: instruction q of a block covers LDS rows 8q .. 8q + 7, one
+  // 16-byte chunk per lane; waves take q = wave, wave + 8, ...
+  constexpr int CPW = (C::Q + RT_WAVES - 1) / RT_WAVES;   // copies per wave (upper bound)
+  const int cnt = (C::Q - wave + RT_WAVES - 1) / RT_WAVES; // this wave's copies per block
+  constexpr int EL = 16 / (int)sizeof(T);                   // elements per chunk
+  const T* src[CPW];
+  int dst[CPW];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-
-  const int tok = min(t0 + r, T_ - 1);
-  const T* xrow = x + (size_t)tok * H + 8 * g;
-  // experts beyond E read row E - 1 (valid memory); their columns are never
-  // stored as logits, so no branch is needed around the loads
-  const T* wrow[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) wrow[j] = wr + (size_t)min(j * 16 + r, E - 1) * H + 8 * g;
-
-  // wave w takes blocks of CPB consecutive 32-wide k-chunks: w, w + 8, ...;
-  // all loads of a block are issued before its MFMAs
-  constexpr int CPB = 4;
-  const int nchunk = H / 32;
-  const int nfull = nchunk / CPB;           // full blocks
-  for (int blk = wave; blk < nfull; blk += RT_WAVES) {
-    chunk8<T> a[CPB];
-    chunk8<T> b[CPB][NT];
-#pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      const int k0 = 32 * (blk * CPB + u);
-      a[u] = load_chunk<T>(xrow + k0);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) b[u][j] = load_chunk<T>(wrow[j] + k0);
-    }
-#pragma unroll
-    for (int u = 0; u < CPB; ++u)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = mfma_16x16x32(a[u], b[u][j], acc[j]);
+  for (int u = 0; u < CPW; ++u) {
+    const int q = min(wave + RT_WAVES * u, C::Q - 1);
+    const int row = 8 * q + (lane >> 3);
+    const int chunk = (lane & 7) ^ rt_swz(row);
+    const T* rowp = row < RT_TOK ? x + (size_t)min(t0 + row, T_ - 1) * H
+                                 : wr + (size_t)min(row - RT_TOK, E - 1) * H;
+    src[u] = rowp + EL * chunk;
+    dst[u] = q * 1024;
   }
-  // leftover chunks (H / 32 not a multiple of CPB)
-  for (int c = nfull * CPB + wave; c < nchunk; c += RT_WAVES) {
-    const int k0 = 32 * c;
-    const chunk8<T> a = load_chunk<T>(xrow + k0);
+  const int nblk = H / C::KB;
+  auto issue = [&](int blk) {
+    unsigned char* base = smem + (blk % NS) * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = mfma_16x16x32(a, load_chunk<T>(wrow[j] + k0), acc[j]);
-  }
+    for (int u = 0; u < CPW; ++u)
+      if (u < cnt) rt_copy16(src[u] + (size_t)blk * C::KB, base + dst[u]);
+  };
+  // Wait until block b has landed: the blocks this wave issued after it may
+  // stay in flight.  Steady state has NS - 2 of them; near the end, drain.
+  auto wait_block = [&](int b) {
+    const int after = min(b == 0 ? NS - 1 : NS - 2, nblk - 1 - b);
+    if (after == NS - 1) {
+      if (cnt == CPW) rt_wait_vmcnt<(NS - 1) * CPW>();
+      else rt_wait_vmcnt<(NS - 1) * (CPW - 1)>();
+    } else if (after == NS - 2) {
+      if (cnt == CPW) rt_wait_vmcnt<(NS - 2) * CPW>();
+      else rt_wait_vmcnt<(NS - 2) * (CPW - 1)>();
+    } else {
+      rt_wait_vmcnt<0>();
+    }
+  };
 
-  // ---- fixed-order tree: 8 -> 4 -> 2 -> 1 partial tiles
+  // ---- MFMA operands: lane (g, r) takes chunks 2 g and 2 g + 1 of row r of
+  // the x block and of row r of each of its expert tiles (tiles wave,
+  // wave + 8); the swizzle of a row depends on r only.  bf16: one MFMA per
+  // chunk (k = 16 g .. + 7 and 16 g + 8 .. + 15 of the block); float: the two
+  // chunks form one chunk8 (k = 8 g .. + 7).  x and Wr use the same k
+  // assignment, which is all the contraction needs.
+  constexpr int TPW = (NT + RT_WAVES - 1) / RT_WAVES;   // expert tiles per wave
+  const int c0 = 16 * ((2 * g) ^ rt_swz(r));
+  const int c1 = 16 * ((2 * g + 1) ^ rt_swz(r));
+  f32x4_v acc[TPW];
 #pragma unroll
-  for (int half = RT_WAVES / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half) {
+  for (int j = 0; j < TPW; ++j) acc[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  auto rd = [&](const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p); };
+  auto compute = [&](const unsigned char* base) {
+    const unsigned char* xr = base + r * 128;
+    const u32x4 xa = rd(xr + c0), xb = rd(xr + c1);
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_red[wave - half][4 * g + i][16 * j + r] = acc[j][i];
-    }
-    __syncthreads();
-    if (wave < half) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] += s_red[wave][4 * g + i][16 * j + r];
-    }
-    __syncthreads();
-  }
-  if (wave == 0) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int e = 16 * j + r;
-      if (e < E) {
-        const float b = bias ? bias[e] : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_red[0][4 * g + i][e] = acc[j][i] + b;
+    for (int jj = 0; jj < TPW; ++jj) {
+      const int j = wave + RT_WAVES * jj;
+      if (j < NT) {
+        const unsigned char* wrw = base + (RT_TOK + 16 * j + r) * 128;
+        const u32x4 wa = rd(wrw + c0), wb = rd(wrw + c1);
+        if constexpr (sizeof(T) == 2) {
+          acc[jj] = mfma_16x16x32(chunk8<bf16_t>{xa}, chunk8<bf16_t>{wa}, acc[jj]);
+          acc[jj] = mfma_16x16x32(chunk8<bf16_t>{xb}, chunk8<bf16_t>{wb}, acc[jj]);
+        } else {
+          acc[jj] = mfma_16x16x32(chunk8<float>{xa, xb}, chunk8<float>{wa, wb}, acc[jj]);
+        }
       }
+    }
+  };
+
+  // ---- K loop: one barrier per block publishes it and retires the slot
+  // every wave finished reading in the previous iteration, which is then
+  // refilled right away
+#pragma unroll
+  for (int p = 0; p < NS; ++p)
+    if (p < nblk) issue(p);
+  for (int b = 0; b < nblk; ++b) {
+    wait_block(b);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (b >= 1 && b - 1 + NS < nblk) issue(b - 1 + NS);
+    compute(smem + (b % NS) * C::STAGE);
+  }
+
+  // ---- logits tile to LDS (+ bias): acc[jj][q] = L[token 4g + q][expert 16 j + r]
+#pragma unroll
+  for (int jj = 0; jj < TPW; ++jj) {
+    const int j = wave + RT_WAVES * jj;
+    const int e = 16 * j + r;
+    if (j < NT && e < E) {
+      const float bv = bias ? bias[e] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_log[(4 * g + q) * C::LDE + e] = acc[jj][q] + bv;
     }
   }
   __syncthreads();
+  if (logits_out) {
+    for (int idx = threadIdx.x; idx < RT_TOK * E; idx += RT_WAVES * 64) {
+      const int tr = idx / E, e = idx - tr * E;
+      if (t0 + tr < T_) logits_out[(size_t)(t0 + tr) * E + e] = s_log[tr * C::LDE + e];
+    }
+  }
 
-  // ---- Epilogue: wave w handles tokens 2w, 2w + 1 of this workgroup.
-  for (int q = 0; q < RT_TOK / RT_WAVES; ++q) {
-    const int row = (RT_TOK / RT_WAVES) * wave + q;
-    const int t = t0 + row;
-    if (t >= T_) break;
-    // lane owns experts lane, lane + 64, lane + 128, lane + 192
-    float v[4];
-    unsigned avail = 0;
+  // ---- epilogue: lanes 0-31 take token 2 wave, lanes 32-63 token 2 wave + 1
+  const int half = lane >> 5, hl = lane & 31;
+  const int trow = 2 * wave + half;
+  const int t = t0 + trow;
+  const float* L = s_log + trow * C::LDE;
+  // selected keys: the ring is free (every wave passed the barrier above
+  // after its last LDS read of the ring)
+  uint64_t* sel = reinterpret_cast<uint64_t*>(smem) + (size_t)trow * k;
+
+  uint64_t cand[C::CPL];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = lane + 64 * c;
-      if (e < E) {
-        v[c] = s_red[0][row][e];
-        avail |= 1u << c;
-        if (logits_out) logits_out[(size_t)t * E + e] = v[c];
-      } else {
-        v[c] = -INFINITY;
-      }
+  for (int c = 0; c < C::CPL; ++c) {
+    const int e = hl + 32 * c;
+    cand[c] = e < E ? rank_key(L[e], e) : 0ull;
+  }
+  // this lane's keys in descending order (insertion network)
+#pragma unroll
+  for (int p = 1; p < C::CPL; ++p)
+#pragma unroll
+    for (int q = p; q > 0; --q) {
+      const uint64_t lo = cand[q - 1], hi = cand[q];
+      cand[q - 1] = hi > lo ? hi : lo;
+      cand[q] = hi > lo ? lo : hi;
     }
-    // top-k by repeated wave arg-max under the (value desc, id asc) order
-    float sel_v[4] = {0.f, 0.f, 0.f, 0.f};
-    int sel_e[4] = {0, 0, 0, 0};
-    float m = 0.f;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
+  // k rounds: the half-wave's largest head key is the next selection; the one
+  // lane holding it advances to its next key (keys are unique)
+  for (int j = 0; j < k; ++j) {
+    const uint64_t rm = row_max(cand[0]);
+    const uint64_t r0 = readlane64(rm, 0), r1 = readlane64(rm, 16);
+    const uint64_t r2 = readlane64(rm, 32), r3 = readlane64(rm, 48);
+    const uint64_t wa = r0 > r1 ? r0 : r1, wb = r2 > r3 ? r2 : r3;
+    const uint64_t win = half ? wb : wa;
+    const bool pop = cand[0] == win;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (avail & (1u << c)) {
-          const int e = lane + 64 * c;
-          if (be == 0x7fffffff || ranks_before(v[c], e, bv, be)) { bv = v[c]; be = e; }
-        }
-      }
+    for (int c = 0; c + 1 < C::CPL; ++c) cand[c] = pop ? cand[c + 1] : cand[c];
+    if (pop) cand[C::CPL - 1] = 0ull;
+    if (hl == 0) sel[j] = win;
+  }
+  // LDS accesses of one wave complete in order, so the keys written above
+  // are visible to the reads below
+  const float m = key_value(sel[0]);          // the largest logit
+  float part = 0.f;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        if (oe != 0x7fffffff && (be == 0x7fffffff || ranks_before(ov, oe, bv, be))) { bv = ov; be = oe; }
-      }
-      if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
-      if (j == 0) m = bv;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if ((j >> 6) == c && (j & 63) == lane) { sel_v[c] = bv; sel_e[c] = be; }
-    }
-    // softmax denominator over all experts (max-subtracted), and the sum of
-    // the selected probabilities' numerators
-    float part = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (lane + 64 * c < E) part += expf(v[c] - m);
-    const float denom = wave_sum(part);
-    float selpart = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (lane + 64 * c < k) selpart += expf(sel_v[c] - m);
-    const float selsum = wave_sum(selpart);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = lane + 64 * c;
+  for (int c = 0; c < C::CPL; ++c) {
+    const int e = hl + 32 * c;
+    if (e < E) part += expf(L[e] - m);
+  }
+  const float den = half_sum(part, half);
+  float sp = 0.f;
+  for (int jb = 0; jb < k; jb += 32) {
+    const int j = jb + hl;
+    if (j < k) sp += expf(key_value(sel[j]) - m);
+  }
+  const float selsum = half_sum(sp, half);
+  if (t < T_) {
+    for (int jb = 0; jb < k; jb += 32) {
+      const int j = jb + hl;
       if (j < k) {
-        const float num = expf(sel_v[c] - m);
-        const float w = norm ? num / selsum : num / denom;
-        ids_out[(size_t)t * k + j] = sel_e[c];
-        w_out[(size_t)t * k + j] = w;
-        if (counts) atomicAdd(&counts[sel_e[c]], 1);
+        const uint64_t key = sel[j];
+        const int e = key_expert(key);
+        const float num = expf(key_value(key) - m);
+        ids_out[(size_t)t * k + j] = e;
+        w_out[(size_t)t * k + j] = norm ? num / selsum : num / den;
+        if (counts) atomicAdd(&counts[e], 1);
       }
     }
   }
@@ -195,6 +330,20 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
+}
+
+template <typename V, int NT>
+hipError_t launch_route_t(const void* x, const void* wr, const float* bias, int T, int H, int E,
+                          int k, int norm, float* logits, int32_t* ids, float* w,
+                          int32_t* counts, hipStream_t s) {
+  using C = rcfg<V, NT>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)route_kernel<V, NT>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((T + RT_TOK - 1) / RT_TOK);
+  route_kernel<V, NT><<<grid, RT_WAVES * 64, C::LDS, s>>>((const V*)x, (const V*)wr, bias, T, H,
+                                                          E, k, norm, logits, ids, w, counts);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -213,26 +362,18 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
     if (e != hipSuccess) return e;
   }
   if (T <= 0) return hipSuccess;
-  const dim3 grid((T + RT_TOK - 1) / RT_TOK);
-  const dim3 block(RT_WAVES * 64);
   const int nt = (E + 15) / 16;
-#define MOE_ROUTE(NT)                                                                          \
-  do {                                                                                         \
-    if (bf16)                                                                                  \
-      route_kernel<bf16_t, NT><<<grid, block, 0, s>>>((const bf16_t*)x, (const bf16_t*)wr,     \
-                                                      bias, T, H, E, k, norm, logits, ids, w, \
-                                                      counts);                                 \
-    else                                                                                       \
-      route_kernel<float, NT><<<grid, block, 0, s>>>((const float*)x, (const float*)wr, bias,  \
-                                                     T, H, E, k, norm, logits, ids, w, counts);\
-  } while (0)
+#define MOE_ROUTE(NT)                                                                        \
+  return bf16 ? launch_route_t<bf16_t, NT>(x, wr, bias, T, H, E, k, norm, logits, ids, w,    \
+                                           counts, s)                                        \
+              : launch_route_t<float, NT>(x, wr, bias, T, H, E, k, norm, logits, ids, w,     \
+                                          counts, s)
   if (nt <= 1) MOE_ROUTE(1);
-  else if (nt <= 2) MOE_ROUTE(2);
-  else if (nt <= 4) MOE_ROUTE(4);
-  else if (nt <= 8) MOE_ROUTE(8);
-  else MOE_ROUTE(16);
+  if (nt <= 2) MOE_ROUTE(2);
+  if (nt <= 4) MOE_ROUTE(4);
+  if (nt <= 8) MOE_ROUTE(8);
+  MOE_ROUTE(16);
 #undef MOE_ROUTE
-  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -12,10 +12,10 @@
 //     global_load_lds_dwordx4 (lane i of a wave instruction lands at
 //     base + 16 i); each lane picks the global 16-byte chunk that belongs at
 //     its LDS slot, which realises an XOR swizzle of the 4 chunks of a row
-//     by f(row) = ((row >> 1) ^ (row >> 3)) & 3.  Reads are ds_read_b128.
+//     by f(row) = (row ^ (row >> 2)) & 3.  Reads are ds_read_b128.
 //   * weights: 32 rows (k) x BN columns in their natural [k][n] layout
 //     (n contiguous), loaded the same way with 32-byte segments of a row
-//     XOR-swizzled by h(row) = (row & 3) | ((row >> 1) & 4).  The MFMA
+//     XOR-swizzled by h(row) = ((row & 3) << 1) | ((row >> 3) & 1).  The MFMA
 //     operand needs 8 consecutive k of one column per lane; two
 //     ds_read_b64_tr_b16 deliver that: within each 16-lane group, lane s
 //     reads 4 consecutive columns of row (kbase + s / 4) and lane j receives
@@ -44,8 +44,11 @@ typedef short i16x4_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_v;
 typedef __attribute__((address_space(3))) i16x4_v lds_i16x4;
 
-__device__ __forceinline__ int fswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int hswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// Swizzles chosen by timing every lane pattern the kernel reads against the
+// conflict-free rate (ds_read_b128: 4 clocks per wave instruction,
+// ds_read_b64_tr_b16: 2 clocks).
+__device__ __forceinline__ int fswz(int row) { return (row ^ (row >> 2)) & 3; }
+__device__ __forceinline__ int hswz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -198,8 +201,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   // of the tile and the same k values; 16-lane group q reads columns
   // 16 (q & 1) .. + 15 and k 8 (q >> 1) .. + 7 with two transposing reads of
   // 4 rows each.  Those rows are 16 kk + 8 (q >> 1) + 4 hf + s / 4, whose
-  // swizzle h = s / 4 | (q >> 1) << 2 does not depend on kk or hf, so kk and
-  // hf are constant offsets too.
+  // swizzle h = (s / 4) << 1 | (q >> 1) does not depend on kk or hf, so kk
+  // and hf are constant offsets too.
   const int l32 = lane & 31, hl = lane >> 5;
   constexpr int XI = 32 * WM * 64;                 // bytes between a wave's m-tiles
   int xa_off[2];
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
       min(G::TM, max(0, ((rows + 31) / 32 - wm + WM - 1) / WM)));
   const int gq = lane >> 4, s16 = lane & 15;
   const int wrow = 8 * (gq >> 1) + (s16 >> 2);
-  const int wsw = (s16 >> 2) | ((gq >> 1) << 2);
+  const int wsw = ((s16 >> 2) << 1) | (gq >> 1);
   int wb_off[G::TN];
 #pragma unroll
   for (int j = 0; j < G::TN; ++j) {
@@ -251,13 +254,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   constexpr int PER = G::A_PER + G::B_PER;   // copies per block, every wave
   // Wait until at most `nb` of this wave's most recent blocks are in flight.
   auto wait_blocks = [&](int nb) {
-    static_assert(STAGES <= 6 && 4 * PER < 64, "wait table");
+    static_assert(STAGES <= 8 && (STAGES - 1) * PER < 64, "wait table");
     switch (nb) {
       case 0: wait_vmcnt<0>(); break;
       case 1: wait_vmcnt<PER>(); break;
       case 2: wait_vmcnt<2 * PER>(); break;
       case 3: wait_vmcnt<3 * PER>(); break;
-      default: wait_vmcnt<4 * PER>(); break;
+      case 4: wait_vmcnt<4 * PER>(); break;
+      case 5: wait_vmcnt<5 * PER>(); break;
+      case 6: wait_vmcnt<6 * PER>(); break;
+      default: wait_vmcnt<7 * PER>(); break;
     }
   };
 
@@ -362,53 +368,70 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   }
 
   // ---- epilogue.  acc[i][j][q] = C[row m][col cb_j + 8 (q / 4) + 4 hl + q % 4]
-  // with m = 32 * mtile + l % 32.  Each wave stages one 32-row m-tile of its
-  // output (32 x CW bf16) in a private LDS area, then writes whole row
-  // segments of 2 * CW bytes with 16-byte stores.
-  constexpr int OB = G::CW * 2;              // bytes per staged output row
-  constexpr int LPR = OB / 16;               // lanes per row (16 bytes each)
-  constexpr int RPI = 64 / LPR;              // rows per store instruction
-  static_assert(32 * OB * G::NW <= G::LDS, "output staging fits in the ring");
+  // with m = 32 * mtile + l % 32.  Results go through LDS so that global
+  // stores write whole row segments with 16-byte lanes.  Staged rows are
+  // padded by 8 bytes: the 32 rows a wave writes at once then fall on
+  // distinct banks.
+  auto to_bf16x4 = [](const float (&v)[4]) {
+    return make_uint2((uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+                      (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16));
+  };
   __builtin_amdgcn_s_barrier();              // every wave is done with the ring
   asm volatile("" ::: "memory");
-  unsigned char* stg = smem + wave * 32 * OB;
+  {
+    // Each wave stages one 32-row m-tile of its CW columns at a time and
+    // stores every row segment of 2 CW bytes (rows of the second GEMM are
+    // scattered through c_index).  The destination rows are loaded up front,
+    // all at once, rather than one m-tile at a time.
+    constexpr int OB = G::CW * 2;              // bytes per staged output row
+    constexpr int OBP = OB + 8;                // padded row stride
+    constexpr int LPR = OB / 16;               // lanes per row (16 bytes each)
+    constexpr int RPI = 64 / LPR;              // rows per store instruction
+    constexpr int NRI = 32 / RPI;              // store instructions per m-tile
+    static_assert(32 * OBP * G::NW <= G::RING, "output staging fits in the ring");
+    int dsts[G::TM][NRI];
 #pragma unroll
-  for (int i = 0; i < G::TM; ++i) {
-    if (i >= tm_on) continue;
+    for (int i = 0; i < G::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < G::TNO; ++j)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float g = acc[i][j][4 * a + q];
-          if constexpr (SWIGLU) {
-            // silu(g) * u in float32; rounded to bf16 on store
-            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-            v[q] = sg * acc[i][G::TNO + j][4 * a + q];
-          } else {
-            v[q] = g;
-          }
-        }
-        const uint32_t d0 = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-        const uint32_t d1 = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-        *reinterpret_cast<uint2*>(stg + l32 * OB + 2 * (32 * j + 8 * a + 4 * hl)) = make_uint2(d0, d1);
+      for (int rr = 0; rr < NRI; ++rr) {
+        const int m = 32 * (wm + WM * i) + rr * RPI + lane / LPR;
+        int dst = -1;
+        if (i < tm_on && m < rows) dst = (!SWIGLU && c_index) ? c_index[row0 + m] : row0 + m;
+        dsts[i][rr] = dst;
       }
-    // LDS writes above and reads below are this wave's own: program order
-    // plus the compiler's lgkmcnt waits order them.
-    const int mrow0 = 32 * (wm + WM * i);
+    unsigned char* stg = smem + wave * 32 * OBP;
 #pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += RPI) {
-      const int r = r0 + lane / LPR;
-      const int m = mrow0 + r;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * OB + 16 * (lane % LPR));
-      if (m < rows) {
-        const int p = row0 + m;
-        int dst = p;
-        if constexpr (!SWIGLU) dst = c_index ? c_index[p] : p;
+    for (int i = 0; i < G::TM; ++i) {
+      if (i >= tm_on) continue;
+#pragma unroll
+      for (int j = 0; j < G::TNO; ++j)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float g = acc[i][j][4 * a + q];
+            if constexpr (SWIGLU) {
+              // silu(g) * u in float32; rounded to bf16 on store
+              const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+              v[q] = sg * acc[i][G::TNO + j][4 * a + q];
+            } else {
+              v[q] = g;
+            }
+          }
+          *reinterpret_cast<uint2*>(stg + l32 * OBP + 2 * (32 * j + 8 * a + 4 * hl)) = to_bf16x4(v);
+        }
+      // LDS writes above and reads below are this wave's own: program order
+      // plus the compiler's lgkmcnt waits order them.
+#pragma unroll
+      for (int rr = 0; rr < NRI; ++rr) {
+        const int r = rr * RPI + lane / LPR;
+        const uint2 lo = *reinterpret_cast<const uint2*>(stg + r * OBP + 16 * (lane % LPR));
+        const uint2 hi = *reinterpret_cast<const uint2*>(stg + r * OBP + 16 * (lane % LPR) + 8);
+        const int dst = dsts[i][rr];
         if (dst >= 0 && dst < c_rows)
-          *reinterpret_cast<u32x4*>(C + (long long)dst * ldc + n0 + wn * G::CW + 8 * (lane % LPR)) = v;
+          *reinterpret_cast<u32x4*>(C + (long long)dst * ldc + n0 + wn * G::CW + 8 * (lane % LPR)) =
+              u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     }
   }

@@ -115,9 +115,11 @@ __device__ __forceinline__ void rt_wait_vmcnt() {
 }
 
 // Rows of a K block in LDS are 128 bytes (8 chunks of 16 bytes); chunk c of
-// row r sits at physical chunk c ^ f(r), which makes the 16 rows read by one
-// MFMA operand load hit 16 distinct bank groups.
-__device__ __forceinline__ int rt_swz(int row) { return (row >> 1) & 7; }
+// row r sits at physical chunk c ^ f(r & 15).  f was chosen by timing the
+// MFMA operand reads (16 rows, lane group g reading chunks 2 g and 2 g + 1)
+// against the conflict-free rate; it depends on the row within its 16-row
+// group only, so x rows and every Wr tile share the same offsets.
+__device__ __forceinline__ int rt_swz(int row) { return (row ^ ((row & 15) >> 3)) & 7; }
 
 template <typename T, int NT>
 struct rcfg {

@@ -37,7 +37,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 struct LayerWs {
   int32_t *ids, *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
-  float* weights;
+  float *weights, *logits;
   void *perm, *h, *y, *tiles_up, *tiles_down;
   size_t total;
 };
@@ -54,6 +54,7 @@ LayerWs layer_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
   };
   w.ids = (int32_t*)take(N * 4);
   w.weights = (float*)take(N * 4);
+  w.logits = (float*)take((size_t)T * E * 4);
   w.counts = (int32_t*)take((size_t)E * 4);
   w.offsets = (int32_t*)take((size_t)(E + 1) * 4);
   w.sorted_token = (int32_t*)take(N * 4);
@@ -264,6 +265,7 @@ int moe_layer_forward(const void* x, const void* wr, const float* bias, const vo
   if (!ids) ids = w.ids;
   if (!weights) weights = w.weights;
   if (!counts) counts = w.counts;
+  if (!logits) logits = w.logits;
   const bool bf16 = dt == MOE_BF16;
   const int N = T * k;
   auto mark = [&](int i) {

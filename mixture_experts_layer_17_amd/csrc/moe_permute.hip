@@ -13,6 +13,7 @@
 //      among equal lanes below it is a popcount.  Per-expert counts of the 16
 //      segments of a chunk are prefix-summed in LDS, giving each slot its
 //      stable rank inside the chunk and the chunk's histogram.
+//   (N <= 1024: both passes in one workgroup.)
 //   2. place pass (one workgroup per chunk): every workgroup sums the chunk
 //      histograms per expert (all chunks -> counts, earlier chunks -> the
 //      chunk's base within the expert), scans the counts over experts into
@@ -156,6 +157,77 @@ __global__ __launch_bounds__(1024) void permute_place_kernel(
   if (tiles_b) build_tile_list(E, lo, hi, BM_b, tiles_b, count_b, s_nt, s_start);
 }
 
+// Single-launch variant for N <= 1024 (one chunk): 16 waves, one 64-slot
+// segment each; ranks, counts, offsets, placement and tile lists in one
+// workgroup.
+__global__ __launch_bounds__(1024) void permute_single_kernel(
+    const int32_t* __restrict__ ids, int N, int E, int k, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles_a,
+    int32_t* __restrict__ count_a, int BM_a, int4* __restrict__ tiles_b,
+    int32_t* __restrict__ count_b, int BM_b) {
+  __shared__ int s_cnt[PM_NSEG][PM_MAXE];
+  __shared__ int s_tot[PM_MAXE];
+  __shared__ int s_off[PM_MAXE + 1];
+  __shared__ int s_nt[PM_MAXE];
+  __shared__ int s_start[PM_MAXE + 1];
+  const int lane = threadIdx.x & 63;
+  const int seg = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < PM_NSEG * PM_MAXE; i += 1024) (&s_cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int i = threadIdx.x;
+  int e = (i < N) ? ids[i] : -1;
+  const bool valid = (e >= 0 && e < E);
+  if (!valid) e = -1;
+  unsigned long long match = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const unsigned long long bb = __ballot(bit);
+    match &= bit ? bb : ~bb;
+  }
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rk_seg = valid ? __popcll(match & below) : 0;
+  if (valid && (match & below) == 0ull) s_cnt[seg][e] = __popcll(match);
+  __syncthreads();
+  // per-expert exclusive prefix over the 16 segments (threads 0..255)
+  if (threadIdx.x < PM_MAXE) {
+    const int ee = threadIdx.x;
+    int run = 0;
+#pragma unroll
+    for (int sg = 0; sg < PM_NSEG; ++sg) {
+      const int v = ee < E ? s_cnt[sg][ee] : 0;
+      s_cnt[sg][ee] = run;
+      run += v;
+    }
+    s_tot[ee] = run;
+  }
+  __syncthreads();
+  block_scan256(s_tot, s_off);
+  if (i < N) {
+    int pos = -1;
+    if (valid) {
+      pos = s_off[e] + s_cnt[seg][e] + rk_seg;
+      if (pos >= N) pos = -1;
+    }
+    if (pos >= 0) {
+      sorted_token[pos] = i / k;
+      if (sorted_slot) sorted_slot[pos] = i;
+    }
+    slot_pos[i] = pos;
+  }
+  const int ee = threadIdx.x & (PM_MAXE - 1);
+  if (threadIdx.x < PM_MAXE && ee < E) {
+    counts[ee] = s_tot[ee];
+    offsets[ee] = s_off[ee];
+  }
+  if (threadIdx.x == 0) offsets[E] = s_off[E];
+  if (tiles_a == nullptr && tiles_b == nullptr) return;   // uniform over the block
+  const int lo = min(s_off[ee], N), hi = min(s_off[ee] + s_tot[ee], N);
+  if (tiles_a) build_tile_list(E, lo, hi, BM_a, tiles_a, count_a, s_nt, s_start);
+  if (tiles_b) build_tile_list(E, lo, hi, BM_b, tiles_b, count_b, s_nt, s_start);
+}
+
 // Rank-major mode, pass 1 (one workgroup of 256 threads): prefix tables of
 // the count matrix.
 //   rm_start[r * E + e]: first received row of block (r, e) (rank-major order)
@@ -269,10 +341,16 @@ hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E, int32_t*
     return launch_fill_i32(offsets, E + 1, 0, s);
   }
   const int nchunk = (N + PM_CHUNK - 1) / PM_CHUNK;
+  auto tl = [](void* w) { return w ? (int4*)((char*)w + 256) : (int4*)nullptr; };
+  if (nchunk == 1) {
+    permute_single_kernel<<<1, 1024, 0, s>>>(ids, N, E, k, sorted_token, sorted_slot, slot_pos,
+                                             counts, offsets, tl(tile_ws_a), (int32_t*)tile_ws_a,
+                                             BM_a, tl(tile_ws_b), (int32_t*)tile_ws_b, BM_b);
+    return hipGetLastError();
+  }
   int32_t* hist = (int32_t*)ws;
   int32_t* rank = (int32_t*)((char*)ws + align256((size_t)nchunk * E * sizeof(int32_t)));
   permute_chunk_kernel<<<nchunk, 256, 0, s>>>(ids, N, E, hist, rank);
-  auto tl = [](void* w) { return w ? (int4*)((char*)w + 256) : (int4*)nullptr; };
   permute_place_kernel<<<nchunk, 1024, 0, s>>>(ids, rank, hist, nchunk, N, E, k, sorted_token,
                                                sorted_slot, slot_pos, counts, offsets,
                                                tl(tile_ws_a), (int32_t*)tile_ws_a, BM_a,

@@ -30,6 +30,7 @@ namespace {
 
 constexpr int RT_TOK = 16;     // tokens per workgroup
 constexpr int RT_WAVES = 8;
+constexpr int RT_SPLIT_MAX_TILES = 32;   // up to 512 tokens take the split path
 
 // Order-preserving key: larger key <=> larger logit, or equal logits
 // (IEEE equality, so -0 == +0) and a lower expert id.
@@ -120,6 +121,83 @@ __device__ __forceinline__ void rt_wait_vmcnt() {
 // against the conflict-free rate; it depends on the row within its 16-row
 // group only, so x rows and every Wr tile share the same offsets.
 __device__ __forceinline__ int rt_swz(int row) { return (row ^ ((row & 15) >> 3)) & 7; }
+
+// Top-k selection, softmax and renormalisation for the 16 tokens of a
+// workgroup of 8 waves, whose float32 logits are in LDS (row stride lde).
+// Wave w takes rows 2 w (lanes 0-31) and 2 w + 1 (lanes 32-63); each lane
+// holds the keys of experts hl, hl + 32, ... (CPL of them).  sel is LDS
+// scratch of 16 * k keys.
+template <int CPL>
+__device__ __forceinline__ void select_tokens(const float* s_log, int lde, uint64_t* sel_base,
+                                              int t0, int wave, int lane, int T_, int E, int k,
+                                              int norm, int32_t* __restrict__ ids_out,
+                                              float* __restrict__ w_out,
+                                              int32_t* __restrict__ counts) {
+  const int half = lane >> 5, hl = lane & 31;
+  const int trow = 2 * wave + half;
+  const int t = t0 + trow;
+  const float* L = s_log + trow * lde;
+  uint64_t* sel = sel_base + (size_t)trow * k;
+
+  uint64_t cand[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = hl + 32 * c;
+    cand[c] = e < E ? rank_key(L[e], e) : 0ull;
+  }
+  // this lane's keys in descending order (insertion network)
+#pragma unroll
+  for (int p = 1; p < CPL; ++p)
+#pragma unroll
+    for (int q = p; q > 0; --q) {
+      const uint64_t lo = cand[q - 1], hi = cand[q];
+      cand[q - 1] = hi > lo ? hi : lo;
+      cand[q] = hi > lo ? lo : hi;
+    }
+  // k rounds: the half-wave's largest head key is the next selection; the one
+  // lane holding it advances to its next key (keys are unique)
+  for (int j = 0; j < k; ++j) {
+    const uint64_t rm = row_max(cand[0]);
+    const uint64_t r0 = readlane64(rm, 0), r1 = readlane64(rm, 16);
+    const uint64_t r2 = readlane64(rm, 32), r3 = readlane64(rm, 48);
+    const uint64_t wa = r0 > r1 ? r0 : r1, wb = r2 > r3 ? r2 : r3;
+    const uint64_t win = half ? wb : wa;
+    const bool pop = cand[0] == win;
+#pragma unroll
+    for (int c = 0; c + 1 < CPL; ++c) cand[c] = pop ? cand[c + 1] : cand[c];
+    if (pop) cand[CPL - 1] = 0ull;
+    if (hl == 0) sel[j] = win;
+  }
+  // LDS accesses of one wave complete in order, so the keys written above
+  // are visible to the reads below
+  const float m = key_value(sel[0]);          // the largest logit
+  float part = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = hl + 32 * c;
+    if (e < E) part += expf(L[e] - m);
+  }
+  const float den = half_sum(part, half);
+  float sp = 0.f;
+  for (int jb = 0; jb < k; jb += 32) {
+    const int j = jb + hl;
+    if (j < k) sp += expf(key_value(sel[j]) - m);
+  }
+  const float selsum = half_sum(sp, half);
+  if (t < T_) {
+    for (int jb = 0; jb < k; jb += 32) {
+      const int j = jb + hl;
+      if (j < k) {
+        const uint64_t key = sel[j];
+        const int e = key_expert(key);
+        const float num = expf(key_value(key) - m);
+        ids_out[(size_t)t * k + j] = e;
+        w_out[(size_t)t * k + j] = norm ? num / selsum : num / den;
+        if (counts) atomicAdd(&counts[e], 1);
+      }
+    }
+  }
+}
 
 template <typename T, int NT>
 struct rcfg {
@@ -260,73 +338,94 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(
     }
   }
 
-  // ---- epilogue: lanes 0-31 take token 2 wave, lanes 32-63 token 2 wave + 1
-  const int half = lane >> 5, hl = lane & 31;
-  const int trow = 2 * wave + half;
-  const int t = t0 + trow;
-  const float* L = s_log + trow * C::LDE;
-  // selected keys: the ring is free (every wave passed the barrier above
-  // after its last LDS read of the ring)
-  uint64_t* sel = reinterpret_cast<uint64_t*>(smem) + (size_t)trow * k;
+  // ---- top-k epilogue; the ring is free for the selected keys (every wave
+  // passed the barrier above after its last LDS read of the ring)
+  select_tokens<C::CPL>(s_log, C::LDE, reinterpret_cast<uint64_t*>(smem), t0, wave, lane, T_, E,
+                        k, norm, ids_out, w_out, counts);
+}
 
-  uint64_t cand[C::CPL];
+// ---- Small-batch path.  With few tokens the kernel above runs on few CUs,
+// each streaming all of Wr; here the logits are spread over (16-token tile,
+// 16-expert tile) workgroups first, then one workgroup per 16 tokens selects.
+
+// Logits of one 16 x 16 tile: 4 waves split K in 64-wide blocks (wave w
+// takes blocks w, w + 4, ...), loading MFMA operands straight from global
+// memory D blocks ahead; the 4 partial tiles are added in wave order in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void route_logits_kernel(
+    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias, int T_,
+    int H, int E, float* __restrict__ logits) {
+  constexpr int NWV = 4, D = 4, P = 2, KB = 32 * P;
+  __shared__ float s_acc[NWV][16][17];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const int g = lane >> 4, r = lane & 15;
+  const T* xrow = x + (size_t)min(t0 + r, T_ - 1) * H + 8 * P * g;
+  const T* wrow = wr + (size_t)min(e0 + r, E - 1) * H + 8 * P * g;
+  const int nblk = H / KB;
+  const int iters = (nblk + NWV - 1) / NWV;
+  f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+  chunk8<T> a[D][P], b[D][P];
+  auto load = [&](int s, int i) {
+    const int c = KB * min(wave + NWV * i, nblk - 1);
 #pragma unroll
-  for (int c = 0; c < C::CPL; ++c) {
-    const int e = hl + 32 * c;
-    cand[c] = e < E ? rank_key(L[e], e) : 0ull;
-  }
-  // this lane's keys in descending order (insertion network)
-#pragma unroll
-  for (int p = 1; p < C::CPL; ++p)
-#pragma unroll
-    for (int q = p; q > 0; --q) {
-      const uint64_t lo = cand[q - 1], hi = cand[q];
-      cand[q - 1] = hi > lo ? hi : lo;
-      cand[q] = hi > lo ? lo : hi;
+    for (int h = 0; h < P; ++h) {
+      a[s][h] = load_chunk<T>(xrow + c + 8 * h);
+      b[s][h] = load_chunk<T>(wrow + c + 8 * h);
     }
-  // k rounds: the half-wave's largest head key is the next selection; the one
-  // lane holding it advances to its next key (keys are unique)
-  for (int j = 0; j < k; ++j) {
-    const uint64_t rm = row_max(cand[0]);
-    const uint64_t r0 = readlane64(rm, 0), r1 = readlane64(rm, 16);
-    const uint64_t r2 = readlane64(rm, 32), r3 = readlane64(rm, 48);
-    const uint64_t wa = r0 > r1 ? r0 : r1, wb = r2 > r3 ? r2 : r3;
-    const uint64_t win = half ? wb : wa;
-    const bool pop = cand[0] == win;
+  };
+  auto mma = [&](int s, int i) {
+    const bool on = wave + NWV * i < nblk;
 #pragma unroll
-    for (int c = 0; c + 1 < C::CPL; ++c) cand[c] = pop ? cand[c + 1] : cand[c];
-    if (pop) cand[C::CPL - 1] = 0ull;
-    if (hl == 0) sel[j] = win;
-  }
-  // LDS accesses of one wave complete in order, so the keys written above
-  // are visible to the reads below
-  const float m = key_value(sel[0]);          // the largest logit
-  float part = 0.f;
+    for (int h = 0; h < P; ++h) acc = mfma_16x16x32(on ? a[s][h] : zero_chunk<T>(), b[s][h], acc);
+  };
+  const int groups = (iters + D - 1) / D;
 #pragma unroll
-  for (int c = 0; c < C::CPL; ++c) {
-    const int e = hl + 32 * c;
-    if (e < E) part += expf(L[e] - m);
-  }
-  const float den = half_sum(part, half);
-  float sp = 0.f;
-  for (int jb = 0; jb < k; jb += 32) {
-    const int j = jb + hl;
-    if (j < k) sp += expf(key_value(sel[j]) - m);
-  }
-  const float selsum = half_sum(sp, half);
-  if (t < T_) {
-    for (int jb = 0; jb < k; jb += 32) {
-      const int j = jb + hl;
-      if (j < k) {
-        const uint64_t key = sel[j];
-        const int e = key_expert(key);
-        const float num = expf(key_value(key) - m);
-        ids_out[(size_t)t * k + j] = e;
-        w_out[(size_t)t * k + j] = norm ? num / selsum : num / den;
-        if (counts) atomicAdd(&counts[e], 1);
-      }
+  for (int s = 0; s < D; ++s) load(s, s);
+  for (int gi = 0; gi + 1 < groups; ++gi) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      mma(s, gi * D + s);
+      load(s, (gi + 1) * D + s);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+#pragma unroll
+  for (int s = 0; s < D; ++s) mma(s, (groups - 1) * D + s);
+  // acc[q] = partial L[token 4 g + q][expert r]
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s_acc[wave][4 * g + q][r] = acc[q];
+  __syncthreads();
+  const int tr = threadIdx.x >> 4, ec = threadIdx.x & 15;   // 16 x 16 outputs, one per thread
+  const int t = t0 + tr, e = e0 + ec;
+  if (t < T_ && e < E) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) v += s_acc[w][tr][ec];
+    if (bias) v += bias[e];
+    logits[(size_t)t * E + e] = v;
+  }
+}
+
+// Selection for 16 tokens from their logits in global memory.
+template <int NT>
+__global__ __launch_bounds__(RT_WAVES * 64) void route_select_kernel(
+    const float* __restrict__ logits, int T_, int E, int k, int norm,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ counts) {
+  constexpr int LDE = NT * 16 + 4;
+  constexpr int CPL = (NT * 16 + 31) / 32;
+  __shared__ float s_log[RT_TOK * LDE];
+  extern __shared__ __align__(16) unsigned char s_sel[];   // 16 * k keys
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * RT_TOK;
+  for (int idx = threadIdx.x; idx < RT_TOK * E; idx += RT_WAVES * 64) {
+    const int tr = idx / E, e = idx - tr * E;
+    s_log[tr * LDE + e] = logits[(size_t)min(t0 + tr, T_ - 1) * E + e];
+  }
+  __syncthreads();
+  select_tokens<CPL>(s_log, LDE, reinterpret_cast<uint64_t*>(s_sel), t0, wave, lane, T_, E, k,
+                     norm, ids_out, w_out, counts);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
@@ -365,6 +464,30 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
   }
   if (T <= 0) return hipSuccess;
   const int nt = (E + 15) / 16;
+  const int tiles = (T + RT_TOK - 1) / RT_TOK;
+  // Small batches (and a logits buffer to pass through) take the split path.
+  if (logits && tiles <= RT_SPLIT_MAX_TILES && H % 64 == 0) {
+    const dim3 g1(tiles, nt);
+    if (bf16)
+      route_logits_kernel<bf16_t><<<g1, 256, 0, s>>>((const bf16_t*)x, (const bf16_t*)wr, bias, T,
+                                                     H, E, logits);
+    else
+      route_logits_kernel<float><<<g1, 256, 0, s>>>((const float*)x, (const float*)wr, bias, T, H,
+                                                    E, logits);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t sel_bytes = (size_t)RT_TOK * k * sizeof(uint64_t);
+#define MOE_SELECT(NT)                                                                        \
+  route_select_kernel<NT><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(logits, T, E, k, norm, ids, w, \
+                                                                  counts)
+    if (nt <= 1) MOE_SELECT(1);
+    else if (nt <= 2) MOE_SELECT(2);
+    else if (nt <= 4) MOE_SELECT(4);
+    else if (nt <= 8) MOE_SELECT(8);
+    else MOE_SELECT(16);
+#undef MOE_SELECT
+    return hipGetLastError();
+  }
 #define MOE_ROUTE(NT)                                                                        \
   return bf16 ? launch_route_t<bf16_t, NT>(x, wr, bias, T, H, E, k, norm, logits, ids, w,    \
                                            counts, s)                                        \

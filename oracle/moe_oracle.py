@@ -46,6 +46,7 @@ import numpy as np
 
 __all__ = [
     "router_logits", "select_topk", "routing_weights", "route",
+    "router_scores", "limited_group_mask", "route_variant", "update_expert_bias",
     "expert_counts", "expert_offsets", "permutation", "gather_rows",
     "silu", "swiglu_expert", "grouped_swiglu", "combine", "unpermute",
     "moe_layer_forward", "moe_layer_forward_brute", "moe_layer_forward_tokens",
@@ -115,6 +116,97 @@ def route(x, w_router, bias, top_k: int, norm_topk_prob: bool):
     ids = select_topk(L, top_k)
     w = routing_weights(L, ids, norm_topk_prob)
     return L, ids, w
+
+
+# ---------------------------------------------------------------------------
+# Router variants  ([HP] TokenChoiceTopKRouter.forward and
+# _get_node_limited_routing_scores; MoE.update_expert_bias)
+# ---------------------------------------------------------------------------
+
+def router_scores(logits32, score_func: str = "sigmoid", route_scale: float = 1.0) -> np.ndarray:
+    """Routing scores ([HP] ``TokenChoiceTopKRouter.forward``): the float32
+    gate output through a sigmoid (the page's default) or a softmax over the
+    experts, then multiplied by ``route_scale``.  Float64."""
+    L = _f64(logits32)
+    if score_func == "sigmoid":
+        s = 1.0 / (1.0 + np.exp(-L))
+    elif score_func == "softmax":
+        p = np.exp(L - L.max(axis=1, keepdims=True))
+        s = p / p.sum(axis=1, keepdims=True)
+    else:
+        raise ValueError("score_func must be 'sigmoid' or 'softmax'")
+    return s * float(route_scale)
+
+
+def limited_group_mask(scores, n_groups: int, n_limited: int) -> np.ndarray:
+    """Node-limited routing ([HP] ``_get_node_limited_routing_scores``):
+    experts are cut into ``n_groups`` contiguous groups, a group's score is the
+    largest score among its experts, and each token keeps the ``n_limited``
+    groups with the largest group scores.  Returns the boolean ``[T, E]`` mask
+    of experts that stay selectable.  The group ranking is decided on float32
+    group scores (the page works in float32), ties going to the lower group
+    id."""
+    S = _f64(scores)
+    T, E = S.shape
+    if n_groups < 1 or E % n_groups or not 1 <= n_limited <= n_groups:
+        raise ValueError("need E % n_groups == 0 and 1 <= n_limited <= n_groups")
+    epg = E // n_groups
+    gs = S.reshape(T, n_groups, epg).max(axis=2).astype(np.float32)
+    gid = np.broadcast_to(np.arange(n_groups), gs.shape)
+    keep = np.lexsort((gid, -gs.astype(np.float64)), axis=-1)[:, :n_limited]
+    mask = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(mask, keep, True, axis=1)
+    return np.repeat(mask, epg, axis=1)
+
+
+def route_variant(logits32, top_k: int, norm_topk_prob: bool = False, score_func: str = "sigmoid",
+                  route_scale: float = 1.0, expert_bias=None, n_groups: int = 0,
+                  n_limited: int = 0):
+    """Generalised token-choice router ([HP] ``TokenChoiceTopKRouter.forward``).
+
+    1. scores = score_func(float32 logits) * route_scale;
+    2. with node-limited routing, experts outside the token's best groups are
+       not selectable;
+    3. the selection key is score + expert_bias (the bias steers selection
+       only), decided in float32; the top-k keys are taken in descending
+       order, equal keys going to the lower expert id;
+    4. the routing weights are the unbiased scores of the selected experts,
+       divided by their sum when ``norm_topk_prob``.
+
+    Returns ``(ids[T, k] int32, weights[T, k] float64, scores[T, E] float64,
+    keys[T, E] float32)`` where non-selectable experts have key -inf."""
+    s = router_scores(logits32, score_func, route_scale)
+    T, E = s.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k must be in [1, E]")
+    key = s + (0.0 if expert_bias is None else _f64(expert_bias)[None, :])
+    key32 = key.astype(np.float32)
+    if n_groups:
+        allowed = limited_group_mask(s, n_groups, n_limited)
+        if top_k > allowed[0].sum():
+            raise ValueError("top_k exceeds the experts of the kept groups")
+        key32 = np.where(allowed, key32, np.float32(-np.inf))
+    eid = np.broadcast_to(np.arange(E), s.shape)
+    ids = np.lexsort((eid, -key32.astype(np.float64)), axis=-1)[:, :top_k].astype(np.int32)
+    w = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    if norm_topk_prob:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids, w, s, key32
+
+
+def update_expert_bias(expert_bias, tokens_per_expert, lr: float = 1e-3,
+                       num_recomputations: int = 1):
+    """Auxiliary-loss-free bias step ([HP] ``MoE.update_expert_bias``): the
+    accumulated token counts are divided by the number of forward passes per
+    step, every expert's bias moves by ``lr`` toward the mean load
+    (``lr * sign(mean - load)``), the step is centred to zero mean, and the
+    accumulator is cleared.  Returns ``(new_bias, new_tokens_per_expert)``."""
+    tpe = _f64(tokens_per_expert)
+    if num_recomputations > 1:
+        tpe = tpe / num_recomputations
+    delta = float(lr) * np.sign(tpe.mean() - tpe)
+    delta = delta - delta.mean()
+    return _f64(expert_bias) + delta, np.zeros_like(tpe)
 
 
 # ---------------------------------------------------------------------------

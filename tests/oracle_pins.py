@@ -21,7 +21,13 @@ What pins what:
   mixture, zero token, the scalar closed form at H = I = 1, permute + combine
   with an identity expert;
 * expert-parallel rank: a hand-worked reshuffle, and equality with the
-  token-choice layer when one rank owns every expert.
+  token-choice layer when one rank owns every expert;
+* router variants (sigmoid / softmax scores, route scale, selection-only
+  expert bias, node-limited groups): equal scores make the bias order the
+  selection (closed form), sigmoid weights against scipy's expit, the
+  softmax variant against the default router, a hand-worked group example,
+  and the group invariant on random inputs;
+* expert-bias update: hand-worked steps, zero-mean steps, recomputation.
 """
 from __future__ import annotations
 
@@ -380,6 +386,96 @@ def pin_page_shape_examples():
     dn = r.standard_normal((m["num_experts"], m["hidden_dim"], d))
     out = O.moe_layer_forward(x, wr, None, gu, dn, m["top_k"], True)["out"]
     assert list(out.reshape(b, s, d).shape) == m["out_shape"]
+
+
+# ---- router variants -------------------------------------------------------
+
+def pin_variant_bias_steers_selection():
+    # zero logits: every sigmoid score is 0.5 * scale, so the selection
+    # follows the bias alone and the weights do not see it
+    T, E, k, scale = 5, 8, 3, 2.5
+    L = np.zeros((T, E), np.float32)
+    bias = np.array([0.3, -0.2, 0.9, 0.1, 0.5, -0.7, 0.0, 0.2])
+    ids, w, s, _ = O.route_variant(L, k, False, "sigmoid", scale, bias)
+    assert (ids == np.array([2, 4, 0])[None, :]).all()
+    assert np.array_equal(w, np.full((T, k), 0.5 * scale))
+    ids, w, _, _ = O.route_variant(L, k, True, "sigmoid", scale, bias)
+    assert np.allclose(w, 1.0 / k, rtol=0, atol=1e-15)
+    # softmax of equal logits is 1/E
+    ids, w, _, _ = O.route_variant(L, k, False, "softmax", 1.0, bias)
+    assert (ids == np.array([2, 4, 0])[None, :]).all() and np.allclose(w, 1.0 / E, atol=1e-15)
+
+
+def pin_variant_sigmoid_matches_expit():
+    r = _rng(7)
+    L = r.standard_normal((40, 16)).astype(np.float32) * 3
+    k, scale = 4, 1.7
+    ids, w, s, _ = O.route_variant(L, k, False, "sigmoid", scale)
+    # sigmoid is monotone: without bias or groups the logit order decides
+    assert np.array_equal(ids, O.select_topk(L, k))
+    ref = scipy.special.expit(L.astype(np.float64)) * scale
+    assert np.allclose(w, np.take_along_axis(ref, ids.astype(np.int64), 1), rtol=1e-14, atol=0)
+    assert np.allclose(s, ref, rtol=1e-14, atol=0)
+
+
+def pin_variant_softmax_equals_default_router():
+    x, wr, _, _ = _layer(24, 32, 8, 16, seed=3)
+    L, ids, w = O.route(x, wr, None, 4, True)
+    ids2, w2, _, _ = O.route_variant(L, 4, True, "softmax", 1.0)
+    assert np.array_equal(ids, ids2) and np.allclose(w, w2, rtol=1e-12, atol=0)
+
+
+def pin_variant_groups_worked_example():
+    # E = 8 in 4 groups of 2; group maxima 5, 4.5, 4, 3 (sigmoid keeps the
+    # order).  Two groups kept: experts 0-3 only.
+    L = np.array([[0, 5, 4.5, 1, 4, 0, 3, 2]], np.float32)
+    ids, _, _, _ = O.route_variant(L, 3, False, "sigmoid", 1.0, None, 4, 2)
+    assert ids.tolist() == [[1, 2, 3]]
+    ids, _, _, _ = O.route_variant(L, 3, False, "sigmoid")
+    assert ids.tolist() == [[1, 2, 4]]          # unrestricted: expert 4 wins
+    ids, _, _, _ = O.route_variant(L, 2, False, "sigmoid", 1.0, None, 4, 1)
+    assert ids.tolist() == [[1, 0]]             # only group 0
+    # the bias moves selection inside the kept groups but not the groups
+    ids, w, s, _ = O.route_variant(L, 2, False, "sigmoid", 1.0, np.array([0, 0, 0, 0, 9, 9, 0, 0.]),
+                                   4, 2)
+    assert ids.tolist() == [[1, 2]]
+    assert np.allclose(w, scipy.special.expit(np.array([[5.0, 4.5]])), rtol=1e-14)
+
+
+def pin_variant_groups_invariant():
+    r = _rng(11)
+    T, E, G, lim, k = 60, 32, 8, 3, 6
+    L = r.standard_normal((T, E)).astype(np.float32)
+    bias = r.standard_normal(E) * 0.3
+    ids, w, s, key = O.route_variant(L, k, False, "sigmoid", 1.0, bias, G, lim)
+    epg = E // G
+    gmax = s.reshape(T, G, epg).max(axis=2)
+    for t in range(T):
+        groups = set(int(e) // epg for e in ids[t])
+        assert len(groups) <= lim
+        # the kept groups are the lim largest group maxima
+        kept = sorted(range(G), key=lambda g: (-np.float32(gmax[t, g]), g))[:lim]
+        allowed = [e for e in range(E) if e // epg in kept]
+        assert set(int(e) // epg for e in ids[t]) <= set(kept)
+        # and the selection is the k largest keys among them
+        best = sorted(allowed, key=lambda e: (-np.float32(s[t, e] + bias[e]), e))[:k]
+        assert ids[t].tolist() == best
+        assert np.allclose(w[t], s[t, ids[t]], rtol=0, atol=0)
+
+
+def pin_update_expert_bias_worked():
+    b, z = O.update_expert_bias(np.zeros(4), np.array([3, 1, 2, 2.0]), lr=0.1)
+    assert np.allclose(b, [-0.1, 0.1, 0.0, 0.0], atol=1e-15) and not z.any()
+    # the step is centred: mean load 2, signs (+, +, +, -), mean step 0.05
+    b, _ = O.update_expert_bias(np.array([1.0, 2, 3, 4]), np.array([1, 1, 1, 5.0]), lr=0.1)
+    assert np.allclose(b, [1.05, 2.05, 3.05, 3.85], atol=1e-15)
+    # counts accumulated over two forward passes are halved first
+    b2, _ = O.update_expert_bias(np.array([1.0, 2, 3, 4]), np.array([2, 2, 2, 10.0]), lr=0.1,
+                                 num_recomputations=2)
+    assert np.allclose(b2, b, atol=1e-15)
+    r = _rng(5)
+    d, _ = O.update_expert_bias(np.zeros(64), r.integers(0, 100, 64).astype(float), lr=0.01)
+    assert abs(d.sum()) < 1e-12
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

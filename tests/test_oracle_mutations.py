@@ -73,8 +73,35 @@ def _off_by_one_offsets(counts):
     return o
 
 
+def _biased_weights(logits32, top_k, norm_topk_prob=False, score_func="sigmoid", route_scale=1.0,
+                    expert_bias=None, n_groups=0, n_limited=0):
+    ids, w, s, key = _orig["route_variant"](logits32, top_k, norm_topk_prob, score_func,
+                                            route_scale, expert_bias, n_groups, n_limited)
+    if expert_bias is not None:
+        w = w + np.asarray(expert_bias, np.float64)[ids]
+    return ids, w, s, key
+
+
+def _group_sum_mask(scores, n_groups, n_limited):
+    S = np.asarray(scores, np.float64)
+    T, E = S.shape
+    epg = E // n_groups
+    gs = S.reshape(T, n_groups, epg).sum(axis=2)
+    keep = np.argsort(-gs, axis=1, kind="stable")[:, :n_limited]
+    mask = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(mask, keep, True, axis=1)
+    return np.repeat(mask, epg, axis=1)
+
+
+def _uncentred_bias_update(expert_bias, tokens_per_expert, lr=1e-3, num_recomputations=1):
+    tpe = np.asarray(tokens_per_expert, np.float64)
+    if num_recomputations > 1:
+        tpe = tpe / num_recomputations
+    return np.asarray(expert_bias, np.float64) + lr * np.sign(tpe.mean() - tpe), np.zeros_like(tpe)
+
+
 _orig = {n: getattr(O, n) for n in ("routing_weights", "combine", "permutation",
-                                     "router_logits", "expert_offsets")}
+                                     "router_logits", "expert_offsets", "route_variant")}
 
 MUTATIONS = {
     "swiglu_expert": _swapped_gate_up,
@@ -85,6 +112,9 @@ MUTATIONS = {
     "permutation": _unstable_perm,
     "router_logits": _bf16_logits,
     "expert_offsets": _off_by_one_offsets,
+    "route_variant": _biased_weights,
+    "limited_group_mask": _group_sum_mask,
+    "update_expert_bias": _uncentred_bias_update,
 }
 
 

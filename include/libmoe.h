@@ -239,6 +239,76 @@ int moe_layer_forward(const void* hidden_states, const void* router_weight,
                       void* workspace, size_t workspace_bytes,
                       hipEvent_t* stage_events, hipStream_t stream);
 
+/*
+ * Router variants — MindSpore hyper-parallel moe.py page,
+ * TokenChoiceTopKRouter.forward and _get_node_limited_routing_scores
+ * (auxiliary-loss-free load balancing: MoE.update_expert_bias).
+ *
+ *   score[t, e] = score_func(router_logits[t, e]) * route_scale, where
+ *                 score_func is a sigmoid, or a softmax over the experts;
+ *   with num_expert_groups = G > 0 the experts form G contiguous groups of
+ *   E / G, a group's score is its largest expert score, and only the
+ *   num_limited_groups groups with the largest group scores (equal scores:
+ *   lower group first) stay selectable for the token;
+ *   topk_ids[t, :]   = the top_k selectable experts by score + expert_bias
+ *                      (bias for selection only; equal keys: lower id first),
+ *                      in decreasing key order; keys are float32;
+ *   topk_weights     = the unbiased scores of those experts, divided by
+ *                      their sum when norm_topk_prob != 0;
+ *   tokens_per_expert (float [E], optional) += selections per expert.
+ *
+ * All pointers in the struct are device pointers (or NULL); expert_bias and
+ * tokens_per_expert have E entries.  Requirements: score_func is one of the
+ * two constants, route_scale is finite, and with G > 0: E % G == 0,
+ * 1 <= num_limited_groups <= G and top_k <= num_limited_groups * E / G.
+ * Violations return MOE_ERR_SHAPE (or MOE_ERR_UNSUPPORTED for an unknown
+ * score_func) before anything is enqueued.
+ */
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+
+typedef struct moe_router_config {
+  int score_func;
+  float route_scale;
+  const float* expert_bias;
+  int num_expert_groups;
+  int num_limited_groups;
+  float* tokens_per_expert;
+} moe_router_config;
+
+/* moe_route with a router variant.  cfg == NULL is exactly moe_route (the
+ * softmax router that ranks the logits).  router_bias is added to the
+ * logits (it is part of router_logits); cfg->expert_bias only steers
+ * selection. */
+int moe_route_cfg(const void* hidden_states, const void* router_weight,
+                  const float* router_bias, int T, int H, int E, int top_k,
+                  int norm_topk_prob, moe_dtype dt, const moe_router_config* cfg,
+                  float* router_logits, int32_t* topk_ids, float* topk_weights,
+                  int32_t* num_tokens_per_expert, hipStream_t stream);
+
+/* moe_layer_forward with a router variant (cfg == NULL: moe_layer_forward).
+ * The combine weights each expert output by topk_weights as above. */
+int moe_layer_forward_cfg(const void* hidden_states, const void* router_weight,
+                          const float* router_bias, const void* gate_up,
+                          const void* down, int T, int H, int I, int E, int top_k,
+                          int norm_topk_prob, moe_dtype dt, const moe_router_config* cfg,
+                          void* out, float* router_logits, int32_t* topk_ids,
+                          float* topk_weights, int32_t* num_tokens_per_expert,
+                          void* workspace, size_t workspace_bytes,
+                          hipEvent_t* stage_events, hipStream_t stream);
+
+/*
+ * moe_update_expert_bias — one auxiliary-loss-free bias step (MindSpore
+ * moe.py, MoE.update_expert_bias), in place on device float arrays of E
+ * entries (1 <= E <= 256):
+ *   load = tokens_per_expert / num_recomputations   (when it is > 1)
+ *   step[e] = lr * sign(mean(load) - load[e]);  step -= mean(step)
+ *   expert_bias += step;  tokens_per_expert = 0
+ * Sums are float32 in a fixed order.  MOE_ERR_NULL / MOE_ERR_SHAPE on bad
+ * arguments.
+ */
+int moe_update_expert_bias(float* expert_bias, float* tokens_per_expert, int E, float lr,
+                           int num_recomputations, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

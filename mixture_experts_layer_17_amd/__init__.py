@@ -18,7 +18,8 @@ lib = _lib.load()
 
 __all__ = ["lib", "route", "permute", "permute_rank_major", "gather_rows",
            "grouped_gate_up_swiglu", "grouped_down", "grouped_swiglu", "combine",
-           "layer_forward", "workspace_size", "MoEError"]
+           "layer_forward", "workspace_size", "router_config", "update_expert_bias",
+           "LayerBuffers", "MoEError"]
 
 MoEError = _lib.MoEError
 
@@ -77,10 +78,46 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Tuple[int, in
     return t.data_ptr(), nbytes, t
 
 
+def router_config(score_func: str = "sigmoid", route_scale: float = 1.0,
+                  expert_bias: Optional[torch.Tensor] = None, num_expert_groups: int = 0,
+                  num_limited_groups: int = 0,
+                  tokens_per_expert: Optional[torch.Tensor] = None) -> "_lib.RouterConfig":
+    """A router variant (struct moe_router_config): score function, route
+    scale, selection-only expert bias [E] float32, node-limited groups and an
+    optional float32 [E] accumulator of selections."""
+    funcs = {"softmax": _lib.MOE_SCORE_SOFTMAX, "sigmoid": _lib.MOE_SCORE_SIGMOID}
+    if score_func not in funcs:
+        raise ValueError("score_func must be 'sigmoid' or 'softmax'")
+    _chk(expert_bias, "expert_bias", torch.float32)
+    _chk(tokens_per_expert, "tokens_per_expert", torch.float32)
+    cfg = _lib.RouterConfig(funcs[score_func], float(route_scale),
+                            expert_bias.data_ptr() if expert_bias is not None else None,
+                            int(num_expert_groups), int(num_limited_groups),
+                            tokens_per_expert.data_ptr() if tokens_per_expert is not None else None)
+    cfg._keep = (expert_bias, tokens_per_expert)   # the tensors outlive the struct's use
+    return cfg
+
+
+def _cfg_ptr(cfg):
+    import ctypes
+    return ctypes.addressof(cfg) if cfg is not None else None
+
+
+def update_expert_bias(expert_bias: torch.Tensor, tokens_per_expert: torch.Tensor,
+                       lr: float = 1e-3, num_recomputations: int = 1) -> None:
+    """In place: one auxiliary-loss-free bias step; clears the accumulator."""
+    E = expert_bias.shape[0]
+    _chk(expert_bias, "expert_bias", torch.float32, (E,))
+    _chk(tokens_per_expert, "tokens_per_expert", torch.float32, (E,))
+    _call("moe_update_expert_bias", expert_bias.data_ptr(), tokens_per_expert.data_ptr(), E,
+          float(lr), int(num_recomputations), _stream(expert_bias.device))
+
+
 def route(x: torch.Tensor, router_weight: torch.Tensor, top_k: int,
           norm_topk_prob: bool = True, router_bias: Optional[torch.Tensor] = None,
-          with_logits: bool = True, with_counts: bool = True):
-    """Router logits, top-k ids and routing weights (and tokens per expert)."""
+          with_logits: bool = True, with_counts: bool = True, config=None):
+    """Router logits, top-k ids and routing weights (and tokens per expert).
+    ``config`` (from ``router_config``) selects a router variant."""
     T, H = x.shape
     E = router_weight.shape[0]
     dev = x.device
@@ -91,9 +128,10 @@ def route(x: torch.Tensor, router_weight: torch.Tensor, top_k: int,
     ids = torch.empty(T, top_k, dtype=torch.int32, device=dev)
     w = torch.empty(T, top_k, dtype=torch.float32, device=dev)
     counts = torch.empty(E, dtype=torch.int32, device=dev) if with_counts else None
-    _call("moe_route", x.data_ptr(), router_weight.data_ptr(), _chk(router_bias, "router_bias"),
-          T, H, E, top_k, int(norm_topk_prob), _dt(x), _chk(logits, "logits"), ids.data_ptr(),
-          w.data_ptr(), _chk(counts, "counts"), _stream(dev))
+    _call("moe_route_cfg", x.data_ptr(), router_weight.data_ptr(),
+          _chk(router_bias, "router_bias"), T, H, E, top_k, int(norm_topk_prob), _dt(x),
+          _cfg_ptr(config), _chk(logits, "logits"), ids.data_ptr(), w.data_ptr(),
+          _chk(counts, "counts"), _stream(dev))
     return logits, ids, w, counts
 
 
@@ -243,9 +281,10 @@ class LayerBuffers:
 def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
                   down: torch.Tensor, top_k: int, norm_topk_prob: bool = True,
                   router_bias: Optional[torch.Tensor] = None,
-                  buffers: Optional[LayerBuffers] = None):
+                  buffers: Optional[LayerBuffers] = None, config=None):
     """The whole MoE layer forward; returns (out, router_logits, topk_ids,
-    topk_weights, num_tokens_per_expert)."""
+    topk_weights, num_tokens_per_expert).  ``config`` (from
+    ``router_config``) selects a router variant."""
     T, H = x.shape
     E = router_weight.shape[0]
     I = gate_up.shape[2] // 2
@@ -255,9 +294,9 @@ def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.T
     _chk(down, "down", x.dtype, (E, I, H))
     _chk(router_bias, "router_bias", torch.float32, (E,))
     b = buffers if buffers is not None else LayerBuffers(T, H, I, E, top_k, x.dtype, x.device)
-    _call("moe_layer_forward", x.data_ptr(), router_weight.data_ptr(),
+    _call("moe_layer_forward_cfg", x.data_ptr(), router_weight.data_ptr(),
           _chk(router_bias, "router_bias"), gate_up.data_ptr(), down.data_ptr(), T, H, I, E,
-          top_k, int(norm_topk_prob), _dt(x), b.out.data_ptr(), b.logits.data_ptr(),
-          b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(), b.workspace.data_ptr(),
-          b.ws_bytes, None, _stream(x.device))
+          top_k, int(norm_topk_prob), _dt(x), _cfg_ptr(config), b.out.data_ptr(),
+          b.logits.data_ptr(), b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(),
+          b.workspace.data_ptr(), b.ws_bytes, None, _stream(x.device))
     return b.out, b.logits, b.ids, b.weights, b.counts

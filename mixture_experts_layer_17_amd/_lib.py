@@ -21,13 +21,25 @@ MOE_OP_DOWN = 3
 MOE_OP_GROUPED_SWIGLU = 4
 MOE_OP_LAYER = 5
 
+MOE_SCORE_SOFTMAX = 0
+MOE_SCORE_SIGMOID = 1
+
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_UNSUPPORTED", -6: "MOE_ERR_HIP",
           -7: "MOE_ERR_ALIGN"}
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
+_f = ctypes.c_float
 _sz = ctypes.c_size_t
+
+
+class RouterConfig(ctypes.Structure):
+    """struct moe_router_config (include/libmoe.h)."""
+    _fields_ = [("score_func", ctypes.c_int), ("route_scale", ctypes.c_float),
+                ("expert_bias", ctypes.c_void_p), ("num_expert_groups", ctypes.c_int),
+                ("num_limited_groups", ctypes.c_int), ("tokens_per_expert", ctypes.c_void_p)]
+
 
 # name -> (restype, argtypes); must match include/libmoe.h
 SIGNATURES = {
@@ -43,6 +55,10 @@ SIGNATURES = {
     "moe_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p]),
     "moe_layer_forward": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
                                _p, _p, _sz, _p, _p]),
+    "moe_route_cfg": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
+    "moe_layer_forward_cfg": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
+                                   _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_update_expert_bias": (_i, [_p, _p, _i, _f, _i, _p]),
 }
 
 
@@ -56,7 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             f"libmoe.so not found at {path}; build it with "
-            "`python -m mixture_experts_layer_17_amd.build` (hipcc, gfx950)")
+            "`python mixture_experts_layer_17_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -1,6 +1,7 @@
 """Builds libmoe.so (gfx950) in-tree with hipcc.
 
-Usage: python -m mixture_experts_layer_17_amd.build  [--verbose]
+Usage: python mixture_experts_layer_17_amd/build.py  [--verbose]
+(run as a script: importing the package loads the library being built)
 """
 from __future__ import annotations
 

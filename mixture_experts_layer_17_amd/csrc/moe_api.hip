@@ -3,6 +3,8 @@
 #include <stdint.h>
 
 #include "../../include/libmoe.h"
+#include <cmath>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -81,6 +83,29 @@ size_t swiglu_ws(int N, int H, int I, int E, moe_dtype dt, size_t* h_bytes,
   return *h_bytes + *up_bytes + tile_list_bytes(N, E, cd.BM);
 }
 
+// Router variant from the public config (validated), or NULL for the
+// default softmax router.
+int router_variant(const moe_router_config* c, int E, int k, RouterVariant* out,
+                   const RouterVariant** use) {
+  *use = nullptr;
+  if (!c) return MOE_OK;
+  if (c->score_func != MOE_SCORE_SOFTMAX && c->score_func != MOE_SCORE_SIGMOID)
+    return MOE_ERR_UNSUPPORTED;
+  if (!std::isfinite(c->route_scale)) return MOE_ERR_SHAPE;
+  const int G = c->num_expert_groups;
+  if (G < 0) return MOE_ERR_SHAPE;
+  if (G > 0) {
+    if (E % G != 0 || c->num_limited_groups < 1 || c->num_limited_groups > G ||
+        (long long)k > (long long)c->num_limited_groups * (E / G))
+      return MOE_ERR_SHAPE;
+  }
+  *out = RouterVariant{c->score_func == MOE_SCORE_SIGMOID ? 1 : 0, c->route_scale,
+                       c->expert_bias, G, G > 0 ? c->num_limited_groups : 0,
+                       c->tokens_per_expert};
+  *use = out;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,16 +158,32 @@ size_t moe_workspace_size(int op, int T, int H, int I, int E, int top_k, int R, 
   }
 }
 
-int moe_route(const void* x, const void* wr, const float* bias, int T, int H, int E, int k,
-              int norm, moe_dtype dt, float* logits, int32_t* ids, float* w, int32_t* counts,
-              hipStream_t s) {
+int moe_route_cfg(const void* x, const void* wr, const float* bias, int T, int H, int E, int k,
+                  int norm, moe_dtype dt, const moe_router_config* cfg, float* logits,
+                  int32_t* ids, float* w, int32_t* counts, hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (T < 0 || !rows_ok(T) || E < 1 || E > kMaxE || k < 1 || k > E || H <= 0 || H % 64 != 0)
     return MOE_ERR_SHAPE;
+  RouterVariant rv;
+  const RouterVariant* var = nullptr;
+  const int st = router_variant(cfg, E, k, &rv, &var);
+  if (st != MOE_OK) return st;
   if (T > 0 && (!x || !wr || !ids || !w)) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(wr)) return MOE_ERR_ALIGN;
   return hip_status(launch_route(dt == MOE_BF16, x, wr, bias, T, H, E, k, norm, logits, ids, w,
-                                 counts, s));
+                                 counts, s, var));
+}
+
+int moe_route(const void* x, const void* wr, const float* bias, int T, int H, int E, int k,
+              int norm, moe_dtype dt, float* logits, int32_t* ids, float* w, int32_t* counts,
+              hipStream_t s) {
+  return moe_route_cfg(x, wr, bias, T, H, E, k, norm, dt, nullptr, logits, ids, w, counts, s);
+}
+
+int moe_update_expert_bias(float* bias, float* tpe, int E, float lr, int nrec, hipStream_t s) {
+  if (E < 1 || E > kMaxE || nrec < 1 || !std::isfinite(lr)) return MOE_ERR_SHAPE;
+  if (!bias || !tpe) return MOE_ERR_NULL;
+  return hip_status(launch_update_expert_bias(bias, tpe, E, lr, nrec, s));
 }
 
 int moe_permute(const int32_t* ids, int T, int k, const int32_t* C, int R, int N, int E,
@@ -247,14 +288,18 @@ int moe_combine(const void* y, const int32_t* slot_pos, const float* w, int T, i
   return hip_status(launch_combine(dt == MOE_BF16, y, slot_pos, w, T, k, H, out, s));
 }
 
-int moe_layer_forward(const void* x, const void* wr, const float* bias, const void* gate_up,
-                      const void* down, int T, int H, int I, int E, int k, int norm,
-                      moe_dtype dt, void* out, float* logits, int32_t* ids, float* weights,
-                      int32_t* counts, void* ws, size_t ws_bytes, hipEvent_t* stage_events,
-                      hipStream_t s) {
+int moe_layer_forward_cfg(const void* x, const void* wr, const float* bias,
+                          const void* gate_up, const void* down, int T, int H, int I, int E,
+                          int k, int norm, moe_dtype dt, const moe_router_config* cfg, void* out,
+                          float* logits, int32_t* ids, float* weights, int32_t* counts, void* ws,
+                          size_t ws_bytes, hipEvent_t* stage_events, hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
     return MOE_ERR_SHAPE;
+  RouterVariant rv;
+  const RouterVariant* var = nullptr;
+  const int st = router_variant(cfg, E, k, &rv, &var);
+  if (st != MOE_OK) return st;
   if (T > 0 && (!x || !wr || !gate_up || !down || !out)) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(wr) || !aligned16(gate_up) || !aligned16(down) ||
       !aligned16(out))
@@ -273,7 +318,8 @@ int moe_layer_forward(const void* x, const void* wr, const float* bias, const vo
   };
   mark(0);
   // the histogram comes from the permutation pass, so the router skips it
-  hipError_t e = launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr, s);
+  hipError_t e =
+      launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr, s, var);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(1);
   const GemmTileCfg cu = pick_gate_up_cfg(bf16, N, H, I, E);
@@ -300,6 +346,15 @@ int moe_layer_forward(const void* x, const void* wr, const float* bias, const vo
   e = launch_combine(bf16, w.y, nullptr, weights, T, k, H, out, s);
   mark(5);
   return hip_status(e);
+}
+
+int moe_layer_forward(const void* x, const void* wr, const float* bias, const void* gate_up,
+                      const void* down, int T, int H, int I, int E, int k, int norm,
+                      moe_dtype dt, void* out, float* logits, int32_t* ids, float* weights,
+                      int32_t* counts, void* ws, size_t ws_bytes, hipEvent_t* stage_events,
+                      hipStream_t s) {
+  return moe_layer_forward_cfg(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, nullptr, out,
+                               logits, ids, weights, counts, ws, ws_bytes, stage_events, s);
 }
 
 }  // extern "C"

@@ -16,9 +16,26 @@ struct GemmTileCfg {
 
 // Router: logits, top-k ids/weights, optional counts (counts must be zeroed
 // first; launch_fill_i32 does that).
+// Router variant (MindSpore moe.py, TokenChoiceTopKRouter.forward): scores
+// are sigmoid (or softmax) of the logits times `scale`; with groups > 0 only
+// the `limited` groups with the largest maximum score stay selectable;
+// selection ranks score + ebias[e]; weights are the unbiased scores.  tpe,
+// when set, accumulates the selections per expert.
+struct RouterVariant {
+  int sigmoid;
+  float scale;
+  const float* ebias;
+  int groups;
+  int limited;
+  float* tpe;
+};
+
 hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* bias,
                         int T, int H, int E, int k, int norm, float* logits,
-                        int32_t* ids, float* w, int32_t* counts, hipStream_t s);
+                        int32_t* ids, float* w, int32_t* counts, hipStream_t s,
+                        const RouterVariant* var = nullptr);
+hipError_t launch_update_expert_bias(float* bias, float* tpe, int E, float lr, int nrec,
+                                     hipStream_t s);
 
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 

@@ -127,25 +127,26 @@ __device__ __forceinline__ int rt_swz(int row) { return (row ^ ((row & 15) >> 3)
 // Wave w takes rows 2 w (lanes 0-31) and 2 w + 1 (lanes 32-63); each lane
 // holds the keys of experts hl, hl + 32, ... (CPL of them).  sel is LDS
 // scratch of 16 * k keys.
-template <int CPL>
-__device__ __forceinline__ void select_tokens(const float* s_log, int lde, uint64_t* sel_base,
-                                              int t0, int wave, int lane, int T_, int E, int k,
-                                              int norm, int32_t* __restrict__ ids_out,
-                                              float* __restrict__ w_out,
-                                              int32_t* __restrict__ counts) {
-  const int half = lane >> 5, hl = lane & 31;
-  const int trow = 2 * wave + half;
-  const int t = t0 + trow;
-  const float* L = s_log + trow * lde;
-  uint64_t* sel = sel_base + (size_t)trow * k;
+// Largest float over the 32 lanes of this lane's half-wave.
+__device__ __forceinline__ float half_max(float v, int half) {
+  v = fmaxf(v, __uint_as_float(dpp32<DPP_QUAD_1032>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp32<DPP_QUAD_2301>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp32<DPP_ROR4>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp32<DPP_ROR8>(__float_as_uint(v))));
+  const float a = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+  const float b = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 16));
+  const float c = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 32));
+  const float d = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 48));
+  return half ? fmaxf(c, d) : fmaxf(a, b);
+}
 
-  uint64_t cand[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int e = hl + 32 * c;
-    cand[c] = e < E ? rank_key(L[e], e) : 0ull;
-  }
-  // this lane's keys in descending order (insertion network)
+// The k largest of the half-wave's keys, in descending order, into sel[0..k):
+// each lane sorts its CPL keys, then k rounds take the half-wave's largest
+// head key (DPP row max, then the two rows), and the one lane holding it
+// advances to its next key (keys are unique).
+template <int CPL>
+__device__ __forceinline__ void select_keys(uint64_t (&cand)[CPL], uint64_t* sel, int k, int half,
+                                            int hl) {
 #pragma unroll
   for (int p = 1; p < CPL; ++p)
 #pragma unroll
@@ -168,6 +169,27 @@ __device__ __forceinline__ void select_tokens(const float* s_log, int lde, uint6
     if (pop) cand[CPL - 1] = 0ull;
     if (hl == 0) sel[j] = win;
   }
+}
+
+template <int CPL>
+__device__ __forceinline__ void select_tokens(const float* s_log, int lde, uint64_t* sel_base,
+                                              int t0, int wave, int lane, int T_, int E, int k,
+                                              int norm, int32_t* __restrict__ ids_out,
+                                              float* __restrict__ w_out,
+                                              int32_t* __restrict__ counts) {
+  const int half = lane >> 5, hl = lane & 31;
+  const int trow = 2 * wave + half;
+  const int t = t0 + trow;
+  const float* L = s_log + trow * lde;
+  uint64_t* sel = sel_base + (size_t)trow * k;
+
+  uint64_t cand[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = hl + 32 * c;
+    cand[c] = e < E ? rank_key(L[e], e) : 0ull;
+  }
+  select_keys<CPL>(cand, sel, k, half, hl);
   // LDS accesses of one wave complete in order, so the keys written above
   // are visible to the reads below
   const float m = key_value(sel[0]);          // the largest logit
@@ -199,6 +221,114 @@ __device__ __forceinline__ void select_tokens(const float* s_log, int lde, uint6
   }
 }
 
+// The router variant's epilogue (MindSpore moe.py, TokenChoiceTopKRouter:
+// score function, route_scale, node-limited groups, selection-only expert
+// bias).  Same lane layout as select_tokens; the token's logits row in LDS
+// is overwritten with its scores; gscr holds 16 rows of E floats for the
+// group maxima.
+template <int CPL>
+__device__ __forceinline__ void select_tokens_var(float* s_log, int lde, uint64_t* sel_base,
+                                                  float* gscr, int t0, int wave, int lane,
+                                                  int T_, int E, int k, int norm,
+                                                  const RouterVariant& v,
+                                                  int32_t* __restrict__ ids_out,
+                                                  float* __restrict__ w_out,
+                                                  int32_t* __restrict__ counts) {
+  const int half = lane >> 5, hl = lane & 31;
+  const int trow = 2 * wave + half;
+  const int t = t0 + trow;
+  float* L = s_log + trow * lde;
+  uint64_t* sel = sel_base + (size_t)trow * k;
+
+  // scores: sigmoid, or softmax over the experts, then times the scale
+  float sc[CPL];
+  if (v.sigmoid) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = hl + 32 * c;
+      sc[c] = e < E ? (1.0f / (1.0f + expf(-L[e]))) * v.scale : 0.f;
+    }
+  } else {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = hl + 32 * c;
+      if (e < E) mx = fmaxf(mx, L[e]);
+    }
+    mx = half_max(mx, half);
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = hl + 32 * c;
+      sc[c] = e < E ? expf(L[e] - mx) : 0.f;
+      part += sc[c];
+    }
+    const float den = half_sum(part, half);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) sc[c] = (sc[c] / den) * v.scale;
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = hl + 32 * c;
+    if (e < E) L[e] = sc[c];
+  }
+  // node-limited routing: group maxima, then each expert's group rank
+  bool keep[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) keep[c] = true;
+  if (v.groups > 0) {
+    const int epg = E / v.groups;
+    float* gm = gscr + trow * E;
+    for (int gi = hl; gi < v.groups; gi += 32) {
+      float m = -INFINITY;
+      for (int q = 0; q < epg; ++q) m = fmaxf(m, L[gi * epg + q]);
+      gm[gi] = m;
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = hl + 32 * c;
+      if (e < E) {
+        const int gi = e / epg;
+        const float mine = gm[gi];
+        int rank = 0;
+        for (int gj = 0; gj < v.groups; ++gj) {
+          const float o = gm[gj];
+          rank += (o > mine || (o == mine && gj < gi)) ? 1 : 0;
+        }
+        keep[c] = rank < v.limited;
+      }
+    }
+  }
+  uint64_t cand[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = hl + 32 * c;
+    const float key = sc[c] + (v.ebias ? v.ebias[min(e, E - 1)] : 0.f);
+    cand[c] = (e < E && keep[c]) ? rank_key(key, e) : 0ull;
+  }
+  select_keys<CPL>(cand, sel, k, half, hl);
+  // weights: the unbiased scores of the selected experts
+  float sp = 0.f;
+  for (int jb = 0; jb < k; jb += 32) {
+    const int j = jb + hl;
+    if (j < k) sp += L[key_expert(sel[j])];
+  }
+  const float selsum = half_sum(sp, half);
+  if (t < T_) {
+    for (int jb = 0; jb < k; jb += 32) {
+      const int j = jb + hl;
+      if (j < k) {
+        const int e = key_expert(sel[j]);
+        const float s = L[e];
+        ids_out[(size_t)t * k + j] = e;
+        w_out[(size_t)t * k + j] = norm ? s / selsum : s;
+        if (counts) atomicAdd(&counts[e], 1);
+        if (v.tpe) atomicAdd(&v.tpe[e], 1.0f);
+      }
+    }
+  }
+}
+
 template <typename T, int NT>
 struct rcfg {
   static constexpr int KB = 128 / (int)sizeof(T);   // K elements per block (128-byte rows)
@@ -215,12 +345,12 @@ struct rcfg {
   static_assert(ROWS % 8 == 0, "whole copy instructions");
 };
 
-template <typename T, int NT>
+template <typename T, int NT, bool VAR>
 __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias,
     int T_, int H, int E, int k, int norm, float* __restrict__ logits_out,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-    int32_t* __restrict__ counts) {
+    int32_t* __restrict__ counts, RouterVariant var) {
   using C = rcfg<T, NT>;
   constexpr int NS = C::NS;
   // NS ring stages of [x rows | Wr rows] x 128 bytes, then the logits
@@ -340,8 +470,13 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(
 
   // ---- top-k epilogue; the ring is free for the selected keys (every wave
   // passed the barrier above after its last LDS read of the ring)
-  select_tokens<C::CPL>(s_log, C::LDE, reinterpret_cast<uint64_t*>(smem), t0, wave, lane, T_, E,
-                        k, norm, ids_out, w_out, counts);
+  if constexpr (VAR)
+    select_tokens_var<C::CPL>(s_log, C::LDE, reinterpret_cast<uint64_t*>(smem),
+                              reinterpret_cast<float*>(smem + RT_TOK * k * 8), t0, wave, lane, T_,
+                              E, k, norm, var, ids_out, w_out, counts);
+  else
+    select_tokens<C::CPL>(s_log, C::LDE, reinterpret_cast<uint64_t*>(smem), t0, wave, lane, T_,
+                          E, k, norm, ids_out, w_out, counts);
 }
 
 // ---- Small-batch path.  With few tokens the kernel above runs on few CUs,
@@ -408,14 +543,15 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
 }
 
 // Selection for 16 tokens from their logits in global memory.
-template <int NT>
+template <int NT, bool VAR>
 __global__ __launch_bounds__(RT_WAVES * 64) void route_select_kernel(
     const float* __restrict__ logits, int T_, int E, int k, int norm,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ counts) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
+    RouterVariant var) {
   constexpr int LDE = NT * 16 + 4;
   constexpr int CPL = (NT * 16 + 31) / 32;
   __shared__ float s_log[RT_TOK * LDE];
-  extern __shared__ __align__(16) unsigned char s_sel[];   // 16 * k keys
+  extern __shared__ __align__(16) unsigned char s_sel[];   // 16 * k keys (+ 16 * E floats)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * RT_TOK;
@@ -424,8 +560,13 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_select_kernel(
     s_log[tr * LDE + e] = logits[(size_t)min(t0 + tr, T_ - 1) * E + e];
   }
   __syncthreads();
-  select_tokens<CPL>(s_log, LDE, reinterpret_cast<uint64_t*>(s_sel), t0, wave, lane, T_, E, k,
-                     norm, ids_out, w_out, counts);
+  if constexpr (VAR)
+    select_tokens_var<CPL>(s_log, LDE, reinterpret_cast<uint64_t*>(s_sel),
+                           reinterpret_cast<float*>(s_sel + RT_TOK * k * 8), t0, wave, lane, T_, E,
+                           k, norm, var, ids_out, w_out, counts);
+  else
+    select_tokens<CPL>(s_log, LDE, reinterpret_cast<uint64_t*>(s_sel), t0, wave, lane, T_, E, k,
+                       norm, ids_out, w_out, counts);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
@@ -433,17 +574,18 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
-template <typename V, int NT>
+template <typename V, int NT, bool VAR>
 hipError_t launch_route_t(const void* x, const void* wr, const float* bias, int T, int H, int E,
                           int k, int norm, float* logits, int32_t* ids, float* w,
-                          int32_t* counts, hipStream_t s) {
+                          int32_t* counts, hipStream_t s, const RouterVariant& var) {
   using C = rcfg<V, NT>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)route_kernel<V, NT>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)route_kernel<V, NT, VAR>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (attr != hipSuccess) return attr;
   const dim3 grid((T + RT_TOK - 1) / RT_TOK);
-  route_kernel<V, NT><<<grid, RT_WAVES * 64, C::LDS, s>>>((const V*)x, (const V*)wr, bias, T, H,
-                                                          E, k, norm, logits, ids, w, counts);
+  route_kernel<V, NT, VAR><<<grid, RT_WAVES * 64, C::LDS, s>>>(
+      (const V*)x, (const V*)wr, bias, T, H, E, k, norm, logits, ids, w, counts, var);
   return hipGetLastError();
 }
 
@@ -457,12 +599,15 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
 
 hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* bias,
                         int T, int H, int E, int k, int norm, float* logits,
-                        int32_t* ids, float* w, int32_t* counts, hipStream_t s) {
+                        int32_t* ids, float* w, int32_t* counts, hipStream_t s,
+                        const RouterVariant* var) {
   if (counts) {
     hipError_t e = launch_fill_i32(counts, E, 0, s);
     if (e != hipSuccess) return e;
   }
   if (T <= 0) return hipSuccess;
+  const RouterVariant v = var ? *var : RouterVariant{0, 1.0f, nullptr, 0, 0, nullptr};
+  const bool isvar = var != nullptr;
   const int nt = (E + 15) / 16;
   const int tiles = (T + RT_TOK - 1) / RT_TOK;
   // Small batches (and a logits buffer to pass through) take the split path.
@@ -476,10 +621,19 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
                                                     E, logits);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t sel_bytes = (size_t)RT_TOK * k * sizeof(uint64_t);
-#define MOE_SELECT(NT)                                                                        \
-  route_select_kernel<NT><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(logits, T, E, k, norm, ids, w, \
-                                                                  counts)
+    const size_t sel_bytes = (size_t)RT_TOK * k * sizeof(uint64_t) +
+                             (isvar ? (size_t)RT_TOK * E * sizeof(float) : 0);
+#define MOE_SELECT(NT)                                                                          \
+  do {                                                                                          \
+    if (isvar)                                                                                  \
+      route_select_kernel<NT, true><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(logits, T, E, k,   \
+                                                                            norm, ids, w,      \
+                                                                            counts, v);        \
+    else                                                                                        \
+      route_select_kernel<NT, false><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(logits, T, E, k,  \
+                                                                             norm, ids, w,     \
+                                                                             counts, v);       \
+  } while (0)
     if (nt <= 1) MOE_SELECT(1);
     else if (nt <= 2) MOE_SELECT(2);
     else if (nt <= 4) MOE_SELECT(4);
@@ -488,17 +642,62 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
 #undef MOE_SELECT
     return hipGetLastError();
   }
-#define MOE_ROUTE(NT)                                                                        \
-  return bf16 ? launch_route_t<bf16_t, NT>(x, wr, bias, T, H, E, k, norm, logits, ids, w,    \
-                                           counts, s)                                        \
-              : launch_route_t<float, NT>(x, wr, bias, T, H, E, k, norm, logits, ids, w,     \
-                                          counts, s)
+#define MOE_ROUTE(NT)                                                                         \
+  return bf16 ? (isvar ? launch_route_t<bf16_t, NT, true>(x, wr, bias, T, H, E, k, norm,     \
+                                                          logits, ids, w, counts, s, v)      \
+                       : launch_route_t<bf16_t, NT, false>(x, wr, bias, T, H, E, k, norm,    \
+                                                           logits, ids, w, counts, s, v))    \
+              : (isvar ? launch_route_t<float, NT, true>(x, wr, bias, T, H, E, k, norm,      \
+                                                         logits, ids, w, counts, s, v)       \
+                       : launch_route_t<float, NT, false>(x, wr, bias, T, H, E, k, norm,     \
+                                                          logits, ids, w, counts, s, v))
   if (nt <= 1) MOE_ROUTE(1);
   if (nt <= 2) MOE_ROUTE(2);
   if (nt <= 4) MOE_ROUTE(4);
   if (nt <= 8) MOE_ROUTE(8);
   MOE_ROUTE(16);
 #undef MOE_ROUTE
+}
+
+// Expert-bias step (MindSpore moe.py, MoE.update_expert_bias): one
+// workgroup; sums in a fixed tree.
+__global__ __launch_bounds__(256) void update_expert_bias_kernel(float* __restrict__ bias,
+                                                                 float* __restrict__ tpe, int E,
+                                                                 float lr, int nrec) {
+  __shared__ float s_v[256];
+  const int t = threadIdx.x;
+  float c = t < E ? tpe[t] : 0.f;
+  if (nrec > 1) c = c / (float)nrec;
+  s_v[t] = c;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) s_v[t] += s_v[t + off];
+    __syncthreads();
+  }
+  const float avg = s_v[0] / (float)E;
+  __syncthreads();
+  float d = 0.f;
+  if (t < E) {
+    const float diff = avg - c;
+    d = lr * (diff > 0.f ? 1.f : (diff < 0.f ? -1.f : 0.f));
+  }
+  s_v[t] = d;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) s_v[t] += s_v[t + off];
+    __syncthreads();
+  }
+  const float dm = s_v[0] / (float)E;
+  if (t < E) {
+    bias[t] += d - dm;
+    tpe[t] = 0.f;
+  }
+}
+
+hipError_t launch_update_expert_bias(float* bias, float* tpe, int E, float lr, int nrec,
+                                     hipStream_t s) {
+  update_expert_bias_kernel<<<1, 256, 0, s>>>(bias, tpe, E, lr, nrec);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -64,3 +64,23 @@ def test_validation_happens_before_any_launch(lib):
     assert lib.moe_combine(fake, None, None, 4, 0, 128, 1, fake, None) == -2
     assert lib.moe_grouped_down(fake, fake, None, 8, 128, 64, 8, fake, 1, fake, fake, 8, None) == -4
     assert lib.moe_gather_rows(None, 4, fake, 8, 128, 1, fake, None) == -1
+
+
+def test_router_variant_validation(lib):
+    fake = 4096  # never dereferenced: every call below fails validation
+    cfg = _lib.RouterConfig(7, 1.0, None, 0, 0, None)          # unknown score function
+    args = lambda c, k=2: (fake, fake, None, 4, 128, 8, k, 1, 1, ctypes.addressof(c), None, fake,
+                           fake, None, None)
+    assert lib.moe_route_cfg(*args(cfg)) == -5
+    cfg = _lib.RouterConfig(1, 1.0, None, 3, 1, None)          # 8 experts in 3 groups
+    assert lib.moe_route_cfg(*args(cfg)) == -2
+    cfg = _lib.RouterConfig(1, 1.0, None, 4, 1, None)          # top_k 3 > 1 group of 2
+    assert lib.moe_route_cfg(*args(cfg, 3)) == -2
+    cfg = _lib.RouterConfig(1, 1.0, None, 4, 5, None)          # more kept groups than groups
+    assert lib.moe_route_cfg(*args(cfg)) == -2
+    cfg = _lib.RouterConfig(1, float("inf"), None, 0, 0, None)
+    assert lib.moe_route_cfg(*args(cfg)) == -2
+    assert lib.moe_update_expert_bias(fake, fake, 0, 1e-3, 1, None) == -2
+    assert lib.moe_update_expert_bias(fake, fake, 300, 1e-3, 1, None) == -2
+    assert lib.moe_update_expert_bias(fake, fake, 8, 1e-3, 0, None) == -2
+    assert lib.moe_update_expert_bias(None, fake, 8, 1e-3, 1, None) == -1

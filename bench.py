@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--workload", default="qwen3_30b_a3b_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--router", default="softmax", choices=["softmax", "sigmoid-groups"],
+                    help="softmax: the default router; sigmoid-groups: sigmoid scores, route "
+                         "scale 2.5, 8 expert groups of which 4 are kept, a selection-only "
+                         "expert bias")
     return ap.parse_args()
 
 
@@ -179,6 +183,12 @@ def main():
     out = torch.empty(T, H, dtype=wl.dtype, device=dev)
     L = moe.lib
 
+    cfg = None
+    if args.router == "sigmoid-groups":
+        g = torch.Generator().manual_seed(1)
+        ebias = (torch.randn(E, generator=g) * 0.05).to(dev)
+        cfg = moe.router_config("sigmoid", 2.5, ebias, 8, 4)
+    cfg_p = ctypes.addressof(cfg) if cfg is not None else None
     nws = L.moe_workspace_size(_lib.MOE_OP_LAYER, T, H, I, E, k, 0, N, dt)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     s = torch.cuda.current_stream(dev)
@@ -201,9 +211,9 @@ def main():
         return ev
 
     def step(evs=None):
-        st = L.moe_layer_forward(P(x), P(wr), P(bias), P(gu), P(dn), T, H, I, E, k,
-                                 int(wl.norm_topk_prob), dt, P(out), P(logits), P(ids), P(w),
-                                 P(counts), P(ws), nws, evs, sp)
+        st = L.moe_layer_forward_cfg(P(x), P(wr), P(bias), P(gu), P(dn), T, H, I, E, k,
+                                     int(wl.norm_topk_prob), dt, cfg_p, P(out), P(logits), P(ids),
+                                     P(w), P(counts), P(ws), nws, evs, sp)
         if st != 0:
             raise RuntimeError(f"moe_layer_forward failed with status {st}")
 
@@ -283,7 +293,7 @@ def main():
         "data": "synthetic: seeded Gaussian inputs and random-init weights of the named layer shape",
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "top_k": k,
                    "norm_topk_prob": wl.norm_topk_prob, "routed_rows": N,
-                   "experts_hit": hit},
+                   "experts_hit": hit, "router": args.router},
         "layer_tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "layer_mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / peak_f, 4),
         "roofline": roof,

@@ -23,7 +23,8 @@ Pages and sections cited below:
   (gate -> fp32 softmax -> top-k -> optional renormalisation).
 * [HP] MindSpore hyper-parallel coverage page for ``moe.py``:
   ``TokenChoiceTopKRouter.forward``, ``_run_experts_for_loop``,
-  ``MoE.permutation``, ``MoE.unpermutation``, ``MoE.forward``.
+  ``MoE.permutation``, ``MoE.unpermutation``, ``MoE.forward``, and
+  ``FeedForward`` (the always-active shared expert).
 * [TP] transformers PR "Qwen3 moe": ``Ep2DpParallel._token_dispatch`` (layout of
   the rows one expert-parallel rank receives) and ``_token_combine``.
 * [ED] transformers "Expert parallelism" docs, section "Token dispatch"
@@ -48,7 +49,7 @@ __all__ = [
     "router_logits", "select_topk", "routing_weights", "route",
     "router_scores", "limited_group_mask", "route_variant", "update_expert_bias",
     "expert_counts", "expert_offsets", "permutation", "gather_rows",
-    "silu", "swiglu_expert", "grouped_swiglu", "combine", "unpermute",
+    "silu", "swiglu_expert", "grouped_swiglu", "combine", "unpermute", "feed_forward",
     "moe_layer_forward", "moe_layer_forward_brute", "moe_layer_forward_tokens",
     "dispatch_rank_major", "reshuffle_rank_to_expert", "ep_rank_forward",
 ]
@@ -320,18 +321,42 @@ def unpermute(y_expert_major, slot_pos) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Shared expert  ([HP] FeedForward; MoE.forward adds its output to the
+# unpermuted routed output)
+# ---------------------------------------------------------------------------
+
+def feed_forward(x, w1, w2, w3) -> np.ndarray:
+    """[HP] ``FeedForward.forward``: ``w2(silu(w1(x)) * w3(x))`` with the
+    weights as ``nn.Linear`` stores them (``w1``, ``w3``: [Is, H]; ``w2``:
+    [H, Is]; no bias), so a linear layer maps a row ``x`` to ``x W^T``."""
+    x = _f64(x)
+    return (silu(x @ _f64(w1).T) * (x @ _f64(w3).T)) @ _f64(w2).T
+
+
+def _add_shared(out, x, shared):
+    """[HP] ``MoE.forward``: the shared expert sees every token (``x_flat``)
+    and its output is added, unweighted, after the unpermutation."""
+    if shared is None:
+        return out, None
+    s = feed_forward(x, *shared)
+    return out + s, s
+
+
+# ---------------------------------------------------------------------------
 # The layer  ([QO] SpeedupMoeSparseMoeBlock.forward + SpeedupMoeExperts training
 # path; [HP] MoE.forward)
 # ---------------------------------------------------------------------------
 
 def moe_layer_forward(x, w_router, bias, gate_up, down, top_k: int,
-                      norm_topk_prob: bool) -> dict:
-    """Full layer: route, permute, per-expert SwiGLU loop, combine.
+                      norm_topk_prob: bool, shared=None) -> dict:
+    """Full layer: route, permute, per-expert SwiGLU loop, combine, and the
+    optional shared expert ``shared = (w1, w2, w3)`` (``FeedForward`` weights).
 
     Returns a dict with ``logits`` (float32 [T, E]), ``ids`` ([T, k]),
     ``weights`` ([T, k] float64), ``counts``, ``offsets``, ``sorted_slot``,
     ``sorted_token``, ``slot_pos``, ``y`` (expert-major expert outputs, float64
-    [N, H]) and ``out`` (float64 [T, H])."""
+    [N, H]), ``shared_out`` (float64 [T, H] or None) and ``out`` (float64
+    [T, H])."""
     x = np.asarray(x)
     E = np.asarray(w_router).shape[0]
     L, ids, w = route(x, w_router, bias, top_k, norm_topk_prob)
@@ -344,14 +369,14 @@ def moe_layer_forward(x, w_router, bias, gate_up, down, top_k: int,
         if hi == lo:
             continue
         y[lo:hi] = swiglu_expert(gather_rows(x, sorted_token[lo:hi]), gate_up[e], down[e])
-    out = combine(unpermute(y, slot_pos), w)
+    out, shared_out = _add_shared(combine(unpermute(y, slot_pos), w), x, shared)
     return dict(logits=L, ids=ids, weights=w, counts=counts, offsets=offsets,
                 sorted_slot=sorted_slot, sorted_token=sorted_token,
-                slot_pos=slot_pos, y=y, out=out)
+                slot_pos=slot_pos, y=y, shared_out=shared_out, out=out)
 
 
 def moe_layer_forward_brute(x, w_router, bias, gate_up, down, top_k: int,
-                            norm_topk_prob: bool) -> np.ndarray:
+                            norm_topk_prob: bool, shared=None) -> np.ndarray:
     """Every expert applied to every token, then masked by the selection and
     weighted ([QO] ``SpeedupMoeExperts`` eval path: ``bmm`` over all experts,
     one-hot mask times routing weights, sum over experts).  Small inputs only."""
@@ -363,11 +388,12 @@ def moe_layer_forward_brute(x, w_router, bias, gate_up, down, top_k: int,
         y_all = swiglu_expert(x, gate_up[e], down[e])          # [T, H]
         mask_w = np.where(ids == e, w, 0.0).sum(axis=1)        # [T]
         out += mask_w[:, None] * y_all
-    return out
+    return _add_shared(out, x, shared)[0]
 
 
 def moe_layer_forward_tokens(x, w_router, bias, gate_up, down, top_k: int,
-                             norm_topk_prob: bool, tokens: Sequence[int]) -> dict:
+                             norm_topk_prob: bool, tokens: Sequence[int],
+                             shared=None) -> dict:
     """The layer output for a chosen subset of tokens only.  Each token is
     routed and combined on its own, so its row equals the full layer's row
     ([QO] per-token reading of the forward).  Used to spot-check large
@@ -379,6 +405,7 @@ def moe_layer_forward_tokens(x, w_router, bias, gate_up, down, top_k: int,
         for e in np.unique(ids[:, j]):
             rows = np.flatnonzero(ids[:, j] == e)
             out[rows] += w[rows, j:j + 1] * swiglu_expert(xs[rows], gate_up[int(e)], down[int(e)])
+    out, _ = _add_shared(out, xs, shared)
     return dict(logits=L, ids=ids, weights=w, out=out)
 
 

@@ -27,7 +27,12 @@ What pins what:
   selection (closed form), sigmoid weights against scipy's expit, the
   softmax variant against the default router, a hand-worked group example,
   and the group invariant on random inputs;
-* expert-bias update: hand-worked steps, zero-mean steps, recomputation.
+* expert-bias update: hand-worked steps, zero-mean steps, recomputation;
+* shared expert: the FeedForward formula by scalar loops on tiny inputs
+  (nn.Linear convention, gate w1 and up w3 kept apart), the closed form at
+  H = Is = 1, routed experts that are copies of the shared one (the output is
+  (1 + sum of the routing weights) times the FFN), zero routed outputs, and
+  the all-expert brute-force path.
 """
 from __future__ import annotations
 
@@ -476,6 +481,108 @@ def pin_update_expert_bias_worked():
     r = _rng(5)
     d, _ = O.update_expert_bias(np.zeros(64), r.integers(0, 100, 64).astype(float), lr=0.01)
     assert abs(d.sum()) < 1e-12
+
+
+# ---- shared expert ----------------------------------------------------------
+
+def _ffn_loops(x, w1, w2, w3):
+    """FeedForward row by row with scalar loops: a linear layer with weight
+    W [out, in] maps x to y[o] = sum_i W[o][i] x[i]."""
+    out = []
+    for row in np.asarray(x, np.float64).tolist():
+        h = []
+        for i in range(len(w1)):
+            g = sum(a * b for a, b in zip(np.asarray(w1[i], np.float64).tolist(), row))
+            u = sum(a * b for a, b in zip(np.asarray(w3[i], np.float64).tolist(), row))
+            h.append(g / (1.0 + math.exp(-g)) * u)
+        out.append([sum(a * b for a, b in zip(np.asarray(w2[o], np.float64).tolist(), h))
+                    for o in range(len(w2))])
+    return np.array(out)
+
+
+def _ffn_weights(r, H, Is, scale=0.5):
+    return (r.standard_normal((Is, H)) * scale, r.standard_normal((H, Is)) * scale,
+            r.standard_normal((Is, H)) * scale)
+
+
+def pin_feed_forward_loops():
+    r = _rng(21)
+    x = r.standard_normal((3, 4))
+    w1, w2, w3 = _ffn_weights(r, 4, 5)
+    assert np.allclose(O.feed_forward(x, w1, w2, w3), _ffn_loops(x, w1, w2, w3),
+                       rtol=1e-13, atol=1e-15)
+
+
+def pin_feed_forward_scalar():
+    # H = Is = 1: out = c * silu(a x) * (b x), gate a = w1, up b = w3, down c = w2
+    for x, a, b, c in ((1.5, 2.0, -0.5, 3.0), (-2.0, 0.25, 4.0, -1.0), (0.0, 1.0, 1.0, 1.0),
+                       (3.0, 0.0, 2.0, 5.0)):
+        z = a * x
+        ref = c * (z / (1.0 + math.exp(-z))) * (b * x)
+        got = O.feed_forward([[x]], [[a]], [[c]], [[b]])
+        assert got.shape == (1, 1) and abs(got[0, 0] - ref) <= 1e-15 * max(1.0, abs(ref))
+    # silu(0) = 0 kills the row whatever the up projection is
+    assert O.feed_forward([[1.0]], [[0.0]], [[7.0]], [[9.0]])[0, 0] == 0.0
+
+
+def _routed_copies(w1, w2, w3, E):
+    """Routed experts in the concatenated layout that equal FeedForward(w1, w2,
+    w3): gate columns x w1^T first, then up x w3^T; down is w2^T."""
+    gu = np.concatenate([np.asarray(w1).T, np.asarray(w3).T], axis=1)
+    return np.repeat(gu[None], E, 0), np.repeat(np.asarray(w2).T[None], E, 0)
+
+
+def pin_shared_equals_routed_copies():
+    r = _rng(22)
+    T, H, Is, E, k = 12, 6, 4, 5, 2
+    x = r.standard_normal((T, H))
+    wr = r.standard_normal((E, H)).astype(np.float32)
+    w1, w2, w3 = _ffn_weights(r, H, Is)
+    gu, dn = _routed_copies(w1, w2, w3, E)
+    ffn = _ffn_loops(x, w1, w2, w3)
+    for norm in (True, False):
+        res = O.moe_layer_forward(x, wr, None, gu, dn, k, norm, shared=(w1, w2, w3))
+        wsum = res["weights"].sum(axis=1, keepdims=True)
+        if norm:
+            assert np.allclose(wsum, 1.0, atol=1e-15)
+        else:
+            assert np.all(wsum < 1.0)
+        # the routed part is the FFN times the weight sum; the shared part is
+        # added once, unweighted
+        assert np.allclose(res["out"], (1.0 + wsum) * ffn, rtol=1e-12, atol=1e-13)
+        assert np.allclose(res["shared_out"], ffn, rtol=1e-12, atol=1e-13)
+
+
+def pin_shared_zero_routed():
+    r = _rng(23)
+    T, H, I, Is, E, k = 9, 8, 6, 10, 4, 3
+    x = r.standard_normal((T, H))
+    wr = r.standard_normal((E, H)).astype(np.float32)
+    gu = r.standard_normal((E, H, 2 * I))
+    w1, w2, w3 = _ffn_weights(r, H, Is)
+    res = O.moe_layer_forward(x, wr, None, gu, np.zeros((E, I, H)), k, True, shared=(w1, w2, w3))
+    assert np.allclose(res["out"], _ffn_loops(x, w1, w2, w3), rtol=1e-12, atol=1e-13)
+    # a shared expert with zero down projection adds nothing
+    dn = r.standard_normal((E, I, H))
+    a = O.moe_layer_forward(x, wr, None, gu, dn, k, True, shared=(w1, np.zeros((H, Is)), w3))
+    b = O.moe_layer_forward(x, wr, None, gu, dn, k, True)
+    assert np.array_equal(a["out"], b["out"]) and b["shared_out"] is None
+
+
+def pin_shared_brute_and_tokens():
+    r = _rng(24)
+    T, H, I, Is, E, k = 16, 8, 4, 12, 6, 2
+    x = r.standard_normal((T, H)).astype(np.float32)
+    wr = r.standard_normal((E, H)).astype(np.float32)
+    gu = r.standard_normal((E, H, 2 * I)) * 0.5
+    dn = r.standard_normal((E, I, H)) * 0.5
+    sh = _ffn_weights(r, H, Is)
+    full = O.moe_layer_forward(x, wr, None, gu, dn, k, False, shared=sh)["out"]
+    brute = O.moe_layer_forward_brute(x, wr, None, gu, dn, k, False, shared=sh)
+    assert np.allclose(full, brute, rtol=1e-12, atol=1e-12)
+    toks = [3, 0, 15, 7]
+    sub = O.moe_layer_forward_tokens(x, wr, None, gu, dn, k, False, toks, shared=sh)["out"]
+    assert np.allclose(sub, full[toks], rtol=1e-12, atol=1e-12)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

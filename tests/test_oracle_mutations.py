@@ -100,8 +100,21 @@ def _uncentred_bias_update(expert_bias, tokens_per_expert, lr=1e-3, num_recomput
     return np.asarray(expert_bias, np.float64) + lr * np.sign(tpe.mean() - tpe), np.zeros_like(tpe)
 
 
+def _ffn_gate_up_swapped(x, w1, w2, w3):
+    return _orig["feed_forward"](x, w3, w2, w1)
+
+
+def _shared_weighted(out, x, shared):
+    # the shared output scaled as if it carried a routing weight
+    if shared is None:
+        return out, None
+    s = 0.5 * _orig["feed_forward"](x, *shared)
+    return out + s, s
+
+
 _orig = {n: getattr(O, n) for n in ("routing_weights", "combine", "permutation",
-                                     "router_logits", "expert_offsets", "route_variant")}
+                                     "router_logits", "expert_offsets", "route_variant",
+                                     "feed_forward")}
 
 MUTATIONS = {
     "swiglu_expert": _swapped_gate_up,
@@ -115,6 +128,8 @@ MUTATIONS = {
     "route_variant": _biased_weights,
     "limited_group_mask": _group_sum_mask,
     "update_expert_bias": _uncentred_bias_update,
+    "feed_forward": _ffn_gate_up_swapped,
+    "_add_shared": _shared_weighted,
 }
 
 

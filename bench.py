@@ -13,6 +13,9 @@ Other modes:
   --workload NAME        another named workload (decode, skewed, tiny)
   --copy-calibration     only run a plain 1 GiB device copy (for scaling the
                          rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+  --router sigmoid-groups  a sigmoid, node-limited, biased router variant
+  --shared-I IS          add a shared expert (FeedForward) of intermediate
+                         size IS
 """
 from __future__ import annotations
 
@@ -47,10 +50,12 @@ def parse():
                     help="softmax: the default router; sigmoid-groups: sigmoid scores, route "
                          "scale 2.5, 8 expert groups of which 4 are kept, a selection-only "
                          "expert bias")
+    ap.add_argument("--shared-I", type=int, default=0,
+                    help="intermediate size of a shared expert (0: none)")
     return ap.parse_args()
 
 
-def algorithmic(wl, counts):
+def algorithmic(wl, counts, Is=0, fused=False):
     """Per-kernel algorithmic FLOPs and HBM bytes for one layer pass.
     Weights count once per expert that received rows; gathered rows count
     once per token; intermediates count once written and once read."""
@@ -72,6 +77,19 @@ def algorithmic(wl, counts):
         "down": hit * I * H * es + N * I * es + N * H * es,
         "combine": N * H * es + N * 4 + T * H * es,
     }
+    if Is and fused:
+        # the shared expert inside the grouped launches: its weights once, x
+        # read once more, h written and read, its output written and then
+        # read by the combine
+        f["gate_up_swiglu"] += 2.0 * T * H * 2 * Is
+        b["gate_up_swiglu"] += H * 2 * Is * es + T * H * es + T * Is * es
+        f["down"] += 2.0 * T * Is * H
+        b["down"] += Is * H * es + T * Is * es + T * H * es
+        b["combine"] += T * H * es
+    elif Is:
+        # on its own, in the last stage with the combine
+        f["combine"] += 2.0 * T * H * 2 * Is + 2.0 * T * Is * H
+        b["combine"] += 3 * H * Is * es + T * H * es + 2 * T * Is * es + 2 * T * H * es
     return f, b, hit
 
 
@@ -87,7 +105,7 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
 
 
-def cpu_baseline(wl, budget_s=12.0):
+def cpu_baseline(wl, budget_s=12.0, shared=None):
     """The CPU oracle, as it stands, on this host: the whole workload, run
     until about budget_s seconds of work are done (at least once)."""
     import numpy as np
@@ -104,7 +122,7 @@ def cpu_baseline(wl, budget_s=12.0):
     bias = wl.router_bias.numpy() if wl.router_bias is not None else None
     runs, t0 = 0, time.perf_counter()
     while True:
-        O.moe_layer_forward(x, wr, bias, gu, dn, wl.top_k, wl.norm_topk_prob)
+        O.moe_layer_forward(x, wr, bias, gu, dn, wl.top_k, wl.norm_topk_prob, shared=shared)
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 5:
@@ -189,7 +207,23 @@ def main():
         ebias = (torch.randn(E, generator=g) * 0.05).to(dev)
         cfg = moe.router_config("sigmoid", 2.5, ebias, 8, 4)
     cfg_p = ctypes.addressof(cfg) if cfg is not None else None
-    nws = L.moe_workspace_size(_lib.MOE_OP_LAYER, T, H, I, E, k, 0, N, dt)
+    Is = args.shared_I
+    sh_w = sh_p = None
+    fused = False
+    kernels = KERNELS
+    if Is:
+        sh_w = workloads.shared_expert_weights(H, Is, wl.dtype)
+        w1, w2, w3 = sh_w
+        sgu = torch.cat([w1.t(), w3.t()], dim=1).contiguous().to(dev)
+        sdn = w2.t().contiguous().to(dev)
+        sh = moe.shared_expert(sgu, sdn)
+        sh_p = ctypes.addressof(sh)
+        # bf16 with Is a multiple of 128: the library runs the shared expert
+        # inside the two grouped GEMM launches, else in the last stage
+        fused = bf16 and Is % 128 == 0
+        if not fused:
+            kernels = KERNELS[:-1] + ("shared_ffn_combine",)
+    nws = L.moe_workspace_size(_lib.MOE_OP_LAYER, T, H, I, E, k, Is, N, dt)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     s = torch.cuda.current_stream(dev)
     sp = s.cuda_stream
@@ -211,9 +245,9 @@ def main():
         return ev
 
     def step(evs=None):
-        st = L.moe_layer_forward_cfg(P(x), P(wr), P(bias), P(gu), P(dn), T, H, I, E, k,
-                                     int(wl.norm_topk_prob), dt, cfg_p, P(out), P(logits), P(ids),
-                                     P(w), P(counts), P(ws), nws, evs, sp)
+        st = L.moe_layer_forward_ex(P(x), P(wr), P(bias), P(gu), P(dn), T, H, I, E, k,
+                                    int(wl.norm_topk_prob), dt, cfg_p, sh_p, P(out), P(logits),
+                                    P(ids), P(w), P(counts), P(ws), nws, evs, sp)
         if st != 0:
             raise RuntimeError(f"moe_layer_forward failed with status {st}")
 
@@ -237,7 +271,7 @@ def main():
     ms_per_step = total_ms / args.steps
     per_kernel_ms = {}
     f = ctypes.c_float()
-    for j, kname in enumerate(KERNELS):
+    for j, kname in enumerate(kernels):
         acc = []
         for arr in ev_arrays:
             if hip.hipEventElapsedTime(ctypes.byref(f), arr[j], arr[j + 1]) != 0:
@@ -249,10 +283,12 @@ def main():
             hip.hipEventDestroy(arr[j])
 
     c_np = counts.cpu().numpy()
-    flops, bytes_, hit = algorithmic(wl, c_np)
+    flops, bytes_, hit = algorithmic(wl, c_np, Is, fused)
+    flops = dict(zip(kernels, flops.values()))
+    bytes_ = dict(zip(kernels, bytes_.values()))
     peak_f = PEAK_BF16_FLOPS if bf16 else PEAK_F32_FLOPS
     kern = {}
-    for kname in KERNELS:
+    for kname in kernels:
         t_s = per_kernel_ms[kname] * 1e-3
         kern[kname] = {
             "avg_us": round(per_kernel_ms[kname] * 1e3, 2),
@@ -261,7 +297,7 @@ def main():
             "mfma_frac": round(flops[kname] / t_s / peak_f, 4),
             "hbm_frac": round(bytes_[kname] / t_s / PEAK_HBM, 4),
         }
-    dom = max(KERNELS, key=lambda n: per_kernel_ms[n])
+    dom = max(kernels, key=lambda n: per_kernel_ms[n])
     t_dom = per_kernel_ms[dom] * 1e-3
     hbm_floor = bytes_[dom] / PEAK_HBM
     mfma_floor = flops[dom] / peak_f
@@ -293,7 +329,7 @@ def main():
         "data": "synthetic: seeded Gaussian inputs and random-init weights of the named layer shape",
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "top_k": k,
                    "norm_topk_prob": wl.norm_topk_prob, "routed_rows": N,
-                   "experts_hit": hit, "router": args.router},
+                   "experts_hit": hit, "router": args.router, "shared_I": Is},
         "layer_tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "layer_mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / peak_f, 4),
         "roofline": roof,
@@ -302,7 +338,8 @@ def main():
         "host": platform.node(),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(
+            wl, shared=tuple(t.float().numpy() for t in sh_w) if sh_w is not None else None)
     print(json.dumps(result), flush=True)
 
 

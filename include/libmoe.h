@@ -73,13 +73,16 @@ enum {
   MOE_OP_GATE_UP = 2,
   MOE_OP_DOWN = 3,
   MOE_OP_GROUPED_SWIGLU = 4,
-  MOE_OP_LAYER = 5
+  MOE_OP_LAYER = 5,
+  MOE_OP_SHARED = 6
 };
 
 /* Bytes of device workspace entry point `op` needs for these sizes.
  * N is the number of routed rows (T * top_k for token choice; for the
  * rank-major permutation and the grouped calls, the caller's row count).
- * R is the number of source ranks (rank-major permutation only, else 0).
+ * R is the number of source ranks for the rank-major permutation; for
+ * MOE_OP_LAYER it is the shared expert's intermediate size (0: none); else 0.
+ * For MOE_OP_SHARED, I is the shared expert's intermediate size.
  * Returns 0 if the op needs none, (size_t)-1 for invalid sizes. */
 size_t moe_workspace_size(int op, int T, int H, int I, int E, int top_k, int R,
                           int N, moe_dtype dt);
@@ -308,6 +311,53 @@ int moe_layer_forward_cfg(const void* hidden_states, const void* router_weight,
  */
 int moe_update_expert_bias(float* expert_bias, float* tokens_per_expert, int E, float lr,
                            int num_recomputations, hipStream_t stream);
+
+/*
+ * Shared expert — MindSpore moe.py, FeedForward (a SwiGLU feed-forward that
+ * every token passes through) and MoE.forward (its output is added to the
+ * unpermuted routed output, without a routing weight).
+ *
+ * With nn.Linear weights w1, w3 [Is, H] and w2 [H, Is], FeedForward is
+ *   shared(x) = w2(silu(w1 x) * w3 x).
+ * The library takes them transposed, in the routed experts' layout:
+ *   gate_up [H, 2 * Is] dt: columns [0, Is) are w1^T (gate), [Is, 2 * Is)
+ *                           are w3^T (up);
+ *   down    [Is, H] dt:     w2^T.
+ * Is (intermediate_size) must be a positive multiple of 64.
+ */
+typedef struct moe_shared_expert {
+  const void* gate_up;
+  const void* down;
+  int intermediate_size;
+} moe_shared_expert;
+
+/* The shared expert alone on T tokens: out [T, H] dt = shared(x) for each
+ * row, the hidden h [T, Is] rounded to dt between the two GEMMs (as the
+ * routed experts do), float32 accumulation.  Workspace:
+ * moe_workspace_size(MOE_OP_SHARED, T, H, Is, 1, 1, 0, T, dt). */
+int moe_shared_expert_forward(const void* hidden_states, const void* gate_up,
+                              const void* down, int T, int H, int Is, moe_dtype dt,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* moe_layer_forward_cfg plus an optional shared expert (shared == NULL: no
+ * shared expert, exactly moe_layer_forward_cfg).  With one,
+ *   out[t, :] = sum_j w[t, j] * y[t * k + j, :] + shared(x[t, :])
+ * where shared(x) is rounded to dt and joins the combine's float32 sum last,
+ * before the single rounding of out.  Workspace:
+ * moe_workspace_size(MOE_OP_LAYER, T, H, I, E, top_k, Is, T * top_k, dt).
+ * For bf16 with Is a multiple of 128 the shared expert's GEMMs run inside
+ * the two grouped launches (stage events 2-3 and 3-4); otherwise they run
+ * on their own between stage events 4 and 5, before the combine. */
+int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
+                         const float* router_bias, const void* gate_up,
+                         const void* down, int T, int H, int I, int E, int top_k,
+                         int norm_topk_prob, moe_dtype dt, const moe_router_config* cfg,
+                         const moe_shared_expert* shared, void* out, float* router_logits,
+                         int32_t* topk_ids, float* topk_weights,
+                         int32_t* num_tokens_per_expert, void* workspace,
+                         size_t workspace_bytes, hipEvent_t* stage_events,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

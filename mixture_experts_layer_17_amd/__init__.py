@@ -19,7 +19,7 @@ lib = _lib.load()
 __all__ = ["lib", "route", "permute", "permute_rank_major", "gather_rows",
            "grouped_gate_up_swiglu", "grouped_down", "grouped_swiglu", "combine",
            "layer_forward", "workspace_size", "router_config", "update_expert_bias",
-           "LayerBuffers", "MoEError"]
+           "shared_expert", "shared_expert_forward", "LayerBuffers", "MoEError"]
 
 MoEError = _lib.MoEError
 
@@ -264,27 +264,57 @@ def combine(y: torch.Tensor, T: int, top_k: int, topk_weights: Optional[torch.Te
 
 
 class LayerBuffers:
-    """Preallocated outputs and workspace for repeated layer_forward calls."""
+    """Preallocated outputs and workspace for repeated layer_forward calls
+    (``shared_I``: the shared expert's intermediate size, 0 for none)."""
 
-    def __init__(self, T, H, I, E, top_k, dtype, device):
+    def __init__(self, T, H, I, E, top_k, dtype, device, shared_I=0):
         self.out = torch.empty(T, H, dtype=dtype, device=device)
         self.logits = torch.empty(T, E, dtype=torch.float32, device=device)
         self.ids = torch.empty(T, top_k, dtype=torch.int32, device=device)
         self.weights = torch.empty(T, top_k, dtype=torch.float32, device=device)
         self.counts = torch.empty(E, dtype=torch.int32, device=device)
         dt = _lib.MOE_BF16 if dtype == torch.bfloat16 else _lib.MOE_F32
-        nb = lib.moe_workspace_size(_lib.MOE_OP_LAYER, T, H, I, E, top_k, 0, T * top_k, dt)
+        nb = lib.moe_workspace_size(_lib.MOE_OP_LAYER, T, H, I, E, top_k, shared_I, T * top_k,
+                                    dt)
         self.workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
         self.ws_bytes = nb
+
+
+def shared_expert(gate_up: torch.Tensor, down: torch.Tensor) -> "_lib.SharedExpert":
+    """struct moe_shared_expert for FeedForward weights in the library's layout:
+    ``gate_up`` [H, 2 Is] (w1^T | w3^T) and ``down`` [Is, H] (w2^T)."""
+    H, Is2 = gate_up.shape
+    _chk(gate_up, "shared gate_up", gate_up.dtype, (H, Is2))
+    _chk(down, "shared down", gate_up.dtype, (Is2 // 2, H))
+    sh = _lib.SharedExpert(gate_up.data_ptr(), down.data_ptr(), Is2 // 2)
+    sh._keep = (gate_up, down)
+    return sh
+
+
+def shared_expert_forward(x: torch.Tensor, gate_up: torch.Tensor,
+                          down: torch.Tensor) -> torch.Tensor:
+    """The shared expert (FeedForward) on every row of ``x`` [T, H]."""
+    T, H = x.shape
+    Is = gate_up.shape[1] // 2
+    _chk(x, "x")
+    _chk(gate_up, "gate_up", x.dtype, (H, 2 * Is))
+    _chk(down, "down", x.dtype, (Is, H))
+    out = torch.empty(T, H, dtype=x.dtype, device=x.device)
+    nb = lib.moe_workspace_size(_lib.MOE_OP_SHARED, T, H, Is, 1, 1, 0, T, _dt(x))
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=x.device)
+    _call("moe_shared_expert_forward", x.data_ptr(), gate_up.data_ptr(), down.data_ptr(), T, H,
+          Is, _dt(x), out.data_ptr(), ws.data_ptr(), nb, _stream(x.device))
+    return out
 
 
 def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
                   down: torch.Tensor, top_k: int, norm_topk_prob: bool = True,
                   router_bias: Optional[torch.Tensor] = None,
-                  buffers: Optional[LayerBuffers] = None, config=None):
+                  buffers: Optional[LayerBuffers] = None, config=None, shared=None):
     """The whole MoE layer forward; returns (out, router_logits, topk_ids,
     topk_weights, num_tokens_per_expert).  ``config`` (from
-    ``router_config``) selects a router variant."""
+    ``router_config``) selects a router variant; ``shared`` = (gate_up [H,
+    2 Is], down [Is, H]) adds a shared expert."""
     T, H = x.shape
     E = router_weight.shape[0]
     I = gate_up.shape[2] // 2
@@ -293,10 +323,16 @@ def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.T
     _chk(gate_up, "gate_up", x.dtype, (E, H, 2 * I))
     _chk(down, "down", x.dtype, (E, I, H))
     _chk(router_bias, "router_bias", torch.float32, (E,))
-    b = buffers if buffers is not None else LayerBuffers(T, H, I, E, top_k, x.dtype, x.device)
-    _call("moe_layer_forward_cfg", x.data_ptr(), router_weight.data_ptr(),
+    sh = None
+    if shared is not None:
+        _chk(shared[0], "shared gate_up", x.dtype)
+        sh = shared_expert(*shared)
+    Is = sh.intermediate_size if sh is not None else 0
+    b = buffers if buffers is not None else LayerBuffers(T, H, I, E, top_k, x.dtype, x.device,
+                                                         Is)
+    _call("moe_layer_forward_ex", x.data_ptr(), router_weight.data_ptr(),
           _chk(router_bias, "router_bias"), gate_up.data_ptr(), down.data_ptr(), T, H, I, E,
-          top_k, int(norm_topk_prob), _dt(x), _cfg_ptr(config), b.out.data_ptr(),
+          top_k, int(norm_topk_prob), _dt(x), _cfg_ptr(config), _cfg_ptr(sh), b.out.data_ptr(),
           b.logits.data_ptr(), b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(),
           b.workspace.data_ptr(), b.ws_bytes, None, _stream(x.device))
     return b.out, b.logits, b.ids, b.weights, b.counts

@@ -20,6 +20,7 @@ MOE_OP_GATE_UP = 2
 MOE_OP_DOWN = 3
 MOE_OP_GROUPED_SWIGLU = 4
 MOE_OP_LAYER = 5
+MOE_OP_SHARED = 6
 
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
@@ -32,6 +33,12 @@ _p = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
 _sz = ctypes.c_size_t
+
+
+class SharedExpert(ctypes.Structure):
+    """struct moe_shared_expert (include/libmoe.h)."""
+    _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("intermediate_size", ctypes.c_int)]
 
 
 class RouterConfig(ctypes.Structure):
@@ -59,6 +66,9 @@ SIGNATURES = {
     "moe_layer_forward_cfg": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
                                    _p, _p, _p, _p, _sz, _p, _p]),
     "moe_update_expert_bias": (_i, [_p, _p, _i, _f, _i, _p]),
+    "moe_shared_expert_forward": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _sz, _p]),
+    "moe_layer_forward_ex": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
+                                  _p, _p, _p, _p, _sz, _p, _p]),
 }
 
 

@@ -41,10 +41,48 @@ struct LayerWs {
   int32_t *ids, *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
   float *weights, *logits;
   void *perm, *h, *y, *tiles_up, *tiles_down;
+  void *h_s, *y_s, *tiles_s_up, *tiles_s_down;  // shared expert (Is > 0)
   size_t total;
 };
 
-LayerWs layer_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
+// The shared expert's region: h_s [T, Is], y_s [T, H] when with_y, and the
+// two dense tile lists.
+struct SharedWs {
+  void *h, *y, *tiles_up, *tiles_down;
+  size_t total;
+};
+
+SharedWs shared_ws(char* base, int T, int H, int Is, moe_dtype dt, bool with_y) {
+  SharedWs w{};
+  const bool bf16 = dt == MOE_BF16;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? base + off : nullptr;
+    off += al(bytes);
+    return p;
+  };
+  w.h = take((size_t)T * Is * esize(dt));
+  if (with_y) w.y = take((size_t)T * H * esize(dt));
+  w.tiles_up = take(tile_list_bytes(T, 1, pick_dense_cfg(bf16, T, Is, true).BM));
+  w.tiles_down = take(tile_list_bytes(T, 1, pick_dense_cfg(bf16, T, H, false).BM));
+  w.total = off;
+  return w;
+}
+
+// FeedForward on every token: gate/up GEMM with SwiGLU into h, down GEMM into
+// y.  No offsets: the tile builders take one group of T rows.
+hipError_t run_shared(bool bf16, const void* x, const void* gate_up, const void* down, int T,
+                      int H, int Is, const SharedWs& w, void* y, hipStream_t s) {
+  const GemmTileCfg cu = pick_dense_cfg(bf16, T, Is, true);
+  const GemmTileCfg cd = pick_dense_cfg(bf16, T, H, false);
+  hipError_t e = launch_gate_up(bf16, cu, x, T, nullptr, nullptr, T, H, Is, 1, gate_up, w.h,
+                                w.tiles_up, false, s);
+  if (e != hipSuccess) return e;
+  return launch_down(bf16, cd, w.h, nullptr, nullptr, T, H, Is, 1, down, y, w.tiles_down, false,
+                     s);
+}
+
+LayerWs layer_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt, int Is = 0) {
   LayerWs w{};
   const size_t N = (size_t)T * k;
   const bool bf16 = dt == MOE_BF16;
@@ -69,6 +107,15 @@ LayerWs layer_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
   const GemmTileCfg cd = pick_down_cfg(bf16, (int)N, H, I, E);
   w.tiles_up = take(tile_list_bytes((int)N, E, cu.BM));
   w.tiles_down = take(tile_list_bytes((int)N, E, cd.BM));
+  if (Is > 0) {
+    const SharedWs sw = shared_ws(nullptr, T, H, Is, dt, true);
+    const SharedWs sp = shared_ws(base ? base + off : nullptr, T, H, Is, dt, true);
+    w.h_s = sp.h;
+    w.y_s = sp.y;
+    w.tiles_s_up = sp.tiles_up;
+    w.tiles_s_down = sp.tiles_down;
+    off += sw.total;
+  }
   w.total = off;
   return w;
 }
@@ -151,9 +198,14 @@ size_t moe_workspace_size(int op, int T, int H, int I, int E, int top_k, int R, 
       return swiglu_ws(N, H, I, E, dt, &hb, &ub);
     }
     case MOE_OP_LAYER:
-      if (check_dims(H, I, E, top_k) != MOE_OK || T < 0 || !rows_ok((long long)T * top_k))
+      // R: the shared expert's intermediate size (0: no shared expert)
+      if (check_dims(H, I, E, top_k) != MOE_OK || T < 0 || !rows_ok((long long)T * top_k) ||
+          R < 0 || R % 64 != 0)
         return bad;
-      return layer_ws(nullptr, T, H, I, E, top_k, dt).total;
+      return layer_ws(nullptr, T, H, I, E, top_k, dt, R).total;
+    case MOE_OP_SHARED:
+      if (check_dims(H, I, 1, 1) != MOE_OK || I == 0 || T < 0 || !rows_ok(T)) return bad;
+      return shared_ws(nullptr, T, H, I, dt, false).total;
     default: return bad;
   }
 }
@@ -285,14 +337,29 @@ int moe_combine(const void* y, const int32_t* slot_pos, const float* w, int T, i
   if (T == 0) return MOE_OK;
   if (!y || !out) return MOE_ERR_NULL;
   if (!aligned16(y) || !aligned16(out)) return MOE_ERR_ALIGN;
-  return hip_status(launch_combine(dt == MOE_BF16, y, slot_pos, w, T, k, H, out, s));
+  return hip_status(launch_combine(dt == MOE_BF16, y, slot_pos, w, T, k, H, nullptr, out, s));
 }
 
-int moe_layer_forward_cfg(const void* x, const void* wr, const float* bias,
-                          const void* gate_up, const void* down, int T, int H, int I, int E,
-                          int k, int norm, moe_dtype dt, const moe_router_config* cfg, void* out,
-                          float* logits, int32_t* ids, float* weights, int32_t* counts, void* ws,
-                          size_t ws_bytes, hipEvent_t* stage_events, hipStream_t s) {
+int moe_shared_expert_forward(const void* x, const void* gate_up, const void* down, int T,
+                              int H, int Is, moe_dtype dt, void* out, void* ws, size_t ws_bytes,
+                              hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (check_dims(H, Is, 1, 1) != MOE_OK || Is == 0 || T < 0 || !rows_ok(T)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !gate_up || !down || !out) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(gate_up) || !aligned16(down) || !aligned16(out))
+    return MOE_ERR_ALIGN;
+  if (!ws || ws_bytes < shared_ws(nullptr, T, H, Is, dt, false).total) return MOE_ERR_WORKSPACE;
+  const SharedWs w = shared_ws((char*)ws, T, H, Is, dt, false);
+  return hip_status(run_shared(dt == MOE_BF16, x, gate_up, down, T, H, Is, w, out, s));
+}
+
+int moe_layer_forward_ex(const void* x, const void* wr, const float* bias, const void* gate_up,
+                         const void* down, int T, int H, int I, int E, int k, int norm,
+                         moe_dtype dt, const moe_router_config* cfg,
+                         const moe_shared_expert* shared, void* out, float* logits, int32_t* ids,
+                         float* weights, int32_t* counts, void* ws, size_t ws_bytes,
+                         hipEvent_t* stage_events, hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
     return MOE_ERR_SHAPE;
@@ -300,13 +367,17 @@ int moe_layer_forward_cfg(const void* x, const void* wr, const float* bias,
   const RouterVariant* var = nullptr;
   const int st = router_variant(cfg, E, k, &rv, &var);
   if (st != MOE_OK) return st;
+  const int Is = shared ? shared->intermediate_size : 0;
+  if (shared && (Is <= 0 || Is % 64 != 0)) return MOE_ERR_SHAPE;
   if (T > 0 && (!x || !wr || !gate_up || !down || !out)) return MOE_ERR_NULL;
+  if (T > 0 && shared && (!shared->gate_up || !shared->down)) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(wr) || !aligned16(gate_up) || !aligned16(down) ||
       !aligned16(out))
     return MOE_ERR_ALIGN;
-  const size_t need = layer_ws(nullptr, T, H, I, E, k, dt).total;
+  if (shared && (!aligned16(shared->gate_up) || !aligned16(shared->down))) return MOE_ERR_ALIGN;
+  const size_t need = layer_ws(nullptr, T, H, I, E, k, dt, Is).total;
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  LayerWs w = layer_ws((char*)ws, T, H, I, E, k, dt);
+  LayerWs w = layer_ws((char*)ws, T, H, I, E, k, dt, Is);
   if (!ids) ids = w.ids;
   if (!weights) weights = w.weights;
   if (!counts) counts = w.counts;
@@ -329,9 +400,20 @@ int moe_layer_forward_cfg(const void* x, const void* wr, const float* bias,
                           w.slot_pos, w.perm, s, w.tiles_up, cu.BM, w.tiles_down, cd.BM);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(2);
+  // The shared expert (MindSpore moe.py, MoE.forward) sees every token and
+  // its output joins the combine's float32 sum.  On the LDS kernels it runs
+  // as a dense second problem inside the two grouped launches, so its tiles
+  // share the machine with the experts' instead of running on their own.
+  DenseAux aux_up{}, aux_down{};
+  bool fused = false;
+  if (shared && T > 0 && lds_cfg_id(cu.id) && lds_cfg_id(cd.id)) {
+    aux_up = dense_aux(cu, true, x, H, shared->gate_up, 2 * Is, H, Is, w.h_s, Is, T, Is);
+    aux_down = dense_aux(cd, false, w.h_s, Is, shared->down, H, Is, 0, w.y_s, H, T, H);
+    fused = aux_up.jobs > 0 && aux_down.jobs > 0;
+  }
   if (N > 0) {
     e = launch_gate_up(bf16, cu, x, T, w.sorted_token, w.offsets, N, H, I, E, gate_up, w.h,
-                       w.tiles_up, true, s);
+                       w.tiles_up, true, s, fused ? &aux_up : nullptr);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   mark(3);
@@ -339,13 +421,27 @@ int moe_layer_forward_cfg(const void* x, const void* wr, const float* bias,
   // token's k rows contiguously.
   if (N > 0) {
     e = launch_down(bf16, cd, w.h, w.offsets, w.sorted_slot, N, H, I, E, down, w.y,
-                    w.tiles_down, true, s);
+                    w.tiles_down, true, s, fused ? &aux_down : nullptr);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   mark(4);
-  e = launch_combine(bf16, w.y, nullptr, weights, T, k, H, out, s);
+  if (shared && T > 0 && !fused) {
+    const SharedWs sw{w.h_s, w.y_s, w.tiles_s_up, w.tiles_s_down, 0};
+    e = run_shared(bf16, x, shared->gate_up, shared->down, T, H, Is, sw, w.y_s, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  e = launch_combine(bf16, w.y, nullptr, weights, T, k, H, shared ? w.y_s : nullptr, out, s);
   mark(5);
   return hip_status(e);
+}
+
+int moe_layer_forward_cfg(const void* x, const void* wr, const float* bias,
+                          const void* gate_up, const void* down, int T, int H, int I, int E,
+                          int k, int norm, moe_dtype dt, const moe_router_config* cfg, void* out,
+                          float* logits, int32_t* ids, float* weights, int32_t* counts, void* ws,
+                          size_t ws_bytes, hipEvent_t* stage_events, hipStream_t s) {
+  return moe_layer_forward_ex(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, cfg, nullptr,
+                              out, logits, ids, weights, counts, ws, ws_bytes, stage_events, s);
 }
 
 int moe_layer_forward(const void* x, const void* wr, const float* bias, const void* gate_up,

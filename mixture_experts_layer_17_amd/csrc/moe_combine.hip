@@ -1,10 +1,13 @@
-// Weighted un-permute / combine: out[t] = sum_j w[t, j] * y[src(t, j)].
+// Weighted un-permute / combine: out[t] = sum_j w[t, j] * y[src(t, j)],
+// plus the shared expert's row when there is one.
 //
 // Semantics: Qwen3-Omni issue #115, SpeedupMoeExperts.forward (expert output
 // times routing weight, index_add_ into the token rows); MindSpore moe.py,
 // MoE.unpermutation (scatter_add back to token order).  Here each token's k
 // rows are gathered and summed in float32 in ascending j, then rounded once:
-// no atomics, so the result is bitwise deterministic.
+// no atomics, so the result is bitwise deterministic.  The shared expert's
+// output (MindSpore moe.py, MoE.forward: added after the unpermutation) joins
+// the same float32 sum last, before that single rounding.
 //
 // Each thread owns 8 consecutive columns (one 16-byte bf16 load per row), so
 // a wave reads 1 KB contiguous per source row: HBM-bound streaming.
@@ -18,7 +21,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ w, int T_, int k,
-                                                      int H, T* __restrict__ out) {
+                                                      int H, const T* __restrict__ add,
+                                                      T* __restrict__ out) {
   const int per_row = H / 8;
   const int N = T_ * k;
   const long long total = (long long)T_ * per_row;
@@ -50,6 +54,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
         }
       }
     }
+    if (add) {
+      const chunk8<T> v = load_chunk<T>(add + (size_t)t * H + 8 * c);
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t* d = reinterpret_cast<const uint32_t*>(&v.v);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          acc[2 * x] += bf16_bits_to_f32(d[x] & 0xffffu);
+          acc[2 * x + 1] += bf16_bits_to_f32(d[x] >> 16);
+        }
+      } else {
+        const float* f0 = reinterpret_cast<const float*>(&v.lo);
+        const float* f1 = reinterpret_cast<const float*>(&v.hi);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          acc[x] += f0[x];
+          acc[4 + x] += f1[x];
+        }
+      }
+    }
     T* o = out + (size_t)t * H + 8 * c;
     if constexpr (sizeof(T) == 2) {
       uint32_t d[4];
@@ -68,16 +91,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
 }  // namespace
 
 hipError_t launch_combine(bool bf16, const void* y, const int32_t* slot_pos, const float* w,
-                          int T, int k, int H, void* out, hipStream_t s) {
+                          int T, int k, int H, const void* add, void* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const long long total = (long long)T * (H / 8);
   const int grid = (int)std::min<long long>((total + 255) / 256, 16384);
   if (bf16)
     combine_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)y, slot_pos, w, T, k, H,
-                                                (bf16_t*)out);
+                                                (const bf16_t*)add, (bf16_t*)out);
   else
     combine_kernel<float><<<grid, 256, 0, s>>>((const float*)y, slot_pos, w, T, k, H,
-                                               (float*)out);
+                                               (const float*)add, (float*)out);
   return hipGetLastError();
 }
 

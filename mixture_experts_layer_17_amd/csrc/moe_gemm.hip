@@ -49,9 +49,11 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
   __shared__ int s_start[257];
   const int e = threadIdx.x;
   int lo = 0, hi = 0;
-  if (e < E) {
+  if (e < E && offsets) {
     lo = min(max(offsets[e], 0), N);
     hi = min(max(offsets[e + 1], lo), N);
+  } else if (e == 0) {
+    hi = N;  // no offsets: one group of all N rows
   }
   build_tile_list(E, lo, hi, BM, tiles, tiles_count, s_nt, s_start);
 }
@@ -399,6 +401,14 @@ GemmTileCfg pick_gate_up_cfg(bool bf16, int N, int H, int I, int E) {
   return pick_cfg(bf16, N, E, I, true);
 }
 
+GemmTileCfg pick_dense_cfg(bool bf16, int rows, int cols, bool swiglu) {
+  if (bf16) {
+    const GemmTileCfg c = pick_lds_dense_cfg(rows, cols, swiglu);
+    if (c.id >= 0) return c;
+  }
+  return pick_cfg(bf16, rows, 1, cols, swiglu);
+}
+
 GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E) {
   (void)I;
   if (bf16) {
@@ -411,12 +421,15 @@ GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E) {
 hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_rows,
                           const int32_t* row_index, const int32_t* offsets, int N, int H, int I,
                           int E, const void* gate_up, void* h, void* tile_ws, bool tiles_ready,
-                          hipStream_t s) {
-  if (N <= 0) return hipSuccess;
-  if (lds_cfg_id(c.id))
+                          hipStream_t s, const DenseAux* aux) {
+  if (lds_cfg_id(c.id)) {
+    if (N <= 0 && !(aux && aux->jobs > 0)) return hipSuccess;
     return launch_lds_gemm(true, c, x, H, row_index, x_rows, gate_up, (long long)H * 2 * I, 2 * I,
                            H, I, h, I, nullptr, N, offsets, N, E, I / (c.BN / 2), tile_ws,
-                           tiles_ready, s);
+                           tiles_ready, s, aux);
+  }
+  if (aux && aux->jobs > 0) return hipErrorInvalidValue;
+  if (N <= 0) return hipSuccess;
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
   if (!tiles_ready) build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);
@@ -429,11 +442,15 @@ hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_
 
 hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h, const int32_t* offsets,
                        const int32_t* out_index, int N, int H, int I, int E, const void* down,
-                       void* y, void* tile_ws, bool tiles_ready, hipStream_t s) {
-  if (N <= 0) return hipSuccess;
-  if (lds_cfg_id(c.id))
+                       void* y, void* tile_ws, bool tiles_ready, hipStream_t s,
+                       const DenseAux* aux) {
+  if (lds_cfg_id(c.id)) {
+    if (N <= 0 && !(aux && aux->jobs > 0)) return hipSuccess;
     return launch_lds_gemm(false, c, h, I, nullptr, N, down, (long long)I * H, H, I, 0, y, H,
-                           out_index, N, offsets, N, E, H / c.BN, tile_ws, tiles_ready, s);
+                           out_index, N, offsets, N, E, H / c.BN, tile_ws, tiles_ready, s, aux);
+  }
+  if (aux && aux->jobs > 0) return hipErrorInvalidValue;
+  if (N <= 0) return hipSuccess;
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
   if (!tiles_ready) build_tiles_kernel<<<1, 256, 0, s>>>(offsets, E, N, c.BM, tiles, count);

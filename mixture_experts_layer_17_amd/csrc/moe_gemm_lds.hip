@@ -38,6 +38,7 @@ namespace moe {
 namespace {
 
 constexpr int NUM_XCD = 8;
+constexpr int NUM_CU = 256;
 constexpr int BK = 32;   // k per stage
 
 typedef short i16x4_v __attribute__((ext_vector_type(4)));
@@ -109,10 +110,11 @@ struct lcfg {
 
 template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
-    const bf16_t* __restrict__ X, int ldx, const int32_t* __restrict__ x_index, int x_rows,
-    const bf16_t* __restrict__ W, long long w_estride, int ldw, int K, int up_off,
-    bf16_t* __restrict__ C, int ldc, const int32_t* __restrict__ c_index, int c_rows,
-    const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count, int n_ntiles) {
+    const bf16_t* __restrict__ gX, int g_ldx, const int32_t* __restrict__ g_x_index,
+    int g_x_rows, const bf16_t* __restrict__ gW, long long g_w_estride, int g_ldw, int g_K,
+    int g_up_off, bf16_t* __restrict__ gC, int g_ldc, const int32_t* __restrict__ g_c_index,
+    int g_c_rows, const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count,
+    int g_n_ntiles, DenseAux aux) {
   using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU>;
   static_assert(STAGES >= 2, "at least double buffering");
   // STAGES ring slots of STAGE_BYTES.  The copies are invisible to the
@@ -121,18 +123,50 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   // asm memory clobbers keep the compiler from moving LDS reads across them.
   extern __shared__ __align__(16) unsigned char smem[];
 
-  // ---- job (M-tile, N-tile), XCD-aware: consecutive jobs share an XCD
-  const int jobs = tiles_count[0] * n_ntiles;
-  const int per_xcd = (jobs + NUM_XCD - 1) / NUM_XCD;
+  // ---- job (M-tile, N-tile), XCD-aware: consecutive jobs share an XCD.
+  // Each XCD takes an equal contiguous share of the dense problem's jobs
+  // first, then an equal contiguous share of the grouped tiles' jobs.
+  const int g_jobs = tiles_count[0] * g_n_ntiles;
+  const int d_per = (aux.jobs + NUM_XCD - 1) / NUM_XCD;
+  const int g_per = (g_jobs + NUM_XCD - 1) / NUM_XCD;
   const int xcd = blockIdx.x % NUM_XCD;
   const int local = blockIdx.x / NUM_XCD;
-  if (local >= per_xcd) return;
-  const int job = xcd * per_xcd + local;
-  if (job >= jobs) return;
+  const bool dense = local < d_per;   // uniform over the work-group
+  int job;
+  if (dense) {
+    job = xcd * d_per + local;
+    if (job >= aux.jobs) return;
+  } else {
+    if (local - d_per >= g_per) return;
+    job = xcd * g_per + (local - d_per);
+    if (job >= g_jobs) return;
+  }
+  const int n_ntiles = dense ? aux.n_ntiles : g_n_ntiles;
   const int mt = job / n_ntiles;
   const int nt = job - mt * n_ntiles;
-  const int4 tile = tiles[mt];
-  const int e = tile.x, row0 = tile.y, rows = tile.z;
+  int e = 0, row0, rows;
+  if (dense) {
+    row0 = mt * BM;
+    rows = min(BM, aux.rows - row0);
+  } else {
+    const int4 tile = tiles[mt];
+    e = tile.x;
+    row0 = tile.y;
+    rows = tile.z;
+  }
+  const bf16_t* __restrict__ X = dense ? (const bf16_t*)aux.X : gX;
+  const int ldx = dense ? aux.ldx : g_ldx;
+  const int32_t* __restrict__ x_index = dense ? nullptr : g_x_index;
+  const int x_rows = dense ? aux.rows : g_x_rows;
+  const bf16_t* __restrict__ W = dense ? (const bf16_t*)aux.W : gW;
+  const long long w_estride = dense ? 0 : g_w_estride;
+  const int ldw = dense ? aux.ldw : g_ldw;
+  const int K = dense ? aux.K : g_K;
+  const int up_off = dense ? aux.up_off : g_up_off;
+  bf16_t* __restrict__ C = dense ? (bf16_t*)aux.C : gC;
+  const int ldc = dense ? aux.ldc : g_ldc;
+  const int32_t* __restrict__ c_index = dense ? nullptr : g_c_index;
+  const int c_rows = dense ? aux.rows : g_c_rows;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -441,7 +475,8 @@ template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU>
 hipError_t launch_lds(const void* X, int ldx, const int32_t* x_index, int x_rows, const void* W,
                       long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                       const int32_t* c_index, int c_rows, const int4* tiles,
-                      const int32_t* tiles_count, int n_ntiles, int grid, hipStream_t s) {
+                      const int32_t* tiles_count, int n_ntiles, int grid, hipStream_t s,
+                      const DenseAux& aux) {
   using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU>,
@@ -450,7 +485,7 @@ hipError_t launch_lds(const void* X, int ldx, const int32_t* x_index, int x_rows
   hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU>), dim3(grid),
                      dim3(G::THREADS), G::LDS, s, (const bf16_t*)X, ldx, x_index, x_rows,
                      (const bf16_t*)W, w_estride, ldw, K, up_off, (bf16_t*)C, ldc, c_index,
-                     c_rows, tiles, tiles_count, n_ntiles);
+                     c_rows, tiles, tiles_count, n_ntiles, aux);
   return hipGetLastError();
 }
 
@@ -468,9 +503,9 @@ hipError_t launch_lds_cfg(bool swiglu, int id, const void* X, int ldx, const int
                           int x_rows, const void* W, long long w_estride, int ldw, int K,
                           int up_off, void* C, int ldc, const int32_t* c_index, int c_rows,
                           const int4* tiles, const int32_t* tiles_count, int n_ntiles, int grid,
-                          hipStream_t s) {
+                          hipStream_t s, const DenseAux& aux) {
 #define MOE_ARGS X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C, ldc, c_index, c_rows, \
-                 tiles, tiles_count, n_ntiles, grid, s
+                 tiles, tiles_count, n_ntiles, grid, s, aux
 #define MOE_CASE(ID, BM, BN, WM, WN, ST)                                    \
   case ID:                                                                \
     return swiglu ? launch_lds<BM, BN, WM, WN, ST, true>(MOE_ARGS)        \
@@ -504,23 +539,52 @@ GemmTileCfg pick_lds_cfg(int N, int E, int cols, bool swiglu) {
   return GemmTileCfg{kLds[id - 10].BM, kLds[id - 10].BN, id};
 }
 
+GemmTileCfg pick_lds_dense_cfg(int rows, int cols, bool swiglu) {
+  // One group of `rows` rows: the tallest row tile that still gives every
+  // compute unit a job, else the shortest.
+  const int need = swiglu ? 128 : 256;
+  if (cols % need != 0) return GemmTileCfg{0, 0, -1};
+  const long long n_ntiles = cols / need;
+  constexpr int kOrder[] = {14, 10, 11, 12, 13};
+  for (const int id : kOrder) {
+    const LdsCfg& g = kLds[id - 10];
+    if (((long long)rows + g.BM - 1) / g.BM * n_ntiles >= NUM_CU) return GemmTileCfg{g.BM, g.BN, id};
+  }
+  return GemmTileCfg{kLds[3].BM, kLds[3].BN, 13};
+}
+
+DenseAux dense_aux(const GemmTileCfg& c, bool swiglu, const void* X, int ldx, const void* W,
+                   int ldw, int K, int up_off, void* C, int ldc, int rows, int cols) {
+  DenseAux a{X, W, C, ldx, ldw, K, up_off, ldc, rows, 0, 0};
+  const int per_tile = swiglu ? c.BN / 2 : c.BN;   // output columns per job
+  if (rows <= 0 || cols % per_tile != 0) return a;
+  a.n_ntiles = cols / per_tile;
+  a.jobs = (rows + c.BM - 1) / c.BM * a.n_ntiles;
+  return a;
+}
+
 hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int ldx,
                            const int32_t* x_index, int x_rows, const void* W,
                            long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                            const int32_t* c_index, int c_rows, const int32_t* offsets, int N,
-                           int E, int n_ntiles, void* tile_ws, bool tiles_ready, hipStream_t s) {
+                           int E, int n_ntiles, void* tile_ws, bool tiles_ready, hipStream_t s,
+                           const DenseAux* aux) {
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
   if (!tiles_ready) {
     const hipError_t err = launch_build_tiles(offsets, E, N, c.BM, tile_ws, s);
     if (err != hipSuccess) return err;
   }
+  const DenseAux none{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
+  const DenseAux& a = aux ? *aux : none;
+  // one work-group slot per job of each XCD's two shares (the grouped tile
+  // count on the device never exceeds max_tiles)
   const long long max_tiles = (long long)N / c.BM + std::min(E, N);
-  long long jobs = max_tiles * n_ntiles;
-  jobs = (jobs + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
-  const int grid = (int)std::max<long long>(jobs, NUM_XCD);
+  const long long g_per = (max_tiles * n_ntiles + NUM_XCD - 1) / NUM_XCD;
+  const long long d_per = ((long long)a.jobs + NUM_XCD - 1) / NUM_XCD;
+  const int grid = (int)std::max<long long>((g_per + d_per) * NUM_XCD, NUM_XCD);
   return launch_lds_cfg(swiglu, c.id, X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C,
-                        ldc, c_index, c_rows, tiles, count, n_ntiles, grid, s);
+                        ldc, c_index, c_rows, tiles, count, n_ntiles, grid, s, a);
 }
 
 }  // namespace moe

@@ -56,8 +56,24 @@ hipError_t launch_permute_rank_major(const int32_t* counts_rm, int R, int N, int
 hipError_t launch_gather_rows(bool bf16, const void* x, int x_rows, const int32_t* idx, int N,
                               int H, void* out, hipStream_t s);
 
+// out[t] = sum_j w[t, j] * y[slot(t, j)] (+ add[t] when add is set), summed in
+// float32 and rounded once.
 hipError_t launch_combine(bool bf16, const void* y, const int32_t* slot_pos,
-                          const float* w, int T, int k, int H, void* out, hipStream_t s);
+                          const float* w, int T, int k, int H, const void* add, void* out,
+                          hipStream_t s);
+
+// A dense second problem run in the same LDS grouped-GEMM launch (the shared
+// expert): `rows` rows of X read in order against one weight matrix, outputs
+// stored in row order.  Its jobs (ceil(rows / BM) * n_ntiles) come before the
+// grouped ones; jobs == 0 means there is none.
+struct DenseAux {
+  const void* X;
+  const void* W;
+  void* C;
+  int ldx, ldw, K, up_off, ldc, rows, n_ntiles, jobs;
+};
+DenseAux dense_aux(const GemmTileCfg& c, bool swiglu, const void* X, int ldx, const void* W,
+                   int ldw, int K, int up_off, void* C, int ldc, int rows, int cols);
 
 // Grouped GEMMs.  Configs with id >= 10 run the LDS-ring kernel
 // (moe_gemm_lds.hip); the others the register-transpose kernel.
@@ -67,20 +83,26 @@ hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int
                            const int32_t* x_index, int x_rows, const void* W,
                            long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                            const int32_t* c_index, int c_rows, const int32_t* offsets, int N,
-                           int E, int n_ntiles, void* tile_ws, bool tiles_ready, hipStream_t s);
+                           int E, int n_ntiles, void* tile_ws, bool tiles_ready, hipStream_t s,
+                           const DenseAux* aux = nullptr);
 // Builds the tile list of row-tile height BM into tile_ws (one block).
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int N, int BM, void* tile_ws,
                               hipStream_t s);
+// One dense group of `rows` rows (a shared expert): with offsets == NULL the
+// tile builders take the single group [0, N).
+GemmTileCfg pick_lds_dense_cfg(int rows, int cols, bool swiglu);
+GemmTileCfg pick_dense_cfg(bool bf16, int rows, int cols, bool swiglu);
 GemmTileCfg pick_gate_up_cfg(bool bf16, int N, int H, int I, int E);
 GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E);
 size_t tile_list_bytes(int N, int E, int BM);
+// `aux` (LDS configs only) adds a dense problem to the same launch.
 hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_rows,
                           const int32_t* row_index, const int32_t* offsets, int N, int H,
                           int I, int E, const void* gate_up, void* h, void* tile_ws,
-                          bool tiles_ready, hipStream_t s);
+                          bool tiles_ready, hipStream_t s, const DenseAux* aux = nullptr);
 hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h,
                        const int32_t* offsets, const int32_t* out_index, int N, int H,
                        int I, int E, const void* down, void* y, void* tile_ws,
-                       bool tiles_ready, hipStream_t s);
+                       bool tiles_ready, hipStream_t s, const DenseAux* aux = nullptr);
 
 }  // namespace moe

@@ -84,3 +84,35 @@ def test_router_variant_validation(lib):
     assert lib.moe_update_expert_bias(fake, fake, 300, 1e-3, 1, None) == -2
     assert lib.moe_update_expert_bias(fake, fake, 8, 1e-3, 0, None) == -2
     assert lib.moe_update_expert_bias(None, fake, 8, 1e-3, 1, None) == -1
+
+
+def test_shared_expert_validation_and_workspace(lib):
+    ws = lambda *a: lib.moe_workspace_size(*a)
+    plain = ws(_lib.MOE_OP_LAYER, 4096, 2048, 768, 128, 8, 0, 32768, 1)
+    with_shared = ws(_lib.MOE_OP_LAYER, 4096, 2048, 768, 128, 8, 768, 32768, 1)
+    # the shared expert adds h_s [T, Is] and y_s [T, H] in bf16
+    assert with_shared - plain >= 4096 * (768 + 2048) * 2
+    assert ws(_lib.MOE_OP_LAYER, 64, 2048, 768, 128, 8, 100, 512, 1) == SIZE_MAX  # Is % 64
+    alone = ws(_lib.MOE_OP_SHARED, 4096, 2048, 768, 1, 1, 0, 4096, 1)
+    assert 4096 * 768 * 2 <= alone < with_shared - plain
+    assert ws(_lib.MOE_OP_SHARED, 64, 2048, 0, 1, 1, 0, 64, 1) == SIZE_MAX
+    fake = 4096  # never dereferenced: every call below fails validation
+    f = lib.moe_shared_expert_forward
+    assert f(fake, fake, fake, 4, 2048, 96, 1, fake, fake, 1 << 20, None) == -2     # Is % 64
+    assert f(fake, fake, fake, 4, 100, 64, 1, fake, fake, 1 << 20, None) == -2      # H % 128
+    assert f(None, fake, fake, 4, 128, 64, 1, fake, fake, 1 << 20, None) == -1
+    assert f(fake, fake, fake + 8, 4, 128, 64, 1, fake, fake, 1 << 20, None) == -7
+    assert f(fake, fake, fake, 4, 128, 64, 1, fake, fake, 16, None) == -4
+    assert f(fake, fake, fake, 0, 128, 64, 1, fake, None, 0, None) == 0              # T = 0
+    lay = lambda sh: lib.moe_layer_forward_ex(
+        fake, fake, None, fake, fake, 4, 128, 64, 8, 2, 1, 1, None, ctypes.addressof(sh), fake,
+        None, None, None, None, fake, 1 << 30, None, None)
+    assert lay(_lib.SharedExpert(fake, fake, 0)) == -2
+    assert lay(_lib.SharedExpert(fake, fake, 96)) == -2
+    assert lay(_lib.SharedExpert(None, fake, 64)) == -1
+    assert lay(_lib.SharedExpert(fake, fake + 4, 64)) == -7
+    small = lambda sh: lib.moe_layer_forward_ex(
+        fake, fake, None, fake, fake, 4, 128, 64, 8, 2, 1, 1, None, ctypes.addressof(sh), fake,
+        None, None, None, None, fake, ws(_lib.MOE_OP_LAYER, 4, 128, 64, 8, 2, 0, 8, 1), None,
+        None)
+    assert small(_lib.SharedExpert(fake, fake, 64)) == -4   # room for the routed part only

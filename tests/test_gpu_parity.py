@@ -34,21 +34,32 @@ def _np32(t):
     return t.float().numpy()
 
 
-def run_layer(moe, wl, check_counts=True):
-    """Full layer on the GPU vs the oracle's per-expert loop."""
-    say(f"layer {wl.name} T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.top_k} {wl.dtype}")
+def shared_layout(w1, w2, w3):
+    """FeedForward's nn.Linear weights in the library's layout: gate_up
+    [H, 2 Is] = (w1^T | w3^T), down [Is, H] = w2^T."""
+    return torch.cat([w1.t(), w3.t()], dim=1).contiguous(), w2.t().contiguous()
+
+
+def run_layer(moe, wl, check_counts=True, shared=None):
+    """Full layer on the GPU vs the oracle's per-expert loop.  ``shared`` =
+    (w1, w2, w3): a shared expert in nn.Linear layout."""
+    say(f"layer {wl.name} T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.top_k} {wl.dtype}"
+        + (f" shared Is={shared[0].shape[0]}" if shared is not None else ""))
     x = wl.hidden_states.to(DEV)
     wr = wl.router_weight.to(DEV)
     gu = wl.gate_up.to(DEV)
     dn = wl.down.to(DEV)
     b = wl.router_bias.to(DEV) if wl.router_bias is not None else None
+    sh = tuple(t.to(DEV) for t in shared_layout(*shared)) if shared is not None else None
     out, logits, ids, w, counts = moe.layer_forward(x, wr, gu, dn, wl.top_k, wl.norm_topk_prob,
-                                                    router_bias=b)
+                                                    router_bias=b, shared=sh)
     torch.cuda.synchronize()
     out, logits, ids, w, counts = (t.cpu() for t in (out, logits, ids, w, counts))
     bias_np = wl.router_bias.numpy() if wl.router_bias is not None else None
     ref = O.moe_layer_forward(_np32(wl.hidden_states), _np32(wl.router_weight), bias_np,
-                              _np32(wl.gate_up), _np32(wl.down), wl.top_k, wl.norm_topk_prob)
+                              _np32(wl.gate_up), _np32(wl.down), wl.top_k, wl.norm_topk_prob,
+                              shared=tuple(_np32(t) for t in shared) if shared is not None
+                              else None)
     U.assert_close(logits, ref["logits"], wl.dtype, "router logits")
     decided, same = U.routing_check(logits.numpy(), ids.numpy(), ref["logits"], ref["ids"],
                                     wl.top_k)
@@ -133,6 +144,63 @@ def test_layer_deterministic(moe):
     b = moe.layer_forward(x, wr, gu, dn, 4)[0].clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ shared expert
+
+@pytest.mark.parametrize("T,H,Is,dtype", [
+    (4096, 2048, 768, torch.bfloat16),    # prefill tokens, Qwen3-30B-A3B width
+    (64, 2048, 768, torch.bfloat16),      # decode tokens
+    (300, 256, 256, torch.bfloat16),      # several row tiles, ragged tail
+    (1, 256, 128, torch.bfloat16),        # one token
+    (200, 384, 192, torch.bfloat16),      # Is not a multiple of 128: narrow-tile fallback
+    (37, 128, 64, torch.float32),
+    (513, 256, 128, torch.float32),
+])
+def test_shared_expert_alone(moe, T, H, Is, dtype):
+    say(f"shared expert T={T} H={H} Is={Is} {dtype}")
+    g = torch.Generator().manual_seed(T + Is)
+    x = torch.randn(T, H, generator=g).to(dtype)
+    w1, w2, w3 = workloads.shared_expert_weights(H, Is, dtype, seed=T)
+    gu, dn = shared_layout(w1, w2, w3)
+    out = moe.shared_expert_forward(x.to(DEV), gu.to(DEV), dn.to(DEV))
+    torch.cuda.synchronize()
+    ref = O.feed_forward(_np32(x), _np32(w1), _np32(w2), _np32(w3))
+    U.assert_close(out.cpu(), ref, dtype, "shared expert")
+
+
+@pytest.mark.parametrize("name,Is", [("qwen3_30b_a3b_decode", 768),
+                                     ("qwen3_30b_a3b_prefill", 768),
+                                     ("tiny_fp32", 128)])
+def test_layer_with_shared_expert(moe, name, Is):
+    wl = workloads.make(name)
+    run_layer(moe, wl, shared=workloads.shared_expert_weights(wl.H, Is, wl.dtype))
+
+
+@pytest.mark.parametrize("T,H,I,E,k,Is", [
+    (37, 256, 128, 32, 4, 192),     # Is not a multiple of 128: shared GEMMs on their own
+    (37, 256, 128, 32, 4, 256),     # inside the grouped launches, ragged tail
+    (1000, 256, 128, 8, 2, 384),    # inside, many dense row tiles next to wide expert tiles
+    (1, 512, 64, 6, 6, 128),        # one token, k = E
+])
+def test_layer_shared_small(moe, T, H, I, E, k, Is):
+    wl = workloads.make_layer(f"shared_{T}_{Is}", T=T, H=H, I=I, E=E, top_k=k, seed=7,
+                              norm_topk_prob=False)
+    run_layer(moe, wl, shared=workloads.shared_expert_weights(H, Is, wl.dtype, seed=7))
+
+
+def test_layer_shared_zero_tokens(moe):
+    say("layer with shared expert, T = 0")
+    H, I, E, Is = 256, 128, 8, 128
+    x = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    wr = torch.zeros(E, H, dtype=torch.bfloat16, device=DEV)
+    gu = torch.zeros(E, H, 2 * I, dtype=torch.bfloat16, device=DEV)
+    dn = torch.zeros(E, I, H, dtype=torch.bfloat16, device=DEV)
+    sh = (torch.zeros(H, 2 * Is, dtype=torch.bfloat16, device=DEV),
+          torch.zeros(Is, H, dtype=torch.bfloat16, device=DEV))
+    out, _, _, _, counts = moe.layer_forward(x, wr, gu, dn, 2, True, shared=sh)
+    torch.cuda.synchronize()
+    assert out.shape == (0, H) and not counts.cpu().any()
 
 
 # ------------------------------------------------------------ sub-steps

@@ -29,7 +29,8 @@ from typing import Dict, Optional
 import torch
 
 __all__ = ["Workload", "EPWorkload", "CONFIGS", "make", "make_layer",
-           "make_ep_rank", "zipf_router_bias", "integer_grid_layer"]
+           "make_ep_rank", "zipf_router_bias", "integer_grid_layer",
+           "shared_expert_weights"]
 
 
 @dataclasses.dataclass
@@ -100,6 +101,19 @@ def make_layer(name: str, T: int, H: int, I: int, E: int, top_k: int,
     x = _normal(g, (T, H), x_std, dtype)
     return Workload(name, T, H, I, E, top_k, norm_topk_prob, dtype, x, wr,
                     router_bias, gu, dn)
+
+
+def shared_expert_weights(H: int, Is: int, dtype: torch.dtype = torch.bfloat16, seed: int = 0,
+                          weight_std: float = 0.02):
+    """Weights of a shared expert (the MindSpore moe.py page's FeedForward)
+    as nn.Linear stores them: w1 [Is, H], w2 [H, Is], w3 [Is, H], drawn in
+    that order from their own generator (seed + 1000, so they never repeat a
+    layer's draws)."""
+    g = torch.Generator().manual_seed(seed + 1000)
+    w1 = _normal(g, (Is, H), weight_std, dtype)
+    w2 = _normal(g, (H, Is), weight_std, dtype)
+    w3 = _normal(g, (Is, H), weight_std, dtype)
+    return w1, w2, w3
 
 
 def make_ep_rank(name: str = "ep_rank_235b", R: int = 8, T_per_rank: int = 4096,

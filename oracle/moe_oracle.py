@@ -51,6 +51,7 @@ __all__ = [
     "expert_counts", "expert_offsets", "permutation", "gather_rows",
     "silu", "swiglu_expert", "grouped_swiglu", "combine", "unpermute", "feed_forward",
     "moe_layer_forward", "moe_layer_forward_brute", "moe_layer_forward_tokens",
+    "silu_grad", "moe_layer_backward",
     "dispatch_rank_major", "reshuffle_rank_to_expert", "ep_rank_forward",
 ]
 
@@ -407,6 +408,94 @@ def moe_layer_forward_tokens(x, w_router, bias, gate_up, down, top_k: int,
             out[rows] += w[rows, j:j + 1] * swiglu_expert(xs[rows], gate_up[int(e)], down[int(e)])
     out, _ = _add_shared(out, xs, shared)
     return dict(logits=L, ids=ids, weights=w, out=out)
+
+
+# ---------------------------------------------------------------------------
+# The layer backward: the gradient of moe_layer_forward (the pages train this
+# layer with autograd: [QO] SpeedupMoeExperts' training path, [HP] MoE.forward)
+# ---------------------------------------------------------------------------
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz silu(z) = s(z) (1 + z (1 - s(z))) with s the logistic sigmoid."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_prob: bool,
+                       dout) -> dict:
+    """Gradients of ``sum(dout * out)`` for the layer of ``moe_layer_forward``.
+
+    The routing decision (which experts) is piecewise constant, so gradients
+    flow through the routing weights' values, the experts and the combine
+    only.  Steps, from the output back:
+
+    * combine: ``out[t] = sum_j w[t, j] y[t, j]`` gives
+      ``d_weights[t, j] = <dout[t], y[t, j]>`` and ``dy[t, j] = w[t, j] dout[t]``;
+    * expert e on its rows: ``y = h Wd``, ``h = silu(g) * u``, ``[g | u] = X Wgu``:
+      ``dWd = h^T dy``, ``dh = dy Wd^T``, ``du = dh silu(g)``,
+      ``dg = dh u silu'(g)``, ``dWgu = X^T [dg | du]``,
+      ``dX = [dg | du] Wgu^T`` added into each row's token;
+    * routing weights: ``w = softmax(L)[ids]`` gives
+      ``dL = p (g - <g, p>)`` with ``g`` the scattered ``d_weights``; with
+      renormalisation ``w`` is the softmax over the selected logits, so
+      ``dL[ids] = w (d_weights - <d_weights, w>)`` and zero elsewhere;
+    * router: ``dx += dL Wr``, ``dWr = dL^T x``, ``db = sum_t dL``.
+
+    Returns float64 ``dx``, ``d_router_weight``, ``d_router_bias``,
+    ``d_gate_up``, ``d_down``, ``d_weights`` [T, k] and ``d_logits`` [T, E],
+    plus the forward's dict under ``forward``."""
+    fwd = moe_layer_forward(x, w_router, bias, gate_up, down, top_k, norm_topk_prob)
+    X = _f64(x)
+    D = _f64(dout)
+    T, H = X.shape
+    k = top_k
+    gu, dn = _f64(gate_up), _f64(down)
+    E, I = gu.shape[0], gu.shape[2] // 2
+    ids, w = fwd["ids"], fwd["weights"]
+    # combine
+    y_slot = unpermute(fwd["y"], fwd["slot_pos"]).reshape(T, k, H)
+    d_w = np.einsum("th,tjh->tj", D, y_slot)
+    dy = (w[:, :, None] * D[:, None, :]).reshape(T * k, H)
+    # experts
+    dx = np.zeros((T, H))
+    dgu = np.zeros_like(gu)
+    ddn = np.zeros_like(dn)
+    offsets, sorted_slot = fwd["offsets"], fwd["sorted_slot"]
+    for e in range(E):
+        slots = sorted_slot[offsets[e]:offsets[e + 1]].astype(np.int64)
+        if slots.size == 0:
+            continue
+        tok = slots // k
+        Xe = X[tok]
+        G = Xe @ gu[e]
+        g, u = G[:, :I], G[:, I:]
+        h = silu(g) * u
+        dY = dy[slots]
+        ddn[e] = h.T @ dY
+        dh = dY @ dn[e].T
+        dG = np.concatenate([dh * u * silu_grad(g), dh * silu(g)], axis=1)
+        dgu[e] = Xe.T @ dG
+        np.add.at(dx, tok, dG @ gu[e].T)
+    # routing weights -> logits
+    L = _f64(fwd["logits"])
+    ii = ids.astype(np.int64)
+    dL = np.zeros((T, E))
+    if norm_topk_prob:
+        inner = (d_w * w).sum(axis=1, keepdims=True)
+        np.put_along_axis(dL, ii, w * (d_w - inner), axis=1)
+    else:
+        p = np.exp(L - L.max(axis=1, keepdims=True))
+        p = p / p.sum(axis=1, keepdims=True)
+        gsc = np.zeros((T, E))
+        np.put_along_axis(gsc, ii, d_w, axis=1)
+        dL = p * (gsc - (gsc * p).sum(axis=1, keepdims=True))
+    # router
+    Wr = _f64(w_router)
+    dx += dL @ Wr
+    return dict(dx=dx, d_router_weight=dL.T @ X, d_router_bias=dL.sum(axis=0),
+                d_gate_up=dgu, d_down=ddn, d_weights=d_w, d_logits=dL, forward=fwd)
 
 
 # ---------------------------------------------------------------------------

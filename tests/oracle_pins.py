@@ -32,7 +32,12 @@ What pins what:
   (nn.Linear convention, gate w1 and up w3 kept apart), the closed form at
   H = Is = 1, routed experts that are copies of the shared one (the output is
   (1 + sum of the routing weights) times the FFN), zero routed outputs, and
-  the all-expert brute-force path.
+  the all-expert brute-force path;
+* layer backward: central finite differences of the (pinned) forward on every
+  input and weight entry of small layers, with and without renormalisation
+  and with a router bias; the closed form of the scalar layer; the softmax
+  gradient summing to zero per token; zero gradients for experts without
+  rows.
 """
 from __future__ import annotations
 
@@ -583,6 +588,116 @@ def pin_shared_brute_and_tokens():
     toks = [3, 0, 15, 7]
     sub = O.moe_layer_forward_tokens(x, wr, None, gu, dn, k, False, toks, shared=sh)["out"]
     assert np.allclose(sub, full[toks], rtol=1e-12, atol=1e-12)
+
+
+# ---- layer backward -----------------------------------------------------------
+
+def _fd_layer(seed, norm, with_bias, T=4, H=6, I=3, E=5, k=2, eps=1e-3):
+    r = _rng(seed)
+    x = r.standard_normal((T, H))
+    wr = r.standard_normal((E, H)) * 0.7
+    b = r.standard_normal(E) * 0.3 if with_bias else None
+    gu = r.standard_normal((E, H, 2 * I)) * 0.5
+    dn = r.standard_normal((E, I, H)) * 0.5
+    dout = r.standard_normal((T, H))
+    g = O.moe_layer_backward(x, wr, b, gu, dn, k, norm, dout)
+    ids0 = g["forward"]["ids"]
+
+    def loss(x_, wr_, b_, gu_, dn_):
+        f = O.moe_layer_forward(x_, wr_, b_, gu_, dn_, k, norm)
+        assert np.array_equal(f["ids"], ids0), "perturbation changed the routing"
+        return float((f["out"] * dout).sum())
+
+    args = [x, wr, b, gu, dn]
+    names = ["dx", "d_router_weight", "d_router_bias", "d_gate_up", "d_down"]
+    for a, name in enumerate(names):
+        if args[a] is None:
+            continue
+        fd = np.zeros_like(args[a])
+        for idx in np.ndindex(args[a].shape):
+            plus = [t.copy() if t is not None else None for t in args]
+            minus = [t.copy() if t is not None else None for t in args]
+            plus[a][idx] += eps
+            minus[a][idx] -= eps
+            fd[idx] = (loss(*plus) - loss(*minus)) / (2 * eps)
+        an = g[name]
+        err = np.abs(fd - an).max()
+        # float32 logits add ~1e-7 / eps of noise to the differences
+        assert err <= 2e-4 * max(1.0, np.abs(an).max()), f"{name}: finite differences off by {err}"
+    return g
+
+
+def pin_backward_finite_differences_renorm():
+    g = _fd_layer(31, True, True)
+    # renormalised: only the selected logits get a gradient
+    mask = np.zeros_like(g["d_logits"], dtype=bool)
+    np.put_along_axis(mask, g["forward"]["ids"].astype(np.int64), True, axis=1)
+    assert np.all(g["d_logits"][~mask] == 0.0)
+
+
+def pin_backward_finite_differences_plain():
+    _fd_layer(32, False, False)
+
+
+def pin_backward_finite_differences_k1_bias():
+    _fd_layer(33, False, True, T=3, H=4, I=2, E=3, k=1)
+
+
+def pin_backward_scalar_closed_form():
+    # H = I = 1, E = 2, k = 1, renormalised: w = 1, so the router gets no
+    # gradient, and out = silu(x g) (x u) d
+    x = np.array([[0.7], [-1.3], [2.0]])
+    wr = np.array([[1.0], [-0.5]])
+    gu = np.array([[[0.8, -1.1]], [[0.4, 0.9]]])
+    dn = np.array([[[1.5]], [[-0.6]]])
+    dout = np.array([[0.3], [-2.0], [1.1]])
+    g = O.moe_layer_backward(x, wr, None, gu, dn, 1, True, dout)
+    assert np.all(g["d_router_weight"] == 0) and np.all(g["d_router_bias"] == 0)
+    sg = lambda z: 1.0 / (1.0 + math.exp(-z))  # noqa: E731
+    dgu = np.zeros_like(gu)
+    ddn = np.zeros_like(dn)
+    for t in range(3):
+        xv, dv = float(x[t, 0]), float(dout[t, 0])
+        e = int(g["forward"]["ids"][t, 0])
+        a, b, c = float(gu[e, 0, 0]), float(gu[e, 0, 1]), float(dn[e, 0, 0])
+        z = a * xv
+        s = sg(z)
+        silu_z, dsilu = z * s, s * (1 + z * (1 - s))
+        # out = silu(a x) (b x) c
+        assert abs(g["dx"][t, 0] - dv * c * (dsilu * a * b * xv + silu_z * b)) < 1e-12
+        dgu[e, 0, 0] += dv * c * dsilu * xv * b * xv
+        dgu[e, 0, 1] += dv * c * silu_z * xv
+        ddn[e, 0, 0] += dv * silu_z * b * xv
+        assert abs(g["d_weights"][t, 0] - dv * silu_z * b * xv * c) < 1e-12
+    assert np.allclose(g["d_gate_up"], dgu, rtol=0, atol=1e-12)
+    assert np.allclose(g["d_down"], ddn, rtol=0, atol=1e-12)
+
+
+def pin_backward_softmax_gradient_sums_to_zero():
+    r = _rng(34)
+    T, H, I, E, k = 20, 8, 4, 12, 3
+    x = r.standard_normal((T, H))
+    wr = r.standard_normal((E, H))
+    gu = r.standard_normal((E, H, 2 * I)) * 0.3
+    dn = r.standard_normal((E, I, H)) * 0.3
+    dout = r.standard_normal((T, H))
+    for norm in (True, False):
+        g = O.moe_layer_backward(x, wr, None, gu, dn, k, norm, dout)
+        assert np.allclose(g["d_logits"].sum(axis=1), 0.0, atol=1e-13)
+        assert np.allclose(g["d_router_bias"], g["d_logits"].sum(axis=0), atol=1e-13)
+
+
+def pin_backward_idle_experts_get_zero():
+    r = _rng(35)
+    T, H, I, E, k = 10, 8, 4, 6, 2
+    x = r.standard_normal((T, H))
+    wr = np.zeros((E, H))
+    b = np.array([5.0, 4.0, 0.0, 0.0, 0.0, 0.0])    # every token picks experts 0 and 1
+    gu = r.standard_normal((E, H, 2 * I))
+    dn = r.standard_normal((E, I, H))
+    g = O.moe_layer_backward(x, wr, b, gu, dn, k, False, r.standard_normal((T, H)))
+    assert np.all(g["d_gate_up"][2:] == 0) and np.all(g["d_down"][2:] == 0)
+    assert np.abs(g["d_gate_up"][:2]).max() > 0 and np.abs(g["d_down"][:2]).max() > 0
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

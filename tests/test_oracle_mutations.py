@@ -112,9 +112,32 @@ def _shared_weighted(out, x, shared):
     return out + s, s
 
 
+def _silu_grad_no_product_rule(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))
+
+
+def _backward_without_router_dx(x, w_router, bias, gate_up, down, top_k, norm, dout):
+    g = _orig["moe_layer_backward"](x, w_router, bias, gate_up, down, top_k, norm, dout)
+    g["dx"] = g["dx"] - g["d_logits"] @ np.asarray(w_router, np.float64)
+    return g
+
+
+def _backward_unweighted_down_grad(x, w_router, bias, gate_up, down, top_k, norm, dout):
+    # the down-projection gradient taken from dout without the routing weight
+    g = _orig["moe_layer_backward"](x, w_router, bias, gate_up, down, top_k, norm, dout)
+    f = g["forward"]
+    k = top_k
+    wsum = np.zeros(np.asarray(down).shape[0])
+    for e in range(len(wsum)):
+        sl = f["sorted_slot"][f["offsets"][e]:f["offsets"][e + 1]]
+        wsum[e] = f["weights"].reshape(-1)[sl].mean() if len(sl) else 1.0
+    g["d_down"] = g["d_down"] / wsum[:, None, None]
+    return g
+
+
 _orig = {n: getattr(O, n) for n in ("routing_weights", "combine", "permutation",
                                      "router_logits", "expert_offsets", "route_variant",
-                                     "feed_forward")}
+                                     "feed_forward", "moe_layer_backward")}
 
 MUTATIONS = {
     "swiglu_expert": _swapped_gate_up,
@@ -130,7 +153,14 @@ MUTATIONS = {
     "update_expert_bias": _uncentred_bias_update,
     "feed_forward": _ffn_gate_up_swapped,
     "_add_shared": _shared_weighted,
+    "silu_grad": _silu_grad_no_product_rule,
+    "moe_layer_backward": _backward_without_router_dx,
 }
+
+
+def test_unweighted_down_grad_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "moe_layer_backward", _backward_unweighted_down_grad)
+    assert _some_pin_fails()
 
 
 def test_unmutated_oracle_passes_all_pins():

@@ -74,7 +74,8 @@ enum {
   MOE_OP_DOWN = 3,
   MOE_OP_GROUPED_SWIGLU = 4,
   MOE_OP_LAYER = 5,
-  MOE_OP_SHARED = 6
+  MOE_OP_SHARED = 6,
+  MOE_OP_LAYER_BACKWARD = 7
 };
 
 /* Bytes of device workspace entry point `op` needs for these sizes.
@@ -358,6 +359,64 @@ int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
                          int32_t* num_tokens_per_expert, void* workspace,
                          size_t workspace_bytes, hipEvent_t* stage_events,
                          hipStream_t stream);
+
+/*
+ * Training: the layer forward that keeps what its backward needs, and the
+ * backward.  The pages train this layer through autograd (Qwen3-Omni issue
+ * #115, SpeedupMoeExperts' per-expert training loop and
+ * SpeedupMoeSparseMoeBlock's softmax routing weights; MindSpore moe.py,
+ * MoE.forward and MoE.unpermutation); the backward is the gradient of
+ * sum(dout * out) for the default router (softmax, optionally renormalised,
+ * optional router_bias) without a shared expert.  The top-k choice is
+ * piecewise constant: gradients flow through the routing weights' values.
+ * bf16 only, I a multiple of 128 (else MOE_ERR_UNSUPPORTED).
+ *
+ * moe_layer_forward_train: moe_layer_forward plus
+ *   saved_gate_up    [T*k, 2I] dt: the gate/up pre-activations x.gate_up[e]
+ *                    of every routed row, rows in the expert-major order of
+ *                    moe_permute (stable in the flat slot index), gate in
+ *                    columns [0, I), up in [I, 2I);
+ *   saved_expert_out [T*k, H] dt: each slot's expert output, row t*k + j.
+ * router_logits, topk_ids and topk_weights are required (the backward reads
+ * them).  Workspace: moe_workspace_size(MOE_OP_LAYER, ...).
+ */
+int moe_layer_forward_train(const void* hidden_states, const void* router_weight,
+                            const float* router_bias, const void* gate_up,
+                            const void* down, int T, int H, int I, int E, int top_k,
+                            int norm_topk_prob, moe_dtype dt, void* out,
+                            float* router_logits, int32_t* topk_ids,
+                            float* topk_weights, int32_t* num_tokens_per_expert,
+                            void* saved_gate_up, void* saved_expert_out,
+                            void* workspace, size_t workspace_bytes,
+                            hipEvent_t* stage_events, hipStream_t stream);
+
+/*
+ * moe_layer_backward — from dout [T, H] dt and the training forward's
+ * router_logits, topk_ids, topk_weights, saved_gate_up and saved_expert_out:
+ *   d_topk_weights[t, j] = <dout[t], y[t, j]>            float32 [T, k], or NULL
+ *   dL (router logits): renormalised  w (d_w - <d_w, w>) on the selected
+ *                       experts, 0 elsewhere; otherwise p (g - <g, p>) with
+ *                       p = softmax(logits), g = d_w scattered to the ids
+ *   per expert e on its rows, dY = w dout[token]:
+ *     d_down[e]    = h^T dY        [E, I, H] dt   (h = silu(g) * u)
+ *     dH = dY down[e]^T;  du = dH silu(g);  dg = dH u silu'(g)
+ *     d_gate_up[e] = X^T [dg | du] [E, H, 2I] dt  (experts without rows: 0)
+ *   dx = sum_j [dg | du] gate_up[e]^T (per slot) + dL router_weight   [T, H] dt
+ *   d_router_weight = dL^T x  [E, H] float32;  d_router_bias = sum_t dL  [E]
+ *   float32 or NULL.
+ * Every sum is float32 in a fixed order: deterministic.  Weight gradients
+ * overwrite their buffers (no accumulation).  Workspace:
+ * moe_workspace_size(MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, 0, T*top_k, dt).
+ */
+int moe_layer_backward(const void* hidden_states, const void* router_weight,
+                       const void* gate_up, const void* down, int T, int H, int I, int E,
+                       int top_k, int norm_topk_prob, moe_dtype dt,
+                       const float* router_logits, const int32_t* topk_ids,
+                       const float* topk_weights, const void* saved_gate_up,
+                       const void* saved_expert_out, const void* dout, void* dx,
+                       float* d_router_weight, float* d_router_bias, void* d_gate_up,
+                       void* d_down, float* d_topk_weights, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,8 @@ lib = _lib.load()
 __all__ = ["lib", "route", "permute", "permute_rank_major", "gather_rows",
            "grouped_gate_up_swiglu", "grouped_down", "grouped_swiglu", "combine",
            "layer_forward", "workspace_size", "router_config", "update_expert_bias",
-           "shared_expert", "shared_expert_forward", "LayerBuffers", "MoEError"]
+           "shared_expert", "shared_expert_forward", "layer_forward_train", "layer_backward",
+           "LayerBuffers", "MoEError"]
 
 MoEError = _lib.MoEError
 
@@ -336,3 +337,64 @@ def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.T
           b.logits.data_ptr(), b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(),
           b.workspace.data_ptr(), b.ws_bytes, None, _stream(x.device))
     return b.out, b.logits, b.ids, b.weights, b.counts
+
+
+def layer_forward_train(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
+                        down: torch.Tensor, top_k: int, norm_topk_prob: bool = True,
+                        router_bias: Optional[torch.Tensor] = None):
+    """The layer forward that also keeps what the backward needs.  Returns
+    (out, saved) where ``saved`` holds router_logits, topk_ids, topk_weights,
+    num_tokens_per_expert, gate_up_out [T*k, 2I] (expert-major
+    pre-activations) and expert_out [T*k, H] (flat slot order)."""
+    T, H = x.shape
+    E = router_weight.shape[0]
+    I = gate_up.shape[2] // 2
+    _chk(x, "x")
+    _chk(router_weight, "router_weight", x.dtype, (E, H))
+    _chk(gate_up, "gate_up", x.dtype, (E, H, 2 * I))
+    _chk(down, "down", x.dtype, (E, I, H))
+    _chk(router_bias, "router_bias", torch.float32, (E,))
+    b = LayerBuffers(T, H, I, E, top_k, x.dtype, x.device)
+    N = T * top_k
+    g = torch.empty(N, 2 * I, dtype=x.dtype, device=x.device)
+    y = torch.empty(N, H, dtype=x.dtype, device=x.device)
+    _call("moe_layer_forward_train", x.data_ptr(), router_weight.data_ptr(),
+          _chk(router_bias, "router_bias"), gate_up.data_ptr(), down.data_ptr(), T, H, I, E,
+          top_k, int(norm_topk_prob), _dt(x), b.out.data_ptr(), b.logits.data_ptr(),
+          b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(), g.data_ptr(),
+          y.data_ptr(), b.workspace.data_ptr(), b.ws_bytes, None, _stream(x.device))
+    saved = dict(router_logits=b.logits, topk_ids=b.ids, topk_weights=b.weights,
+                 num_tokens_per_expert=b.counts, gate_up_out=g, expert_out=y)
+    return b.out, saved
+
+
+def layer_backward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
+                   down: torch.Tensor, top_k: int, norm_topk_prob: bool, saved: dict,
+                   dout: torch.Tensor, with_bias_grad: bool = True) -> dict:
+    """Gradients of sum(dout * out) given ``saved`` from layer_forward_train:
+    dx, d_router_weight (float32), d_router_bias (float32), d_gate_up,
+    d_down and d_topk_weights (float32)."""
+    T, H = x.shape
+    E = router_weight.shape[0]
+    I = gate_up.shape[2] // 2
+    dev = x.device
+    _chk(dout, "dout", x.dtype, (T, H))
+    N = T * top_k
+    g = dict(dx=torch.empty(T, H, dtype=x.dtype, device=dev),
+             d_router_weight=torch.empty(E, H, dtype=torch.float32, device=dev),
+             d_router_bias=torch.empty(E, dtype=torch.float32, device=dev) if with_bias_grad
+             else None,
+             d_gate_up=torch.empty(E, H, 2 * I, dtype=x.dtype, device=dev),
+             d_down=torch.empty(E, I, H, dtype=x.dtype, device=dev),
+             d_topk_weights=torch.empty(T, top_k, dtype=torch.float32, device=dev))
+    nb = lib.moe_workspace_size(_lib.MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, 0, N, _dt(x))
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _call("moe_layer_backward", x.data_ptr(), router_weight.data_ptr(), gate_up.data_ptr(),
+          down.data_ptr(), T, H, I, E, top_k, int(norm_topk_prob), _dt(x),
+          saved["router_logits"].data_ptr(), saved["topk_ids"].data_ptr(),
+          saved["topk_weights"].data_ptr(), saved["gate_up_out"].data_ptr(),
+          saved["expert_out"].data_ptr(), dout.data_ptr(), g["dx"].data_ptr(),
+          g["d_router_weight"].data_ptr(), _chk(g["d_router_bias"], "d_router_bias"),
+          g["d_gate_up"].data_ptr(), g["d_down"].data_ptr(), g["d_topk_weights"].data_ptr(),
+          ws.data_ptr(), nb, _stream(dev))
+    return g

@@ -21,6 +21,7 @@ MOE_OP_DOWN = 3
 MOE_OP_GROUPED_SWIGLU = 4
 MOE_OP_LAYER = 5
 MOE_OP_SHARED = 6
+MOE_OP_LAYER_BACKWARD = 7
 
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
@@ -69,6 +70,10 @@ SIGNATURES = {
     "moe_shared_expert_forward": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _sz, _p]),
     "moe_layer_forward_ex": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
                                   _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_layer_forward_train": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
+                                     _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_layer_backward": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
+                                _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
 }
 
 

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 
 SOURCES = ["moe_api.hip", "moe_route.hip", "moe_permute.hip", "moe_gemm.hip",
-           "moe_gemm_lds.hip", "moe_combine.hip"]
+           "moe_gemm_lds.hip", "moe_combine.hip", "moe_gemm_bwd.hip", "moe_backward.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

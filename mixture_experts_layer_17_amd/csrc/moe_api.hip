@@ -153,6 +153,43 @@ int router_variant(const moe_router_config* c, int E, int k, RouterVariant* out,
   return MOE_OK;
 }
 
+// Backward workspace: permutation of the forward's ids, the dgrad tile list,
+// d_weights, dL, dG [N, 2I], w h [N, I], dX [N, H] and a zero row.
+struct BwdWs {
+  int32_t *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
+  void *perm, *tiles;
+  float *dw, *dL;
+  void *dG, *hw, *dX, *zero;
+  size_t zero_bytes, total;
+};
+
+BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
+  BwdWs w{};
+  const size_t N = (size_t)T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? base + off : nullptr;
+    off += al(bytes);
+    return p;
+  };
+  w.counts = (int32_t*)take((size_t)E * 4);
+  w.offsets = (int32_t*)take((size_t)(E + 1) * 4);
+  w.sorted_token = (int32_t*)take(N * 4);
+  w.sorted_slot = (int32_t*)take(N * 4);
+  w.slot_pos = (int32_t*)take(N * 4);
+  w.perm = take(permute_ws_bytes((int)N, E, 0));
+  w.tiles = take(tile_list_bytes((int)N, E, dgrad_bm(pick_dgrad_cfg((int)N, E))));
+  w.dw = (float*)take(N * 4);
+  w.dL = (float*)take((size_t)T * E * 4);
+  w.dG = take(N * 2 * (size_t)I * esize(dt));
+  w.hw = take(N * (size_t)I * esize(dt));
+  w.dX = take(N * (size_t)H * esize(dt));
+  w.zero_bytes = al((size_t)std::max(H, 2 * I) * esize(dt));
+  w.zero = take(w.zero_bytes);
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +240,11 @@ size_t moe_workspace_size(int op, int T, int H, int I, int E, int top_k, int R, 
           R < 0 || R % 64 != 0)
         return bad;
       return layer_ws(nullptr, T, H, I, E, top_k, dt, R).total;
+    case MOE_OP_LAYER_BACKWARD:
+      if (check_dims(H, I, E, top_k) != MOE_OK || I == 0 || T < 0 ||
+          !rows_ok((long long)T * top_k))
+        return bad;
+      return bwd_ws(nullptr, T, H, I, E, top_k, dt).total;
     case MOE_OP_SHARED:
       if (check_dims(H, I, 1, 1) != MOE_OK || I == 0 || T < 0 || !rows_ok(T)) return bad;
       return shared_ws(nullptr, T, H, I, dt, false).total;
@@ -354,12 +396,19 @@ int moe_shared_expert_forward(const void* x, const void* gate_up, const void* do
   return hip_status(run_shared(dt == MOE_BF16, x, gate_up, down, T, H, Is, w, out, s));
 }
 
-int moe_layer_forward_ex(const void* x, const void* wr, const float* bias, const void* gate_up,
-                         const void* down, int T, int H, int I, int E, int k, int norm,
-                         moe_dtype dt, const moe_router_config* cfg,
-                         const moe_shared_expert* shared, void* out, float* logits, int32_t* ids,
-                         float* weights, int32_t* counts, void* ws, size_t ws_bytes,
-                         hipEvent_t* stage_events, hipStream_t s) {
+}  // extern "C"
+
+namespace {
+
+// The layer forward.  g_save / y_out (training forward): also keep the
+// gate/up pre-activations [N, 2I] in expert-major order and write the expert
+// outputs [N, H] (flat slot order) to the caller's buffer.
+int layer_forward_impl(const void* x, const void* wr, const float* bias, const void* gate_up,
+                       const void* down, int T, int H, int I, int E, int k, int norm,
+                       moe_dtype dt, const moe_router_config* cfg,
+                       const moe_shared_expert* shared, void* out, float* logits, int32_t* ids,
+                       float* weights, int32_t* counts, void* g_save, void* y_out, void* ws,
+                       size_t ws_bytes, hipEvent_t* stage_events, hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
     return MOE_ERR_SHAPE;
@@ -411,16 +460,17 @@ int moe_layer_forward_ex(const void* x, const void* wr, const float* bias, const
     aux_down = dense_aux(cd, false, w.h_s, Is, shared->down, H, Is, 0, w.y_s, H, T, H);
     fused = aux_up.jobs > 0 && aux_down.jobs > 0;
   }
+  void* y = y_out ? y_out : w.y;
   if (N > 0) {
     e = launch_gate_up(bf16, cu, x, T, w.sorted_token, w.offsets, N, H, I, E, gate_up, w.h,
-                       w.tiles_up, true, s, fused ? &aux_up : nullptr);
+                       w.tiles_up, true, s, fused ? &aux_up : nullptr, g_save);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   mark(3);
   // outputs land in flat-slot order (row t * k + j), so the combine reads each
   // token's k rows contiguously.
   if (N > 0) {
-    e = launch_down(bf16, cd, w.h, w.offsets, w.sorted_slot, N, H, I, E, down, w.y,
+    e = launch_down(bf16, cd, w.h, w.offsets, w.sorted_slot, N, H, I, E, down, y,
                     w.tiles_down, true, s, fused ? &aux_down : nullptr);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -430,8 +480,99 @@ int moe_layer_forward_ex(const void* x, const void* wr, const float* bias, const
     e = run_shared(bf16, x, shared->gate_up, shared->down, T, H, Is, sw, w.y_s, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  e = launch_combine(bf16, w.y, nullptr, weights, T, k, H, shared ? w.y_s : nullptr, out, s);
+  e = launch_combine(bf16, y, nullptr, weights, T, k, H, shared ? w.y_s : nullptr, out, s);
   mark(5);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_ex(const void* x, const void* wr, const float* bias, const void* gate_up,
+                         const void* down, int T, int H, int I, int E, int k, int norm,
+                         moe_dtype dt, const moe_router_config* cfg,
+                         const moe_shared_expert* shared, void* out, float* logits, int32_t* ids,
+                         float* weights, int32_t* counts, void* ws, size_t ws_bytes,
+                         hipEvent_t* stage_events, hipStream_t s) {
+  return layer_forward_impl(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, cfg, shared, out,
+                            logits, ids, weights, counts, nullptr, nullptr, ws, ws_bytes,
+                            stage_events, s);
+}
+
+int moe_layer_forward_train(const void* x, const void* wr, const float* bias,
+                            const void* gate_up, const void* down, int T, int H, int I, int E,
+                            int k, int norm, moe_dtype dt, void* out, float* logits, int32_t* ids,
+                            float* weights, int32_t* counts, void* saved_gate_up,
+                            void* saved_expert_out, void* ws, size_t ws_bytes,
+                            hipEvent_t* stage_events, hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (dt != MOE_BF16 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!saved_gate_up || !saved_expert_out || !logits || !ids || !weights))
+    return MOE_ERR_NULL;
+  if (!aligned16(saved_gate_up) || !aligned16(saved_expert_out)) return MOE_ERR_ALIGN;
+  return layer_forward_impl(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, nullptr, nullptr,
+                            out, logits, ids, weights, counts, saved_gate_up, saved_expert_out,
+                            ws, ws_bytes, stage_events, s);
+}
+
+int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const void* down,
+                       int T, int H, int I, int E, int k, int norm, moe_dtype dt,
+                       const float* logits, const int32_t* ids, const float* weights,
+                       const void* saved_gate_up, const void* saved_expert_out, const void* dout,
+                       void* dx, float* d_router_weight, float* d_router_bias, void* d_gate_up,
+                       void* d_down, float* d_weights, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
+    return MOE_ERR_SHAPE;
+  if (dt != MOE_BF16 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!x || !wr || !gate_up || !down || !logits || !ids || !weights || !saved_gate_up ||
+                !saved_expert_out || !dout || !dx || !d_router_weight || !d_gate_up || !d_down))
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wr) || !aligned16(gate_up) || !aligned16(down) ||
+      !aligned16(saved_gate_up) || !aligned16(saved_expert_out) || !aligned16(dout) ||
+      !aligned16(dx) || !aligned16(d_router_weight) || !aligned16(d_gate_up) ||
+      !aligned16(d_down))
+    return MOE_ERR_ALIGN;
+  const size_t need = bwd_ws(nullptr, T, H, I, E, k, dt).total;
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const BwdWs w = bwd_ws((char*)ws, T, H, I, E, k, dt);
+  const bool bf16 = true;
+  const int N = T * k;
+  float* dw = d_weights ? d_weights : w.dw;
+  const int id = pick_dgrad_cfg(N, E);
+  hipError_t e = launch_permute_topk(ids, T, k, E, w.counts, w.offsets, w.sorted_token,
+                                     w.sorted_slot, w.slot_pos, w.perm, s, w.tiles, dgrad_bm(id));
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (T == 0) {
+    // no tokens: every weight gradient is zero
+    e = launch_fill_u32(d_router_weight, (long long)E * H, 0u, s);
+    if (e == hipSuccess && d_router_bias) e = launch_fill_u32(d_router_bias, E, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(d_gate_up, (long long)E * H * I, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(d_down, (long long)E * I * H / 2, 0u, s);
+    return hip_status(e);
+  }
+  e = launch_fill_u32(w.zero, (long long)(w.zero_bytes / 4), 0u, s);
+  // d_weights = <dout, y>, then the softmax / router gradient
+  if (e == hipSuccess) e = launch_weight_grad(bf16, dout, saved_expert_out, N, k, H, dw, s);
+  if (e == hipSuccess) e = launch_router_grad(logits, ids, weights, dw, T, E, k, norm, w.dL, s);
+  // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot order
+  if (e == hipSuccess)
+    e = launch_dgrad_down_swiglu(id, dout, T, w.sorted_token, down, N, H, I, E, saved_gate_up,
+                                 weights, w.sorted_slot, w.dG, w.hw, w.tiles, s);
+  if (e == hipSuccess)
+    e = launch_dgrad_gate_up(id, w.dG, gate_up, N, H, I, E, w.sorted_slot, w.dX, w.tiles, s);
+  if (e == hipSuccess) e = launch_input_grad(bf16, w.dX, w.dL, wr, T, k, E, H, dx, s);
+  // wgrad: d down[e] = (w h)_e^T dout_e, d gate_up[e] = X_e^T dG_e
+  if (e == hipSuccess)
+    e = launch_wgrad(w.hw, I, nullptr, dout, H, w.sorted_token, w.zero, w.offsets, E, I, H,
+                     d_down, s);
+  if (e == hipSuccess)
+    e = launch_wgrad(x, H, w.sorted_token, w.dG, 2 * I, nullptr, w.zero, w.offsets, E, H, 2 * I,
+                     d_gate_up, s);
+  if (e == hipSuccess)
+    e = launch_router_weight_grad(bf16, x, w.dL, w.offsets, w.sorted_token, T, E, H, norm,
+                                  d_router_weight, d_router_bias, s);
   return hip_status(e);
 }
 

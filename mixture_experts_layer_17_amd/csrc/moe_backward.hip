@@ -1,0 +1,267 @@
+// Backward of the MoE layer outside the grouped GEMMs: the routing-weight
+// gradient, the softmax/router gradient, the token reduction of dX and the
+// router's weight gradient.  All sums run in a fixed order in float32, so
+// results are deterministic.
+//
+// The pages train the layer through autograd (Qwen3-Omni issue #115,
+// SpeedupMoeSparseMoeBlock: softmax routing weights, optionally renormalised;
+// MindSpore moe.py, MoE.forward and MoE.unpermutation).  With dout the
+// output gradient:
+//   d_weights[t, j] = <dout[t], y[t, j]>
+//   renormalised:   dL[t, ids] = w (d_weights - <d_weights, w>), 0 elsewhere
+//   plain softmax:  dL[t, e]   = p_e (g_e - <g, p>), g = d_weights scattered
+//   dx[t]  = sum_j dX[t k + j] + sum_e dL[t, e] Wr[e]
+//   dWr[e] = sum_t dL[t, e] x[t],   d_bias[e] = sum_t dL[t, e]
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&f)[8]) {
+  const chunk8<T> c = load_chunk<T>(p);
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t* d = reinterpret_cast<const uint32_t*>(&c.v);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      f[2 * x] = bf16_bits_to_f32(d[x] & 0xffffu);
+      f[2 * x + 1] = bf16_bits_to_f32(d[x] >> 16);
+    }
+  } else {
+    const float* a = reinterpret_cast<const float*>(&c.lo);
+    const float* b = reinterpret_cast<const float*>(&c.hi);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      f[x] = a[x];
+      f[4 + x] = b[x];
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&f)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t d[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      d[x] = (uint32_t)f32_to_bf16_bits(f[2 * x]) | ((uint32_t)f32_to_bf16_bits(f[2 * x + 1]) << 16);
+    *reinterpret_cast<u32x4*>(p) = u32x4{d[0], d[1], d[2], d[3]};
+  } else {
+    reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+}
+
+// d_weights[i] = <dout[i / k], y[i]>: one wave per flat slot, each lane a
+// strided set of 8-column chunks, then a fixed butterfly sum.
+template <typename T>
+__global__ __launch_bounds__(256) void weight_grad_kernel(const T* __restrict__ dout,
+                                                          const T* __restrict__ y, int N, int k,
+                                                          int H, float* __restrict__ dw) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= N) return;
+  const T* d = dout + (size_t)(i / k) * H;
+  const T* r = y + (size_t)i * H;
+  float s = 0.f;
+  for (int c = 8 * lane; c < H; c += 512) {
+    float a[8], b[8];
+    load8(d + c, a);
+    load8(r + c, b);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) s = fmaf(a[x], b[x], s);
+  }
+  s = wave_sum(s);
+  if (lane == 0) dw[i] = s;
+}
+
+// dL[t, :] from the routing-weight gradient: one wave per token.
+__global__ __launch_bounds__(256) void router_grad_kernel(const float* __restrict__ logits,
+                                                          const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ w,
+                                                          const float* __restrict__ dw, int T,
+                                                          int E, int k, int norm,
+                                                          float* __restrict__ dL) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const float* L = logits + (size_t)t * E;
+  float* out = dL + (size_t)t * E;
+  // <d_weights, w> in slot order (w are the softmax probabilities of the
+  // selected experts, renormalised or not)
+  float inner = 0.f;
+  for (int j = 0; j < k; ++j) inner = fmaf(dw[(size_t)t * k + j], w[(size_t)t * k + j], inner);
+  if (norm) {
+    for (int e = lane; e < E; e += 64) {
+      float g = 0.f;
+      for (int j = 0; j < k; ++j)
+        if (ids[(size_t)t * k + j] == e)
+          g = w[(size_t)t * k + j] * (dw[(size_t)t * k + j] - inner);
+      out[e] = g;
+    }
+    return;
+  }
+  float m = -INFINITY;
+  for (int e = lane; e < E; e += 64) m = fmaxf(m, L[e]);
+  m = wave_max(m);
+  float z = 0.f;
+  for (int e = lane; e < E; e += 64) z += __expf(L[e] - m);
+  z = wave_sum(z);
+  const float rz = 1.0f / z;
+  for (int e = lane; e < E; e += 64) {
+    float g = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (ids[(size_t)t * k + j] == e) g = dw[(size_t)t * k + j];
+    const float p = __expf(L[e] - m) * rz;
+    out[e] = p * (g - inner);
+  }
+}
+
+// dx[t] = sum_j dX[t k + j] + sum_e dL[t, e] Wr[e]; one thread per 8 columns.
+template <typename T>
+__global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ dX,
+                                                         const float* __restrict__ dL,
+                                                         const T* __restrict__ wr, int T_, int k,
+                                                         int E, int H, T* __restrict__ dx) {
+  const int per_row = H / 8;
+  const long long total = (long long)T_ * per_row;
+  for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (long long)gridDim.x * 256) {
+    const int t = (int)(q / per_row);
+    const int c = 8 * (int)(q - (long long)t * per_row);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      float v[8];
+      load8(dX + ((size_t)t * k + j) * H + c, v);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[x] += v[x];
+    }
+    const float* l = dL + (size_t)t * E;
+    for (int e = 0; e < E; ++e) {
+      const float g = l[e];
+      if (g == 0.f) continue;
+      float v[8];
+      load8(wr + (size_t)e * H + c, v);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
+    }
+    store8(dx + (size_t)t * H + c, acc);
+  }
+}
+
+// dWr[e, :] = sum_t dL[t, e] x[t, :] and d_bias[e] = sum_t dL[t, e].  With
+// renormalised weights dL[t, e] is nonzero only where token t chose e, so
+// the sum runs over the expert's rows of the permutation (ascending token);
+// otherwise over every token.  One thread per (expert, 8 columns).
+template <typename T>
+__global__ __launch_bounds__(256) void router_weight_grad_kernel(
+    const T* __restrict__ x, const float* __restrict__ dL, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_token, int T_, int E, int H, int sparse,
+    float* __restrict__ dwr, float* __restrict__ dbias) {
+  const int per_row = H / 8;
+  const long long total = (long long)E * per_row;
+  for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (long long)gridDim.x * 256) {
+    const int e = (int)(q / per_row);
+    const int c = 8 * (int)(q - (long long)e * per_row);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float bsum = 0.f;
+    const int lo = sparse ? offsets[e] : 0;
+    const int hi = sparse ? offsets[e + 1] : T_;
+    for (int p = lo; p < hi; ++p) {
+      const int t = sparse ? sorted_token[p] : p;
+      const float g = dL[(size_t)t * E + e];
+      bsum += g;
+      float v[8];
+      load8(x + (size_t)t * H + c, v);
+#pragma unroll
+      for (int xx = 0; xx < 8; ++xx) acc[xx] = fmaf(g, v[xx], acc[xx]);
+    }
+    reinterpret_cast<float4*>(dwr + (size_t)e * H + c)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(dwr + (size_t)e * H + c)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (dbias && c == 0) dbias[e] = bsum;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, long long n, uint32_t v) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (long long)gridDim.x * 256)
+    p[i] = v;
+}
+
+int grid_for_total(long long total) {
+  return (int)std::max<long long>(1, std::min<long long>((total + 255) / 256, 16384));
+}
+
+}  // namespace
+
+hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N, int k, int H,
+                              float* dw, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int grid = (N + 3) / 4;
+  if (bf16)
+    weight_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)dout, (const bf16_t*)y, N, k,
+                                                    H, dw);
+  else
+    weight_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)dout, (const float*)y, N, k, H,
+                                                   dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_grad(const float* logits, const int32_t* ids, const float* w,
+                              const float* dw, int T, int E, int k, int norm, float* dL,
+                              hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  router_grad_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, dw, T, E, k, norm, dL);
+  return hipGetLastError();
+}
+
+hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const void* wr, int T,
+                             int k, int E, int H, void* dx, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int grid = grid_for_total((long long)T * (H / 8));
+  if (bf16)
+    input_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)dX, dL, (const bf16_t*)wr, T,
+                                                   k, E, H, (bf16_t*)dx);
+  else
+    input_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)dX, dL, (const float*)wr, T, k,
+                                                  E, H, (float*)dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_weight_grad(bool bf16, const void* x, const float* dL,
+                                     const int32_t* offsets, const int32_t* sorted_token, int T,
+                                     int E, int H, int sparse, float* dwr, float* dbias,
+                                     hipStream_t s) {
+  const int grid = grid_for_total((long long)E * (H / 8));
+  if (bf16)
+    router_weight_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, dL, offsets,
+                                                           sorted_token, T, E, H, sparse, dwr,
+                                                           dbias);
+  else
+    router_weight_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)x, dL, offsets,
+                                                          sorted_token, T, E, H, sparse, dwr,
+                                                          dbias);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(void* p, long long n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_u32_kernel<<<grid_for_total(n), 256, 0, s>>>((uint32_t*)p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace moe

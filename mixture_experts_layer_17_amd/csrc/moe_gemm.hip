@@ -421,14 +421,14 @@ GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E) {
 hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_rows,
                           const int32_t* row_index, const int32_t* offsets, int N, int H, int I,
                           int E, const void* gate_up, void* h, void* tile_ws, bool tiles_ready,
-                          hipStream_t s, const DenseAux* aux) {
+                          hipStream_t s, const DenseAux* aux, void* g_save) {
   if (lds_cfg_id(c.id)) {
     if (N <= 0 && !(aux && aux->jobs > 0)) return hipSuccess;
     return launch_lds_gemm(true, c, x, H, row_index, x_rows, gate_up, (long long)H * 2 * I, 2 * I,
                            H, I, h, I, nullptr, N, offsets, N, E, I / (c.BN / 2), tile_ws,
-                           tiles_ready, s, aux);
+                           tiles_ready, s, aux, g_save);
   }
-  if (aux && aux->jobs > 0) return hipErrorInvalidValue;
+  if ((aux && aux->jobs > 0) || g_save) return hipErrorInvalidValue;
   if (N <= 0) return hipSuccess;
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);

@@ -1,0 +1,583 @@
+// Backward grouped GEMMs of the MoE layer on gfx950: bf16 operands, MFMA
+// 32x32x16 with float32 accumulation.
+//
+// The layer is trained through autograd on the pages (Qwen3-Omni issue #115,
+// SpeedupMoeExperts' per-expert training loop; MindSpore moe.py,
+// _run_experts_for_loop and MoE.forward).  Per expert e over its rows in
+// expert-major order, with dY = w * dout[token] and dG = [dg | du]:
+//   dgrad   dH_e = dout_e . down[e]^T          rows x I,  K = H
+//           dX_e = dG_e . gate_up[e]^T         rows x H,  K = 2I
+//   wgrad   d down[e]    = (w h)_e^T . dout_e  I x H,     K = rows of e
+//           d gate_up[e] = X_e^T . dG_e        H x 2I,    K = rows of e
+//
+// dgrad: the weight is used as stored ([n][k], k contiguous), so both
+// operands are row tiles of 64 bytes of k per block, XOR-swizzled like the
+// forward's activation tile and read with ds_read_b128; no transposed copy of
+// any weight exists.  The first dgrad's epilogue is the SwiGLU backward.
+//
+// wgrad: K runs over the expert's rows, so both operands arrive as k-rows
+// with their output dimension contiguous, the layout of the forward's weight
+// tile: 32-byte segments XOR-swizzled per row and read with the transposing
+// ds_read_b64_tr_b16.  Gathered rows (x or dout through sorted_token) are
+// addressed through indices fetched with uniform (scalar) loads, so they do
+// not enter the vector-memory counter that orders the asynchronous copies.
+// Rows past the expert's end read a zero row.  Every output element is
+// reduced by one work-group over all of K: deterministic, no atomics; experts
+// without rows get exact zeros.
+#include <type_traits>
+
+#include "moe_common.h"
+#include "moe_internal.h"
+#include "moe_lds.h"
+
+namespace moe {
+namespace {
+
+using namespace lds;
+
+// ---------------------------------------------------------------- dgrad
+
+enum { DG_PLAIN = 0, DG_SWIGLU_BWD = 1 };
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct dcfg {
+  static constexpr int NW = WM * WN;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int TM = BM / 32 / WM;            // 32-row m-tiles per wave
+  static constexpr int CW = BN / WN;                 // output columns per wave
+  static constexpr int TN = CW / 32;                 // 32-column n-tiles per wave
+  static constexpr int STAGE_BYTES = (BM + BN) * 64; // A rows then B rows, 64 B each
+  static constexpr int RING = STAGES * STAGE_BYTES;
+  static constexpr int INST = STAGE_BYTES / 1024;    // wave copies per stage (16 rows)
+  static constexpr int PER = INST / NW;
+  static constexpr int OBF = CW * 4 + 16;            // fp32 staging row stride
+  static constexpr int OBP = CW * 2 + 8;             // bf16 staging row stride
+  static constexpr int STG = 32 * OBF * NW;
+  static constexpr int LDS = RING > STG ? RING : STG;
+  static_assert(BM % (32 * WM) == 0 && TM >= 1 && TN >= 1, "wave tiles");
+  static_assert(INST % NW == 0, "copies split evenly over the waves");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// Epilogue operands of the SwiGLU backward (DG_SWIGLU_BWD).
+struct SwigluBwd {
+  const bf16_t* G;        // [N, 2I] pre-activations saved by the forward
+  int ldg, up_off;        // 2I, I
+  const float* w;         // routing weights, flat slot order
+  const int32_t* slot;    // sorted_slot: flat slot of each expert-major row
+  bf16_t* dG;             // [N, 2I]
+  bf16_t* hw;             // [N, I]  w * silu(g) * u
+  int ldh;
+};
+
+template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
+    const bf16_t* __restrict__ X, int ldx, const int32_t* __restrict__ x_index, int x_rows,
+    const bf16_t* __restrict__ W, long long w_estride, int ldw, int K,
+    bf16_t* __restrict__ C, int ldc, const int32_t* __restrict__ c_index, int c_rows,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count, int n_ntiles,
+    SwigluBwd sb) {
+  using G = dcfg<BM, BN, WM, WN, STAGES>;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int jobs = tiles_count[0] * n_ntiles;
+  const int per_xcd = (jobs + NUM_XCD - 1) / NUM_XCD;
+  const int xcd = blockIdx.x % NUM_XCD;
+  const int local = blockIdx.x / NUM_XCD;
+  if (local >= per_xcd) return;
+  const int job = xcd * per_xcd + local;
+  if (job >= jobs) return;
+  const int mt = job / n_ntiles;
+  const int nt = job - mt * n_ntiles;
+  const int4 tile = tiles[mt];
+  const int e = tile.x, row0 = tile.y, rows = tile.z;
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const bf16_t* We = W + (long long)e * w_estride;
+
+  // copy assignments: stage row r < BM is activation row r of the tile, row
+  // BM + c is weight row n0 + c; lane q of a copy moves chunk (q & 3) ^ f(r)
+  const bf16_t* src[G::PER];
+#pragma unroll
+  for (int u = 0; u < G::PER; ++u) {
+    const int inst = wave + u * G::NW;
+    const int q = inst * 64 + lane;
+    const int r = q >> 2;
+    const int c = (q & 3) ^ fswz(r);
+    if (r < BM) {
+      int s = row0 + min(r, rows - 1);
+      if (x_index) s = x_index[s];
+      s = min(max(s, 0), x_rows - 1);
+      src[u] = X + (long long)s * ldx + 8 * c;
+    } else {
+      src[u] = We + (long long)(n0 + r - BM) * ldw + 8 * c;
+    }
+  }
+  auto issue = [&](unsigned char* base) {
+#pragma unroll
+    for (int u = 0; u < G::PER; ++u) {
+      copy16_to_lds(src[u], base + (wave + u * G::NW) * 1024);
+      src[u] += BK;
+    }
+  };
+  const int KT = K / BK;
+  auto wait_blocks = [&](int nb) {
+    static_assert(STAGES <= 4 && (STAGES - 1) * G::PER < 64, "wait table");
+    switch (nb) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<G::PER>(); break;
+      case 2: wait_vmcnt<2 * G::PER>(); break;
+      default: wait_vmcnt<3 * G::PER>(); break;
+    }
+  };
+
+  // fragment offsets: lane l reads row 32 t + l % 32, k chunk 2 kk + l / 32
+  const int l32 = lane & 31, hl = lane >> 5;
+  int a_off[G::TM][2], b_off[G::TN][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int ch = 16 * ((2 * kk + hl) ^ fswz(l32));
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) a_off[i][kk] = (32 * (wm + WM * i) + l32) * 64 + ch;
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) b_off[j][kk] = (BM + wn * G::CW + 32 * j + l32) * 64 + ch;
+  }
+
+  f32x16_v acc[G::TM][G::TN];
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+#pragma unroll
+  for (int p = 0; p < STAGES; ++p)
+    if (p < KT) issue(smem + p * G::STAGE_BYTES);
+  for (int kb = 0; kb < KT; ++kb) {
+    unsigned char* cur = smem + (kb % STAGES) * G::STAGE_BYTES;
+    wait_blocks(min(KT, kb + STAGES) - 1 - kb);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_v af[G::TM], bf[G::TN];
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(cur + a_off[i][kk]));
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+        bf[j] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(cur + b_off[j][kk]));
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kb + STAGES < KT) issue(cur);
+  }
+
+  // ---- epilogue.  acc[i][j][q] = C[row 32 (wm + WM i) + l % 32]
+  //                                 [col wn CW + 32 j + 8 (q / 4) + 4 hl + q % 4]
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if constexpr (EPI == DG_PLAIN) {
+    constexpr int LPR = G::CW * 2 / 16;        // lanes per staged row
+    constexpr int RPI = 64 / LPR;
+    unsigned char* stg = smem + wave * 32 * G::OBP;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x16_v& v = acc[i][j];
+          const uint2 d = make_uint2(
+              (uint32_t)f32_to_bf16_bits(v[4 * a]) | ((uint32_t)f32_to_bf16_bits(v[4 * a + 1]) << 16),
+              (uint32_t)f32_to_bf16_bits(v[4 * a + 2]) |
+                  ((uint32_t)f32_to_bf16_bits(v[4 * a + 3]) << 16));
+          *reinterpret_cast<uint2*>(stg + l32 * G::OBP + 2 * (32 * j + 8 * a + 4 * hl)) = d;
+        }
+#pragma unroll
+      for (int rr = 0; rr < 32 / RPI; ++rr) {
+        const int r = rr * RPI + lane / LPR;
+        const int m = 32 * (wm + WM * i) + r;
+        const uint2 lo = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR));
+        const uint2 hi = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR) + 8);
+        if (m < rows) {
+          const int dst = c_index ? c_index[row0 + m] : row0 + m;
+          if (dst >= 0 && dst < c_rows)
+            *reinterpret_cast<u32x4*>(C + (long long)dst * ldc + n0 + wn * G::CW +
+                                      8 * (lane % LPR)) = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
+    }
+  } else {
+    // SwiGLU backward.  z = dout . down^T for row p, column n of I:
+    //   h = silu(g) u,  dh = w z,  du = dh silu(g),  dg = dh u silu'(g),
+    //   hw = w h   (the first operand of the down-projection's wgrad)
+    constexpr int LPR = G::CW * 4 / 16;        // lanes per staged fp32 row
+    constexpr int RPI = 64 / LPR;
+    unsigned char* stg = smem + wave * 32 * G::OBF;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x16_v& v = acc[i][j];
+          *reinterpret_cast<float4*>(stg + l32 * G::OBF + 4 * (32 * j + 8 * a + 4 * hl)) =
+              make_float4(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
+        }
+#pragma unroll
+      for (int rr = 0; rr < 32 / RPI; ++rr) {
+        const int r = rr * RPI + lane / LPR;
+        const int m = 32 * (wm + WM * i) + r;
+        const float4 z = *reinterpret_cast<const float4*>(stg + r * G::OBF + 16 * (lane % LPR));
+        if (m < rows) {
+          const int p = row0 + m;
+          const int n = n0 + wn * G::CW + 4 * (lane % LPR);
+          const float wt = sb.w[sb.slot[p]];
+          const uint2 g2 = *reinterpret_cast<const uint2*>(sb.G + (long long)p * sb.ldg + n);
+          const uint2 u2 = *reinterpret_cast<const uint2*>(sb.G + (long long)p * sb.ldg + sb.up_off + n);
+          const float zz[4] = {z.x, z.y, z.z, z.w};
+          const uint32_t gw[2] = {g2.x, g2.y}, uw[2] = {u2.x, u2.y};
+          uint32_t dg[2], du[2], hv[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            float o_dg[2], o_du[2], o_h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const float g = bf16_bits_to_f32(hh ? gw[c] >> 16 : gw[c] & 0xffffu);
+              const float u = bf16_bits_to_f32(hh ? uw[c] >> 16 : uw[c] & 0xffffu);
+              const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+              const float a = g * s;
+              const float dh = wt * zz[2 * c + hh];
+              o_du[hh] = dh * a;
+              o_dg[hh] = dh * u * (s * (1.0f + g * (1.0f - s)));
+              o_h[hh] = wt * (a * u);
+            }
+            dg[c] = (uint32_t)f32_to_bf16_bits(o_dg[0]) | ((uint32_t)f32_to_bf16_bits(o_dg[1]) << 16);
+            du[c] = (uint32_t)f32_to_bf16_bits(o_du[0]) | ((uint32_t)f32_to_bf16_bits(o_du[1]) << 16);
+            hv[c] = (uint32_t)f32_to_bf16_bits(o_h[0]) | ((uint32_t)f32_to_bf16_bits(o_h[1]) << 16);
+          }
+          *reinterpret_cast<uint2*>(sb.dG + (long long)p * sb.ldg + n) = make_uint2(dg[0], dg[1]);
+          *reinterpret_cast<uint2*>(sb.dG + (long long)p * sb.ldg + sb.up_off + n) =
+              make_uint2(du[0], du[1]);
+          *reinterpret_cast<uint2*>(sb.hw + (long long)p * sb.ldh + n) = make_uint2(hv[0], hv[1]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- wgrad
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct wcfg {
+  static constexpr int NW = WM * WN;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int TM = BM / 32 / WM;            // 32-row m-tiles per wave
+  static constexpr int CW = BN / WN;                 // output columns per wave
+  static constexpr int TN = CW / 32;
+  static constexpr int A_ROWB = BM * 2;              // bytes per k-row
+  static constexpr int B_ROWB = BN * 2;
+  static constexpr int A_BYTES = BK * A_ROWB;
+  static constexpr int B_BYTES = BK * B_ROWB;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int RING = STAGES * STAGE_BYTES;
+  static constexpr int A_INST = A_BYTES / 1024;
+  static constexpr int INST = STAGE_BYTES / 1024;
+  static constexpr int PER = INST / NW;
+  static constexpr int OBP = CW * 2 + 8;
+  static constexpr int STG = 32 * OBP * NW;
+  static constexpr int LDS = RING > STG ? RING : STG;
+  static_assert(BM / 16 >= 8 && BN / 16 >= 8, "swizzle needs 8 segments per row");
+  static_assert(INST % NW == 0 && A_BYTES % 1024 == 0, "copies split evenly");
+  static_assert(TM >= 1 && TN >= 1, "wave tiles");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
+    const bf16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index,
+    const bf16_t* __restrict__ B, int ldb, const int32_t* __restrict__ b_index,
+    const bf16_t* __restrict__ zero_row, const int32_t* __restrict__ offsets, int E, int M,
+    int N, bf16_t* __restrict__ C, long long c_estride, int ldc) {
+  using G = wcfg<BM, BN, WM, WN, STAGES>;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  // ---- job (expert, m-tile, n-tile); consecutive jobs share an expert's rows
+  const int m_tiles = M / BM, n_tiles = N / BN;
+  const int jobs = E * m_tiles * n_tiles;
+  const int per_xcd = (jobs + NUM_XCD - 1) / NUM_XCD;
+  const int xcd = blockIdx.x % NUM_XCD;
+  const int local = blockIdx.x / NUM_XCD;
+  if (local >= per_xcd) return;
+  const int job = xcd * per_xcd + local;
+  if (job >= jobs) return;
+  const int e = job / (m_tiles * n_tiles);
+  const int rem = job - e * m_tiles * n_tiles;
+  const int mt = rem / n_tiles;
+  const int nt = rem - mt * n_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int lo = offsets[e];
+  const int hi = max(offsets[e + 1], lo);
+  const int KT = (hi - lo + BK - 1) / BK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const bf16_t* zr = zero_row;
+
+  // copy u of this wave moves 1 KB = 1024 / ROWB k-rows of the A or B tile;
+  // lane q takes 16-byte piece p of k-row r, whose 32-byte segment is
+  // swizzled by h(r)
+  int c_col[G::PER], c_row[G::PER], c_lds[G::PER];
+  bool c_isa[G::PER];
+#pragma unroll
+  for (int u = 0; u < G::PER; ++u) {
+    const int inst = wave + u * G::NW;
+    const bool isa = inst < G::A_INST;
+    const int rowb = isa ? G::A_ROWB : G::B_ROWB;
+    const int local_inst = isa ? inst : inst - G::A_INST;
+    const int q = local_inst * 64 + lane;
+    const int r = q / (rowb / 16);
+    const int p = q % (rowb / 16);
+    const int seg = (p >> 1) ^ hswz(r);
+    c_isa[u] = isa;
+    c_row[u] = r;
+    c_col[u] = 16 * seg + 8 * (p & 1) + (isa ? m0 : n0);
+    c_lds[u] = (isa ? 0 : G::A_BYTES) + local_inst * 1024;
+  }
+  // source of copy u for K-block kb.  The row's index is a uniform value:
+  // the k-rows of one copy are consecutive, and each lane picks its own.
+  auto issue = [&](unsigned char* base, int kb) {
+#pragma unroll
+    for (int u = 0; u < G::PER; ++u) {
+      const int inst = wave + u * G::NW;
+      const bool isa = c_isa[u];
+      const int rows_per = 1024 / (isa ? G::A_ROWB : G::B_ROWB);
+      const int first = (isa ? inst : inst - G::A_INST) * rows_per;   // uniform
+      const int32_t* idx = isa ? a_index : b_index;
+      int srow = -1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < rows_per) {
+          const int rg = lo + kb * BK + first + t;                   // uniform
+          int s = -1;
+          if (rg < hi) s = idx ? idx[rg] : rg;
+          if (c_row[u] == first + t) srow = s;
+        }
+      }
+      const bf16_t* g = srow >= 0 ? (isa ? A + (long long)srow * lda : B + (long long)srow * ldb)
+                                  : zr;
+      copy16_to_lds(g + c_col[u], base + c_lds[u]);
+    }
+  };
+  auto wait_blocks = [&](int nb) {
+    static_assert(STAGES <= 4 && (STAGES - 1) * G::PER < 64, "wait table");
+    switch (nb) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<G::PER>(); break;
+      case 2: wait_vmcnt<2 * G::PER>(); break;
+      default: wait_vmcnt<3 * G::PER>(); break;
+    }
+  };
+
+  // transposing fragment reads: 16-lane group q reads columns 16 (q & 1) ..
+  // + 15 and k 8 (q >> 1) .. + 7 of a 32-column sub-tile
+  const int gq = lane >> 4, s16 = lane & 15;
+  const int wrow = 8 * (gq >> 1) + (s16 >> 2);
+  const int wsw = ((s16 >> 2) << 1) | (gq >> 1);
+  auto frag_off = [&](int rowb, int cb) {
+    const int col = cb + 16 * (gq & 1) + 4 * (s16 & 3);
+    return wrow * rowb + 32 * ((col >> 4) ^ wsw) + 2 * (col & 15);
+  };
+  int a_off[G::TM], b_off[G::TN];
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i) a_off[i] = frag_off(G::A_ROWB, (BM / WM) * wm + 32 * i);
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) b_off[j] = G::A_BYTES + frag_off(G::B_ROWB, G::CW * wn + 32 * j);
+  auto read_tr = [](const unsigned char* p, int rowb) {
+    const i16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * rowb));
+    return __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16_v acc[G::TM][G::TN];
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+#pragma unroll
+  for (int p = 0; p < STAGES; ++p)
+    if (p < KT) issue(smem + p * G::STAGE_BYTES, p);
+  for (int kb = 0; kb < KT; ++kb) {
+    unsigned char* cur = smem + (kb % STAGES) * G::STAGE_BYTES;
+    wait_blocks(min(KT, kb + STAGES) - 1 - kb);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_v af[G::TM], bf[G::TN];
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i) af[i] = read_tr(cur + a_off[i] + 16 * kk * G::A_ROWB, G::A_ROWB);
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) bf[j] = read_tr(cur + b_off[j] + 16 * kk * G::B_ROWB, G::B_ROWB);
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kb + STAGES < KT) issue(cur, kb + STAGES);
+  }
+
+  // ---- epilogue: acc[i][j][q] = C[m0 + (BM / WM) wm + 32 i + l % 32]
+  //                                [n0 + CW wn + 32 j + 8 (q / 4) + 4 hl + q % 4]
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const int l32 = lane & 31, hl = lane >> 5;
+  constexpr int LPR = G::CW * 2 / 16;
+  constexpr int RPI = 64 / LPR;
+  unsigned char* stg = smem + wave * 32 * G::OBP;
+  bf16_t* Ce = C + (long long)e * c_estride;
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x16_v& v = acc[i][j];
+        const uint2 d = make_uint2(
+            (uint32_t)f32_to_bf16_bits(v[4 * a]) | ((uint32_t)f32_to_bf16_bits(v[4 * a + 1]) << 16),
+            (uint32_t)f32_to_bf16_bits(v[4 * a + 2]) | ((uint32_t)f32_to_bf16_bits(v[4 * a + 3]) << 16));
+        *reinterpret_cast<uint2*>(stg + l32 * G::OBP + 2 * (32 * j + 8 * a + 4 * hl)) = d;
+      }
+#pragma unroll
+    for (int rr = 0; rr < 32 / RPI; ++rr) {
+      const int r = rr * RPI + lane / LPR;
+      const int m = m0 + (BM / WM) * wm + 32 * i + r;
+      const uint2 x0 = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR));
+      const uint2 x1 = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR) + 8);
+      *reinterpret_cast<u32x4*>(Ce + (long long)m * ldc + n0 + wn * G::CW + 8 * (lane % LPR)) =
+          u32x4{x0.x, x0.y, x1.x, x1.y};
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
+hipError_t launch_dgrad_t(const void* X, int ldx, const int32_t* x_index, int x_rows,
+                          const void* W, long long w_estride, int ldw, int K, void* C, int ldc,
+                          const int32_t* c_index, int c_rows, const void* tile_ws, int N, int E,
+                          int n_ntiles, const SwigluBwd& sb, hipStream_t s) {
+  using G = dcfg<BM, BN, WM, WN, STAGES>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)dgrad_kernel<BM, BN, WM, WN, STAGES, EPI>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+  if (attr != hipSuccess) return attr;
+  const long long max_tiles = (long long)N / BM + std::min(E, N);
+  const long long jobs = (max_tiles * n_ntiles + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+  const int grid = (int)std::max<long long>(jobs, NUM_XCD);
+  hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, STAGES, EPI>), dim3(grid), dim3(G::THREADS),
+                     G::LDS, s, (const bf16_t*)X, ldx, x_index, x_rows, (const bf16_t*)W,
+                     w_estride, ldw, K, (bf16_t*)C, ldc, c_index, c_rows,
+                     (const int4*)((const char*)tile_ws + 256), (const int32_t*)tile_ws, n_ntiles,
+                     sb);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_dgrad_cfg(int id, const void* X, int ldx, const int32_t* x_index, int x_rows,
+                            const void* W, long long w_estride, int ldw, int K, void* C, int ldc,
+                            const int32_t* c_index, int c_rows, const void* tile_ws, int N, int E,
+                            int n_ntiles, const SwigluBwd& sb, hipStream_t s) {
+#define MOE_DG(ID, BM, BN, WM, WN, ST)                                                        \
+  case ID:                                                                                 \
+    return launch_dgrad_t<BM, BN, WM, WN, ST, EPI>(X, ldx, x_index, x_rows, W, w_estride, ldw, \
+                                                   K, C, ldc, c_index, c_rows, tile_ws, N, E,  \
+                                                   n_ntiles, sb, s);
+  switch (id) {
+    MOE_DG(0, 128, 128, 2, 2, 4)
+    MOE_DG(1, 64, 128, 2, 2, 4)
+    MOE_DG(2, 32, 128, 1, 2, 4)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_DG
+}
+
+constexpr int kDgradBM[] = {128, 64, 32};
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+hipError_t launch_wgrad_t(const void* A, int lda, const int32_t* a_index, const void* B, int ldb,
+                          const int32_t* b_index, const void* zero_row, const int32_t* offsets,
+                          int E, int M, int N, void* C, long long c_estride, int ldc,
+                          hipStream_t s) {
+  using G = wcfg<BM, BN, WM, WN, STAGES>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)wgrad_kernel<BM, BN, WM, WN, STAGES>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+  if (attr != hipSuccess) return attr;
+  const long long jobs = (long long)E * (M / BM) * (N / BN);
+  const int grid = (int)std::max<long long>((jobs + NUM_XCD - 1) / NUM_XCD * NUM_XCD, NUM_XCD);
+  hipLaunchKernelGGL((wgrad_kernel<BM, BN, WM, WN, STAGES>), dim3(grid), dim3(G::THREADS), G::LDS,
+                     s, (const bf16_t*)A, lda, a_index, (const bf16_t*)B, ldb, b_index,
+                     (const bf16_t*)zero_row, offsets, E, M, N, (bf16_t*)C, c_estride, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int pick_dgrad_cfg(int N, int E) {
+  const double mean_rows = E > 0 ? (double)N / E : 0.0;
+  return mean_rows >= 96.0 ? 0 : mean_rows >= 40.0 ? 1 : 2;
+}
+
+int dgrad_bm(int id) { return kDgradBM[id]; }
+
+hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
+                                    const void* down, int N, int H, int I, int E,
+                                    const void* G, const float* w, const int32_t* sorted_slot,
+                                    void* dG, void* hw, const void* tile_ws, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const SwigluBwd sb{(const bf16_t*)G, 2 * I, I, w, sorted_slot, (bf16_t*)dG, (bf16_t*)hw, I};
+  return launch_dgrad_cfg<DG_SWIGLU_BWD>(id, dout, H, sorted_token, T, down, (long long)I * H, H,
+                                         H, nullptr, 0, nullptr, 0, tile_ws, N, E, I / 128, sb, s);
+}
+
+hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int N, int H, int I,
+                                int E, const int32_t* out_index, void* dX, const void* tile_ws,
+                                hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const SwigluBwd none{};
+  return launch_dgrad_cfg<DG_PLAIN>(id, dG, 2 * I, nullptr, N, gate_up, (long long)H * 2 * I,
+                                    2 * I, 2 * I, dX, H, out_index, N, tile_ws, N, E, H / 128,
+                                    none, s);
+}
+
+hipError_t launch_wgrad(const void* A, int lda, const int32_t* a_index, const void* B, int ldb,
+                        const int32_t* b_index, const void* zero_row, const int32_t* offsets,
+                        int E, int M, int N, void* C, hipStream_t s) {
+  if (N % 256 == 0)
+    return launch_wgrad_t<128, 256, 2, 2, 3>(A, lda, a_index, B, ldb, b_index, zero_row, offsets,
+                                             E, M, N, C, (long long)M * N, N, s);
+  return launch_wgrad_t<128, 128, 2, 2, 4>(A, lda, a_index, B, ldb, b_index, zero_row, offsets, E,
+                                           M, N, C, (long long)M * N, N, s);
+}
+
+}  // namespace moe

@@ -33,50 +33,12 @@
 
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "moe_lds.h"
 
 namespace moe {
 namespace {
 
-constexpr int NUM_XCD = 8;
-constexpr int NUM_CU = 256;
-constexpr int BK = 32;   // k per stage
-
-typedef short i16x4_v __attribute__((ext_vector_type(4)));
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_v;
-typedef __attribute__((address_space(3))) i16x4_v lds_i16x4;
-
-// Swizzles chosen by timing every lane pattern the kernel reads against the
-// conflict-free rate (ds_read_b128: 4 clocks per wave instruction,
-// ds_read_b64_tr_b16: 2 clocks).
-__device__ __forceinline__ int fswz(int row) { return (row ^ (row >> 2)) & 3; }
-__device__ __forceinline__ int hswz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
-
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-
-// One 16-byte-per-lane asynchronous copy global -> LDS: lane i's 16 bytes
-// land at lds + 16 i (lds is wave-uniform, passed in M0).  Issued from asm
-// so that the compiler's wait-count pass, which cannot tell the four stage
-// buffers apart across loop iterations, does not drain every copy in flight
-// before each LDS read; completion is tracked with explicit vmcnt waits
-// below.  The instruction writes no registers, so nothing the compiler
-// allocates can be overwritten while it is in flight.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(const void* g, const unsigned char* lds) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const lds_u8*)lds;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(a)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Waits until at most N of this wave's vector-memory loads are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
+using namespace lds;
 
 template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU>
 struct lcfg {
@@ -114,7 +76,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     int g_x_rows, const bf16_t* __restrict__ gW, long long g_w_estride, int g_ldw, int g_K,
     int g_up_off, bf16_t* __restrict__ gC, int g_ldc, const int32_t* __restrict__ g_c_index,
     int g_c_rows, const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count,
-    int g_n_ntiles, DenseAux aux) {
+    int g_n_ntiles, DenseAux aux, bf16_t* __restrict__ g_save) {
   using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU>;
   static_assert(STAGES >= 2, "at least double buffering");
   // STAGES ring slots of STAGE_BYTES.  The copies are invisible to the
@@ -467,6 +429,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
           *reinterpret_cast<u32x4*>(C + (long long)dst * ldc + n0 + wn * G::CW + 8 * (lane % LPR)) =
               u32x4{lo.x, lo.y, hi.x, hi.y};
       }
+      if constexpr (SWIGLU) {
+        // training forward: also keep the pre-activations, gate at column n
+        // and up at column up_off + n of the [rows, 2 up_off] buffer
+        if (g_save && !dense) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int j = 0; j < G::TNO; ++j)
+#pragma unroll
+              for (int a = 0; a < 4; ++a) {
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = acc[i][half * G::TNO + j][4 * a + q];
+                *reinterpret_cast<uint2*>(stg + l32 * OBP + 2 * (32 * j + 8 * a + 4 * hl)) =
+                    to_bf16x4(v);
+              }
+#pragma unroll
+            for (int rr = 0; rr < NRI; ++rr) {
+              const int r = rr * RPI + lane / LPR;
+              const uint2 lo = *reinterpret_cast<const uint2*>(stg + r * OBP + 16 * (lane % LPR));
+              const uint2 hi =
+                  *reinterpret_cast<const uint2*>(stg + r * OBP + 16 * (lane % LPR) + 8);
+              const int dst = dsts[i][rr];
+              if (dst >= 0 && dst < c_rows)
+                *reinterpret_cast<u32x4*>(g_save + (long long)dst * (2 * up_off) + half * up_off +
+                                          n0 + wn * G::CW + 8 * (lane % LPR)) =
+                    u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+          }
+        }
+      }
     }
   }
 }
@@ -476,7 +469,7 @@ hipError_t launch_lds(const void* X, int ldx, const int32_t* x_index, int x_rows
                       long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                       const int32_t* c_index, int c_rows, const int4* tiles,
                       const int32_t* tiles_count, int n_ntiles, int grid, hipStream_t s,
-                      const DenseAux& aux) {
+                      const DenseAux& aux, void* g_save) {
   using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU>,
@@ -485,7 +478,7 @@ hipError_t launch_lds(const void* X, int ldx, const int32_t* x_index, int x_rows
   hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU>), dim3(grid),
                      dim3(G::THREADS), G::LDS, s, (const bf16_t*)X, ldx, x_index, x_rows,
                      (const bf16_t*)W, w_estride, ldw, K, up_off, (bf16_t*)C, ldc, c_index,
-                     c_rows, tiles, tiles_count, n_ntiles, aux);
+                     c_rows, tiles, tiles_count, n_ntiles, aux, (bf16_t*)g_save);
   return hipGetLastError();
 }
 
@@ -503,9 +496,9 @@ hipError_t launch_lds_cfg(bool swiglu, int id, const void* X, int ldx, const int
                           int x_rows, const void* W, long long w_estride, int ldw, int K,
                           int up_off, void* C, int ldc, const int32_t* c_index, int c_rows,
                           const int4* tiles, const int32_t* tiles_count, int n_ntiles, int grid,
-                          hipStream_t s, const DenseAux& aux) {
+                          hipStream_t s, const DenseAux& aux, void* g_save) {
 #define MOE_ARGS X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C, ldc, c_index, c_rows, \
-                 tiles, tiles_count, n_ntiles, grid, s, aux
+                 tiles, tiles_count, n_ntiles, grid, s, aux, g_save
 #define MOE_CASE(ID, BM, BN, WM, WN, ST)                                    \
   case ID:                                                                \
     return swiglu ? launch_lds<BM, BN, WM, WN, ST, true>(MOE_ARGS)        \
@@ -568,7 +561,7 @@ hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int
                            long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                            const int32_t* c_index, int c_rows, const int32_t* offsets, int N,
                            int E, int n_ntiles, void* tile_ws, bool tiles_ready, hipStream_t s,
-                           const DenseAux* aux) {
+                           const DenseAux* aux, void* g_save) {
   int32_t* count = (int32_t*)tile_ws;
   int4* tiles = (int4*)((char*)tile_ws + 256);
   if (!tiles_ready) {
@@ -584,7 +577,7 @@ hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int
   const long long d_per = ((long long)a.jobs + NUM_XCD - 1) / NUM_XCD;
   const int grid = (int)std::max<long long>((g_per + d_per) * NUM_XCD, NUM_XCD);
   return launch_lds_cfg(swiglu, c.id, X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C,
-                        ldc, c_index, c_rows, tiles, count, n_ntiles, grid, s, a);
+                        ldc, c_index, c_rows, tiles, count, n_ntiles, grid, s, a, g_save);
 }
 
 }  // namespace moe

@@ -84,7 +84,7 @@ hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int
                            long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                            const int32_t* c_index, int c_rows, const int32_t* offsets, int N,
                            int E, int n_ntiles, void* tile_ws, bool tiles_ready, hipStream_t s,
-                           const DenseAux* aux = nullptr);
+                           const DenseAux* aux = nullptr, void* g_save = nullptr);
 // Builds the tile list of row-tile height BM into tile_ws (one block).
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int N, int BM, void* tile_ws,
                               hipStream_t s);
@@ -95,14 +95,44 @@ GemmTileCfg pick_dense_cfg(bool bf16, int rows, int cols, bool swiglu);
 GemmTileCfg pick_gate_up_cfg(bool bf16, int N, int H, int I, int E);
 GemmTileCfg pick_down_cfg(bool bf16, int N, int H, int I, int E);
 size_t tile_list_bytes(int N, int E, int BM);
-// `aux` (LDS configs only) adds a dense problem to the same launch.
+// `aux` (LDS configs only) adds a dense problem to the same launch;
+// `g_save` (LDS configs only) also stores the pre-activations [N, 2I].
 hipError_t launch_gate_up(bool bf16, const GemmTileCfg& c, const void* x, int x_rows,
                           const int32_t* row_index, const int32_t* offsets, int N, int H,
                           int I, int E, const void* gate_up, void* h, void* tile_ws,
-                          bool tiles_ready, hipStream_t s, const DenseAux* aux = nullptr);
+                          bool tiles_ready, hipStream_t s, const DenseAux* aux = nullptr,
+                          void* g_save = nullptr);
 hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h,
                        const int32_t* offsets, const int32_t* out_index, int N, int H,
                        int I, int E, const void* down, void* y, void* tile_ws,
                        bool tiles_ready, hipStream_t s, const DenseAux* aux = nullptr);
+
+// Backward (moe_gemm_bwd.hip, moe_backward.hip).  bf16 only; I % 128 == 0,
+// H % 128 == 0.  The dgrad GEMMs use the row-tile list of height
+// dgrad_bm(id).
+int pick_dgrad_cfg(int N, int E);
+int dgrad_bm(int id);
+hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
+                                    const void* down, int N, int H, int I, int E,
+                                    const void* G, const float* w, const int32_t* sorted_slot,
+                                    void* dG, void* hw, const void* tile_ws, hipStream_t s);
+hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int N, int H, int I,
+                                int E, const int32_t* out_index, void* dX, const void* tile_ws,
+                                hipStream_t s);
+hipError_t launch_wgrad(const void* A, int lda, const int32_t* a_index, const void* B, int ldb,
+                        const int32_t* b_index, const void* zero_row, const int32_t* offsets,
+                        int E, int M, int N, void* C, hipStream_t s);
+hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N, int k, int H,
+                              float* dw, hipStream_t s);
+hipError_t launch_router_grad(const float* logits, const int32_t* ids, const float* w,
+                              const float* dw, int T, int E, int k, int norm, float* dL,
+                              hipStream_t s);
+hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const void* wr, int T,
+                             int k, int E, int H, void* dx, hipStream_t s);
+hipError_t launch_router_weight_grad(bool bf16, const void* x, const float* dL,
+                                     const int32_t* offsets, const int32_t* sorted_token, int T,
+                                     int E, int H, int sparse, float* dwr, float* dbias,
+                                     hipStream_t s);
+hipError_t launch_fill_u32(void* p, long long n, uint32_t v, hipStream_t s);
 
 }  // namespace moe

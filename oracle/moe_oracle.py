@@ -349,9 +349,12 @@ def _add_shared(out, x, shared):
 # ---------------------------------------------------------------------------
 
 def moe_layer_forward(x, w_router, bias, gate_up, down, top_k: int,
-                      norm_topk_prob: bool, shared=None) -> dict:
+                      norm_topk_prob: bool, shared=None, ids=None) -> dict:
     """Full layer: route, permute, per-expert SwiGLU loop, combine, and the
     optional shared expert ``shared = (w1, w2, w3)`` (``FeedForward`` weights).
+    ``ids`` replaces the top-k decision with one taken elsewhere (a device's
+    top-k of its own float32 logits, checked separately); the routing weights
+    are then this module's softmax at those ids.
 
     Returns a dict with ``logits`` (float32 [T, E]), ``ids`` ([T, k]),
     ``weights`` ([T, k] float64), ``counts``, ``offsets``, ``sorted_slot``,
@@ -360,7 +363,12 @@ def moe_layer_forward(x, w_router, bias, gate_up, down, top_k: int,
     [T, H])."""
     x = np.asarray(x)
     E = np.asarray(w_router).shape[0]
-    L, ids, w = route(x, w_router, bias, top_k, norm_topk_prob)
+    if ids is None:
+        L, ids, w = route(x, w_router, bias, top_k, norm_topk_prob)
+    else:
+        L = router_logits(x, w_router, bias)
+        ids = np.asarray(ids, dtype=np.int32)
+        w = routing_weights(L, ids, norm_topk_prob)
     counts = expert_counts(ids, E)
     offsets = expert_offsets(counts)
     sorted_slot, sorted_token, slot_pos = permutation(ids, E)
@@ -424,7 +432,7 @@ def silu_grad(z: np.ndarray) -> np.ndarray:
 
 
 def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_prob: bool,
-                       dout) -> dict:
+                       dout, ids=None) -> dict:
     """Gradients of ``sum(dout * out)`` for the layer of ``moe_layer_forward``.
 
     The routing decision (which experts) is piecewise constant, so gradients
@@ -445,8 +453,9 @@ def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_p
 
     Returns float64 ``dx``, ``d_router_weight``, ``d_router_bias``,
     ``d_gate_up``, ``d_down``, ``d_weights`` [T, k] and ``d_logits`` [T, E],
-    plus the forward's dict under ``forward``."""
-    fwd = moe_layer_forward(x, w_router, bias, gate_up, down, top_k, norm_topk_prob)
+    plus the forward's dict under ``forward``.  ``ids`` as in
+    ``moe_layer_forward``."""
+    fwd = moe_layer_forward(x, w_router, bias, gate_up, down, top_k, norm_topk_prob, ids=ids)
     X = _f64(x)
     D = _f64(dout)
     T, H = X.shape

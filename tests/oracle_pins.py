@@ -700,4 +700,20 @@ def pin_backward_idle_experts_get_zero():
     assert np.abs(g["d_gate_up"][:2]).max() > 0 and np.abs(g["d_down"][:2]).max() > 0
 
 
+def pin_routing_decision_from_outside():
+    # the oracle's own ids reproduce the default path bit for bit
+    x, wr, gu, dn = _layer(16, 12, 6, 5, seed=36)
+    a = O.moe_layer_forward(x, wr, None, gu, dn, 2, True)
+    b = O.moe_layer_forward(x, wr, None, gu, dn, 2, True, ids=a["ids"])
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["weights"], b["weights"])
+    # a forced choice with k = 1 renormalised: weight 1, the chosen expert's FFN
+    forced = (np.arange(16) % 5).astype(np.int32)[:, None]
+    c = O.moe_layer_forward(x, wr, None, gu, dn, 1, True, ids=forced)
+    assert np.all(c["weights"] == 1.0)
+    for t in range(16):
+        e = int(forced[t, 0])
+        ref = O.swiglu_expert(np.asarray(x)[t:t + 1], gu[e], dn[e])
+        assert np.allclose(c["out"][t:t + 1], ref, rtol=1e-13, atol=1e-15)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,146 @@
+"""Layer backward on the GPU against the oracle's gradients, through the C
+ABI (MI355X only).
+
+The training forward runs first; its routing is checked with the forward's
+protocol (decided tokens bit-exact, the rest a valid top-k of the device's
+own float32 logits), and the oracle's backward then takes the device's
+routing decision, so every gradient is compared element by element.
+
+Gradient tolerance: max|gpu - ref| <= 1e-2 * max|ref| per tensor.  The
+device keeps the pre-activations, dG, w*h and dX in bf16 (relative rounding
+2^-9 each) and sums in float32; the oracle is float64 throughout.
+
+Every case prints its name (flushed) before touching the GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as O
+from tests import parity_util as U
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+DEV = "cuda"
+GRAD_REL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mixture_experts_layer_17_amd as m
+    return m
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _np32(t):
+    return t.float().cpu().numpy()
+
+
+def grad_close(gpu, ref, what):
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    scale = np.abs(r).max() if r.size else 0.0
+    err = np.abs(g - r).max() if r.size else 0.0
+    assert err <= GRAD_REL * scale, f"{what}: max|gpu-ref| = {err:.3e} > {GRAD_REL * scale:.3e}"
+    return err / scale if scale else 0.0
+
+
+def run_backward(moe, wl, seed=0):
+    say(f"backward {wl.name} T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.top_k} "
+        f"norm={wl.norm_topk_prob}")
+    k, norm = wl.top_k, wl.norm_topk_prob
+    x, wr, gu, dn = (t.to(DEV) for t in (wl.hidden_states, wl.router_weight, wl.gate_up, wl.down))
+    b = wl.router_bias.to(DEV) if wl.router_bias is not None else None
+    g = torch.Generator().manual_seed(100 + seed)
+    dout = torch.randn(wl.T, wl.H, generator=g).to(wl.dtype)
+    out, saved = moe.layer_forward_train(x, wr, gu, dn, k, norm, router_bias=b)
+    grads = moe.layer_backward(x, wr, gu, dn, k, norm, saved, dout.to(DEV))
+    torch.cuda.synchronize()
+    logits = saved["router_logits"].cpu().numpy()
+    ids = saved["topk_ids"].cpu().numpy()
+    xs, wrs, gus, dns = (_np32(t) for t in (wl.hidden_states, wl.router_weight, wl.gate_up,
+                                            wl.down))
+    bias = wl.router_bias.numpy() if wl.router_bias is not None else None
+    own = O.moe_layer_forward(xs, wrs, bias, gus, dns, k, norm)
+    U.assert_close(torch.as_tensor(logits), own["logits"], wl.dtype, "router logits")
+    decided, same = U.routing_check(logits, ids, own["logits"], own["ids"], k)
+    ref = O.moe_layer_backward(xs, wrs, bias, gus, dns, k, norm, _np32(dout), ids=ids)
+    f = ref["forward"]
+    # what the training forward kept
+    U.assert_close(out.cpu(), f["out"], wl.dtype, "layer output")
+    U.assert_close(saved["expert_out"].cpu(), O.unpermute(f["y"], f["slot_pos"]), wl.dtype,
+                   "saved expert outputs")
+    G = np.concatenate([xs[f["sorted_token"][f["offsets"][e]:f["offsets"][e + 1]]] @ gus[e]
+                        for e in range(wl.E)], axis=0) if wl.T else np.zeros((0, 2 * wl.I))
+    U.assert_close(saved["gate_up_out"].cpu(), G, wl.dtype, "saved pre-activations")
+    rel = {}
+    for name in ("d_topk_weights", "dx", "d_router_weight", "d_router_bias", "d_down",
+                 "d_gate_up"):
+        refn = ref["d_weights"] if name == "d_topk_weights" else ref[name]
+        rel[name] = grad_close(_np32(grads[name]), refn, name)
+    print("  routed as the oracle: %d/%d; relative errors %s" % (
+        same.sum(), wl.T, {k_: f"{v:.1e}" for k_, v in rel.items()}), flush=True)
+    return grads, ref
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=37, H=256, I=128, E=8, top_k=2),      # ragged tiles, a few rows per expert
+    dict(T=300, H=512, I=256, E=16, top_k=4),    # several K-blocks per expert in wgrad
+    dict(T=1, H=256, I=128, E=8, top_k=8),       # one token, k = E
+    dict(T=500, H=384, I=128, E=1, top_k=1),     # one expert, H not a multiple of 256
+    dict(T=200, H=256, I=128, E=64, top_k=2),    # empty experts get zero gradients
+])
+def test_backward_small(moe, shape):
+    wl = workloads.make_layer(f"bwd_{shape['T']}_{shape['E']}", norm_topk_prob=True, seed=11,
+                              **shape)
+    grads, ref = run_backward(moe, wl)
+    empty = np.flatnonzero(ref["forward"]["counts"] == 0)
+    assert not grads["d_gate_up"].cpu()[empty].any() and not grads["d_down"].cpu()[empty].any()
+
+
+def test_backward_no_renorm_with_bias(moe):
+    wl = workloads.make_layer("bwd_plain", T=160, H=256, I=128, E=16, top_k=4,
+                              norm_topk_prob=False, seed=12,
+                              router_bias=workloads.zipf_router_bias(16))
+    run_backward(moe, wl)
+
+
+def test_backward_decode(moe):
+    run_backward(moe, workloads.make("qwen3_30b_a3b_decode"))
+
+
+def test_backward_prefill(moe):
+    run_backward(moe, workloads.make("qwen3_30b_a3b_prefill"))
+
+
+def test_backward_deterministic(moe):
+    wl = workloads.make_layer("bwd_det", T=256, H=256, I=128, E=16, top_k=4, seed=13)
+    say("backward determinism")
+    x, wr, gu, dn = (t.to(DEV) for t in (wl.hidden_states, wl.router_weight, wl.gate_up, wl.down))
+    dout = torch.randn(wl.T, wl.H, generator=torch.Generator().manual_seed(5)).to(wl.dtype).to(DEV)
+    _, saved = moe.layer_forward_train(x, wr, gu, dn, 4, True)
+    a = moe.layer_backward(x, wr, gu, dn, 4, True, saved, dout)
+    b = moe.layer_backward(x, wr, gu, dn, 4, True, saved, dout)
+    torch.cuda.synchronize()
+    for name in a:
+        if a[name] is not None:
+            assert torch.equal(a[name], b[name]), name
+
+
+def test_backward_unsupported_is_reported(moe):
+    say("backward: float32 and I % 128 != 0 are refused before any launch")
+    wl = workloads.make("tiny_fp32")
+    x, wr, gu, dn = (t.to(DEV) for t in (wl.hidden_states, wl.router_weight, wl.gate_up, wl.down))
+    with pytest.raises(moe.MoEError):
+        moe.layer_forward_train(x, wr, gu, dn, wl.top_k, True)
+    wl = workloads.make_layer("bwd_i64", T=16, H=256, I=64, E=4, top_k=2)
+    x, wr, gu, dn = (t.to(DEV) for t in (wl.hidden_states, wl.router_weight, wl.gate_up, wl.down))
+    with pytest.raises(moe.MoEError):
+        moe.layer_forward_train(x, wr, gu, dn, 2, True)

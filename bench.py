@@ -16,6 +16,8 @@ Other modes:
   --router sigmoid-groups  a sigmoid, node-limited, biased router variant
   --shared-I IS          add a shared expert (FeedForward) of intermediate
                          size IS
+  --backward             time the layer backward instead (one training
+                         forward first, then moe_layer_backward per step)
 """
 from __future__ import annotations
 
@@ -52,7 +54,186 @@ def parse():
                          "expert bias")
     ap.add_argument("--shared-I", type=int, default=0,
                     help="intermediate size of a shared expert (0: none)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_layer_backward (after one moe_layer_forward_train)")
     return ap.parse_args()
+
+
+BWD_STAGES = ("routing_grads", "dgrad_down_swiglu", "dgrad_gate_up_dx", "wgrad_down",
+              "wgrad_gate_up", "router_wgrad")
+
+
+def algorithmic_backward(wl, counts):
+    """Per-stage algorithmic FLOPs and HBM bytes of one layer backward.
+    Weights and weight gradients count once per expert (every expert's
+    gradient is written); rows count once per read or write."""
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.top_k
+    es = 2
+    N = T * k
+    hit = int((counts > 0).sum())
+    f = {
+        "routing_grads": 2.0 * N * H,
+        "dgrad_down_swiglu": 2.0 * N * H * I,
+        "dgrad_gate_up_dx": 2.0 * N * 2 * I * H,
+        "wgrad_down": 2.0 * N * I * H,
+        "wgrad_gate_up": 2.0 * N * H * 2 * I,
+        "router_wgrad": 2.0 * N * H if wl.norm_topk_prob else 2.0 * T * E * H,
+    }
+    b = {
+        "routing_grads": N * H * es + T * H * es + T * E * 4 + 3 * N * 4,
+        "dgrad_down_swiglu": hit * I * H * es + T * H * es + 2 * N * 2 * I * es + N * I * es,
+        "dgrad_gate_up_dx": hit * H * 2 * I * es + N * 2 * I * es + 2 * N * H * es + T * H * es,
+        "wgrad_down": N * I * es + T * H * es + E * I * H * es,
+        "wgrad_gate_up": N * 2 * I * es + T * H * es + E * H * 2 * I * es,
+        "router_wgrad": T * H * es + T * E * 4 + E * H * 4,
+    }
+    return f, b
+
+
+def cpu_baseline_backward(wl, dout, budget_s=12.0):
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    args = [t.float().numpy() for t in (wl.hidden_states, wl.router_weight, wl.gate_up, wl.down)]
+    bias = wl.router_bias.numpy() if wl.router_bias is not None else None
+    d = dout.float().numpy()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        O.moe_layer_backward(args[0], args[1], bias, args[2], args[3], wl.top_k,
+                             wl.norm_topk_prob, d)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 3:
+            break
+    return {"value": wl.T * wl.top_k * runs / el, "unit": "routed tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole {wl.name} workload ({wl.T} tokens), forward recomputed inside, "
+                      f"{runs} run(s), {el:.1f} s, float64 NumPy"}
+
+
+def bench_backward(args, wl):
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_17_amd as moe
+    from mixture_experts_layer_17_amd import _lib
+    dev = torch.device("cuda:0")
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.top_k
+    N = T * k
+    norm = wl.norm_topk_prob
+    x, wr, gu, dn = (t.to(dev).contiguous() for t in (wl.hidden_states, wl.router_weight,
+                                                       wl.gate_up, wl.down))
+    bias = wl.router_bias.to(dev) if wl.router_bias is not None else None
+    dout_cpu = torch.randn(T, H, generator=torch.Generator().manual_seed(100)).to(wl.dtype)
+    dout = dout_cpu.to(dev)
+    _, saved = moe.layer_forward_train(x, wr, gu, dn, k, norm, router_bias=bias)
+    g = dict(dx=torch.empty(T, H, dtype=wl.dtype, device=dev),
+             dwr=torch.empty(E, H, dtype=torch.float32, device=dev),
+             db=torch.empty(E, dtype=torch.float32, device=dev),
+             dgu=torch.empty(E, H, 2 * I, dtype=wl.dtype, device=dev),
+             ddn=torch.empty(E, I, H, dtype=wl.dtype, device=dev),
+             dw=torch.empty(T, k, dtype=torch.float32, device=dev))
+    L = moe.lib
+    nws = L.moe_workspace_size(_lib.MOE_OP_LAYER_BACKWARD, T, H, I, E, k, 0, N, _lib.MOE_BF16)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev)
+    P = lambda t: t.data_ptr()  # noqa: E731
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    nst = len(BWD_STAGES) + 1
+
+    def new_event():
+        ev = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def step(evs=None):
+        st = L.moe_layer_backward(P(x), P(wr), P(gu), P(dn), T, H, I, E, k, int(norm),
+                                  _lib.MOE_BF16, P(saved["router_logits"]), P(saved["topk_ids"]),
+                                  P(saved["topk_weights"]), P(saved["gate_up_out"]),
+                                  P(saved["expert_out"]), P(dout), P(g["dx"]), P(g["dwr"]),
+                                  P(g["db"]), P(g["dgu"]), P(g["ddn"]), P(g["dw"]), P(ws), nws,
+                                  evs, s.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"moe_layer_backward failed with status {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev_arrays = [(ctypes.c_void_p * nst)(*[new_event() for _ in range(nst)])
+                 for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(s)
+    for i in range(args.steps):
+        step(ev_arrays[i])
+    end.record(s)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / args.steps
+    f = ctypes.c_float()
+    per = {}
+    for j, name in enumerate(BWD_STAGES):
+        acc = []
+        for arr in ev_arrays:
+            if hip.hipEventElapsedTime(ctypes.byref(f), arr[j], arr[j + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            acc.append(f.value)
+        per[name] = float(np.mean(acc))
+    for arr in ev_arrays:
+        for j in range(nst):
+            hip.hipEventDestroy(arr[j])
+    flops, bytes_ = algorithmic_backward(wl, saved["num_tokens_per_expert"].cpu().numpy())
+    kern = {}
+    for name in BWD_STAGES:
+        t_s = per[name] * 1e-3
+        kern[name] = {"avg_us": round(per[name] * 1e3, 2),
+                      "tflops": round(flops[name] / t_s / 1e12, 2),
+                      "gbps": round(bytes_[name] / t_s / 1e9, 1),
+                      "mfma_frac": round(flops[name] / t_s / PEAK_BF16_FLOPS, 4),
+                      "hbm_frac": round(bytes_[name] / t_s / PEAK_HBM, 4)}
+    dom = max(BWD_STAGES, key=lambda n_: per[n_])
+    t_dom = per[dom] * 1e-3
+    if bytes_[dom] / PEAK_HBM >= flops[dom] / PEAK_BF16_FLOPS:
+        roof = {"bound": "hbm", "achieved": round(bytes_[dom] / t_dom / 1e9, 1),
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops[dom] / t_dom / 1e12, 2),
+                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = int(bytes_[dom])
+    roof["algorithmic_flops"] = int(flops[dom])
+    total_f = sum(flops.values())
+    result = {
+        "metric": "routed tokens/s per MoE layer backward (bf16)",
+        "value": round(N / (ms_per_step * 1e-3), 1),
+        "unit": "routed tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded Gaussian inputs, output gradient and random-init weights",
+        "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "top_k": k,
+                   "norm_topk_prob": norm, "routed_rows": N, "pass": "backward"},
+        "layer_tflops": round(total_f / (ms_per_step * 1e-3) / 1e12, 2),
+        "layer_mfma_frac": round(total_f / (ms_per_step * 1e-3) / PEAK_BF16_FLOPS, 4),
+        "roofline": roof,
+        "kernels": kern,
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_backward(wl, dout_cpu)
+    print(json.dumps(result), flush=True)
 
 
 def algorithmic(wl, counts, Is=0, fused=False):
@@ -185,6 +366,9 @@ def main():
         print("bench.py times token-choice layers; the EP-rank workload is a parity case",
               file=sys.stderr)
         sys.exit(2)
+    if args.backward:
+        bench_backward(args, wl)
+        return
     dev = torch.device("cuda:0")
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.top_k
     N = T * k

@@ -407,6 +407,11 @@ int moe_layer_forward_train(const void* hidden_states, const void* router_weight
  * Every sum is float32 in a fixed order: deterministic.  Weight gradients
  * overwrite their buffers (no accumulation).  Workspace:
  * moe_workspace_size(MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, 0, T*top_k, dt).
+ * stage_events: NULL, or 7 caller-created events recorded before the
+ * permutation, before the first dgrad GEMM (after d_topk_weights and dL),
+ * before the second dgrad GEMM, before the first wgrad GEMM (after dx),
+ * before the second wgrad GEMM, before the router's weight gradient, and at
+ * the end (NULL entries are skipped).
  */
 int moe_layer_backward(const void* hidden_states, const void* router_weight,
                        const void* gate_up, const void* down, int T, int H, int I, int E,
@@ -416,7 +421,7 @@ int moe_layer_backward(const void* hidden_states, const void* router_weight,
                        const void* saved_expert_out, const void* dout, void* dx,
                        float* d_router_weight, float* d_router_bias, void* d_gate_up,
                        void* d_down, float* d_topk_weights, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+                       size_t workspace_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
 #ifdef __cplusplus
 }

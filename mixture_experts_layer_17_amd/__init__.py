@@ -396,5 +396,5 @@ def layer_backward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.
           saved["expert_out"].data_ptr(), dout.data_ptr(), g["dx"].data_ptr(),
           g["d_router_weight"].data_ptr(), _chk(g["d_router_bias"], "d_router_bias"),
           g["d_gate_up"].data_ptr(), g["d_down"].data_ptr(), g["d_topk_weights"].data_ptr(),
-          ws.data_ptr(), nb, _stream(dev))
+          ws.data_ptr(), nb, None, _stream(dev))
     return g

@@ -159,7 +159,7 @@ struct BwdWs {
   int32_t *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
   void *perm, *tiles;
   float *dw, *dL;
-  void *dG, *hw, *dX, *zero;
+  void *dG, *hw, *dX, *x_perm, *dout_perm, *zero;
   size_t zero_bytes, total;
 };
 
@@ -184,6 +184,8 @@ BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
   w.dG = take(N * 2 * (size_t)I * esize(dt));
   w.hw = take(N * (size_t)I * esize(dt));
   w.dX = take(N * (size_t)H * esize(dt));
+  w.x_perm = take(N * (size_t)H * esize(dt));
+  w.dout_perm = take(N * (size_t)H * esize(dt));
   w.zero_bytes = al((size_t)std::max(H, 2 * I) * esize(dt));
   w.zero = take(w.zero_bytes);
   w.total = off;
@@ -521,7 +523,8 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
                        const float* logits, const int32_t* ids, const float* weights,
                        const void* saved_gate_up, const void* saved_expert_out, const void* dout,
                        void* dx, float* d_router_weight, float* d_router_bias, void* d_gate_up,
-                       void* d_down, float* d_weights, void* ws, size_t ws_bytes, hipStream_t s) {
+                       void* d_down, float* d_weights, void* ws, size_t ws_bytes,
+                       hipEvent_t* stage_events, hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
     return MOE_ERR_SHAPE;
@@ -541,6 +544,10 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   const int N = T * k;
   float* dw = d_weights ? d_weights : w.dw;
   const int id = pick_dgrad_cfg(N, E);
+  auto mark = [&](int i) {
+    if (stage_events && stage_events[i]) (void)hipEventRecord(stage_events[i], s);
+  };
+  mark(0);
   hipError_t e = launch_permute_topk(ids, T, k, E, w.counts, w.offsets, w.sorted_token,
                                      w.sorted_slot, w.slot_pos, w.perm, s, w.tiles, dgrad_bm(id));
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -556,23 +563,31 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   // d_weights = <dout, y>, then the softmax / router gradient
   if (e == hipSuccess) e = launch_weight_grad(bf16, dout, saved_expert_out, N, k, H, dw, s);
   if (e == hipSuccess) e = launch_router_grad(logits, ids, weights, dw, T, E, k, norm, w.dL, s);
+  mark(1);
   // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot order
   if (e == hipSuccess)
     e = launch_dgrad_down_swiglu(id, dout, T, w.sorted_token, down, N, H, I, E, saved_gate_up,
                                  weights, w.sorted_slot, w.dG, w.hw, w.tiles, s);
+  mark(2);
   if (e == hipSuccess)
     e = launch_dgrad_gate_up(id, w.dG, gate_up, N, H, I, E, w.sorted_slot, w.dX, w.tiles, s);
-  if (e == hipSuccess) e = launch_input_grad(bf16, w.dX, w.dL, wr, T, k, E, H, dx, s);
-  // wgrad: d down[e] = (w h)_e^T dout_e, d gate_up[e] = X_e^T dG_e
   if (e == hipSuccess)
-    e = launch_wgrad(w.hw, I, nullptr, dout, H, w.sorted_token, w.zero, w.offsets, E, I, H,
-                     d_down, s);
+    e = launch_input_grad(bf16, w.dX, w.dL, norm ? ids : nullptr, wr, T, k, E, H, dx, s);
+  mark(3);
+  // wgrad: d down[e] = (w h)_e^T dout_e, d gate_up[e] = X_e^T dG_e, with
+  // the gathered rows laid out expert-major first
+  if (e == hipSuccess) e = launch_gather_rows(bf16, dout, T, w.sorted_token, N, H, w.dout_perm, s);
+  if (e == hipSuccess) e = launch_gather_rows(bf16, x, T, w.sorted_token, N, H, w.x_perm, s);
   if (e == hipSuccess)
-    e = launch_wgrad(x, H, w.sorted_token, w.dG, 2 * I, nullptr, w.zero, w.offsets, E, H, 2 * I,
-                     d_gate_up, s);
+    e = launch_wgrad(w.hw, I, w.dout_perm, H, w.zero, w.offsets, E, I, H, d_down, s);
+  mark(4);
   if (e == hipSuccess)
-    e = launch_router_weight_grad(bf16, x, w.dL, w.offsets, w.sorted_token, T, E, H, norm,
-                                  d_router_weight, d_router_bias, s);
+    e = launch_wgrad(w.x_perm, H, w.dG, 2 * I, w.zero, w.offsets, E, H, 2 * I, d_gate_up, s);
+  mark(5);
+  if (e == hipSuccess)
+    e = launch_router_weight_grad(bf16, x, w.x_perm, w.dL, w.offsets, w.sorted_token, T, E, H,
+                                  norm, d_router_weight, d_router_bias, s);
+  mark(6);
   return hip_status(e);
 }
 

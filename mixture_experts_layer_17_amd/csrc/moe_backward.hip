@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void router_grad_kernel(const float* __restric
 template <typename T>
 __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ dX,
                                                          const float* __restrict__ dL,
+                                                         const int32_t* __restrict__ ids,
                                                          const T* __restrict__ wr, int T_, int k,
                                                          int E, int H, T* __restrict__ dx) {
   const int per_row = H / 8;
@@ -150,13 +151,24 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
       for (int x = 0; x < 8; ++x) acc[x] += v[x];
     }
     const float* l = dL + (size_t)t * E;
-    for (int e = 0; e < E; ++e) {
-      const float g = l[e];
-      if (g == 0.f) continue;
-      float v[8];
-      load8(wr + (size_t)e * H + c, v);
+    if (ids) {
+      // dL is zero off the token's selection: its k router rows, slot order
+      for (int j = 0; j < k; ++j) {
+        const int e = min(max(ids[(size_t)t * k + j], 0), E - 1);
+        const float g = l[e];
+        float v[8];
+        load8(wr + (size_t)e * H + c, v);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
+      }
+    } else {
+      for (int e = 0; e < E; ++e) {
+        const float g = l[e];
+        float v[8];
+        load8(wr + (size_t)e * H + c, v);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
+      }
     }
     store8(dx + (size_t)t * H + c, acc);
   }
@@ -164,13 +176,14 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
 
 // dWr[e, :] = sum_t dL[t, e] x[t, :] and d_bias[e] = sum_t dL[t, e].  With
 // renormalised weights dL[t, e] is nonzero only where token t chose e, so
-// the sum runs over the expert's rows of the permutation (ascending token);
-// otherwise over every token.  One thread per (expert, 8 columns).
+// the sum runs over the expert's rows of the permutation (ascending token),
+// read from the expert-major copy x_perm; otherwise over every token.  One
+// thread per (expert, 8 columns).
 template <typename T>
 __global__ __launch_bounds__(256) void router_weight_grad_kernel(
-    const T* __restrict__ x, const float* __restrict__ dL, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_token, int T_, int E, int H, int sparse,
-    float* __restrict__ dwr, float* __restrict__ dbias) {
+    const T* __restrict__ x, const T* __restrict__ x_perm, const float* __restrict__ dL,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token, int T_, int E,
+    int H, int sparse, float* __restrict__ dwr, float* __restrict__ dbias) {
   const int per_row = H / 8;
   const long long total = (long long)E * per_row;
   for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total;
@@ -181,14 +194,23 @@ __global__ __launch_bounds__(256) void router_weight_grad_kernel(
     float bsum = 0.f;
     const int lo = sparse ? offsets[e] : 0;
     const int hi = sparse ? offsets[e + 1] : T_;
-    for (int p = lo; p < hi; ++p) {
-      const int t = sparse ? sorted_token[p] : p;
-      const float g = dL[(size_t)t * E + e];
-      bsum += g;
-      float v[8];
-      load8(x + (size_t)t * H + c, v);
+    // eight rows' loads in flight at a time; the sums stay in row order
+    constexpr int U = 8;
+    for (int p0 = lo; p0 < hi; p0 += U) {
+      float g[U], v[U][8];
 #pragma unroll
-      for (int xx = 0; xx < 8; ++xx) acc[xx] = fmaf(g, v[xx], acc[xx]);
+      for (int u = 0; u < U; ++u) {
+        const int p = min(p0 + u, hi - 1);
+        const int t = sparse ? sorted_token[p] : p;
+        g[u] = p0 + u < hi ? dL[(size_t)t * E + e] : 0.f;
+        load8((sparse ? x_perm + (size_t)p * H : x + (size_t)t * H) + c, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        bsum += g[u];
+#pragma unroll
+        for (int xx = 0; xx < 8; ++xx) acc[xx] = fmaf(g[u], v[u][xx], acc[xx]);
+      }
     }
     reinterpret_cast<float4*>(dwr + (size_t)e * H + c)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     reinterpret_cast<float4*>(dwr + (size_t)e * H + c)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
@@ -229,30 +251,32 @@ hipError_t launch_router_grad(const float* logits, const int32_t* ids, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const void* wr, int T,
-                             int k, int E, int H, void* dx, hipStream_t s) {
+hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const int32_t* ids,
+                             const void* wr, int T, int k, int E, int H, void* dx, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int grid = grid_for_total((long long)T * (H / 8));
   if (bf16)
-    input_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)dX, dL, (const bf16_t*)wr, T,
-                                                   k, E, H, (bf16_t*)dx);
+    input_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)dX, dL, ids, (const bf16_t*)wr,
+                                                   T, k, E, H, (bf16_t*)dx);
   else
-    input_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)dX, dL, (const float*)wr, T, k,
-                                                  E, H, (float*)dx);
+    input_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)dX, dL, ids, (const float*)wr, T,
+                                                  k, E, H, (float*)dx);
   return hipGetLastError();
 }
 
-hipError_t launch_router_weight_grad(bool bf16, const void* x, const float* dL,
+hipError_t launch_router_weight_grad(bool bf16, const void* x, const void* x_perm, const float* dL,
                                      const int32_t* offsets, const int32_t* sorted_token, int T,
                                      int E, int H, int sparse, float* dwr, float* dbias,
                                      hipStream_t s) {
   const int grid = grid_for_total((long long)E * (H / 8));
   if (bf16)
-    router_weight_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, dL, offsets,
+    router_weight_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, (const bf16_t*)x_perm,
+                                                           dL, offsets,
                                                            sorted_token, T, E, H, sparse, dwr,
                                                            dbias);
   else
-    router_weight_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)x, dL, offsets,
+    router_weight_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)x, (const float*)x_perm,
+                                                          dL, offsets,
                                                           sorted_token, T, E, H, sparse, dwr,
                                                           dbias);
   return hipGetLastError();

@@ -18,12 +18,11 @@
 // wgrad: K runs over the expert's rows, so both operands arrive as k-rows
 // with their output dimension contiguous, the layout of the forward's weight
 // tile: 32-byte segments XOR-swizzled per row and read with the transposing
-// ds_read_b64_tr_b16.  Gathered rows (x or dout through sorted_token) are
-// addressed through indices fetched with uniform (scalar) loads, so they do
-// not enter the vector-memory counter that orders the asynchronous copies.
-// Rows past the expert's end read a zero row.  Every output element is
-// reduced by one work-group over all of K: deterministic, no atomics; experts
-// without rows get exact zeros.
+// ds_read_b64_tr_b16.  Both operands are expert-major buffers (the gathered
+// x and dout rows are laid out once, before), so a copy's source is plain
+// address arithmetic.  Rows past the expert's end read a zero row.  Every
+// output element is reduced by one work-group over all of K: deterministic,
+// no atomics; experts without rows get exact zeros.
 #include <type_traits>
 
 #include "moe_common.h"
@@ -307,8 +306,7 @@ struct wcfg {
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
-    const bf16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index,
-    const bf16_t* __restrict__ B, int ldb, const int32_t* __restrict__ b_index,
+    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
     const bf16_t* __restrict__ zero_row, const int32_t* __restrict__ offsets, int E, int M,
     int N, bf16_t* __restrict__ C, long long c_estride, int ldc) {
   using G = wcfg<BM, BN, WM, WN, STAGES>;
@@ -358,28 +356,14 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
     c_col[u] = 16 * seg + 8 * (p & 1) + (isa ? m0 : n0);
     c_lds[u] = (isa ? 0 : G::A_BYTES) + local_inst * 1024;
   }
-  // source of copy u for K-block kb.  The row's index is a uniform value:
-  // the k-rows of one copy are consecutive, and each lane picks its own.
+  // source of copy u for K-block kb: expert-major row lo + 32 kb + r, or
+  // the zero row past the expert's end
   auto issue = [&](unsigned char* base, int kb) {
 #pragma unroll
     for (int u = 0; u < G::PER; ++u) {
-      const int inst = wave + u * G::NW;
-      const bool isa = c_isa[u];
-      const int rows_per = 1024 / (isa ? G::A_ROWB : G::B_ROWB);
-      const int first = (isa ? inst : inst - G::A_INST) * rows_per;   // uniform
-      const int32_t* idx = isa ? a_index : b_index;
-      int srow = -1;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t < rows_per) {
-          const int rg = lo + kb * BK + first + t;                   // uniform
-          int s = -1;
-          if (rg < hi) s = idx ? idx[rg] : rg;
-          if (c_row[u] == first + t) srow = s;
-        }
-      }
-      const bf16_t* g = srow >= 0 ? (isa ? A + (long long)srow * lda : B + (long long)srow * ldb)
-                                  : zr;
+      const int rg = lo + kb * BK + c_row[u];
+      const bf16_t* g = rg < hi ? (c_isa[u] ? A + (long long)rg * lda : B + (long long)rg * ldb)
+                                : zr;
       copy16_to_lds(g + c_col[u], base + c_lds[u]);
     }
   };
@@ -516,18 +500,23 @@ hipError_t launch_dgrad_cfg(int id, const void* X, int ldx, const int32_t* x_ind
     MOE_DG(0, 128, 128, 2, 2, 4)
     MOE_DG(1, 64, 128, 2, 2, 4)
     MOE_DG(2, 32, 128, 1, 2, 4)
+    MOE_DG(3, 256, 256, 2, 4, 4)
+    MOE_DG(4, 256, 128, 2, 2, 4)
     default: return hipErrorInvalidValue;
   }
 #undef MOE_DG
 }
 
-constexpr int kDgradBM[] = {128, 64, 32};
+// Row-tile classes (the tile list's height) and, within the 256-row class,
+// the 256-column config when the output width allows it.
+constexpr int kDgradBM[] = {128, 64, 32, 256};
+
+int dgrad_id(int cls, int n_cols) { return cls == 3 ? (n_cols % 256 == 0 ? 3 : 4) : cls; }
 
 template <int BM, int BN, int WM, int WN, int STAGES>
-hipError_t launch_wgrad_t(const void* A, int lda, const int32_t* a_index, const void* B, int ldb,
-                          const int32_t* b_index, const void* zero_row, const int32_t* offsets,
-                          int E, int M, int N, void* C, long long c_estride, int ldc,
-                          hipStream_t s) {
+hipError_t launch_wgrad_t(const void* A, int lda, const void* B, int ldb, const void* zero_row,
+                          const int32_t* offsets, int E, int M, int N, void* C,
+                          long long c_estride, int ldc, hipStream_t s) {
   using G = wcfg<BM, BN, WM, WN, STAGES>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)wgrad_kernel<BM, BN, WM, WN, STAGES>,
@@ -536,8 +525,8 @@ hipError_t launch_wgrad_t(const void* A, int lda, const int32_t* a_index, const 
   const long long jobs = (long long)E * (M / BM) * (N / BN);
   const int grid = (int)std::max<long long>((jobs + NUM_XCD - 1) / NUM_XCD * NUM_XCD, NUM_XCD);
   hipLaunchKernelGGL((wgrad_kernel<BM, BN, WM, WN, STAGES>), dim3(grid), dim3(G::THREADS), G::LDS,
-                     s, (const bf16_t*)A, lda, a_index, (const bf16_t*)B, ldb, b_index,
-                     (const bf16_t*)zero_row, offsets, E, M, N, (bf16_t*)C, c_estride, ldc);
+                     s, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, (const bf16_t*)zero_row,
+                     offsets, E, M, N, (bf16_t*)C, c_estride, ldc);
   return hipGetLastError();
 }
 
@@ -545,7 +534,7 @@ hipError_t launch_wgrad_t(const void* A, int lda, const int32_t* a_index, const 
 
 int pick_dgrad_cfg(int N, int E) {
   const double mean_rows = E > 0 ? (double)N / E : 0.0;
-  return mean_rows >= 96.0 ? 0 : mean_rows >= 40.0 ? 1 : 2;
+  return mean_rows >= 160.0 ? 3 : mean_rows >= 96.0 ? 0 : mean_rows >= 40.0 ? 1 : 2;
 }
 
 int dgrad_bm(int id) { return kDgradBM[id]; }
@@ -556,8 +545,10 @@ hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32
                                     void* dG, void* hw, const void* tile_ws, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   const SwigluBwd sb{(const bf16_t*)G, 2 * I, I, w, sorted_slot, (bf16_t*)dG, (bf16_t*)hw, I};
-  return launch_dgrad_cfg<DG_SWIGLU_BWD>(id, dout, H, sorted_token, T, down, (long long)I * H, H,
-                                         H, nullptr, 0, nullptr, 0, tile_ws, N, E, I / 128, sb, s);
+  const int cfg = dgrad_id(id, I);
+  const int bn = cfg == 3 ? 256 : 128;
+  return launch_dgrad_cfg<DG_SWIGLU_BWD>(cfg, dout, H, sorted_token, T, down, (long long)I * H, H,
+                                         H, nullptr, 0, nullptr, 0, tile_ws, N, E, I / bn, sb, s);
 }
 
 hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int N, int H, int I,
@@ -565,19 +556,23 @@ hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int
                                 hipStream_t s) {
   if (N <= 0) return hipSuccess;
   const SwigluBwd none{};
-  return launch_dgrad_cfg<DG_PLAIN>(id, dG, 2 * I, nullptr, N, gate_up, (long long)H * 2 * I,
-                                    2 * I, 2 * I, dX, H, out_index, N, tile_ws, N, E, H / 128,
+  const int cfg = dgrad_id(id, H);
+  const int bn = cfg == 3 ? 256 : 128;
+  return launch_dgrad_cfg<DG_PLAIN>(cfg, dG, 2 * I, nullptr, N, gate_up, (long long)H * 2 * I,
+                                    2 * I, 2 * I, dX, H, out_index, N, tile_ws, N, E, H / bn,
                                     none, s);
 }
 
-hipError_t launch_wgrad(const void* A, int lda, const int32_t* a_index, const void* B, int ldb,
-                        const int32_t* b_index, const void* zero_row, const int32_t* offsets,
-                        int E, int M, int N, void* C, hipStream_t s) {
+hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const void* zero_row,
+                        const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s) {
+  if (M % 256 == 0 && N % 256 == 0)
+    return launch_wgrad_t<256, 256, 2, 4, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
+                                             (long long)M * N, N, s);
   if (N % 256 == 0)
-    return launch_wgrad_t<128, 256, 2, 2, 3>(A, lda, a_index, B, ldb, b_index, zero_row, offsets,
-                                             E, M, N, C, (long long)M * N, N, s);
-  return launch_wgrad_t<128, 128, 2, 2, 4>(A, lda, a_index, B, ldb, b_index, zero_row, offsets, E,
-                                           M, N, C, (long long)M * N, N, s);
+    return launch_wgrad_t<128, 256, 2, 2, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
+                                             (long long)M * N, N, s);
+  return launch_wgrad_t<128, 128, 2, 2, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
+                                           (long long)M * N, N, s);
 }
 
 }  // namespace moe

@@ -119,17 +119,20 @@ hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32
 hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int N, int H, int I,
                                 int E, const int32_t* out_index, void* dX, const void* tile_ws,
                                 hipStream_t s);
-hipError_t launch_wgrad(const void* A, int lda, const int32_t* a_index, const void* B, int ldb,
-                        const int32_t* b_index, const void* zero_row, const int32_t* offsets,
-                        int E, int M, int N, void* C, hipStream_t s);
+// C[e] = A_e^T B_e over the expert-major rows [offsets[e], offsets[e + 1]).
+hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const void* zero_row,
+                        const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s);
 hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N, int k, int H,
                               float* dw, hipStream_t s);
 hipError_t launch_router_grad(const float* logits, const int32_t* ids, const float* w,
                               const float* dw, int T, int E, int k, int norm, float* dL,
                               hipStream_t s);
-hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const void* wr, int T,
-                             int k, int E, int H, void* dx, hipStream_t s);
-hipError_t launch_router_weight_grad(bool bf16, const void* x, const float* dL,
+// With ids (renormalised weights: dL is zero off the selection) only the
+// selected experts' router rows are read; ids == NULL reads all E.
+hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const int32_t* ids,
+                             const void* wr, int T, int k, int E, int H, void* dx, hipStream_t s);
+// x_perm: x in expert-major order (read when sparse).
+hipError_t launch_router_weight_grad(bool bf16, const void* x, const void* x_perm, const float* dL,
                                      const int32_t* offsets, const int32_t* sorted_token, int T,
                                      int E, int H, int sparse, float* dwr, float* dbias,
                                      hipStream_t s);

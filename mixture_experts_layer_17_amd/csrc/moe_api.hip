@@ -158,8 +158,8 @@ int router_variant(const moe_router_config* c, int E, int k, RouterVariant* out,
 struct BwdWs {
   int32_t *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
   void *perm, *tiles;
-  float *dw, *dL;
-  void *dG, *hw, *dX, *x_perm, *dout_perm, *zero;
+  float *dw, *dL, *dl_perm;
+  void *dG, *hw, *dX, *x_perm, *dout_perm, *zero, *rw_part;
   size_t zero_bytes, total;
 };
 
@@ -181,6 +181,8 @@ BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
   w.tiles = take(tile_list_bytes((int)N, E, dgrad_bm(pick_dgrad_cfg((int)N, E))));
   w.dw = (float*)take(N * 4);
   w.dL = (float*)take((size_t)T * E * 4);
+  w.dl_perm = (float*)take(N * 4);
+  w.rw_part = take(router_weight_grad_ws(E, H));
   w.dG = take(N * 2 * (size_t)I * esize(dt));
   w.hw = take(N * (size_t)I * esize(dt));
   w.dX = take(N * (size_t)H * esize(dt));
@@ -562,7 +564,9 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   e = launch_fill_u32(w.zero, (long long)(w.zero_bytes / 4), 0u, s);
   // d_weights = <dout, y>, then the softmax / router gradient
   if (e == hipSuccess) e = launch_weight_grad(bf16, dout, saved_expert_out, N, k, H, dw, s);
-  if (e == hipSuccess) e = launch_router_grad(logits, ids, weights, dw, T, E, k, norm, w.dL, s);
+  if (e == hipSuccess)
+    e = launch_router_grad(logits, ids, weights, dw, w.slot_pos, T, E, k, norm, w.dL, w.dl_perm,
+                           s);
   mark(1);
   // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot order
   if (e == hipSuccess)
@@ -585,8 +589,8 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
     e = launch_wgrad(w.x_perm, H, w.dG, 2 * I, w.zero, w.offsets, E, H, 2 * I, d_gate_up, s);
   mark(5);
   if (e == hipSuccess)
-    e = launch_router_weight_grad(bf16, x, w.x_perm, w.dL, w.offsets, w.sorted_token, T, E, H,
-                                  norm, d_router_weight, d_router_bias, s);
+    e = launch_router_weight_grad(bf16, x, w.x_perm, w.dL, w.dl_perm, w.offsets, T, E, H, norm,
+                                  d_router_weight, d_router_bias, w.rw_part, s);
   mark(6);
   return hip_status(e);
 }

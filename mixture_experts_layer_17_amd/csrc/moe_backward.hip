@@ -89,12 +89,16 @@ __global__ __launch_bounds__(256) void weight_grad_kernel(const T* __restrict__ 
 }
 
 // dL[t, :] from the routing-weight gradient: one wave per token.
+// With renormalised weights it also writes the selected entries in the
+// permutation's expert-major order: dl_perm[slot_pos[t k + j]] = dL[t, ids].
 __global__ __launch_bounds__(256) void router_grad_kernel(const float* __restrict__ logits,
                                                           const int32_t* __restrict__ ids,
                                                           const float* __restrict__ w,
-                                                          const float* __restrict__ dw, int T,
-                                                          int E, int k, int norm,
-                                                          float* __restrict__ dL) {
+                                                          const float* __restrict__ dw,
+                                                          const int32_t* __restrict__ slot_pos,
+                                                          int T, int E, int k, int norm,
+                                                          float* __restrict__ dL,
+                                                          float* __restrict__ dl_perm) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
@@ -108,8 +112,10 @@ __global__ __launch_bounds__(256) void router_grad_kernel(const float* __restric
     for (int e = lane; e < E; e += 64) {
       float g = 0.f;
       for (int j = 0; j < k; ++j)
-        if (ids[(size_t)t * k + j] == e)
+        if (ids[(size_t)t * k + j] == e) {
           g = w[(size_t)t * k + j] * (dw[(size_t)t * k + j] - inner);
+          dl_perm[slot_pos[(size_t)t * k + j]] = g;
+        }
       out[e] = g;
     }
     return;
@@ -174,48 +180,65 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
   }
 }
 
-// dWr[e, :] = sum_t dL[t, e] x[t, :] and d_bias[e] = sum_t dL[t, e].  With
+// dWr[e, :] = sum_t dL[t, e] x[t, :] and d_bias[e] = sum_t dL[t, e], in two
+// passes: `splits` work-groups per expert each sum one contiguous share of
+// its rows into a partial, then the partials are added in order.  With
 // renormalised weights dL[t, e] is nonzero only where token t chose e, so
-// the sum runs over the expert's rows of the permutation (ascending token),
-// read from the expert-major copy x_perm; otherwise over every token.  One
-// thread per (expert, 8 columns).
+// the rows are the expert's rows of the permutation (x_perm, dl_perm, both
+// expert-major); otherwise every token's x row with dL[t, e].
 template <typename T>
-__global__ __launch_bounds__(256) void router_weight_grad_kernel(
-    const T* __restrict__ x, const T* __restrict__ x_perm, const float* __restrict__ dL,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token, int T_, int E,
-    int H, int sparse, float* __restrict__ dwr, float* __restrict__ dbias) {
-  const int per_row = H / 8;
-  const long long total = (long long)E * per_row;
-  for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total;
-       q += (long long)gridDim.x * 256) {
-    const int e = (int)(q / per_row);
-    const int c = 8 * (int)(q - (long long)e * per_row);
+__global__ __launch_bounds__(256) void router_weight_grad_part_kernel(
+    const T* __restrict__ rows_x, const float* __restrict__ g, const int32_t* __restrict__ offsets,
+    int T_, int E, int H, int sparse, int splits, float* __restrict__ part,
+    float* __restrict__ part_b) {
+  const int e = blockIdx.x / splits, r = blockIdx.x - (blockIdx.x / splits) * splits;
+  const int lo0 = sparse ? offsets[e] : 0;
+  const int hi0 = sparse ? max(offsets[e + 1], lo0) : T_;
+  const int chunk = (hi0 - lo0 + splits - 1) / splits;
+  const int lo = lo0 + r * chunk;
+  const int hi = min(hi0, lo + chunk);
+  for (int c = 8 * threadIdx.x; c < H; c += 8 * 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float bsum = 0.f;
-    const int lo = sparse ? offsets[e] : 0;
-    const int hi = sparse ? offsets[e + 1] : T_;
-    // eight rows' loads in flight at a time; the sums stay in row order
-    constexpr int U = 8;
+    constexpr int U = 8;   // rows in flight; sums stay in row order
     for (int p0 = lo; p0 < hi; p0 += U) {
-      float g[U], v[U][8];
+      float gv[U], v[U][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int p = min(p0 + u, hi - 1);
-        const int t = sparse ? sorted_token[p] : p;
-        g[u] = p0 + u < hi ? dL[(size_t)t * E + e] : 0.f;
-        load8((sparse ? x_perm + (size_t)p * H : x + (size_t)t * H) + c, v[u]);
+        gv[u] = p0 + u < hi ? (sparse ? g[p] : g[(size_t)p * E + e]) : 0.f;
+        load8(rows_x + (size_t)p * H + c, v[u]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        bsum += g[u];
+        bsum += gv[u];
 #pragma unroll
-        for (int xx = 0; xx < 8; ++xx) acc[xx] = fmaf(g[u], v[u][xx], acc[xx]);
+        for (int xx = 0; xx < 8; ++xx) acc[xx] = fmaf(gv[u], v[u][xx], acc[xx]);
       }
     }
-    reinterpret_cast<float4*>(dwr + (size_t)e * H + c)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    reinterpret_cast<float4*>(dwr + (size_t)e * H + c)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    if (dbias && c == 0) dbias[e] = bsum;
+    float* o = part + ((size_t)r * E + e) * H + c;
+    reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (c == 0) part_b[(size_t)r * E + e] = bsum;
   }
+}
+
+__global__ __launch_bounds__(256) void router_weight_grad_sum_kernel(
+    const float* __restrict__ part, const float* __restrict__ part_b, int E, int H, int splits,
+    float* __restrict__ dwr, float* __restrict__ dbias) {
+  const long long total = (long long)E * H;
+  for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (long long)gridDim.x * 256) {
+    float a = 0.f;
+    for (int r = 0; r < splits; ++r) a += part[(size_t)r * total + q];
+    dwr[q] = a;
+  }
+  if (dbias && blockIdx.x == 0)
+    for (int e = threadIdx.x; e < E; e += 256) {
+      float b = 0.f;
+      for (int r = 0; r < splits; ++r) b += part_b[(size_t)r * E + e];
+      dbias[e] = b;
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, long long n, uint32_t v) {
@@ -223,6 +246,8 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, long long n,
        i += (long long)gridDim.x * 256)
     p[i] = v;
 }
+
+constexpr int kRouterSplits = 8;   // row shares per expert in the router's weight gradient
 
 int grid_for_total(long long total) {
   return (int)std::max<long long>(1, std::min<long long>((total + 255) / 256, 16384));
@@ -244,10 +269,11 @@ hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N,
 }
 
 hipError_t launch_router_grad(const float* logits, const int32_t* ids, const float* w,
-                              const float* dw, int T, int E, int k, int norm, float* dL,
-                              hipStream_t s) {
+                              const float* dw, const int32_t* slot_pos, int T, int E, int k,
+                              int norm, float* dL, float* dl_perm, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  router_grad_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, dw, T, E, k, norm, dL);
+  router_grad_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, dw, slot_pos, T, E, k, norm, dL,
+                                                 dl_perm);
   return hipGetLastError();
 }
 
@@ -264,21 +290,29 @@ hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const i
   return hipGetLastError();
 }
 
-hipError_t launch_router_weight_grad(bool bf16, const void* x, const void* x_perm, const float* dL,
-                                     const int32_t* offsets, const int32_t* sorted_token, int T,
-                                     int E, int H, int sparse, float* dwr, float* dbias,
-                                     hipStream_t s) {
-  const int grid = grid_for_total((long long)E * (H / 8));
+size_t router_weight_grad_ws(int E, int H) {
+  return (size_t)kRouterSplits * E * (H + 1) * sizeof(float);
+}
+
+hipError_t launch_router_weight_grad(bool bf16, const void* x, const void* x_perm,
+                                     const float* dL, const float* dl_perm,
+                                     const int32_t* offsets, int T, int E, int H, int sparse,
+                                     float* dwr, float* dbias, void* ws, hipStream_t s) {
+  float* part = (float*)ws;
+  float* part_b = part + (size_t)kRouterSplits * E * H;
+  const void* rows = sparse ? x_perm : x;
+  const float* g = sparse ? dl_perm : dL;
+  const int grid = E * kRouterSplits;
   if (bf16)
-    router_weight_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, (const bf16_t*)x_perm,
-                                                           dL, offsets,
-                                                           sorted_token, T, E, H, sparse, dwr,
-                                                           dbias);
+    router_weight_grad_part_kernel<bf16_t><<<grid, 256, 0, s>>>(
+        (const bf16_t*)rows, g, offsets, T, E, H, sparse, kRouterSplits, part, part_b);
   else
-    router_weight_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)x, (const float*)x_perm,
-                                                          dL, offsets,
-                                                          sorted_token, T, E, H, sparse, dwr,
-                                                          dbias);
+    router_weight_grad_part_kernel<float><<<grid, 256, 0, s>>>(
+        (const float*)rows, g, offsets, T, E, H, sparse, kRouterSplits, part, part_b);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  router_weight_grad_sum_kernel<<<grid_for_total((long long)E * H), 256, 0, s>>>(
+      part, part_b, E, H, kRouterSplits, dwr, dbias);
   return hipGetLastError();
 }
 

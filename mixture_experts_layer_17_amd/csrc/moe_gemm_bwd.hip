@@ -34,6 +34,75 @@ namespace {
 
 using namespace lds;
 
+// The K loop shared by both kernels: a ring of STAGES LDS slots filled by
+// issue(slot, block); wait_blocks(n) leaves n blocks of this wave's copies
+// in flight.  The fragments of the next 16-k step are read while the MFMAs
+// of the current one run (read_b for the whole step, then each m-tile's
+// read_a right after its MFMAs are issued); sched_barrier keeps that
+// interleave.  One barrier per block sits between its two k-steps: it
+// publishes the next block and retires the one just read, whose slot is
+// refilled at once.
+template <int TM, int TN, int STAGES, class Issue, class Wait, class ReadA, class ReadB>
+__device__ __forceinline__ void pipelined_k_loop(int KT, unsigned char* smem, int stage_bytes,
+                                                 Issue&& issue, Wait&& wait_blocks,
+                                                 ReadA&& read_a, ReadB&& read_b,
+                                                 f32x16_v (&acc)[TM][TN]) {
+#pragma unroll
+  for (int p = 0; p < STAGES; ++p)
+    if (p < KT) issue(smem + p * stage_bytes, p);
+  if (KT <= 0) return;
+  wait_blocks(min(STAGES, KT) - 1);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  bf16x8_v b0[TN], b1[TN], af[TM];
+  auto mma_roll = [&](const bf16x8_v (&bf)[TN], const unsigned char* nbase, int nkk) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+      af[i] = read_a(nbase, nkk, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b0[j] = read_b(smem, 0, j);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) af[i] = read_a(smem, 0, i);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b1[j] = read_b(smem, 1, j);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_roll(b0, smem, 1);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (KT > 1) wait_blocks(min(STAGES - 2, KT - 2));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  int slot = 0;
+  for (int kb = 0; kb + 1 < KT; ++kb) {
+    unsigned char* cur = smem + slot * stage_bytes;
+    slot = (slot + 1 == STAGES) ? 0 : slot + 1;
+    unsigned char* nxt = smem + slot * stage_bytes;
+    if (kb + STAGES < KT) issue(cur, kb + STAGES);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b0[j] = read_b(nxt, 0, j);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_roll(b1, nxt, 0);   // second k-step of block kb, first of kb + 1 read
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b1[j] = read_b(nxt, 1, j);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_roll(b0, nxt, 1);   // first k-step of block kb + 1, its second read
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (kb + 2 < KT) wait_blocks(min(STAGES - 2, KT - 3 - kb));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[j], af[i], acc[i][j], 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- dgrad
 
 enum { DG_PLAIN = 0, DG_SWIGLU_BWD = 1 };
@@ -116,7 +185,8 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
       src[u] = We + (long long)(n0 + r - BM) * ldw + 8 * c;
     }
   }
-  auto issue = [&](unsigned char* base) {
+  // called once per block, in block order
+  auto issue = [&](unsigned char* base, int) {
 #pragma unroll
     for (int u = 0; u < G::PER; ++u) {
       copy16_to_lds(src[u], base + (wave + u * G::NW) * 1024);
@@ -154,34 +224,14 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-#pragma unroll
-  for (int p = 0; p < STAGES; ++p)
-    if (p < KT) issue(smem + p * G::STAGE_BYTES);
-  for (int kb = 0; kb < KT; ++kb) {
-    unsigned char* cur = smem + (kb % STAGES) * G::STAGE_BYTES;
-    wait_blocks(min(KT, kb + STAGES) - 1 - kb);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_v af[G::TM], bf[G::TN];
-#pragma unroll
-      for (int i = 0; i < G::TM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(cur + a_off[i][kk]));
-#pragma unroll
-      for (int j = 0; j < G::TN; ++j)
-        bf[j] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(cur + b_off[j][kk]));
-#pragma unroll
-      for (int i = 0; i < G::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < G::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kb + STAGES < KT) issue(cur);
-  }
+  auto read_a = [&](const unsigned char* base, int kk, int i) {
+    return __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(base + a_off[i][kk]));
+  };
+  auto read_b = [&](const unsigned char* base, int kk, int j) {
+    return __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(base + b_off[j][kk]));
+  };
+  pipelined_k_loop<G::TM, G::TN, STAGES>(KT, smem, G::STAGE_BYTES, issue, wait_blocks, read_a,
+                                         read_b, acc);
 
   // ---- epilogue.  acc[i][j][q] = C[row 32 (wm + WM i) + l % 32]
   //                                 [col wn CW + 32 j + 8 (q / 4) + 4 hl + q % 4]
@@ -405,32 +455,14 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-#pragma unroll
-  for (int p = 0; p < STAGES; ++p)
-    if (p < KT) issue(smem + p * G::STAGE_BYTES, p);
-  for (int kb = 0; kb < KT; ++kb) {
-    unsigned char* cur = smem + (kb % STAGES) * G::STAGE_BYTES;
-    wait_blocks(min(KT, kb + STAGES) - 1 - kb);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_v af[G::TM], bf[G::TN];
-#pragma unroll
-      for (int i = 0; i < G::TM; ++i) af[i] = read_tr(cur + a_off[i] + 16 * kk * G::A_ROWB, G::A_ROWB);
-#pragma unroll
-      for (int j = 0; j < G::TN; ++j) bf[j] = read_tr(cur + b_off[j] + 16 * kk * G::B_ROWB, G::B_ROWB);
-#pragma unroll
-      for (int i = 0; i < G::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < G::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kb + STAGES < KT) issue(cur, kb + STAGES);
-  }
+  auto read_a = [&](const unsigned char* base, int kk, int i) {
+    return read_tr(base + a_off[i] + 16 * kk * G::A_ROWB, G::A_ROWB);
+  };
+  auto read_b = [&](const unsigned char* base, int kk, int j) {
+    return read_tr(base + b_off[j] + 16 * kk * G::B_ROWB, G::B_ROWB);
+  };
+  pipelined_k_loop<G::TM, G::TN, STAGES>(KT, smem, G::STAGE_BYTES, issue, wait_blocks, read_a,
+                                         read_b, acc);
 
   // ---- epilogue: acc[i][j][q] = C[m0 + (BM / WM) wm + 32 i + l % 32]
   //                                [n0 + CW wn + 32 j + 8 (q / 4) + 4 hl + q % 4]

@@ -124,18 +124,22 @@ hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const vo
                         const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s);
 hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N, int k, int H,
                               float* dw, hipStream_t s);
+// dL [T, E]; with norm also dl_perm [N] (dL of each selected entry, in the
+// permutation's expert-major order).
 hipError_t launch_router_grad(const float* logits, const int32_t* ids, const float* w,
-                              const float* dw, int T, int E, int k, int norm, float* dL,
-                              hipStream_t s);
+                              const float* dw, const int32_t* slot_pos, int T, int E, int k,
+                              int norm, float* dL, float* dl_perm, hipStream_t s);
 // With ids (renormalised weights: dL is zero off the selection) only the
 // selected experts' router rows are read; ids == NULL reads all E.
 hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const int32_t* ids,
                              const void* wr, int T, int k, int E, int H, void* dx, hipStream_t s);
-// x_perm: x in expert-major order (read when sparse).
-hipError_t launch_router_weight_grad(bool bf16, const void* x, const void* x_perm, const float* dL,
-                                     const int32_t* offsets, const int32_t* sorted_token, int T,
-                                     int E, int H, int sparse, float* dwr, float* dbias,
-                                     hipStream_t s);
+// Router weight and bias gradients; ws holds router_weight_grad_ws(E, H)
+// bytes of partial sums.  sparse: rows from x_perm / dl_perm (expert-major).
+size_t router_weight_grad_ws(int E, int H);
+hipError_t launch_router_weight_grad(bool bf16, const void* x, const void* x_perm,
+                                     const float* dL, const float* dl_perm,
+                                     const int32_t* offsets, int T, int E, int H, int sparse,
+                                     float* dwr, float* dbias, void* ws, hipStream_t s);
 hipError_t launch_fill_u32(void* p, long long n, uint32_t v, hipStream_t s);
 
 }  // namespace moe

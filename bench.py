@@ -18,6 +18,13 @@ Other modes:
                          size IS
   --backward             time the layer backward instead (one training
                          forward first, then moe_layer_backward per step)
+  --workload ep_rank_235b  one expert-parallel rank: rank-major reshuffle,
+                         grouped SwiGLU, reverse reshuffle
+
+Besides the mean over the timed steps, each line reports per-step median and
+minimum, warm and cold (a 512 MB scratch write before each step evicts L2
+and the MALL), and, as context only, torch's batched bf16 GEMM at the
+average expert's shape.
 """
 from __future__ import annotations
 
@@ -90,6 +97,29 @@ def algorithmic_backward(wl, counts):
     return f, b
 
 
+def dense_gemm_context(wl):
+    """Context only (never on the path): torch's batched bf16 GEMM over the
+    experts at the average expert's gate_up shape, as a ceiling check."""
+    import torch
+    E, H, I = wl.E, wl.H, wl.I
+    m = max(16, wl.T * wl.top_k // E)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(E, m, H, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(E, H, 2 * I, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        torch.bmm(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.bmm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    return {"torch_bmm_bf16": f"{E} x [{m},{H}] x [{H},{2 * I}]",
+            "ms": round(ms, 4), "tflops": round(2.0 * E * m * H * 2 * I / (ms * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline_backward(wl, dout, budget_s=12.0):
     import numpy as np
     from oracle import moe_oracle as O
@@ -113,6 +143,123 @@ def cpu_baseline_backward(wl, dout, budget_s=12.0):
             "kind": "oracle",
             "sample": f"whole {wl.name} workload ({wl.T} tokens), forward recomputed inside, "
                       f"{runs} run(s), {el:.1f} s, float64 NumPy"}
+
+
+def bench_ep_rank(args, wl):
+    """One expert-parallel rank: rows received rank-major from R source
+    ranks (built untimed with the library's router and torch indexing), then
+    the timed span moe_permute (rank-major reshuffle) -> moe_grouped_swiglu
+    (rows gathered in the loads, outputs scattered back to rank-major)."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_17_amd as moe
+    from mixture_experts_layer_17_amd import _lib
+    dev = torch.device("cuda:0")
+    R, H, I, El, k = wl.R, wl.H, wl.I, wl.E_local, wl.top_k
+    wr = wl.router_weight.to(dev)
+    rows, C = [], torch.zeros(R, El, dtype=torch.int32)
+    for r in range(R):
+        xr = wl.source_hidden[r].to(dev)
+        _, ids, _, _ = moe.route(xr, wr, k, wl.norm_topk_prob)
+        loc = ids.long() - wl.local_lo
+        t_idx = torch.arange(xr.shape[0], device=dev).unsqueeze(1).expand_as(loc)
+        sel = (loc >= 0) & (loc < El)
+        e_sel, t_sel = loc[sel], t_idx[sel]
+        order = torch.sort(e_sel * xr.shape[0] + t_sel, stable=True).indices
+        rows.append(xr[t_sel[order]])
+        C[r] = torch.bincount(e_sel, minlength=El).to(torch.int32).cpu()
+    x_rm = torch.cat(rows).contiguous()
+    N = x_rm.shape[0]
+    C_d = C.to(dev)
+    gu, dn = wl.gate_up.to(dev), wl.down.to(dev)
+    perm = {n: torch.empty(sz, dtype=torch.int32, device=dev)
+            for n, sz in (("counts", El), ("offsets", El + 1), ("sorted_token", N),
+                          ("sorted_slot", N), ("slot_pos", N))}
+    y = torch.empty(N, H, dtype=wl.dtype, device=dev)
+    L = moe.lib
+    nb_p = L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 0, 0, 0, El, 1, R, N, _lib.MOE_BF16)
+    nb_g = L.moe_workspace_size(_lib.MOE_OP_GROUPED_SWIGLU, 0, H, I, El, 1, 0, N, _lib.MOE_BF16)
+    ws_p = torch.empty(max(nb_p, 1), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(max(nb_g, 1), dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev)
+    P = lambda t: t.data_ptr()  # noqa: E731
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(s)
+        st = L.moe_permute(None, 0, 1, P(C_d), R, N, El, P(perm["counts"]), P(perm["offsets"]),
+                           P(perm["sorted_token"]), P(perm["sorted_slot"]), P(perm["slot_pos"]),
+                           P(ws_p), nb_p, s.cuda_stream)
+        if evs:
+            evs[1].record(s)
+        st = st or L.moe_grouped_swiglu(P(x_rm), N, P(perm["sorted_token"]),
+                                        P(perm["sorted_token"]), P(perm["offsets"]), N, H, I, El,
+                                        P(gu), P(dn), _lib.MOE_BF16, P(y), P(ws_g), nb_g,
+                                        s.cuda_stream)
+        if evs:
+            evs[2].record(s)
+        if st != 0:
+            raise RuntimeError(f"EP rank step failed with status {st}")
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(s)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(s)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / args.steps
+    perm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    steps = [e[0].elapsed_time(e[2]) for e in evs]
+    counts = C.sum(0).numpy()
+    hit = int((counts > 0).sum())
+    flops = 6.0 * N * H * I
+    bytes_ = hit * 3 * H * I * 2 + 2 * N * H * 2
+    roof = {"bound": "mfma", "achieved": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof.update(traffic=None, kernel="grouped_swiglu (both GEMMs)", algorithmic_flops=int(flops),
+                algorithmic_bytes=int(bytes_))
+    result = {
+        "metric": "routed rows/s per EP-rank expert pass (rank-major reshuffle + grouped SwiGLU "
+                  "+ reverse), bf16",
+        "value": round(N / (ms_per_step * 1e-3), 1), "unit": "routed rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded Gaussian source tokens routed by the library's router",
+        "config": {"workload": wl.name, "R": R, "T_per_rank": wl.T_per_rank, "H": H, "I": I,
+                   "E": wl.E, "E_local": El, "top_k": k, "routed_rows": N, "experts_hit": hit},
+        "layer_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "layer_mfma_frac": round(flops / (ms_per_step * 1e-3) / PEAK_BF16_FLOPS, 4),
+        "roofline": roof,
+        "kernels": {"permute_rank_major": {"avg_us": round(perm_ms * 1e3, 2)},
+                    "grouped_swiglu": {"avg_us": round(gemm_ms * 1e3, 2),
+                                       "tflops": roof["achieved"]}},
+        "step_ms": {"warm_median": round(float(np.median(steps)), 4),
+                    "warm_min": round(float(np.min(steps)), 4)},
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        n0 = int(C[0].sum())
+        xs = x_rm[:n0].float().cpu().numpy()
+        gu_c, dn_c = wl.gate_up.float().numpy(), wl.down.float().numpy()
+        t0 = time.perf_counter()
+        O.ep_rank_forward(xs, C[:1].numpy(), gu_c, dn_c)
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": n0 / el, "unit": "routed rows/s", "cores":
+                                  os.cpu_count(), "kind": "oracle",
+                                  "sample": f"source rank 0's {n0} received rows, one run, "
+                                            f"{el:.1f} s, float64 NumPy"}
+    print(json.dumps(result), flush=True)
 
 
 def bench_backward(args, wl):
@@ -363,9 +510,8 @@ def main():
 
     wl = workloads.make(args.workload)
     if not hasattr(wl, "T"):
-        print("bench.py times token-choice layers; the EP-rank workload is a parity case",
-              file=sys.stderr)
-        sys.exit(2)
+        bench_ep_rank(args, wl)
+        return
     if args.backward:
         bench_backward(args, wl)
         return
@@ -462,9 +608,29 @@ def main():
                 raise RuntimeError("hipEventElapsedTime failed")
             acc.append(f.value)
         per_kernel_ms[kname] = float(np.mean(acc))
+
+    def step_times(arrs):
+        out = []
+        for arr in arrs:
+            if hip.hipEventElapsedTime(ctypes.byref(f), arr[0], arr[nst - 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(f.value)
+        return out
+
+    warm = step_times(ev_arrays)
+    # cold: a 512 MB scratch write before each step evicts L2 and the MALL;
+    # each step is timed on its own by its first and last stage events
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for i in range(args.steps):
+        scratch.fill_(i & 255)
+        step(ev_arrays[i])
+    torch.cuda.synchronize()
+    cold = step_times(ev_arrays)
+    del scratch
     for arr in ev_arrays:
         for j in range(nst):
             hip.hipEventDestroy(arr[j])
+    context = dense_gemm_context(wl) if wl.dtype == torch.bfloat16 else None
 
     c_np = counts.cpu().numpy()
     flops, bytes_, hit = algorithmic(wl, c_np, Is, fused)
@@ -518,6 +684,11 @@ def main():
         "layer_mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / peak_f, 4),
         "roofline": roof,
         "kernels": kern,
+        "step_ms": {"warm_median": round(float(np.median(warm)), 4),
+                    "warm_min": round(float(np.min(warm)), 4),
+                    "cold_median": round(float(np.median(cold)), 4),
+                    "cold_min": round(float(np.min(cold)), 4)},
+        "context": context,
         "wall_s_timed": round(t_wall, 3),
         "host": platform.node(),
     }

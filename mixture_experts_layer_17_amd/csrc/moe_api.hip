@@ -157,7 +157,7 @@ int router_variant(const moe_router_config* c, int E, int k, RouterVariant* out,
 // d_weights, dL, dG [N, 2I], w h [N, I], dX [N, H] and a zero row.
 struct BwdWs {
   int32_t *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
-  void *perm, *tiles;
+  void *perm, *tiles, *tiles1;
   float *dw, *dL, *dl_perm;
   void *dG, *hw, *dX, *x_perm, *dout_perm, *zero, *rw_part;
   size_t zero_bytes, total;
@@ -179,6 +179,7 @@ BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
   w.slot_pos = (int32_t*)take(N * 4);
   w.perm = take(permute_ws_bytes((int)N, E, 0));
   w.tiles = take(tile_list_bytes((int)N, E, dgrad_bm(pick_dgrad_cfg((int)N, E))));
+  w.tiles1 = take(tile_list_bytes((int)N, E, dgrad_bm(pick_dgrad1_cfg((int)N, E))));
   w.dw = (float*)take(N * 4);
   w.dL = (float*)take((size_t)T * E * 4);
   w.dl_perm = (float*)take(N * 4);
@@ -546,12 +547,14 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   const int N = T * k;
   float* dw = d_weights ? d_weights : w.dw;
   const int id = pick_dgrad_cfg(N, E);
+  const int id1 = pick_dgrad1_cfg(N, E);
   auto mark = [&](int i) {
     if (stage_events && stage_events[i]) (void)hipEventRecord(stage_events[i], s);
   };
   mark(0);
   hipError_t e = launch_permute_topk(ids, T, k, E, w.counts, w.offsets, w.sorted_token,
-                                     w.sorted_slot, w.slot_pos, w.perm, s, w.tiles, dgrad_bm(id));
+                                     w.sorted_slot, w.slot_pos, w.perm, s, w.tiles, dgrad_bm(id),
+                                     w.tiles1, dgrad_bm(id1));
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (T == 0) {
     // no tokens: every weight gradient is zero
@@ -570,8 +573,8 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   mark(1);
   // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot order
   if (e == hipSuccess)
-    e = launch_dgrad_down_swiglu(id, dout, T, w.sorted_token, down, N, H, I, E, saved_gate_up,
-                                 weights, w.sorted_slot, w.dG, w.hw, w.tiles, s);
+    e = launch_dgrad_down_swiglu(id1, dout, T, w.sorted_token, down, N, H, I, E, saved_gate_up,
+                                 weights, w.sorted_slot, w.dG, w.hw, w.tiles1, s);
   mark(2);
   if (e == hipSuccess)
     e = launch_dgrad_gate_up(id, w.dG, gate_up, N, H, I, E, w.sorted_slot, w.dX, w.tiles, s);

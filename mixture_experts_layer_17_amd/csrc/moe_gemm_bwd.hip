@@ -571,6 +571,13 @@ int pick_dgrad_cfg(int N, int E) {
 
 int dgrad_bm(int id) { return kDgradBM[id]; }
 
+// The first dgrad has only I / BN column tiles per row tile, so with tall
+// row tiles the grid is short of work-groups; it keeps 128-row tiles.
+int pick_dgrad1_cfg(int N, int E) {
+  const int c = pick_dgrad_cfg(N, E);
+  return c == 3 ? 0 : c;
+}
+
 hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
                                     const void* down, int N, int H, int I, int E,
                                     const void* G, const float* w, const int32_t* sorted_slot,

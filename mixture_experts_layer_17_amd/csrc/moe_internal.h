@@ -111,6 +111,7 @@ hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h,
 // H % 128 == 0.  The dgrad GEMMs use the row-tile list of height
 // dgrad_bm(id).
 int pick_dgrad_cfg(int N, int E);
+int pick_dgrad1_cfg(int N, int E);
 int dgrad_bm(int id);
 hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
                                     const void* down, int N, int H, int I, int E,

@@ -51,7 +51,7 @@ __all__ = [
     "expert_counts", "expert_offsets", "permutation", "gather_rows",
     "silu", "swiglu_expert", "grouped_swiglu", "combine", "unpermute", "feed_forward",
     "moe_layer_forward", "moe_layer_forward_brute", "moe_layer_forward_tokens",
-    "silu_grad", "moe_layer_backward",
+    "silu_grad", "moe_layer_backward", "routing_weight_jacobian",
     "dispatch_rank_major", "reshuffle_rank_to_expert", "ep_rank_forward",
 ]
 
@@ -349,12 +349,15 @@ def _add_shared(out, x, shared):
 # ---------------------------------------------------------------------------
 
 def moe_layer_forward(x, w_router, bias, gate_up, down, top_k: int,
-                      norm_topk_prob: bool, shared=None, ids=None) -> dict:
+                      norm_topk_prob: bool, shared=None, ids=None, router=None) -> dict:
     """Full layer: route, permute, per-expert SwiGLU loop, combine, and the
     optional shared expert ``shared = (w1, w2, w3)`` (``FeedForward`` weights).
     ``ids`` replaces the top-k decision with one taken elsewhere (a device's
     top-k of its own float32 logits, checked separately); the routing weights
-    are then this module's softmax at those ids.
+    are then this module's at those ids.  ``router`` selects a router variant
+    ([HP] ``TokenChoiceTopKRouter``): a dict of ``route_variant``'s keyword
+    arguments ``score_func``, ``route_scale``, ``expert_bias``, ``n_groups``,
+    ``n_limited``.
 
     Returns a dict with ``logits`` (float32 [T, E]), ``ids`` ([T, k]),
     ``weights`` ([T, k] float64), ``counts``, ``offsets``, ``sorted_slot``,
@@ -363,7 +366,17 @@ def moe_layer_forward(x, w_router, bias, gate_up, down, top_k: int,
     [T, H])."""
     x = np.asarray(x)
     E = np.asarray(w_router).shape[0]
-    if ids is None:
+    if router is not None:
+        L = router_logits(x, w_router, bias)
+        if ids is None:
+            ids, w, _, _ = route_variant(L, top_k, norm_topk_prob, **router)
+        else:
+            ids = np.asarray(ids, dtype=np.int32)
+            sc = router_scores(L, router.get("score_func", "sigmoid"), router.get("route_scale", 1.0))
+            w = np.take_along_axis(sc, ids.astype(np.int64), axis=1)
+            if norm_topk_prob:
+                w = w / w.sum(axis=1, keepdims=True)
+    elif ids is None:
         L, ids, w = route(x, w_router, bias, top_k, norm_topk_prob)
     else:
         L = router_logits(x, w_router, bias)
@@ -431,8 +444,41 @@ def silu_grad(z: np.ndarray) -> np.ndarray:
     return sg * (1.0 + z * (1.0 - sg))
 
 
+def routing_weight_jacobian(logits32, ids, norm_topk_prob: bool, score_func: str = "softmax",
+                            route_scale: float = 1.0) -> np.ndarray:
+    """``J[t, j, e] = d w[t, j] / d L[t, e]`` for the routing weights of a
+    router variant ([HP] ``TokenChoiceTopKRouter.forward``): scores
+    ``s = score_func(L) * route_scale`` (softmax: ``ds_a/dL_e = scale
+    p_a (delta_ae - p_e)``; sigmoid: ``scale sg_a (1 - sg_a) delta_ae``), the
+    selected scores, and with renormalisation ``w_j = s_j / Z``,
+    ``dw_j/dL_e = (ds_j/dL_e - w_j sum_i ds_i/dL_e) / Z`` over the selection.
+    The selection itself (bias, groups) has no gradient.  Float64 [T, k, E]."""
+    L = _f64(logits32)
+    T, E = L.shape
+    ii = np.asarray(ids, dtype=np.int64)
+    eye = np.eye(E)
+    if score_func == "softmax":
+        p = np.exp(L - L.max(axis=1, keepdims=True))
+        p = p / p.sum(axis=1, keepdims=True)
+        s = route_scale * p
+        ds = route_scale * p[:, :, None] * (eye[None] - p[:, None, :])      # [T, a, e]
+    elif score_func == "sigmoid":
+        sg = 1.0 / (1.0 + np.exp(-L))
+        s = route_scale * sg
+        ds = (route_scale * sg * (1.0 - sg))[:, :, None] * eye[None]
+    else:
+        raise ValueError("score_func must be 'sigmoid' or 'softmax'")
+    dsel = np.take_along_axis(ds, ii[:, :, None], axis=1)                  # [T, k, E]
+    if not norm_topk_prob:
+        return dsel
+    ssel = np.take_along_axis(s, ii, axis=1)
+    Z = ssel.sum(axis=1)
+    w = ssel / Z[:, None]
+    return (dsel - w[:, :, None] * dsel.sum(axis=1)[:, None, :]) / Z[:, None, None]
+
+
 def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_prob: bool,
-                       dout, ids=None) -> dict:
+                       dout, ids=None, router=None) -> dict:
     """Gradients of ``sum(dout * out)`` for the layer of ``moe_layer_forward``.
 
     The routing decision (which experts) is piecewise constant, so gradients
@@ -453,9 +499,11 @@ def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_p
 
     Returns float64 ``dx``, ``d_router_weight``, ``d_router_bias``,
     ``d_gate_up``, ``d_down``, ``d_weights`` [T, k] and ``d_logits`` [T, E],
-    plus the forward's dict under ``forward``.  ``ids`` as in
-    ``moe_layer_forward``."""
-    fwd = moe_layer_forward(x, w_router, bias, gate_up, down, top_k, norm_topk_prob, ids=ids)
+    plus the forward's dict under ``forward``.  ``ids`` and ``router`` as in
+    ``moe_layer_forward``; with a router variant the logits' gradient is
+    ``sum_j d_weights[t, j] J[t, j, e]`` with ``routing_weight_jacobian``."""
+    fwd = moe_layer_forward(x, w_router, bias, gate_up, down, top_k, norm_topk_prob, ids=ids,
+                            router=router)
     X = _f64(x)
     D = _f64(dout)
     T, H = X.shape
@@ -491,7 +539,13 @@ def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_p
     L = _f64(fwd["logits"])
     ii = ids.astype(np.int64)
     dL = np.zeros((T, E))
-    if norm_topk_prob:
+    if router is not None:
+        sf, sc = router.get("score_func", "sigmoid"), router.get("route_scale", 1.0)
+        for t0 in range(0, T, 256):          # [T, k, E] Jacobians, 256 tokens at a time
+            J = routing_weight_jacobian(L[t0:t0 + 256].astype(np.float32), ids[t0:t0 + 256],
+                                        norm_topk_prob, sf, sc)
+            dL[t0:t0 + 256] = np.einsum("tj,tje->te", d_w[t0:t0 + 256], J)
+    elif norm_topk_prob:
         inner = (d_w * w).sum(axis=1, keepdims=True)
         np.put_along_axis(dL, ii, w * (d_w - inner), axis=1)
     else:

@@ -592,7 +592,7 @@ def pin_shared_brute_and_tokens():
 
 # ---- layer backward -----------------------------------------------------------
 
-def _fd_layer(seed, norm, with_bias, T=4, H=6, I=3, E=5, k=2, eps=1e-3):
+def _fd_layer(seed, norm, with_bias, T=4, H=6, I=3, E=5, k=2, eps=1e-3, router=None):
     r = _rng(seed)
     x = r.standard_normal((T, H))
     wr = r.standard_normal((E, H)) * 0.7
@@ -600,11 +600,11 @@ def _fd_layer(seed, norm, with_bias, T=4, H=6, I=3, E=5, k=2, eps=1e-3):
     gu = r.standard_normal((E, H, 2 * I)) * 0.5
     dn = r.standard_normal((E, I, H)) * 0.5
     dout = r.standard_normal((T, H))
-    g = O.moe_layer_backward(x, wr, b, gu, dn, k, norm, dout)
+    g = O.moe_layer_backward(x, wr, b, gu, dn, k, norm, dout, router=router)
     ids0 = g["forward"]["ids"]
 
     def loss(x_, wr_, b_, gu_, dn_):
-        f = O.moe_layer_forward(x_, wr_, b_, gu_, dn_, k, norm)
+        f = O.moe_layer_forward(x_, wr_, b_, gu_, dn_, k, norm, router=router)
         assert np.array_equal(f["ids"], ids0), "perturbation changed the routing"
         return float((f["out"] * dout).sum())
 
@@ -641,6 +641,42 @@ def pin_backward_finite_differences_plain():
 
 def pin_backward_finite_differences_k1_bias():
     _fd_layer(33, False, True, T=3, H=4, I=2, E=3, k=1)
+
+
+def pin_backward_variant_sigmoid_renorm():
+    _fd_layer(41, True, True, router=dict(score_func="sigmoid", route_scale=2.5))
+
+
+def pin_backward_variant_sigmoid_groups_bias():
+    # bias and groups steer the selection only; the gradient flows through
+    # the unbiased sigmoid scores
+    _fd_layer(42, False, False, T=5, E=6, k=2,
+              router=dict(score_func="sigmoid", route_scale=1.5,
+                          expert_bias=np.array([0.3, -0.2, 0.1, 0.0, 0.4, -0.1]),
+                          n_groups=3, n_limited=2))
+
+
+def pin_backward_variant_softmax_scaled():
+    _fd_layer(43, False, True, router=dict(score_func="softmax", route_scale=1.7))
+
+
+def pin_backward_variant_jacobian_matches_default():
+    # the softmax variant with scale 1 is the default router: the Jacobian
+    # path and the closed forms agree
+    r = _rng(44)
+    T, H, I, E, k = 12, 8, 4, 7, 3
+    x = r.standard_normal((T, H))
+    wr = r.standard_normal((E, H))
+    gu = r.standard_normal((E, H, 2 * I)) * 0.4
+    dn = r.standard_normal((E, I, H)) * 0.4
+    dout = r.standard_normal((T, H))
+    for norm in (True, False):
+        a = O.moe_layer_backward(x, wr, None, gu, dn, k, norm, dout)
+        b = O.moe_layer_backward(x, wr, None, gu, dn, k, norm, dout,
+                                 router=dict(score_func="softmax", route_scale=1.0))
+        assert np.array_equal(a["forward"]["ids"], b["forward"]["ids"])
+        assert np.allclose(a["d_logits"], b["d_logits"], rtol=1e-12, atol=1e-14)
+        assert np.allclose(a["dx"], b["dx"], rtol=1e-12, atol=1e-13)
 
 
 def pin_backward_scalar_closed_form():

@@ -116,15 +116,27 @@ def _silu_grad_no_product_rule(z):
     return 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))
 
 
-def _backward_without_router_dx(x, w_router, bias, gate_up, down, top_k, norm, dout):
-    g = _orig["moe_layer_backward"](x, w_router, bias, gate_up, down, top_k, norm, dout)
+def _backward_without_router_dx(x, w_router, bias, gate_up, down, top_k, norm, dout, **kw):
+    g = _orig["moe_layer_backward"](x, w_router, bias, gate_up, down, top_k, norm, dout, **kw)
     g["dx"] = g["dx"] - g["d_logits"] @ np.asarray(w_router, np.float64)
     return g
 
 
-def _backward_unweighted_down_grad(x, w_router, bias, gate_up, down, top_k, norm, dout):
+def _jacobian_without_renorm_coupling(logits32, ids, norm, score_func="softmax", route_scale=1.0):
+    # renormalisation treated as a constant divisor (the coupling term dropped)
+    J = _orig["routing_weight_jacobian"](logits32, ids, False, score_func, route_scale)
+    if not norm:
+        return J
+    L = np.asarray(logits32, np.float64)
+    s = (1.0 / (1.0 + np.exp(-L))) if score_func == "sigmoid" else \
+        np.exp(L - L.max(1, keepdims=True)) / np.exp(L - L.max(1, keepdims=True)).sum(1, keepdims=True)
+    Z = np.take_along_axis(s * route_scale, np.asarray(ids, np.int64), 1).sum(1)
+    return J / Z[:, None, None]
+
+
+def _backward_unweighted_down_grad(x, w_router, bias, gate_up, down, top_k, norm, dout, **kw):
     # the down-projection gradient taken from dout without the routing weight
-    g = _orig["moe_layer_backward"](x, w_router, bias, gate_up, down, top_k, norm, dout)
+    g = _orig["moe_layer_backward"](x, w_router, bias, gate_up, down, top_k, norm, dout, **kw)
     f = g["forward"]
     k = top_k
     wsum = np.zeros(np.asarray(down).shape[0])
@@ -137,7 +149,8 @@ def _backward_unweighted_down_grad(x, w_router, bias, gate_up, down, top_k, norm
 
 _orig = {n: getattr(O, n) for n in ("routing_weights", "combine", "permutation",
                                      "router_logits", "expert_offsets", "route_variant",
-                                     "feed_forward", "moe_layer_backward")}
+                                     "feed_forward", "moe_layer_backward",
+                                     "routing_weight_jacobian")}
 
 MUTATIONS = {
     "swiglu_expert": _swapped_gate_up,
@@ -155,6 +168,7 @@ MUTATIONS = {
     "_add_shared": _shared_weighted,
     "silu_grad": _silu_grad_no_product_rule,
     "moe_layer_backward": _backward_without_router_dx,
+    "routing_weight_jacobian": _jacobian_without_renorm_coupling,
 }
 
 

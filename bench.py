@@ -304,7 +304,8 @@ def bench_backward(args, wl):
 
     def step(evs=None):
         st = L.moe_layer_backward(P(x), P(wr), P(gu), P(dn), T, H, I, E, k, int(norm),
-                                  _lib.MOE_BF16, P(saved["router_logits"]), P(saved["topk_ids"]),
+                                  _lib.MOE_BF16, None, P(saved["router_logits"]),
+                                  P(saved["topk_ids"]),
                                   P(saved["topk_weights"]), P(saved["gate_up_out"]),
                                   P(saved["expert_out"]), P(dout), P(g["dx"]), P(g["dwr"]),
                                   P(g["db"]), P(g["dgu"]), P(g["ddn"]), P(g["dw"]), P(ws), nws,

@@ -366,9 +366,12 @@ int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
  * #115, SpeedupMoeExperts' per-expert training loop and
  * SpeedupMoeSparseMoeBlock's softmax routing weights; MindSpore moe.py,
  * MoE.forward and MoE.unpermutation); the backward is the gradient of
- * sum(dout * out) for the default router (softmax, optionally renormalised,
- * optional router_bias) without a shared expert.  The top-k choice is
- * piecewise constant: gradients flow through the routing weights' values.
+ * sum(dout * out) for the layer without a shared expert, with the default
+ * router (softmax, optionally renormalised, optional router_bias) or a
+ * router variant (cfg: sigmoid or softmax scores times route_scale; the
+ * expert bias and the group limit steer the selection only).  The top-k
+ * choice is piecewise constant: gradients flow through the routing
+ * weights' values.
  * bf16 only, I a multiple of 128 (else MOE_ERR_UNSUPPORTED).
  *
  * moe_layer_forward_train: moe_layer_forward plus
@@ -378,13 +381,14 @@ int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
  *                    columns [0, I), up in [I, 2I);
  *   saved_expert_out [T*k, H] dt: each slot's expert output, row t*k + j.
  * router_logits, topk_ids and topk_weights are required (the backward reads
- * them).  Workspace: moe_workspace_size(MOE_OP_LAYER, ...).
+ * them).  cfg: a router variant or NULL (moe_layer_forward_cfg); pass the
+ * same cfg to the backward.  Workspace: moe_workspace_size(MOE_OP_LAYER, ...).
  */
 int moe_layer_forward_train(const void* hidden_states, const void* router_weight,
                             const float* router_bias, const void* gate_up,
                             const void* down, int T, int H, int I, int E, int top_k,
-                            int norm_topk_prob, moe_dtype dt, void* out,
-                            float* router_logits, int32_t* topk_ids,
+                            int norm_topk_prob, moe_dtype dt, const moe_router_config* cfg,
+                            void* out, float* router_logits, int32_t* topk_ids,
                             float* topk_weights, int32_t* num_tokens_per_expert,
                             void* saved_gate_up, void* saved_expert_out,
                             void* workspace, size_t workspace_bytes,
@@ -394,9 +398,12 @@ int moe_layer_forward_train(const void* hidden_states, const void* router_weight
  * moe_layer_backward — from dout [T, H] dt and the training forward's
  * router_logits, topk_ids, topk_weights, saved_gate_up and saved_expert_out:
  *   d_topk_weights[t, j] = <dout[t], y[t, j]>            float32 [T, k], or NULL
- *   dL (router logits): renormalised  w (d_w - <d_w, w>) on the selected
- *                       experts, 0 elsewhere; otherwise p (g - <g, p>) with
- *                       p = softmax(logits), g = d_w scattered to the ids
+ *   dL (router logits): the routing weights' Jacobian applied to d_w —
+ *       softmax, renormalised:  w (d_w - <d_w, w>) on the selection, else 0
+ *       softmax, plain:         p (route_scale g - <d_w, w>), p = softmax,
+ *                               g = d_w scattered to the ids
+ *       sigmoid, renormalised:  w (1 - sg) (d_w - <d_w, w>) on the selection
+ *       sigmoid, plain:         d_w w (1 - sg) on the selection
  *   per expert e on its rows, dY = w dout[token]:
  *     d_down[e]    = h^T dY        [E, I, H] dt   (h = silu(g) * u)
  *     dH = dY down[e]^T;  du = dH silu(g);  dg = dH u silu'(g)
@@ -416,7 +423,8 @@ int moe_layer_forward_train(const void* hidden_states, const void* router_weight
 int moe_layer_backward(const void* hidden_states, const void* router_weight,
                        const void* gate_up, const void* down, int T, int H, int I, int E,
                        int top_k, int norm_topk_prob, moe_dtype dt,
-                       const float* router_logits, const int32_t* topk_ids,
+                       const moe_router_config* cfg, const float* router_logits,
+                       const int32_t* topk_ids,
                        const float* topk_weights, const void* saved_gate_up,
                        const void* saved_expert_out, const void* dout, void* dx,
                        float* d_router_weight, float* d_router_bias, void* d_gate_up,

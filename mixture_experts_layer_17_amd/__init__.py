@@ -341,7 +341,7 @@ def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.T
 
 def layer_forward_train(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
                         down: torch.Tensor, top_k: int, norm_topk_prob: bool = True,
-                        router_bias: Optional[torch.Tensor] = None):
+                        router_bias: Optional[torch.Tensor] = None, config=None):
     """The layer forward that also keeps what the backward needs.  Returns
     (out, saved) where ``saved`` holds router_logits, topk_ids, topk_weights,
     num_tokens_per_expert, gate_up_out [T*k, 2I] (expert-major
@@ -360,8 +360,9 @@ def layer_forward_train(x: torch.Tensor, router_weight: torch.Tensor, gate_up: t
     y = torch.empty(N, H, dtype=x.dtype, device=x.device)
     _call("moe_layer_forward_train", x.data_ptr(), router_weight.data_ptr(),
           _chk(router_bias, "router_bias"), gate_up.data_ptr(), down.data_ptr(), T, H, I, E,
-          top_k, int(norm_topk_prob), _dt(x), b.out.data_ptr(), b.logits.data_ptr(),
-          b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(), g.data_ptr(),
+          top_k, int(norm_topk_prob), _dt(x), _cfg_ptr(config), b.out.data_ptr(),
+          b.logits.data_ptr(), b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(),
+          g.data_ptr(),
           y.data_ptr(), b.workspace.data_ptr(), b.ws_bytes, None, _stream(x.device))
     saved = dict(router_logits=b.logits, topk_ids=b.ids, topk_weights=b.weights,
                  num_tokens_per_expert=b.counts, gate_up_out=g, expert_out=y)
@@ -370,7 +371,7 @@ def layer_forward_train(x: torch.Tensor, router_weight: torch.Tensor, gate_up: t
 
 def layer_backward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
                    down: torch.Tensor, top_k: int, norm_topk_prob: bool, saved: dict,
-                   dout: torch.Tensor, with_bias_grad: bool = True) -> dict:
+                   dout: torch.Tensor, with_bias_grad: bool = True, config=None) -> dict:
     """Gradients of sum(dout * out) given ``saved`` from layer_forward_train:
     dx, d_router_weight (float32), d_router_bias (float32), d_gate_up,
     d_down and d_topk_weights (float32)."""
@@ -390,7 +391,7 @@ def layer_backward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.
     nb = lib.moe_workspace_size(_lib.MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, 0, N, _dt(x))
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     _call("moe_layer_backward", x.data_ptr(), router_weight.data_ptr(), gate_up.data_ptr(),
-          down.data_ptr(), T, H, I, E, top_k, int(norm_topk_prob), _dt(x),
+          down.data_ptr(), T, H, I, E, top_k, int(norm_topk_prob), _dt(x), _cfg_ptr(config),
           saved["router_logits"].data_ptr(), saved["topk_ids"].data_ptr(),
           saved["topk_weights"].data_ptr(), saved["gate_up_out"].data_ptr(),
           saved["expert_out"].data_ptr(), dout.data_ptr(), g["dx"].data_ptr(),

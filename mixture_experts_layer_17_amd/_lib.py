@@ -71,9 +71,9 @@ SIGNATURES = {
     "moe_layer_forward_ex": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
                                   _p, _p, _p, _p, _sz, _p, _p]),
     "moe_layer_forward_train": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
-                                     _p, _p, _p, _p, _p, _sz, _p, _p]),
+                                     _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_layer_backward": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
-                                _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+                                _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
 }
 
 

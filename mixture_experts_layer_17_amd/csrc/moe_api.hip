@@ -507,7 +507,8 @@ int moe_layer_forward_ex(const void* x, const void* wr, const float* bias, const
 
 int moe_layer_forward_train(const void* x, const void* wr, const float* bias,
                             const void* gate_up, const void* down, int T, int H, int I, int E,
-                            int k, int norm, moe_dtype dt, void* out, float* logits, int32_t* ids,
+                            int k, int norm, moe_dtype dt, const moe_router_config* cfg,
+                            void* out, float* logits, int32_t* ids,
                             float* weights, int32_t* counts, void* saved_gate_up,
                             void* saved_expert_out, void* ws, size_t ws_bytes,
                             hipEvent_t* stage_events, hipStream_t s) {
@@ -516,14 +517,15 @@ int moe_layer_forward_train(const void* x, const void* wr, const float* bias,
   if (T > 0 && (!saved_gate_up || !saved_expert_out || !logits || !ids || !weights))
     return MOE_ERR_NULL;
   if (!aligned16(saved_gate_up) || !aligned16(saved_expert_out)) return MOE_ERR_ALIGN;
-  return layer_forward_impl(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, nullptr, nullptr,
+  return layer_forward_impl(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, cfg, nullptr,
                             out, logits, ids, weights, counts, saved_gate_up, saved_expert_out,
                             ws, ws_bytes, stage_events, s);
 }
 
 int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const void* down,
                        int T, int H, int I, int E, int k, int norm, moe_dtype dt,
-                       const float* logits, const int32_t* ids, const float* weights,
+                       const moe_router_config* cfg, const float* logits, const int32_t* ids,
+                       const float* weights,
                        const void* saved_gate_up, const void* saved_expert_out, const void* dout,
                        void* dx, float* d_router_weight, float* d_router_bias, void* d_gate_up,
                        void* d_down, float* d_weights, void* ws, size_t ws_bytes,
@@ -532,6 +534,14 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
     return MOE_ERR_SHAPE;
   if (dt != MOE_BF16 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  RouterVariant rv;
+  const RouterVariant* var = nullptr;
+  const int vst = router_variant(cfg, E, k, &rv, &var);
+  if (vst != MOE_OK) return vst;
+  const int sigmoid = var ? var->sigmoid : 0;
+  const float scale = var ? var->scale : 1.0f;
+  // dL is zero off the selection for renormalised or sigmoid scores
+  const int sparse = (norm || sigmoid) ? 1 : 0;
   if (T > 0 && (!x || !wr || !gate_up || !down || !logits || !ids || !weights || !saved_gate_up ||
                 !saved_expert_out || !dout || !dx || !d_router_weight || !d_gate_up || !d_down))
     return MOE_ERR_NULL;
@@ -568,8 +578,8 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   // d_weights = <dout, y>, then the softmax / router gradient
   if (e == hipSuccess) e = launch_weight_grad(bf16, dout, saved_expert_out, N, k, H, dw, s);
   if (e == hipSuccess)
-    e = launch_router_grad(logits, ids, weights, dw, w.slot_pos, T, E, k, norm, w.dL, w.dl_perm,
-                           s);
+    e = launch_router_grad(logits, ids, weights, dw, w.slot_pos, T, E, k, norm, sigmoid, scale,
+                           w.dL, w.dl_perm, s);
   mark(1);
   // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot order
   if (e == hipSuccess)
@@ -579,7 +589,7 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   if (e == hipSuccess)
     e = launch_dgrad_gate_up(id, w.dG, gate_up, N, H, I, E, w.sorted_slot, w.dX, w.tiles, s);
   if (e == hipSuccess)
-    e = launch_input_grad(bf16, w.dX, w.dL, norm ? ids : nullptr, wr, T, k, E, H, dx, s);
+    e = launch_input_grad(bf16, w.dX, w.dL, sparse ? ids : nullptr, wr, T, k, E, H, dx, s);
   mark(3);
   // wgrad: d down[e] = (w h)_e^T dout_e, d gate_up[e] = X_e^T dG_e, with
   // the gathered rows laid out expert-major first
@@ -592,7 +602,7 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
     e = launch_wgrad(w.x_perm, H, w.dG, 2 * I, w.zero, w.offsets, E, H, 2 * I, d_gate_up, s);
   mark(5);
   if (e == hipSuccess)
-    e = launch_router_weight_grad(bf16, x, w.x_perm, w.dL, w.dl_perm, w.offsets, T, E, H, norm,
+    e = launch_router_weight_grad(bf16, x, w.x_perm, w.dL, w.dl_perm, w.offsets, T, E, H, sparse,
                                   d_router_weight, d_router_bias, w.rw_part, s);
   mark(6);
   return hip_status(e);

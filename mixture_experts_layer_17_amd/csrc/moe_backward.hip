@@ -8,8 +8,14 @@
 // MindSpore moe.py, MoE.forward and MoE.unpermutation).  With dout the
 // output gradient:
 //   d_weights[t, j] = <dout[t], y[t, j]>
-//   renormalised:   dL[t, ids] = w (d_weights - <d_weights, w>), 0 elsewhere
-//   plain softmax:  dL[t, e]   = p_e (g_e - <g, p>), g = d_weights scattered
+//   softmax scores (s = route_scale * p):
+//     renormalised:  dL[t, ids] = w (d_weights - <d_weights, w>), 0 elsewhere
+//     plain:         dL[t, e]   = p_e (route_scale g_e - <d_weights, w>),
+//                    g = d_weights scattered to the ids
+//   sigmoid scores (MindSpore moe.py, TokenChoiceTopKRouter: s = scale sg(L)):
+//     renormalised:  dL[t, ids] = w (1 - sg) (d_weights - <d_weights, w>)
+//     plain:         dL[t, ids] = d_weights w (1 - sg)
+//   (bias and group limits steer the selection only: no gradient)
 //   dx[t]  = sum_j dX[t k + j] + sum_e dL[t, e] Wr[e]
 //   dWr[e] = sum_t dL[t, e] x[t],   d_bias[e] = sum_t dL[t, e]
 #include "moe_common.h"
@@ -97,6 +103,7 @@ __global__ __launch_bounds__(256) void router_grad_kernel(const float* __restric
                                                           const float* __restrict__ dw,
                                                           const int32_t* __restrict__ slot_pos,
                                                           int T, int E, int k, int norm,
+                                                          int sigmoid, float scale,
                                                           float* __restrict__ dL,
                                                           float* __restrict__ dl_perm) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -108,12 +115,15 @@ __global__ __launch_bounds__(256) void router_grad_kernel(const float* __restric
   // selected experts, renormalised or not)
   float inner = 0.f;
   for (int j = 0; j < k; ++j) inner = fmaf(dw[(size_t)t * k + j], w[(size_t)t * k + j], inner);
-  if (norm) {
+  if (norm || sigmoid) {
+    // nonzero only on the selection
     for (int e = lane; e < E; e += 64) {
       float g = 0.f;
       for (int j = 0; j < k; ++j)
         if (ids[(size_t)t * k + j] == e) {
-          g = w[(size_t)t * k + j] * (dw[(size_t)t * k + j] - inner);
+          const float wj = w[(size_t)t * k + j], dj = dw[(size_t)t * k + j];
+          const float one_m_sg = sigmoid ? __builtin_amdgcn_rcpf(1.0f + __expf(L[e])) : 1.0f;
+          g = norm ? wj * one_m_sg * (dj - inner) : dj * wj * one_m_sg;
           dl_perm[slot_pos[(size_t)t * k + j]] = g;
         }
       out[e] = g;
@@ -132,7 +142,7 @@ __global__ __launch_bounds__(256) void router_grad_kernel(const float* __restric
     for (int j = 0; j < k; ++j)
       if (ids[(size_t)t * k + j] == e) g = dw[(size_t)t * k + j];
     const float p = __expf(L[e] - m) * rz;
-    out[e] = p * (g - inner);
+    out[e] = p * (scale * g - inner);
   }
 }
 
@@ -270,10 +280,11 @@ hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N,
 
 hipError_t launch_router_grad(const float* logits, const int32_t* ids, const float* w,
                               const float* dw, const int32_t* slot_pos, int T, int E, int k,
-                              int norm, float* dL, float* dl_perm, hipStream_t s) {
+                              int norm, int sigmoid, float scale, float* dL, float* dl_perm,
+                              hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  router_grad_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, dw, slot_pos, T, E, k, norm, dL,
-                                                 dl_perm);
+  router_grad_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, dw, slot_pos, T, E, k, norm,
+                                                 sigmoid, scale, dL, dl_perm);
   return hipGetLastError();
 }
 

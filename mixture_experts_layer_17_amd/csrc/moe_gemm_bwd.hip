@@ -532,7 +532,7 @@ hipError_t launch_dgrad_cfg(int id, const void* X, int ldx, const int32_t* x_ind
     MOE_DG(0, 128, 128, 2, 2, 4)
     MOE_DG(1, 64, 128, 2, 2, 4)
     MOE_DG(2, 32, 128, 1, 2, 4)
-    MOE_DG(3, 256, 256, 2, 4, 4)
+    MOE_DG(3, 256, 256, 4, 2, 4)
     MOE_DG(4, 256, 128, 2, 2, 4)
     default: return hipErrorInvalidValue;
   }
@@ -540,7 +540,10 @@ hipError_t launch_dgrad_cfg(int id, const void* X, int ldx, const int32_t* x_ind
 }
 
 // Row-tile classes (the tile list's height) and, within the 256-row class,
-// the 256-column config when the output width allows it.
+// the 256-column config when the output width allows it.  Wave layouts and
+// stage counts were chosen by timing at the prefill shape (4 x 2 waves for
+// the 256 x 256 dgrad, 3 stages for the 256 x 256 wgrad: 5-10 % over the
+// alternatives).
 constexpr int kDgradBM[] = {128, 64, 32, 256};
 
 int dgrad_id(int cls, int n_cols) { return cls == 3 ? (n_cols % 256 == 0 ? 3 : 4) : cls; }
@@ -605,7 +608,7 @@ hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const void* zero_row,
                         const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s) {
   if (M % 256 == 0 && N % 256 == 0)
-    return launch_wgrad_t<256, 256, 2, 4, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
+    return launch_wgrad_t<256, 256, 2, 4, 3>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
                                              (long long)M * N, N, s);
   if (N % 256 == 0)
     return launch_wgrad_t<128, 256, 2, 2, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,

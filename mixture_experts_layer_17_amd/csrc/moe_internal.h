@@ -125,11 +125,13 @@ hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const vo
                         const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s);
 hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N, int k, int H,
                               float* dw, hipStream_t s);
-// dL [T, E]; with norm also dl_perm [N] (dL of each selected entry, in the
-// permutation's expert-major order).
+// dL [T, E] for softmax or sigmoid scores times `scale`; when dL is zero
+// off the selection (renormalised or sigmoid) also dl_perm [N] (dL of each
+// selected entry, in the permutation's expert-major order).
 hipError_t launch_router_grad(const float* logits, const int32_t* ids, const float* w,
                               const float* dw, const int32_t* slot_pos, int T, int E, int k,
-                              int norm, float* dL, float* dl_perm, hipStream_t s);
+                              int norm, int sigmoid, float scale, float* dL, float* dl_perm,
+                              hipStream_t s);
 // With ids (renormalised weights: dL is zero off the selection) only the
 // selected experts' router rows are read; ids == NULL reads all E.
 hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const int32_t* ids,

@@ -52,26 +52,43 @@ def grad_close(gpu, ref, what):
     return err / scale if scale else 0.0
 
 
-def run_backward(moe, wl, seed=0):
+def run_backward(moe, wl, seed=0, router=None):
+    """``router``: a router variant as the oracle's keyword dict (score_func,
+    route_scale, expert_bias, n_groups, n_limited), or None."""
     say(f"backward {wl.name} T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.top_k} "
-        f"norm={wl.norm_topk_prob}")
+        f"norm={wl.norm_topk_prob} router={router}")
     k, norm = wl.top_k, wl.norm_topk_prob
     x, wr, gu, dn = (t.to(DEV) for t in (wl.hidden_states, wl.router_weight, wl.gate_up, wl.down))
     b = wl.router_bias.to(DEV) if wl.router_bias is not None else None
+    cfg = None
+    if router is not None:
+        eb = router.get("expert_bias")
+        cfg = moe.router_config(router["score_func"], router.get("route_scale", 1.0),
+                                torch.as_tensor(eb, dtype=torch.float32, device=DEV)
+                                if eb is not None else None,
+                                router.get("n_groups", 0), router.get("n_limited", 0))
     g = torch.Generator().manual_seed(100 + seed)
     dout = torch.randn(wl.T, wl.H, generator=g).to(wl.dtype)
-    out, saved = moe.layer_forward_train(x, wr, gu, dn, k, norm, router_bias=b)
-    grads = moe.layer_backward(x, wr, gu, dn, k, norm, saved, dout.to(DEV))
+    out, saved = moe.layer_forward_train(x, wr, gu, dn, k, norm, router_bias=b, config=cfg)
+    grads = moe.layer_backward(x, wr, gu, dn, k, norm, saved, dout.to(DEV), config=cfg)
     torch.cuda.synchronize()
     logits = saved["router_logits"].cpu().numpy()
     ids = saved["topk_ids"].cpu().numpy()
     xs, wrs, gus, dns = (_np32(t) for t in (wl.hidden_states, wl.router_weight, wl.gate_up,
                                             wl.down))
     bias = wl.router_bias.numpy() if wl.router_bias is not None else None
-    own = O.moe_layer_forward(xs, wrs, bias, gus, dns, k, norm)
+    own = O.moe_layer_forward(xs, wrs, bias, gus, dns, k, norm, router=router)
     U.assert_close(torch.as_tensor(logits), own["logits"], wl.dtype, "router logits")
-    decided, same = U.routing_check(logits, ids, own["logits"], own["ids"], k)
-    ref = O.moe_layer_backward(xs, wrs, bias, gus, dns, k, norm, _np32(dout), ids=ids)
+    if router is None:
+        decided, same = U.routing_check(logits, ids, own["logits"], own["ids"], k)
+    else:
+        # the variant's selection from the device's own logits (its checks,
+        # decided-token protocol included, are in test_gpu_router_variants)
+        rid, _, _, _ = O.route_variant(logits, k, norm, **router)
+        same = np.all(ids == rid, axis=1)
+        assert same.mean() > 0.99, f"{(~same).sum()} tokens selected differently"
+    ref = O.moe_layer_backward(xs, wrs, bias, gus, dns, k, norm, _np32(dout), ids=ids,
+                               router=router)
     f = ref["forward"]
     # what the training forward kept
     U.assert_close(out.cpu(), f["out"], wl.dtype, "layer output")
@@ -110,6 +127,26 @@ def test_backward_no_renorm_with_bias(moe):
                               norm_topk_prob=False, seed=12,
                               router_bias=workloads.zipf_router_bias(16))
     run_backward(moe, wl)
+
+
+@pytest.mark.parametrize("norm,router", [
+    (True, dict(score_func="sigmoid", route_scale=2.5)),
+    (False, dict(score_func="sigmoid", route_scale=2.5, n_groups=8, n_limited=4)),
+    (False, dict(score_func="softmax", route_scale=1.5)),
+])
+def test_backward_router_variant_small(moe, norm, router):
+    wl = workloads.make_layer("bwd_variant", T=200, H=256, I=128, E=64, top_k=4,
+                              norm_topk_prob=norm, seed=14)
+    r = dict(router)
+    r["expert_bias"] = (np.random.default_rng(3).standard_normal(64) * 0.05).astype(np.float32)
+    run_backward(moe, wl, router=r)
+
+
+def test_backward_router_variant_decode(moe):
+    wl = workloads.make("qwen3_30b_a3b_decode")
+    r = dict(score_func="sigmoid", route_scale=2.5, n_groups=8, n_limited=4,
+             expert_bias=(np.random.default_rng(1).standard_normal(128) * 0.05).astype(np.float32))
+    run_backward(moe, wl, router=r)
 
 
 def test_backward_decode(moe):

@@ -51,7 +51,7 @@ __all__ = [
     "expert_counts", "expert_offsets", "permutation", "gather_rows",
     "silu", "swiglu_expert", "grouped_swiglu", "combine", "unpermute", "feed_forward",
     "moe_layer_forward", "moe_layer_forward_brute", "moe_layer_forward_tokens",
-    "silu_grad", "moe_layer_backward", "routing_weight_jacobian",
+    "silu_grad", "moe_layer_backward", "routing_weight_jacobian", "feed_forward_backward",
     "dispatch_rank_major", "reshuffle_rank_to_expert", "ep_rank_forward",
 ]
 
@@ -477,8 +477,24 @@ def routing_weight_jacobian(logits32, ids, norm_topk_prob: bool, score_func: str
     return (dsel - w[:, :, None] * dsel.sum(axis=1)[:, None, :]) / Z[:, None, None]
 
 
+def feed_forward_backward(x, w1, w2, w3, dout) -> dict:
+    """Gradients of ``sum(dout * feed_forward(x, w1, w2, w3))`` ([HP]
+    ``FeedForward``): with ``a = x w1^T``, ``b = x w3^T``,
+    ``h = silu(a) * b``: ``dh = dout w2``, ``d_w2 = dout^T h``,
+    ``da = dh * b * silu'(a)``, ``db = dh * silu(a)``, ``d_w1 = da^T x``,
+    ``d_w3 = db^T x``, ``dx = da w1 + db w3``.  Float64, nn.Linear layouts."""
+    X, D = _f64(x), _f64(dout)
+    w1, w2, w3 = _f64(w1), _f64(w2), _f64(w3)
+    a, b = X @ w1.T, X @ w3.T
+    h = silu(a) * b
+    dh = D @ w2
+    da = dh * b * silu_grad(a)
+    db = dh * silu(a)
+    return dict(dx=da @ w1 + db @ w3, d_w1=da.T @ X, d_w2=D.T @ h, d_w3=db.T @ X)
+
+
 def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_prob: bool,
-                       dout, ids=None, router=None) -> dict:
+                       dout, ids=None, router=None, shared=None) -> dict:
     """Gradients of ``sum(dout * out)`` for the layer of ``moe_layer_forward``.
 
     The routing decision (which experts) is piecewise constant, so gradients
@@ -501,9 +517,12 @@ def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_p
     ``d_gate_up``, ``d_down``, ``d_weights`` [T, k] and ``d_logits`` [T, E],
     plus the forward's dict under ``forward``.  ``ids`` and ``router`` as in
     ``moe_layer_forward``; with a router variant the logits' gradient is
-    ``sum_j d_weights[t, j] J[t, j, e]`` with ``routing_weight_jacobian``."""
+    ``sum_j d_weights[t, j] J[t, j, e]`` with ``routing_weight_jacobian``.
+    With a shared expert ``shared = (w1, w2, w3)`` (added unweighted, [HP]
+    ``MoE.forward``) its ``feed_forward_backward`` adds to ``dx`` and the
+    result carries ``d_shared = (d_w1, d_w2, d_w3)``."""
     fwd = moe_layer_forward(x, w_router, bias, gate_up, down, top_k, norm_topk_prob, ids=ids,
-                            router=router)
+                            router=router, shared=shared)
     X = _f64(x)
     D = _f64(dout)
     T, H = X.shape
@@ -557,8 +576,14 @@ def moe_layer_backward(x, w_router, bias, gate_up, down, top_k: int, norm_topk_p
     # router
     Wr = _f64(w_router)
     dx += dL @ Wr
+    d_shared = None
+    if shared is not None:
+        sg = feed_forward_backward(X, *shared, D)
+        dx += sg["dx"]
+        d_shared = (sg["d_w1"], sg["d_w2"], sg["d_w3"])
     return dict(dx=dx, d_router_weight=dL.T @ X, d_router_bias=dL.sum(axis=0),
-                d_gate_up=dgu, d_down=ddn, d_weights=d_w, d_logits=dL, forward=fwd)
+                d_gate_up=dgu, d_down=ddn, d_weights=d_w, d_logits=dL, d_shared=d_shared,
+                forward=fwd)
 
 
 # ---------------------------------------------------------------------------

@@ -679,6 +679,49 @@ def pin_backward_variant_jacobian_matches_default():
         assert np.allclose(a["dx"], b["dx"], rtol=1e-12, atol=1e-13)
 
 
+def pin_backward_shared_expert_finite_differences():
+    r = _rng(45)
+    T, H, I, Is, E, k, eps = 4, 5, 3, 4, 4, 2, 1e-3
+    x = r.standard_normal((T, H))
+    wr = r.standard_normal((E, H))
+    gu = r.standard_normal((E, H, 2 * I)) * 0.5
+    dn = r.standard_normal((E, I, H)) * 0.5
+    sh = [t * 1.0 for t in _ffn_weights(r, H, Is)]
+    dout = r.standard_normal((T, H))
+    g = O.moe_layer_backward(x, wr, None, gu, dn, k, True, dout, shared=tuple(sh))
+    ids0 = g["forward"]["ids"]
+
+    def loss(x_, sh_):
+        f = O.moe_layer_forward(x_, wr, None, gu, dn, k, True, shared=tuple(sh_))
+        assert np.array_equal(f["ids"], ids0)
+        return float((f["out"] * dout).sum())
+
+    for w_i in range(3):
+        fd = np.zeros_like(sh[w_i])
+        for idx in np.ndindex(sh[w_i].shape):
+            p_, m_ = [t.copy() for t in sh], [t.copy() for t in sh]
+            p_[w_i][idx] += eps
+            m_[w_i][idx] -= eps
+            fd[idx] = (loss(x, p_) - loss(x, m_)) / (2 * eps)
+        assert np.abs(fd - g["d_shared"][w_i]).max() <= 2e-4 * max(1.0, np.abs(fd).max())
+    fd = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += eps
+        xm[idx] -= eps
+        fd[idx] = (loss(xp, sh) - loss(xm, sh)) / (2 * eps)
+    assert np.abs(fd - g["dx"]).max() <= 2e-4 * max(1.0, np.abs(fd).max())
+    # the shared expert's gradients alone, against scalar loops at H = Is = 1
+    a_, b_, c_, xv, dv = 0.7, -1.2, 0.9, 1.3, -0.4
+    sgm = lambda z: 1.0 / (1.0 + math.exp(-z))  # noqa: E731
+    z = a_ * xv
+    ffb = O.feed_forward_backward([[xv]], [[a_]], [[c_]], [[b_]], [[dv]])
+    dsilu = sgm(z) * (1 + z * (1 - sgm(z)))
+    assert abs(ffb["d_w2"][0, 0] - dv * z * sgm(z) * b_ * xv) < 1e-12
+    assert abs(ffb["d_w1"][0, 0] - dv * c_ * b_ * xv * dsilu * xv) < 1e-12
+    assert abs(ffb["d_w3"][0, 0] - dv * c_ * z * sgm(z) * xv) < 1e-12
+
+
 def pin_backward_scalar_closed_form():
     # H = I = 1, E = 2, k = 1, renormalised: w = 1, so the router gets no
     # gradient, and out = silu(x g) (x u) d

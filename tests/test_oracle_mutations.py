@@ -134,6 +134,12 @@ def _jacobian_without_renorm_coupling(logits32, ids, norm, score_func="softmax",
     return J / Z[:, None, None]
 
 
+def _ffn_backward_swapped_up_gate(x, w1, w2, w3, dout):
+    g = _orig["feed_forward_backward"](x, w1, w2, w3, dout)
+    g["d_w1"], g["d_w3"] = g["d_w3"], g["d_w1"]
+    return g
+
+
 def _backward_unweighted_down_grad(x, w_router, bias, gate_up, down, top_k, norm, dout, **kw):
     # the down-projection gradient taken from dout without the routing weight
     g = _orig["moe_layer_backward"](x, w_router, bias, gate_up, down, top_k, norm, dout, **kw)
@@ -150,7 +156,7 @@ def _backward_unweighted_down_grad(x, w_router, bias, gate_up, down, top_k, norm
 _orig = {n: getattr(O, n) for n in ("routing_weights", "combine", "permutation",
                                      "router_logits", "expert_offsets", "route_variant",
                                      "feed_forward", "moe_layer_backward",
-                                     "routing_weight_jacobian")}
+                                     "routing_weight_jacobian", "feed_forward_backward")}
 
 MUTATIONS = {
     "swiglu_expert": _swapped_gate_up,
@@ -169,6 +175,7 @@ MUTATIONS = {
     "silu_grad": _silu_grad_no_product_rule,
     "moe_layer_backward": _backward_without_router_dx,
     "routing_weight_jacobian": _jacobian_without_renorm_coupling,
+    "feed_forward_backward": _ffn_backward_swapped_up_gate,
 }
 
 

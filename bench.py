@@ -70,7 +70,7 @@ BWD_STAGES = ("routing_grads", "dgrad_down_swiglu", "dgrad_gate_up_dx", "wgrad_d
               "wgrad_gate_up", "router_wgrad")
 
 
-def algorithmic_backward(wl, counts):
+def algorithmic_backward(wl, counts, Is=0):
     """Per-stage algorithmic FLOPs and HBM bytes of one layer backward.
     Weights and weight gradients count once per expert (every expert's
     gradient is written); rows count once per read or write."""
@@ -94,6 +94,13 @@ def algorithmic_backward(wl, counts):
         "wgrad_gate_up": N * 2 * I * es + T * H * es + E * H * 2 * I * es,
         "router_wgrad": T * H * es + T * E * 4 + E * H * 4,
     }
+    if Is:
+        # the shared expert: its dgrads run in the third stage, its wgrads
+        # after the router's weight gradient
+        f["dgrad_gate_up_dx"] += 6.0 * T * H * Is
+        b["dgrad_gate_up_dx"] += 3 * H * Is * es + 3 * T * 2 * Is * es + 2 * T * H * es
+        f["router_wgrad"] += 6.0 * T * H * Is
+        b["router_wgrad"] += 3 * H * Is * es + 3 * T * Is * es + 2 * T * H * es
     return f, b
 
 
@@ -266,6 +273,7 @@ def bench_backward(args, wl):
     import numpy as np
     import torch
 
+    import workloads
     import mixture_experts_layer_17_amd as moe
     from mixture_experts_layer_17_amd import _lib
     dev = torch.device("cuda:0")
@@ -277,18 +285,27 @@ def bench_backward(args, wl):
     bias = wl.router_bias.to(dev) if wl.router_bias is not None else None
     dout_cpu = torch.randn(T, H, generator=torch.Generator().manual_seed(100)).to(wl.dtype)
     dout = dout_cpu.to(dev)
-    _, saved = moe.layer_forward_train(x, wr, gu, dn, k, norm, router_bias=bias)
+    Is = args.shared_I
+    sh = sh_t = None
+    if Is:
+        w1, w2, w3 = workloads.shared_expert_weights(H, Is, wl.dtype)
+        sh_t = (torch.cat([w1.t(), w3.t()], dim=1).contiguous().to(dev),
+                w2.t().contiguous().to(dev))
+        sh = moe.shared_expert(*sh_t)
+    _, saved = moe.layer_forward_train(x, wr, gu, dn, k, norm, router_bias=bias, shared=sh_t)
     g = dict(dx=torch.empty(T, H, dtype=wl.dtype, device=dev),
              dwr=torch.empty(E, H, dtype=torch.float32, device=dev),
              db=torch.empty(E, dtype=torch.float32, device=dev),
              dgu=torch.empty(E, H, 2 * I, dtype=wl.dtype, device=dev),
              ddn=torch.empty(E, I, H, dtype=wl.dtype, device=dev),
-             dw=torch.empty(T, k, dtype=torch.float32, device=dev))
+             dw=torch.empty(T, k, dtype=torch.float32, device=dev),
+             dsgu=torch.empty(H, 2 * Is, dtype=wl.dtype, device=dev) if Is else None,
+             dsdn=torch.empty(Is, H, dtype=wl.dtype, device=dev) if Is else None)
     L = moe.lib
-    nws = L.moe_workspace_size(_lib.MOE_OP_LAYER_BACKWARD, T, H, I, E, k, 0, N, _lib.MOE_BF16)
+    nws = L.moe_workspace_size(_lib.MOE_OP_LAYER_BACKWARD, T, H, I, E, k, Is, N, _lib.MOE_BF16)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     s = torch.cuda.current_stream(dev)
-    P = lambda t: t.data_ptr()  # noqa: E731
+    P = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -302,13 +319,17 @@ def bench_backward(args, wl):
             raise RuntimeError("hipEventCreate failed")
         return ev
 
+    sv = _lib.TrainSaved(P(saved["gate_up_out"]), P(saved["expert_out"]),
+                         P(saved["shared_gate_up_out"]))
+    gr = _lib.LayerGrads(P(g["dx"]), P(g["dwr"]), P(g["db"]), P(g["dgu"]), P(g["ddn"]),
+                         P(g["dw"]), P(g["dsgu"]), P(g["dsdn"]))
+    sh_p = ctypes.addressof(sh) if sh is not None else None
+
     def step(evs=None):
         st = L.moe_layer_backward(P(x), P(wr), P(gu), P(dn), T, H, I, E, k, int(norm),
-                                  _lib.MOE_BF16, None, P(saved["router_logits"]),
-                                  P(saved["topk_ids"]),
-                                  P(saved["topk_weights"]), P(saved["gate_up_out"]),
-                                  P(saved["expert_out"]), P(dout), P(g["dx"]), P(g["dwr"]),
-                                  P(g["db"]), P(g["dgu"]), P(g["ddn"]), P(g["dw"]), P(ws), nws,
+                                  _lib.MOE_BF16, None, sh_p, P(saved["router_logits"]),
+                                  P(saved["topk_ids"]), P(saved["topk_weights"]),
+                                  ctypes.addressof(sv), P(dout), ctypes.addressof(gr), P(ws), nws,
                                   evs, s.cuda_stream)
         if st != 0:
             raise RuntimeError(f"moe_layer_backward failed with status {st}")
@@ -340,7 +361,7 @@ def bench_backward(args, wl):
     for arr in ev_arrays:
         for j in range(nst):
             hip.hipEventDestroy(arr[j])
-    flops, bytes_ = algorithmic_backward(wl, saved["num_tokens_per_expert"].cpu().numpy())
+    flops, bytes_ = algorithmic_backward(wl, saved["num_tokens_per_expert"].cpu().numpy(), Is)
     kern = {}
     for name in BWD_STAGES:
         t_s = per[name] * 1e-3
@@ -372,7 +393,8 @@ def bench_backward(args, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded Gaussian inputs, output gradient and random-init weights",
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "top_k": k,
-                   "norm_topk_prob": norm, "routed_rows": N, "pass": "backward"},
+                   "norm_topk_prob": norm, "routed_rows": N, "pass": "backward",
+                   "shared_I": Is},
         "layer_tflops": round(total_f / (ms_per_step * 1e-3) / 1e12, 2),
         "layer_mfma_frac": round(total_f / (ms_per_step * 1e-3) / PEAK_BF16_FLOPS, 4),
         "roofline": roof,

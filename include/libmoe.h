@@ -365,38 +365,49 @@ int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
  * backward.  The pages train this layer through autograd (Qwen3-Omni issue
  * #115, SpeedupMoeExperts' per-expert training loop and
  * SpeedupMoeSparseMoeBlock's softmax routing weights; MindSpore moe.py,
- * MoE.forward and MoE.unpermutation); the backward is the gradient of
- * sum(dout * out) for the layer without a shared expert, with the default
- * router (softmax, optionally renormalised, optional router_bias) or a
- * router variant (cfg: sigmoid or softmax scores times route_scale; the
- * expert bias and the group limit steer the selection only).  The top-k
- * choice is piecewise constant: gradients flow through the routing
- * weights' values.
- * bf16 only, I a multiple of 128 (else MOE_ERR_UNSUPPORTED).
+ * MoE.forward, MoE.unpermutation and FeedForward); the backward is the
+ * gradient of sum(dout * out) for the layer with the default router
+ * (softmax, optionally renormalised, optional router_bias) or a router
+ * variant (cfg: sigmoid or softmax scores times route_scale; the expert bias
+ * and the group limit steer the selection only), with or without a shared
+ * expert.  The top-k choice is piecewise constant: gradients flow through
+ * the routing weights' values.
+ * bf16 only, I and Is multiples of 128 (else MOE_ERR_UNSUPPORTED).
  *
- * moe_layer_forward_train: moe_layer_forward plus
- *   saved_gate_up    [T*k, 2I] dt: the gate/up pre-activations x.gate_up[e]
- *                    of every routed row, rows in the expert-major order of
- *                    moe_permute (stable in the flat slot index), gate in
- *                    columns [0, I), up in [I, 2I);
- *   saved_expert_out [T*k, H] dt: each slot's expert output, row t*k + j.
+ * moe_layer_forward_train: moe_layer_forward_ex (router variant cfg and
+ * shared expert optional) that also keeps, in the caller's buffers of
+ * moe_train_saved:
+ *   gate_up_out        [T*k, 2I] dt: the gate/up pre-activations x.gate_up[e]
+ *                      of every routed row, rows in the expert-major order of
+ *                      moe_permute (stable in the flat slot index), gate in
+ *                      columns [0, I), up in [I, 2I);
+ *   expert_out         [T*k, H] dt: each slot's expert output, row t*k + j;
+ *   shared_gate_up_out [T, 2Is] dt: the shared expert's pre-activations
+ *                      (only with a shared expert; Is a multiple of 128).
  * router_logits, topk_ids and topk_weights are required (the backward reads
- * them).  cfg: a router variant or NULL (moe_layer_forward_cfg); pass the
- * same cfg to the backward.  Workspace: moe_workspace_size(MOE_OP_LAYER, ...).
+ * them).  Pass the same cfg and shared expert to the backward.  Workspace:
+ * moe_workspace_size(MOE_OP_LAYER, T, H, I, E, top_k, Is, T*top_k, dt).
  */
+typedef struct moe_train_saved {
+  void* gate_up_out;
+  void* expert_out;
+  void* shared_gate_up_out;
+} moe_train_saved;
+
 int moe_layer_forward_train(const void* hidden_states, const void* router_weight,
                             const float* router_bias, const void* gate_up,
                             const void* down, int T, int H, int I, int E, int top_k,
                             int norm_topk_prob, moe_dtype dt, const moe_router_config* cfg,
-                            void* out, float* router_logits, int32_t* topk_ids,
+                            const moe_shared_expert* shared, void* out,
+                            float* router_logits, int32_t* topk_ids,
                             float* topk_weights, int32_t* num_tokens_per_expert,
-                            void* saved_gate_up, void* saved_expert_out,
-                            void* workspace, size_t workspace_bytes,
-                            hipEvent_t* stage_events, hipStream_t stream);
+                            const moe_train_saved* saved, void* workspace,
+                            size_t workspace_bytes, hipEvent_t* stage_events,
+                            hipStream_t stream);
 
 /*
  * moe_layer_backward — from dout [T, H] dt and the training forward's
- * router_logits, topk_ids, topk_weights, saved_gate_up and saved_expert_out:
+ * router_logits, topk_ids, topk_weights and saved activations:
  *   d_topk_weights[t, j] = <dout[t], y[t, j]>            float32 [T, k], or NULL
  *   dL (router logits): the routing weights' Jacobian applied to d_w —
  *       softmax, renormalised:  w (d_w - <d_w, w>) on the selection, else 0
@@ -408,27 +419,40 @@ int moe_layer_forward_train(const void* hidden_states, const void* router_weight
  *     d_down[e]    = h^T dY        [E, I, H] dt   (h = silu(g) * u)
  *     dH = dY down[e]^T;  du = dH silu(g);  dg = dH u silu'(g)
  *     d_gate_up[e] = X^T [dg | du] [E, H, 2I] dt  (experts without rows: 0)
- *   dx = sum_j [dg | du] gate_up[e]^T (per slot) + dL router_weight   [T, H] dt
+ *   shared expert (weight 1 on every token), in its transposed layout:
+ *     d_shared_down [Is, H] dt = h_s^T dout; d_shared_gate_up [H, 2Is] dt
+ *   dx = sum_j [dg | du] gate_up[e]^T (per slot) + dL router_weight
+ *        (+ the shared expert's input gradient)                   [T, H] dt
  *   d_router_weight = dL^T x  [E, H] float32;  d_router_bias = sum_t dL  [E]
  *   float32 or NULL.
  * Every sum is float32 in a fixed order: deterministic.  Weight gradients
  * overwrite their buffers (no accumulation).  Workspace:
- * moe_workspace_size(MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, 0, T*top_k, dt).
+ * moe_workspace_size(MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, Is, T*top_k, dt).
  * stage_events: NULL, or 7 caller-created events recorded before the
  * permutation, before the first dgrad GEMM (after d_topk_weights and dL),
- * before the second dgrad GEMM, before the first wgrad GEMM (after dx),
- * before the second wgrad GEMM, before the router's weight gradient, and at
- * the end (NULL entries are skipped).
+ * before the second dgrad GEMM, before the first wgrad GEMM (after the shared
+ * expert's dgrads and dx), before the second wgrad GEMM, before the router's
+ * weight gradient (then the shared expert's wgrads), and at the end (NULL
+ * entries are skipped).
  */
+typedef struct moe_layer_grads {
+  void* dx;
+  float* d_router_weight;
+  float* d_router_bias;
+  void* d_gate_up;
+  void* d_down;
+  float* d_topk_weights;
+  void* d_shared_gate_up;
+  void* d_shared_down;
+} moe_layer_grads;
+
 int moe_layer_backward(const void* hidden_states, const void* router_weight,
                        const void* gate_up, const void* down, int T, int H, int I, int E,
                        int top_k, int norm_topk_prob, moe_dtype dt,
-                       const moe_router_config* cfg, const float* router_logits,
-                       const int32_t* topk_ids,
-                       const float* topk_weights, const void* saved_gate_up,
-                       const void* saved_expert_out, const void* dout, void* dx,
-                       float* d_router_weight, float* d_router_bias, void* d_gate_up,
-                       void* d_down, float* d_topk_weights, void* workspace,
+                       const moe_router_config* cfg, const moe_shared_expert* shared,
+                       const float* router_logits, const int32_t* topk_ids,
+                       const float* topk_weights, const moe_train_saved* saved,
+                       const void* dout, const moe_layer_grads* grads, void* workspace,
                        size_t workspace_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
 #ifdef __cplusplus

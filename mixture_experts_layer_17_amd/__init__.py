@@ -341,11 +341,13 @@ def layer_forward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.T
 
 def layer_forward_train(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
                         down: torch.Tensor, top_k: int, norm_topk_prob: bool = True,
-                        router_bias: Optional[torch.Tensor] = None, config=None):
+                        router_bias: Optional[torch.Tensor] = None, config=None, shared=None):
     """The layer forward that also keeps what the backward needs.  Returns
     (out, saved) where ``saved`` holds router_logits, topk_ids, topk_weights,
     num_tokens_per_expert, gate_up_out [T*k, 2I] (expert-major
-    pre-activations) and expert_out [T*k, H] (flat slot order)."""
+    pre-activations), expert_out [T*k, H] (flat slot order) and, with a
+    shared expert ``shared = (gate_up [H, 2Is], down [Is, H])``,
+    shared_gate_up_out [T, 2Is]."""
     T, H = x.shape
     E = router_weight.shape[0]
     I = gate_up.shape[2] // 2
@@ -354,32 +356,41 @@ def layer_forward_train(x: torch.Tensor, router_weight: torch.Tensor, gate_up: t
     _chk(gate_up, "gate_up", x.dtype, (E, H, 2 * I))
     _chk(down, "down", x.dtype, (E, I, H))
     _chk(router_bias, "router_bias", torch.float32, (E,))
-    b = LayerBuffers(T, H, I, E, top_k, x.dtype, x.device)
+    sh = shared_expert(*shared) if shared is not None else None
+    Is = sh.intermediate_size if sh is not None else 0
+    b = LayerBuffers(T, H, I, E, top_k, x.dtype, x.device, Is)
     N = T * top_k
     g = torch.empty(N, 2 * I, dtype=x.dtype, device=x.device)
     y = torch.empty(N, H, dtype=x.dtype, device=x.device)
+    gs = torch.empty(T, 2 * Is, dtype=x.dtype, device=x.device) if Is else None
+    sv = _lib.TrainSaved(g.data_ptr(), y.data_ptr(), gs.data_ptr() if gs is not None else None)
     _call("moe_layer_forward_train", x.data_ptr(), router_weight.data_ptr(),
           _chk(router_bias, "router_bias"), gate_up.data_ptr(), down.data_ptr(), T, H, I, E,
-          top_k, int(norm_topk_prob), _dt(x), _cfg_ptr(config), b.out.data_ptr(),
+          top_k, int(norm_topk_prob), _dt(x), _cfg_ptr(config), _cfg_ptr(sh), b.out.data_ptr(),
           b.logits.data_ptr(), b.ids.data_ptr(), b.weights.data_ptr(), b.counts.data_ptr(),
-          g.data_ptr(),
-          y.data_ptr(), b.workspace.data_ptr(), b.ws_bytes, None, _stream(x.device))
+          _cfg_ptr(sv), b.workspace.data_ptr(), b.ws_bytes, None, _stream(x.device))
     saved = dict(router_logits=b.logits, topk_ids=b.ids, topk_weights=b.weights,
-                 num_tokens_per_expert=b.counts, gate_up_out=g, expert_out=y)
+                 num_tokens_per_expert=b.counts, gate_up_out=g, expert_out=y,
+                 shared_gate_up_out=gs)
     return b.out, saved
 
 
 def layer_backward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.Tensor,
                    down: torch.Tensor, top_k: int, norm_topk_prob: bool, saved: dict,
-                   dout: torch.Tensor, with_bias_grad: bool = True, config=None) -> dict:
-    """Gradients of sum(dout * out) given ``saved`` from layer_forward_train:
-    dx, d_router_weight (float32), d_router_bias (float32), d_gate_up,
-    d_down and d_topk_weights (float32)."""
+                   dout: torch.Tensor, with_bias_grad: bool = True, config=None,
+                   shared=None) -> dict:
+    """Gradients of sum(dout * out) given ``saved`` from layer_forward_train
+    (same config and shared expert): dx, d_router_weight (float32),
+    d_router_bias (float32), d_gate_up, d_down, d_topk_weights (float32) and,
+    with a shared expert, d_shared_gate_up [H, 2Is] and d_shared_down
+    [Is, H]."""
     T, H = x.shape
     E = router_weight.shape[0]
     I = gate_up.shape[2] // 2
     dev = x.device
     _chk(dout, "dout", x.dtype, (T, H))
+    sh = shared_expert(*shared) if shared is not None else None
+    Is = sh.intermediate_size if sh is not None else 0
     N = T * top_k
     g = dict(dx=torch.empty(T, H, dtype=x.dtype, device=dev),
              d_router_weight=torch.empty(E, H, dtype=torch.float32, device=dev),
@@ -387,15 +398,20 @@ def layer_backward(x: torch.Tensor, router_weight: torch.Tensor, gate_up: torch.
              else None,
              d_gate_up=torch.empty(E, H, 2 * I, dtype=x.dtype, device=dev),
              d_down=torch.empty(E, I, H, dtype=x.dtype, device=dev),
-             d_topk_weights=torch.empty(T, top_k, dtype=torch.float32, device=dev))
-    nb = lib.moe_workspace_size(_lib.MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, 0, N, _dt(x))
+             d_topk_weights=torch.empty(T, top_k, dtype=torch.float32, device=dev),
+             d_shared_gate_up=torch.empty(H, 2 * Is, dtype=x.dtype, device=dev) if Is else None,
+             d_shared_down=torch.empty(Is, H, dtype=x.dtype, device=dev) if Is else None)
+    P = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    gr = _lib.LayerGrads(P(g["dx"]), P(g["d_router_weight"]), P(g["d_router_bias"]),
+                         P(g["d_gate_up"]), P(g["d_down"]), P(g["d_topk_weights"]),
+                         P(g["d_shared_gate_up"]), P(g["d_shared_down"]))
+    sv = _lib.TrainSaved(P(saved["gate_up_out"]), P(saved["expert_out"]),
+                         P(saved.get("shared_gate_up_out")))
+    nb = lib.moe_workspace_size(_lib.MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, Is, N, _dt(x))
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     _call("moe_layer_backward", x.data_ptr(), router_weight.data_ptr(), gate_up.data_ptr(),
           down.data_ptr(), T, H, I, E, top_k, int(norm_topk_prob), _dt(x), _cfg_ptr(config),
-          saved["router_logits"].data_ptr(), saved["topk_ids"].data_ptr(),
-          saved["topk_weights"].data_ptr(), saved["gate_up_out"].data_ptr(),
-          saved["expert_out"].data_ptr(), dout.data_ptr(), g["dx"].data_ptr(),
-          g["d_router_weight"].data_ptr(), _chk(g["d_router_bias"], "d_router_bias"),
-          g["d_gate_up"].data_ptr(), g["d_down"].data_ptr(), g["d_topk_weights"].data_ptr(),
+          _cfg_ptr(sh), saved["router_logits"].data_ptr(), saved["topk_ids"].data_ptr(),
+          saved["topk_weights"].data_ptr(), _cfg_ptr(sv), dout.data_ptr(), _cfg_ptr(gr),
           ws.data_ptr(), nb, None, _stream(dev))
     return g

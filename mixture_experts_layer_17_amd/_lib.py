@@ -42,6 +42,20 @@ class SharedExpert(ctypes.Structure):
                 ("intermediate_size", ctypes.c_int)]
 
 
+class TrainSaved(ctypes.Structure):
+    """struct moe_train_saved (include/libmoe.h)."""
+    _fields_ = [("gate_up_out", ctypes.c_void_p), ("expert_out", ctypes.c_void_p),
+                ("shared_gate_up_out", ctypes.c_void_p)]
+
+
+class LayerGrads(ctypes.Structure):
+    """struct moe_layer_grads (include/libmoe.h)."""
+    _fields_ = [("dx", ctypes.c_void_p), ("d_router_weight", ctypes.c_void_p),
+                ("d_router_bias", ctypes.c_void_p), ("d_gate_up", ctypes.c_void_p),
+                ("d_down", ctypes.c_void_p), ("d_topk_weights", ctypes.c_void_p),
+                ("d_shared_gate_up", ctypes.c_void_p), ("d_shared_down", ctypes.c_void_p)]
+
+
 class RouterConfig(ctypes.Structure):
     """struct moe_router_config (include/libmoe.h)."""
     _fields_ = [("score_func", ctypes.c_int), ("route_scale", ctypes.c_float),
@@ -73,7 +87,7 @@ SIGNATURES = {
     "moe_layer_forward_train": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
                                      _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_layer_backward": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
-                                _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+                                _p, _p, _p, _p, _sz, _p, _p]),
 }
 
 

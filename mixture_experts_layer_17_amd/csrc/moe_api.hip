@@ -160,10 +160,12 @@ struct BwdWs {
   void *perm, *tiles, *tiles1;
   float *dw, *dL, *dl_perm;
   void *dG, *hw, *dX, *x_perm, *dout_perm, *zero, *rw_part;
+  void *dG_s, *hw_s, *dx_s, *tiles_s, *tiles_s1;   // shared expert (Is > 0)
+  int32_t* offs_s;
   size_t zero_bytes, total;
 };
 
-BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
+BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt, int Is = 0) {
   BwdWs w{};
   const size_t N = (size_t)T * k;
   size_t off = 0;
@@ -189,7 +191,15 @@ BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt) {
   w.dX = take(N * (size_t)H * esize(dt));
   w.x_perm = take(N * (size_t)H * esize(dt));
   w.dout_perm = take(N * (size_t)H * esize(dt));
-  w.zero_bytes = al((size_t)std::max(H, 2 * I) * esize(dt));
+  if (Is > 0) {
+    w.dG_s = take((size_t)T * 2 * Is * esize(dt));
+    w.hw_s = take((size_t)T * Is * esize(dt));
+    w.dx_s = take((size_t)T * H * esize(dt));
+    w.tiles_s = take(tile_list_bytes(T, 1, dgrad_bm(pick_dgrad_cfg(T, 1))));
+    w.tiles_s1 = take(tile_list_bytes(T, 1, dgrad_bm(pick_dgrad1_cfg(T, 1))));
+    w.offs_s = (int32_t*)take(2 * sizeof(int32_t));
+  }
+  w.zero_bytes = al((size_t)std::max(std::max(H, 2 * I), 2 * Is) * esize(dt));
   w.zero = take(w.zero_bytes);
   w.total = off;
   return w;
@@ -246,10 +256,11 @@ size_t moe_workspace_size(int op, int T, int H, int I, int E, int top_k, int R, 
         return bad;
       return layer_ws(nullptr, T, H, I, E, top_k, dt, R).total;
     case MOE_OP_LAYER_BACKWARD:
+      // R: the shared expert's intermediate size (0: none)
       if (check_dims(H, I, E, top_k) != MOE_OK || I == 0 || T < 0 ||
-          !rows_ok((long long)T * top_k))
+          !rows_ok((long long)T * top_k) || R < 0 || R % 64 != 0)
         return bad;
-      return bwd_ws(nullptr, T, H, I, E, top_k, dt).total;
+      return bwd_ws(nullptr, T, H, I, E, top_k, dt, R).total;
     case MOE_OP_SHARED:
       if (check_dims(H, I, 1, 1) != MOE_OK || I == 0 || T < 0 || !rows_ok(T)) return bad;
       return shared_ws(nullptr, T, H, I, dt, false).total;
@@ -412,8 +423,9 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
                        const void* down, int T, int H, int I, int E, int k, int norm,
                        moe_dtype dt, const moe_router_config* cfg,
                        const moe_shared_expert* shared, void* out, float* logits, int32_t* ids,
-                       float* weights, int32_t* counts, void* g_save, void* y_out, void* ws,
-                       size_t ws_bytes, hipEvent_t* stage_events, hipStream_t s) {
+                       float* weights, int32_t* counts, void* g_save, void* y_out,
+                       void* g_save_shared, void* ws, size_t ws_bytes,
+                       hipEvent_t* stage_events, hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
     return MOE_ERR_SHAPE;
@@ -431,13 +443,20 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
   if (shared && (!aligned16(shared->gate_up) || !aligned16(shared->down))) return MOE_ERR_ALIGN;
   const size_t need = layer_ws(nullptr, T, H, I, E, k, dt, Is).total;
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const bool bf16 = dt == MOE_BF16;
+  const int N = T * k;
+  const GemmTileCfg cu = pick_gate_up_cfg(bf16, N, H, I, E);
+  const GemmTileCfg cd = pick_down_cfg(bf16, N, H, I, E);
+  // the shared expert runs inside the grouped launches when both are LDS
+  // configs and its widths fit their tiles
+  const bool fusable = shared && T > 0 && lds_cfg_id(cu.id) && lds_cfg_id(cd.id) &&
+                       Is % (cu.BN / 2) == 0 && H % cd.BN == 0;
+  if (g_save_shared && shared && T > 0 && !fusable) return MOE_ERR_UNSUPPORTED;
   LayerWs w = layer_ws((char*)ws, T, H, I, E, k, dt, Is);
   if (!ids) ids = w.ids;
   if (!weights) weights = w.weights;
   if (!counts) counts = w.counts;
   if (!logits) logits = w.logits;
-  const bool bf16 = dt == MOE_BF16;
-  const int N = T * k;
   auto mark = [&](int i) {
     if (stage_events && stage_events[i]) (void)hipEventRecord(stage_events[i], s);
   };
@@ -447,8 +466,6 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
       launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr, s, var);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(1);
-  const GemmTileCfg cu = pick_gate_up_cfg(bf16, N, H, I, E);
-  const GemmTileCfg cd = pick_down_cfg(bf16, N, H, I, E);
   // the permutation's scan pass also writes both GEMMs' tile lists
   e = launch_permute_topk(ids, T, k, E, counts, w.offsets, w.sorted_token, w.sorted_slot,
                           w.slot_pos, w.perm, s, w.tiles_up, cu.BM, w.tiles_down, cd.BM);
@@ -460,8 +477,9 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
   // share the machine with the experts' instead of running on their own.
   DenseAux aux_up{}, aux_down{};
   bool fused = false;
-  if (shared && T > 0 && lds_cfg_id(cu.id) && lds_cfg_id(cd.id)) {
+  if (fusable) {
     aux_up = dense_aux(cu, true, x, H, shared->gate_up, 2 * Is, H, Is, w.h_s, Is, T, Is);
+    aux_up.g_save = g_save_shared;
     aux_down = dense_aux(cd, false, w.h_s, Is, shared->down, H, Is, 0, w.y_s, H, T, H);
     fused = aux_up.jobs > 0 && aux_down.jobs > 0;
   }
@@ -501,39 +519,46 @@ int moe_layer_forward_ex(const void* x, const void* wr, const float* bias, const
                          float* weights, int32_t* counts, void* ws, size_t ws_bytes,
                          hipEvent_t* stage_events, hipStream_t s) {
   return layer_forward_impl(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, cfg, shared, out,
-                            logits, ids, weights, counts, nullptr, nullptr, ws, ws_bytes,
+                            logits, ids, weights, counts, nullptr, nullptr, nullptr, ws, ws_bytes,
                             stage_events, s);
 }
 
 int moe_layer_forward_train(const void* x, const void* wr, const float* bias,
                             const void* gate_up, const void* down, int T, int H, int I, int E,
                             int k, int norm, moe_dtype dt, const moe_router_config* cfg,
-                            void* out, float* logits, int32_t* ids,
-                            float* weights, int32_t* counts, void* saved_gate_up,
-                            void* saved_expert_out, void* ws, size_t ws_bytes,
+                            const moe_shared_expert* shared, void* out, float* logits,
+                            int32_t* ids, float* weights, int32_t* counts,
+                            const moe_train_saved* saved, void* ws, size_t ws_bytes,
                             hipEvent_t* stage_events, hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (dt != MOE_BF16 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if (T > 0 && (!saved_gate_up || !saved_expert_out || !logits || !ids || !weights))
+  if (shared && shared->intermediate_size % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!saved) return MOE_ERR_NULL;
+  if (T > 0 && (!saved->gate_up_out || !saved->expert_out || !logits || !ids || !weights))
     return MOE_ERR_NULL;
-  if (!aligned16(saved_gate_up) || !aligned16(saved_expert_out)) return MOE_ERR_ALIGN;
-  return layer_forward_impl(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, cfg, nullptr,
-                            out, logits, ids, weights, counts, saved_gate_up, saved_expert_out,
-                            ws, ws_bytes, stage_events, s);
+  if (T > 0 && shared && !saved->shared_gate_up_out) return MOE_ERR_NULL;
+  if (!aligned16(saved->gate_up_out) || !aligned16(saved->expert_out) ||
+      !aligned16(saved->shared_gate_up_out))
+    return MOE_ERR_ALIGN;
+  return layer_forward_impl(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, cfg, shared,
+                            out, logits, ids, weights, counts, saved->gate_up_out,
+                            saved->expert_out, shared ? saved->shared_gate_up_out : nullptr, ws,
+                            ws_bytes, stage_events, s);
 }
 
 int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const void* down,
                        int T, int H, int I, int E, int k, int norm, moe_dtype dt,
-                       const moe_router_config* cfg, const float* logits, const int32_t* ids,
-                       const float* weights,
-                       const void* saved_gate_up, const void* saved_expert_out, const void* dout,
-                       void* dx, float* d_router_weight, float* d_router_bias, void* d_gate_up,
-                       void* d_down, float* d_weights, void* ws, size_t ws_bytes,
+                       const moe_router_config* cfg, const moe_shared_expert* shared,
+                       const float* logits, const int32_t* ids, const float* weights,
+                       const moe_train_saved* saved, const void* dout,
+                       const moe_layer_grads* grads, void* ws, size_t ws_bytes,
                        hipEvent_t* stage_events, hipStream_t s) {
   if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
   if (check_dims(H, I, E, k) != MOE_OK || I == 0 || T < 0 || !rows_ok((long long)T * k))
     return MOE_ERR_SHAPE;
   if (dt != MOE_BF16 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const int Is = shared ? shared->intermediate_size : 0;
+  if (shared && (Is <= 0 || Is % 128 != 0)) return MOE_ERR_UNSUPPORTED;
   RouterVariant rv;
   const RouterVariant* var = nullptr;
   const int vst = router_variant(cfg, E, k, &rv, &var);
@@ -542,22 +567,34 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   const float scale = var ? var->scale : 1.0f;
   // dL is zero off the selection for renormalised or sigmoid scores
   const int sparse = (norm || sigmoid) ? 1 : 0;
-  if (T > 0 && (!x || !wr || !gate_up || !down || !logits || !ids || !weights || !saved_gate_up ||
-                !saved_expert_out || !dout || !dx || !d_router_weight || !d_gate_up || !d_down))
+  if (!saved || !grads) return MOE_ERR_NULL;
+  const moe_layer_grads& g = *grads;
+  if (T > 0 && (!x || !wr || !gate_up || !down || !logits || !ids || !weights ||
+                !saved->gate_up_out || !saved->expert_out || !dout || !g.dx ||
+                !g.d_router_weight || !g.d_gate_up || !g.d_down))
+    return MOE_ERR_NULL;
+  if (T > 0 && shared && (!shared->gate_up || !shared->down || !saved->shared_gate_up_out ||
+                          !g.d_shared_gate_up || !g.d_shared_down))
     return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(wr) || !aligned16(gate_up) || !aligned16(down) ||
-      !aligned16(saved_gate_up) || !aligned16(saved_expert_out) || !aligned16(dout) ||
-      !aligned16(dx) || !aligned16(d_router_weight) || !aligned16(d_gate_up) ||
-      !aligned16(d_down))
+      !aligned16(saved->gate_up_out) || !aligned16(saved->expert_out) || !aligned16(dout) ||
+      !aligned16(g.dx) || !aligned16(g.d_router_weight) || !aligned16(g.d_gate_up) ||
+      !aligned16(g.d_down))
     return MOE_ERR_ALIGN;
-  const size_t need = bwd_ws(nullptr, T, H, I, E, k, dt).total;
+  if (shared && (!aligned16(shared->gate_up) || !aligned16(shared->down) ||
+                 !aligned16(saved->shared_gate_up_out) || !aligned16(g.d_shared_gate_up) ||
+                 !aligned16(g.d_shared_down)))
+    return MOE_ERR_ALIGN;
+  const size_t need = bwd_ws(nullptr, T, H, I, E, k, dt, Is).total;
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  const BwdWs w = bwd_ws((char*)ws, T, H, I, E, k, dt);
+  const BwdWs w = bwd_ws((char*)ws, T, H, I, E, k, dt, Is);
   const bool bf16 = true;
   const int N = T * k;
-  float* dw = d_weights ? d_weights : w.dw;
+  float* dw = g.d_topk_weights ? g.d_topk_weights : w.dw;
   const int id = pick_dgrad_cfg(N, E);
   const int id1 = pick_dgrad1_cfg(N, E);
+  const int sid = pick_dgrad_cfg(T, 1);
+  const int sid1 = pick_dgrad1_cfg(T, 1);
   auto mark = [&](int i) {
     if (stage_events && stage_events[i]) (void)hipEventRecord(stage_events[i], s);
   };
@@ -568,42 +605,68 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (T == 0) {
     // no tokens: every weight gradient is zero
-    e = launch_fill_u32(d_router_weight, (long long)E * H, 0u, s);
-    if (e == hipSuccess && d_router_bias) e = launch_fill_u32(d_router_bias, E, 0u, s);
-    if (e == hipSuccess) e = launch_fill_u32(d_gate_up, (long long)E * H * I, 0u, s);
-    if (e == hipSuccess) e = launch_fill_u32(d_down, (long long)E * I * H / 2, 0u, s);
+    e = launch_fill_u32(g.d_router_weight, (long long)E * H, 0u, s);
+    if (e == hipSuccess && g.d_router_bias) e = launch_fill_u32(g.d_router_bias, E, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(g.d_gate_up, (long long)E * H * I, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(g.d_down, (long long)E * I * H / 2, 0u, s);
+    if (e == hipSuccess && shared)
+      e = launch_fill_u32(g.d_shared_gate_up, (long long)H * Is, 0u, s);
+    if (e == hipSuccess && shared)
+      e = launch_fill_u32(g.d_shared_down, (long long)Is * H / 2, 0u, s);
     return hip_status(e);
   }
   e = launch_fill_u32(w.zero, (long long)(w.zero_bytes / 4), 0u, s);
+  if (e == hipSuccess && shared) {
+    // the shared expert is one dense group of the T token rows
+    e = launch_build_tiles(nullptr, 1, T, dgrad_bm(sid), w.tiles_s, s);
+    if (e == hipSuccess) e = launch_build_tiles(nullptr, 1, T, dgrad_bm(sid1), w.tiles_s1, s);
+    if (e == hipSuccess) e = launch_fill_u32(w.offs_s, 1, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(w.offs_s + 1, 1, (uint32_t)T, s);
+  }
   // d_weights = <dout, y>, then the softmax / router gradient
-  if (e == hipSuccess) e = launch_weight_grad(bf16, dout, saved_expert_out, N, k, H, dw, s);
+  if (e == hipSuccess) e = launch_weight_grad(bf16, dout, saved->expert_out, N, k, H, dw, s);
   if (e == hipSuccess)
     e = launch_router_grad(logits, ids, weights, dw, w.slot_pos, T, E, k, norm, sigmoid, scale,
                            w.dL, w.dl_perm, s);
   mark(1);
   // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot order
   if (e == hipSuccess)
-    e = launch_dgrad_down_swiglu(id1, dout, T, w.sorted_token, down, N, H, I, E, saved_gate_up,
-                                 weights, w.sorted_slot, w.dG, w.hw, w.tiles1, s);
+    e = launch_dgrad_down_swiglu(id1, dout, T, w.sorted_token, down, N, H, I, E,
+                                 saved->gate_up_out, weights, w.sorted_slot, w.dG, w.hw, w.tiles1,
+                                 s);
   mark(2);
   if (e == hipSuccess)
     e = launch_dgrad_gate_up(id, w.dG, gate_up, N, H, I, E, w.sorted_slot, w.dX, w.tiles, s);
+  // the shared expert (weight 1 on every token): its dgrads into dx_s
+  if (e == hipSuccess && shared)
+    e = launch_dgrad_down_swiglu(sid1, dout, T, nullptr, shared->down, T, H, Is, 1,
+                                 saved->shared_gate_up_out, nullptr, nullptr, w.dG_s, w.hw_s,
+                                 w.tiles_s1, s);
+  if (e == hipSuccess && shared)
+    e = launch_dgrad_gate_up(sid, w.dG_s, shared->gate_up, T, H, Is, 1, nullptr, w.dx_s,
+                             w.tiles_s, s);
   if (e == hipSuccess)
-    e = launch_input_grad(bf16, w.dX, w.dL, sparse ? ids : nullptr, wr, T, k, E, H, dx, s);
+    e = launch_input_grad(bf16, w.dX, w.dL, sparse ? ids : nullptr, wr, T, k, E, H,
+                          shared ? w.dx_s : nullptr, g.dx, s);
   mark(3);
   // wgrad: d down[e] = (w h)_e^T dout_e, d gate_up[e] = X_e^T dG_e, with
   // the gathered rows laid out expert-major first
   if (e == hipSuccess) e = launch_gather_rows(bf16, dout, T, w.sorted_token, N, H, w.dout_perm, s);
   if (e == hipSuccess) e = launch_gather_rows(bf16, x, T, w.sorted_token, N, H, w.x_perm, s);
   if (e == hipSuccess)
-    e = launch_wgrad(w.hw, I, w.dout_perm, H, w.zero, w.offsets, E, I, H, d_down, s);
+    e = launch_wgrad(w.hw, I, w.dout_perm, H, w.zero, w.offsets, E, I, H, g.d_down, s);
   mark(4);
   if (e == hipSuccess)
-    e = launch_wgrad(w.x_perm, H, w.dG, 2 * I, w.zero, w.offsets, E, H, 2 * I, d_gate_up, s);
+    e = launch_wgrad(w.x_perm, H, w.dG, 2 * I, w.zero, w.offsets, E, H, 2 * I, g.d_gate_up, s);
   mark(5);
   if (e == hipSuccess)
     e = launch_router_weight_grad(bf16, x, w.x_perm, w.dL, w.dl_perm, w.offsets, T, E, H, sparse,
-                                  d_router_weight, d_router_bias, w.rw_part, s);
+                                  g.d_router_weight, g.d_router_bias, w.rw_part, s);
+  // the shared expert's weight gradients: h^T dout and x^T dG_s
+  if (e == hipSuccess && shared)
+    e = launch_wgrad(w.hw_s, Is, dout, H, w.zero, w.offs_s, 1, Is, H, g.d_shared_down, s);
+  if (e == hipSuccess && shared)
+    e = launch_wgrad(x, H, w.dG_s, 2 * Is, w.zero, w.offs_s, 1, H, 2 * Is, g.d_shared_gate_up, s);
   mark(6);
   return hip_status(e);
 }

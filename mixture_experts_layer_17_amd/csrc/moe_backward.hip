@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
                                                          const float* __restrict__ dL,
                                                          const int32_t* __restrict__ ids,
                                                          const T* __restrict__ wr, int T_, int k,
-                                                         int E, int H, T* __restrict__ dx) {
+                                                         int E, int H, const T* __restrict__ add,
+                                                         T* __restrict__ dx) {
   const int per_row = H / 8;
   const long long total = (long long)T_ * per_row;
   for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total;
@@ -185,6 +186,12 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
       }
+    }
+    if (add) {
+      float v[8];
+      load8(add + (size_t)t * H + c, v);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[x] += v[x];
     }
     store8(dx + (size_t)t * H + c, acc);
   }
@@ -289,15 +296,16 @@ hipError_t launch_router_grad(const float* logits, const int32_t* ids, const flo
 }
 
 hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const int32_t* ids,
-                             const void* wr, int T, int k, int E, int H, void* dx, hipStream_t s) {
+                             const void* wr, int T, int k, int E, int H, const void* add,
+                             void* dx, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int grid = grid_for_total((long long)T * (H / 8));
   if (bf16)
     input_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)dX, dL, ids, (const bf16_t*)wr,
-                                                   T, k, E, H, (bf16_t*)dx);
+                                                   T, k, E, H, (const bf16_t*)add, (bf16_t*)dx);
   else
     input_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)dX, dL, ids, (const float*)wr, T,
-                                                  k, E, H, (float*)dx);
+                                                  k, E, H, (const float*)add, (float*)dx);
   return hipGetLastError();
 }
 

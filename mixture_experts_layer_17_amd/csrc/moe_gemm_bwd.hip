@@ -293,7 +293,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
         if (m < rows) {
           const int p = row0 + m;
           const int n = n0 + wn * G::CW + 4 * (lane % LPR);
-          const float wt = sb.w[sb.slot[p]];
+          const float wt = sb.w ? sb.w[sb.slot ? sb.slot[p] : p] : 1.0f;
           const uint2 g2 = *reinterpret_cast<const uint2*>(sb.G + (long long)p * sb.ldg + n);
           const uint2 u2 = *reinterpret_cast<const uint2*>(sb.G + (long long)p * sb.ldg + sb.up_off + n);
           const float zz[4] = {z.x, z.y, z.z, z.w};

@@ -457,7 +457,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
       if constexpr (SWIGLU) {
         // training forward: also keep the pre-activations, gate at column n
         // and up at column up_off + n of the [rows, 2 up_off] buffer
-        if (g_save && !dense) {
+        bf16_t* const gs = dense ? (bf16_t*)aux.g_save : g_save;
+        if (gs) {
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
                   *reinterpret_cast<const uint2*>(stg + r * OBP + 16 * (lane % LPR) + 8);
               const int dst = dsts[i][rr];
               if (dst >= 0 && dst < c_rows)
-                *reinterpret_cast<u32x4*>(g_save + (long long)dst * (2 * up_off) + half * up_off +
+                *reinterpret_cast<u32x4*>(gs + (long long)dst * (2 * up_off) + half * up_off +
                                           n0 + wn * G::CW + 8 * (lane % LPR)) =
                     u32x4{lo.x, lo.y, hi.x, hi.y};
             }
@@ -582,7 +583,7 @@ GemmTileCfg pick_lds_dense_cfg(int rows, int cols, bool swiglu) {
 
 DenseAux dense_aux(const GemmTileCfg& c, bool swiglu, const void* X, int ldx, const void* W,
                    int ldw, int K, int up_off, void* C, int ldc, int rows, int cols) {
-  DenseAux a{X, W, C, ldx, ldw, K, up_off, ldc, rows, 0, 0};
+  DenseAux a{X, W, C, ldx, ldw, K, up_off, ldc, rows, 0, 0, nullptr};
   const int per_tile = swiglu ? c.BN / 2 : c.BN;   // output columns per job
   if (rows <= 0 || cols % per_tile != 0) return a;
   a.n_ntiles = cols / per_tile;
@@ -602,7 +603,7 @@ hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int
     const hipError_t err = launch_build_tiles(offsets, E, N, c.BM, tile_ws, s);
     if (err != hipSuccess) return err;
   }
-  const DenseAux none{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
+  const DenseAux none{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, nullptr};
   const DenseAux& a = aux ? *aux : none;
   // one work-group slot per job of each XCD's two shares (the grouped tile
   // count on the device never exceeds max_tiles)

@@ -71,6 +71,7 @@ struct DenseAux {
   const void* W;
   void* C;
   int ldx, ldw, K, up_off, ldc, rows, n_ntiles, jobs;
+  void* g_save;   // training forward: the dense problem's pre-activations, or NULL
 };
 DenseAux dense_aux(const GemmTileCfg& c, bool swiglu, const void* X, int ldx, const void* W,
                    int ldw, int K, int up_off, void* C, int ldc, int rows, int cols);
@@ -113,6 +114,8 @@ hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h,
 int pick_dgrad_cfg(int N, int E);
 int pick_dgrad1_cfg(int N, int E);
 int dgrad_bm(int id);
+// w == NULL: every row's weight is 1 (a shared expert); sorted_slot NULL:
+// row p's weight is w[p].
 hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
                                     const void* down, int N, int H, int I, int E,
                                     const void* G, const float* w, const int32_t* sorted_slot,
@@ -134,8 +137,10 @@ hipError_t launch_router_grad(const float* logits, const int32_t* ids, const flo
                               hipStream_t s);
 // With ids (renormalised weights: dL is zero off the selection) only the
 // selected experts' router rows are read; ids == NULL reads all E.
+// add (optional, [T, H]) joins the sum (the shared expert's input gradient).
 hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const int32_t* ids,
-                             const void* wr, int T, int k, int E, int H, void* dx, hipStream_t s);
+                             const void* wr, int T, int k, int E, int H, const void* add,
+                             void* dx, hipStream_t s);
 // Router weight and bias gradients; ws holds router_weight_grad_ws(E, H)
 // bytes of partial sums.  sparse: rows from x_perm / dl_perm (expert-major).
 size_t router_weight_grad_ws(int E, int H);

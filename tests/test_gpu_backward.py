@@ -52,9 +52,14 @@ def grad_close(gpu, ref, what):
     return err / scale if scale else 0.0
 
 
-def run_backward(moe, wl, seed=0, router=None):
+def _shared_layout(w1, w2, w3):
+    return torch.cat([w1.t(), w3.t()], dim=1).contiguous(), w2.t().contiguous()
+
+
+def run_backward(moe, wl, seed=0, router=None, shared=None):
     """``router``: a router variant as the oracle's keyword dict (score_func,
-    route_scale, expert_bias, n_groups, n_limited), or None."""
+    route_scale, expert_bias, n_groups, n_limited), or None.  ``shared``:
+    FeedForward weights (w1, w2, w3) in nn.Linear layout, or None."""
     say(f"backward {wl.name} T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.top_k} "
         f"norm={wl.norm_topk_prob} router={router}")
     k, norm = wl.top_k, wl.norm_topk_prob
@@ -69,15 +74,18 @@ def run_backward(moe, wl, seed=0, router=None):
                                 router.get("n_groups", 0), router.get("n_limited", 0))
     g = torch.Generator().manual_seed(100 + seed)
     dout = torch.randn(wl.T, wl.H, generator=g).to(wl.dtype)
-    out, saved = moe.layer_forward_train(x, wr, gu, dn, k, norm, router_bias=b, config=cfg)
-    grads = moe.layer_backward(x, wr, gu, dn, k, norm, saved, dout.to(DEV), config=cfg)
+    sh = tuple(t.to(DEV) for t in _shared_layout(*shared)) if shared is not None else None
+    out, saved = moe.layer_forward_train(x, wr, gu, dn, k, norm, router_bias=b, config=cfg,
+                                         shared=sh)
+    grads = moe.layer_backward(x, wr, gu, dn, k, norm, saved, dout.to(DEV), config=cfg, shared=sh)
     torch.cuda.synchronize()
     logits = saved["router_logits"].cpu().numpy()
     ids = saved["topk_ids"].cpu().numpy()
     xs, wrs, gus, dns = (_np32(t) for t in (wl.hidden_states, wl.router_weight, wl.gate_up,
                                             wl.down))
     bias = wl.router_bias.numpy() if wl.router_bias is not None else None
-    own = O.moe_layer_forward(xs, wrs, bias, gus, dns, k, norm, router=router)
+    sh_np = tuple(_np32(t) for t in shared) if shared is not None else None
+    own = O.moe_layer_forward(xs, wrs, bias, gus, dns, k, norm, router=router, shared=sh_np)
     U.assert_close(torch.as_tensor(logits), own["logits"], wl.dtype, "router logits")
     if router is None:
         decided, same = U.routing_check(logits, ids, own["logits"], own["ids"], k)
@@ -88,7 +96,7 @@ def run_backward(moe, wl, seed=0, router=None):
         same = np.all(ids == rid, axis=1)
         assert same.mean() > 0.99, f"{(~same).sum()} tokens selected differently"
     ref = O.moe_layer_backward(xs, wrs, bias, gus, dns, k, norm, _np32(dout), ids=ids,
-                               router=router)
+                               router=router, shared=sh_np)
     f = ref["forward"]
     # what the training forward kept
     U.assert_close(out.cpu(), f["out"], wl.dtype, "layer output")
@@ -102,6 +110,16 @@ def run_backward(moe, wl, seed=0, router=None):
                  "d_gate_up"):
         refn = ref["d_weights"] if name == "d_topk_weights" else ref[name]
         rel[name] = grad_close(_np32(grads[name]), refn, name)
+    if shared is not None:
+        w1, w2, w3 = sh_np
+        U.assert_close(saved["shared_gate_up_out"].cpu(),
+                       np.concatenate([xs @ w1.T, xs @ w3.T], axis=1), wl.dtype,
+                       "saved shared pre-activations")
+        d1, d2, d3 = ref["d_shared"]
+        rel["d_shared_gate_up"] = grad_close(_np32(grads["d_shared_gate_up"]),
+                                             np.concatenate([d1.T, d3.T], axis=1),
+                                             "d_shared_gate_up")
+        rel["d_shared_down"] = grad_close(_np32(grads["d_shared_down"]), d2.T, "d_shared_down")
     print("  routed as the oracle: %d/%d; relative errors %s" % (
         same.sum(), wl.T, {k_: f"{v:.1e}" for k_, v in rel.items()}), flush=True)
     return grads, ref
@@ -147,6 +165,17 @@ def test_backward_router_variant_decode(moe):
     r = dict(score_func="sigmoid", route_scale=2.5, n_groups=8, n_limited=4,
              expert_bias=(np.random.default_rng(1).standard_normal(128) * 0.05).astype(np.float32))
     run_backward(moe, wl, router=r)
+
+
+@pytest.mark.parametrize("name,T,Is", [("bwd_shared_small", 150, 256),
+                                       ("qwen3_30b_a3b_decode", None, 768),
+                                       ("qwen3_30b_a3b_prefill", None, 768)])
+def test_backward_shared_expert(moe, name, T, Is):
+    if T is None:
+        wl = workloads.make(name)
+    else:
+        wl = workloads.make_layer(name, T=T, H=256, I=128, E=16, top_k=4, seed=15)
+    run_backward(moe, wl, shared=workloads.shared_expert_weights(wl.H, Is, wl.dtype, seed=2))
 
 
 def test_backward_decode(moe):

@@ -653,19 +653,25 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   // the gathered rows laid out expert-major first
   if (e == hipSuccess) e = launch_gather_rows(bf16, dout, T, w.sorted_token, N, H, w.dout_perm, s);
   if (e == hipSuccess) e = launch_gather_rows(bf16, x, T, w.sorted_token, N, H, w.x_perm, s);
+  // the shared expert's weight gradients (h_s^T dout and x^T dG_s) run
+  // inside these launches when their tiles fit, else on their own below
+  const bool fold = shared && wgrad_can_fold(I, H, Is, H) && wgrad_can_fold(H, 2 * I, H, 2 * Is);
+  const WgradAux aux_dn{w.hw_s, Is, dout, H, T, Is, H, g.d_shared_down, 0};
+  const WgradAux aux_gu{x, H, w.dG_s, 2 * Is, T, H, 2 * Is, g.d_shared_gate_up, 0};
   if (e == hipSuccess)
-    e = launch_wgrad(w.hw, I, w.dout_perm, H, w.zero, w.offsets, E, I, H, g.d_down, s);
+    e = launch_wgrad(w.hw, I, w.dout_perm, H, w.zero, w.offsets, E, I, H, g.d_down, s,
+                     fold ? &aux_dn : nullptr);
   mark(4);
   if (e == hipSuccess)
-    e = launch_wgrad(w.x_perm, H, w.dG, 2 * I, w.zero, w.offsets, E, H, 2 * I, g.d_gate_up, s);
+    e = launch_wgrad(w.x_perm, H, w.dG, 2 * I, w.zero, w.offsets, E, H, 2 * I, g.d_gate_up, s,
+                     fold ? &aux_gu : nullptr);
   mark(5);
   if (e == hipSuccess)
     e = launch_router_weight_grad(bf16, x, w.x_perm, w.dL, w.dl_perm, w.offsets, T, E, H, sparse,
                                   g.d_router_weight, g.d_router_bias, w.rw_part, s);
-  // the shared expert's weight gradients: h^T dout and x^T dG_s
-  if (e == hipSuccess && shared)
+  if (e == hipSuccess && shared && !fold)
     e = launch_wgrad(w.hw_s, Is, dout, H, w.zero, w.offs_s, 1, Is, H, g.d_shared_down, s);
-  if (e == hipSuccess && shared)
+  if (e == hipSuccess && shared && !fold)
     e = launch_wgrad(x, H, w.dG_s, 2 * Is, w.zero, w.offs_s, 1, H, 2 * Is, g.d_shared_gate_up, s);
   mark(6);
   return hip_status(e);

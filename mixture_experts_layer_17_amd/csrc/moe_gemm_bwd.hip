@@ -356,29 +356,47 @@ struct wcfg {
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
-    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
+    const bf16_t* __restrict__ gA, int g_lda, const bf16_t* __restrict__ gB, int g_ldb,
     const bf16_t* __restrict__ zero_row, const int32_t* __restrict__ offsets, int E, int M,
-    int N, bf16_t* __restrict__ C, long long c_estride, int ldc) {
+    int N, bf16_t* __restrict__ gC, long long g_c_estride, int g_ldc, WgradAux aux) {
   using G = wcfg<BM, BN, WM, WN, STAGES>;
   extern __shared__ __align__(16) unsigned char smem[];
 
   // ---- job (expert, m-tile, n-tile); consecutive jobs share an expert's rows
+  // Each XCD first takes an equal share of the dense problem's jobs (all
+  // of its rows each: the long ones go first), then of the grouped jobs.
   const int m_tiles = M / BM, n_tiles = N / BN;
-  const int jobs = E * m_tiles * n_tiles;
-  const int per_xcd = (jobs + NUM_XCD - 1) / NUM_XCD;
+  const int g_jobs = E * m_tiles * n_tiles;
+  const int d_per = (aux.jobs + NUM_XCD - 1) / NUM_XCD;
+  const int g_per = (g_jobs + NUM_XCD - 1) / NUM_XCD;
   const int xcd = blockIdx.x % NUM_XCD;
   const int local = blockIdx.x / NUM_XCD;
-  if (local >= per_xcd) return;
-  const int job = xcd * per_xcd + local;
-  if (job >= jobs) return;
-  const int e = job / (m_tiles * n_tiles);
-  const int rem = job - e * m_tiles * n_tiles;
-  const int mt = rem / n_tiles;
-  const int nt = rem - mt * n_tiles;
+  const bool dense = local < d_per;   // uniform over the work-group
+  int job;
+  if (dense) {
+    job = xcd * d_per + local;
+    if (job >= aux.jobs) return;
+  } else {
+    if (local - d_per >= g_per) return;
+    job = xcd * g_per + (local - d_per);
+    if (job >= g_jobs) return;
+  }
+  const int nt_of = dense ? aux.N / BN : n_tiles;
+  const int e = dense ? 0 : job / (m_tiles * n_tiles);
+  const int rem = dense ? job : job - e * m_tiles * n_tiles;
+  const int mt = rem / nt_of;
+  const int nt = rem - mt * nt_of;
   const int m0 = mt * BM, n0 = nt * BN;
-  const int lo = offsets[e];
-  const int hi = max(offsets[e + 1], lo);
+  const int lo = dense ? 0 : offsets[e];
+  const int hi = dense ? aux.rows : max(offsets[e + 1], lo);
   const int KT = (hi - lo + BK - 1) / BK;
+  const bf16_t* __restrict__ A = dense ? (const bf16_t*)aux.A : gA;
+  const int lda = dense ? aux.lda : g_lda;
+  const bf16_t* __restrict__ B = dense ? (const bf16_t*)aux.B : gB;
+  const int ldb = dense ? aux.ldb : g_ldb;
+  bf16_t* __restrict__ C = dense ? (bf16_t*)aux.C : gC;
+  const long long c_estride = dense ? 0 : g_c_estride;
+  const int ldc = dense ? aux.N : g_ldc;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -551,17 +569,20 @@ int dgrad_id(int cls, int n_cols) { return cls == 3 ? (n_cols % 256 == 0 ? 3 : 4
 template <int BM, int BN, int WM, int WN, int STAGES>
 hipError_t launch_wgrad_t(const void* A, int lda, const void* B, int ldb, const void* zero_row,
                           const int32_t* offsets, int E, int M, int N, void* C,
-                          long long c_estride, int ldc, hipStream_t s) {
+                          long long c_estride, int ldc, hipStream_t s, const WgradAux& aux) {
   using G = wcfg<BM, BN, WM, WN, STAGES>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)wgrad_kernel<BM, BN, WM, WN, STAGES>,
       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   if (attr != hipSuccess) return attr;
-  const long long jobs = (long long)E * (M / BM) * (N / BN);
-  const int grid = (int)std::max<long long>((jobs + NUM_XCD - 1) / NUM_XCD * NUM_XCD, NUM_XCD);
+  WgradAux a = aux;
+  a.jobs = a.rows > 0 ? (a.M / BM) * (a.N / BN) : 0;
+  const long long g_per = ((long long)E * (M / BM) * (N / BN) + NUM_XCD - 1) / NUM_XCD;
+  const long long d_per = ((long long)a.jobs + NUM_XCD - 1) / NUM_XCD;
+  const int grid = (int)std::max<long long>((g_per + d_per) * NUM_XCD, NUM_XCD);
   hipLaunchKernelGGL((wgrad_kernel<BM, BN, WM, WN, STAGES>), dim3(grid), dim3(G::THREADS), G::LDS,
                      s, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, (const bf16_t*)zero_row,
-                     offsets, E, M, N, (bf16_t*)C, c_estride, ldc);
+                     offsets, E, M, N, (bf16_t*)C, c_estride, ldc, a);
   return hipGetLastError();
 }
 
@@ -605,16 +626,39 @@ hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int
                                     none, s);
 }
 
+// Output tile of the wgrad config chosen for an M x N gradient.
+static void wgrad_tile(int M, int N, int* bm, int* bn) {
+  if (M % 256 == 0 && N % 256 == 0) {
+    *bm = 256;
+    *bn = 256;
+  } else {
+    *bm = 128;
+    *bn = N % 256 == 0 ? 256 : 128;
+  }
+}
+
+bool wgrad_can_fold(int M, int N, int Ma, int Na) {
+  int bm, bn;
+  wgrad_tile(M, N, &bm, &bn);
+  return Ma % bm == 0 && Na % bn == 0;
+}
+
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const void* zero_row,
-                        const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s) {
-  if (M % 256 == 0 && N % 256 == 0)
+                        const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s,
+                        const WgradAux* aux) {
+  const WgradAux none{nullptr, 0, nullptr, 0, 0, 0, 0, nullptr, 0};
+  const WgradAux& a = aux ? *aux : none;
+  if (a.rows > 0 && !wgrad_can_fold(M, N, a.M, a.N)) return hipErrorInvalidValue;
+  int bm, bn;
+  wgrad_tile(M, N, &bm, &bn);
+  if (bm == 256)
     return launch_wgrad_t<256, 256, 2, 4, 3>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
-                                             (long long)M * N, N, s);
-  if (N % 256 == 0)
+                                             (long long)M * N, N, s, a);
+  if (bn == 256)
     return launch_wgrad_t<128, 256, 2, 2, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
-                                             (long long)M * N, N, s);
+                                             (long long)M * N, N, s, a);
   return launch_wgrad_t<128, 128, 2, 2, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
-                                           (long long)M * N, N, s);
+                                           (long long)M * N, N, s, a);
 }
 
 }  // namespace moe

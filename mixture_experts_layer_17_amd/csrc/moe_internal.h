@@ -123,9 +123,23 @@ hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32
 hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int N, int H, int I,
                                 int E, const int32_t* out_index, void* dX, const void* tile_ws,
                                 hipStream_t s);
-// C[e] = A_e^T B_e over the expert-major rows [offsets[e], offsets[e + 1]).
+// A dense problem folded into a wgrad launch (the shared expert): C [M, N]
+// = A^T B over `rows` rows; its jobs run first.
+struct WgradAux {
+  const void* A;
+  int lda;
+  const void* B;
+  int ldb;
+  int rows, M, N;
+  void* C;
+  int jobs;   // set by the launcher
+};
+bool wgrad_can_fold(int M, int N, int Ma, int Na);
+// C[e] = A_e^T B_e over the expert-major rows [offsets[e], offsets[e + 1]);
+// `aux` (when wgrad_can_fold) adds a dense problem to the same launch.
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const void* zero_row,
-                        const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s);
+                        const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s,
+                        const WgradAux* aux = nullptr);
 hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N, int k, int H,
                               float* dw, hipStream_t s);
 // dL [T, E] for softmax or sigmoid scores times `scale`; when dL is zero

@@ -167,14 +167,16 @@ def test_backward_router_variant_decode(moe):
     run_backward(moe, wl, router=r)
 
 
-@pytest.mark.parametrize("name,T,Is", [("bwd_shared_small", 150, 256),
-                                       ("qwen3_30b_a3b_decode", None, 768),
-                                       ("qwen3_30b_a3b_prefill", None, 768)])
-def test_backward_shared_expert(moe, name, T, Is):
+@pytest.mark.parametrize("name,T,I,Is", [
+    ("bwd_shared_small", 150, 128, 256),       # shared wgrads inside the routed launches
+    ("bwd_shared_apart", 150, 256, 128),       # Is does not fit the tile: on their own
+    ("qwen3_30b_a3b_decode", None, None, 768),
+    ("qwen3_30b_a3b_prefill", None, None, 768)])
+def test_backward_shared_expert(moe, name, T, I, Is):
     if T is None:
         wl = workloads.make(name)
     else:
-        wl = workloads.make_layer(name, T=T, H=256, I=128, E=16, top_k=4, seed=15)
+        wl = workloads.make_layer(name, T=T, H=256, I=I, E=16, top_k=4, seed=15)
     run_backward(moe, wl, shared=workloads.shared_expert_weights(wl.H, Is, wl.dtype, seed=2))
 
 

@@ -160,7 +160,7 @@ struct BwdWs {
   void *perm, *tiles, *tiles1;
   float *dw, *dL, *dl_perm;
   void *dG, *hw, *dX, *x_perm, *dout_perm, *zero, *rw_part;
-  void *dG_s, *hw_s, *dx_s, *tiles_s, *tiles_s1;   // shared expert (Is > 0)
+  void *dG_s, *hw_s, *dx_s;   // shared expert (Is > 0)
   int32_t* offs_s;
   size_t zero_bytes, total;
 };
@@ -195,8 +195,6 @@ BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt, int Is
     w.dG_s = take((size_t)T * 2 * Is * esize(dt));
     w.hw_s = take((size_t)T * Is * esize(dt));
     w.dx_s = take((size_t)T * H * esize(dt));
-    w.tiles_s = take(tile_list_bytes(T, 1, dgrad_bm(pick_dgrad_cfg(T, 1))));
-    w.tiles_s1 = take(tile_list_bytes(T, 1, dgrad_bm(pick_dgrad1_cfg(T, 1))));
     w.offs_s = (int32_t*)take(2 * sizeof(int32_t));
   }
   w.zero_bytes = al((size_t)std::max(std::max(H, 2 * I), 2 * Is) * esize(dt));
@@ -593,8 +591,6 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   float* dw = g.d_topk_weights ? g.d_topk_weights : w.dw;
   const int id = pick_dgrad_cfg(N, E);
   const int id1 = pick_dgrad1_cfg(N, E);
-  const int sid = pick_dgrad_cfg(T, 1);
-  const int sid1 = pick_dgrad1_cfg(T, 1);
   auto mark = [&](int i) {
     if (stage_events && stage_events[i]) (void)hipEventRecord(stage_events[i], s);
   };
@@ -617,10 +613,9 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   }
   e = launch_fill_u32(w.zero, (long long)(w.zero_bytes / 4), 0u, s);
   if (e == hipSuccess && shared) {
-    // the shared expert is one dense group of the T token rows
-    e = launch_build_tiles(nullptr, 1, T, dgrad_bm(sid), w.tiles_s, s);
-    if (e == hipSuccess) e = launch_build_tiles(nullptr, 1, T, dgrad_bm(sid1), w.tiles_s1, s);
-    if (e == hipSuccess) e = launch_fill_u32(w.offs_s, 1, 0u, s);
+    // offsets {0, T}: the shared expert as one group, for its wgrads when
+    // they run on their own
+    e = launch_fill_u32(w.offs_s, 1, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(w.offs_s + 1, 1, (uint32_t)T, s);
   }
   // d_weights = <dout, y>, then the softmax / router gradient
@@ -629,22 +624,20 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
     e = launch_router_grad(logits, ids, weights, dw, w.slot_pos, T, E, k, norm, sigmoid, scale,
                            w.dL, w.dl_perm, s);
   mark(1);
-  // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot order
+  // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot
+  // order.  The shared expert (weight 1 on every token) runs inside the same
+  // launches (the first one's 128-column tiles fit any Is multiple of 128).
+  const bool dfold = shared != nullptr;
+  const DgradShared dsh{shared ? shared->gate_up : nullptr, shared ? shared->down : nullptr,
+                        saved->shared_gate_up_out, w.dG_s, w.hw_s, w.dx_s, T, Is};
   if (e == hipSuccess)
     e = launch_dgrad_down_swiglu(id1, dout, T, w.sorted_token, down, N, H, I, E,
                                  saved->gate_up_out, weights, w.sorted_slot, w.dG, w.hw, w.tiles1,
-                                 s);
+                                 s, dfold ? &dsh : nullptr);
   mark(2);
   if (e == hipSuccess)
-    e = launch_dgrad_gate_up(id, w.dG, gate_up, N, H, I, E, w.sorted_slot, w.dX, w.tiles, s);
-  // the shared expert (weight 1 on every token): its dgrads into dx_s
-  if (e == hipSuccess && shared)
-    e = launch_dgrad_down_swiglu(sid1, dout, T, nullptr, shared->down, T, H, Is, 1,
-                                 saved->shared_gate_up_out, nullptr, nullptr, w.dG_s, w.hw_s,
-                                 w.tiles_s1, s);
-  if (e == hipSuccess && shared)
-    e = launch_dgrad_gate_up(sid, w.dG_s, shared->gate_up, T, H, Is, 1, nullptr, w.dx_s,
-                             w.tiles_s, s);
+    e = launch_dgrad_gate_up(id, w.dG, gate_up, N, H, I, E, w.sorted_slot, w.dX, w.tiles, s,
+                             dfold ? &dsh : nullptr);
   if (e == hipSuccess)
     e = launch_input_grad(bf16, w.dX, w.dL, sparse ? ids : nullptr, wr, T, k, E, H,
                           shared ? w.dx_s : nullptr, g.dx, s);

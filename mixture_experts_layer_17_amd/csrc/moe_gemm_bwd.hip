@@ -138,28 +138,73 @@ struct SwigluBwd {
   int ldh;
 };
 
+// A dense problem folded into a dgrad launch (the shared expert): `rows`
+// rows of X read in order against one weight, outputs in row order, with its
+// own epilogue operands.
+struct DgradAux {
+  const bf16_t* X;
+  int ldx;
+  const bf16_t* W;
+  int ldw, K;
+  bf16_t* C;
+  int ldc, rows, n_ntiles, jobs;
+  SwigluBwd sb;
+};
+
 template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
-    const bf16_t* __restrict__ X, int ldx, const int32_t* __restrict__ x_index, int x_rows,
-    const bf16_t* __restrict__ W, long long w_estride, int ldw, int K,
-    bf16_t* __restrict__ C, int ldc, const int32_t* __restrict__ c_index, int c_rows,
-    const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count, int n_ntiles,
-    SwigluBwd sb) {
+    const bf16_t* __restrict__ gX, int g_ldx, const int32_t* __restrict__ g_x_index, int g_x_rows,
+    const bf16_t* __restrict__ gW, long long g_w_estride, int g_ldw, int g_K,
+    bf16_t* __restrict__ gC, int g_ldc, const int32_t* __restrict__ g_c_index, int g_c_rows,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count, int g_n_ntiles,
+    SwigluBwd g_sb, DgradAux aux) {
   using G = dcfg<BM, BN, WM, WN, STAGES>;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int jobs = tiles_count[0] * n_ntiles;
-  const int per_xcd = (jobs + NUM_XCD - 1) / NUM_XCD;
+  // each XCD takes an equal share of the dense jobs first, then of the
+  // grouped ones
+  const int g_jobs = tiles_count[0] * g_n_ntiles;
+  const int d_per = (aux.jobs + NUM_XCD - 1) / NUM_XCD;
+  const int g_per = (g_jobs + NUM_XCD - 1) / NUM_XCD;
   const int xcd = blockIdx.x % NUM_XCD;
   const int local = blockIdx.x / NUM_XCD;
-  if (local >= per_xcd) return;
-  const int job = xcd * per_xcd + local;
-  if (job >= jobs) return;
+  const bool dense = local < d_per;   // uniform over the work-group
+  int job;
+  if (dense) {
+    job = xcd * d_per + local;
+    if (job >= aux.jobs) return;
+  } else {
+    if (local - d_per >= g_per) return;
+    job = xcd * g_per + (local - d_per);
+    if (job >= g_jobs) return;
+  }
+  const int n_ntiles = dense ? aux.n_ntiles : g_n_ntiles;
   const int mt = job / n_ntiles;
   const int nt = job - mt * n_ntiles;
-  const int4 tile = tiles[mt];
-  const int e = tile.x, row0 = tile.y, rows = tile.z;
+  int e = 0, row0, rows;
+  if (dense) {
+    row0 = mt * BM;
+    rows = min(BM, aux.rows - row0);
+  } else {
+    const int4 tile = tiles[mt];
+    e = tile.x;
+    row0 = tile.y;
+    rows = tile.z;
+  }
   const int n0 = nt * BN;
+  const bf16_t* __restrict__ X = dense ? aux.X : gX;
+  const int ldx = dense ? aux.ldx : g_ldx;
+  const int32_t* __restrict__ x_index = dense ? nullptr : g_x_index;
+  const int x_rows = dense ? aux.rows : g_x_rows;
+  const bf16_t* __restrict__ W = dense ? aux.W : gW;
+  const long long w_estride = dense ? 0 : g_w_estride;
+  const int ldw = dense ? aux.ldw : g_ldw;
+  const int K = dense ? aux.K : g_K;
+  bf16_t* __restrict__ C = dense ? aux.C : gC;
+  const int ldc = dense ? aux.ldc : g_ldc;
+  const int32_t* __restrict__ c_index = dense ? nullptr : g_c_index;
+  const int c_rows = dense ? aux.rows : g_c_rows;
+  const SwigluBwd& sb = dense ? aux.sb : g_sb;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -519,20 +564,24 @@ template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
 hipError_t launch_dgrad_t(const void* X, int ldx, const int32_t* x_index, int x_rows,
                           const void* W, long long w_estride, int ldw, int K, void* C, int ldc,
                           const int32_t* c_index, int c_rows, const void* tile_ws, int N, int E,
-                          int n_ntiles, const SwigluBwd& sb, hipStream_t s) {
+                          int n_ntiles, const SwigluBwd& sb, hipStream_t s,
+                          const DgradAux& aux) {
   using G = dcfg<BM, BN, WM, WN, STAGES>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)dgrad_kernel<BM, BN, WM, WN, STAGES, EPI>,
       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   if (attr != hipSuccess) return attr;
+  DgradAux a = aux;
+  a.jobs = a.rows > 0 ? (a.rows + BM - 1) / BM * a.n_ntiles : 0;
   const long long max_tiles = (long long)N / BM + std::min(E, N);
-  const long long jobs = (max_tiles * n_ntiles + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
-  const int grid = (int)std::max<long long>(jobs, NUM_XCD);
+  const long long g_per = (max_tiles * n_ntiles + NUM_XCD - 1) / NUM_XCD;
+  const long long d_per = ((long long)a.jobs + NUM_XCD - 1) / NUM_XCD;
+  const int grid = (int)std::max<long long>((g_per + d_per) * NUM_XCD, NUM_XCD);
   hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, STAGES, EPI>), dim3(grid), dim3(G::THREADS),
                      G::LDS, s, (const bf16_t*)X, ldx, x_index, x_rows, (const bf16_t*)W,
                      w_estride, ldw, K, (bf16_t*)C, ldc, c_index, c_rows,
                      (const int4*)((const char*)tile_ws + 256), (const int32_t*)tile_ws, n_ntiles,
-                     sb);
+                     sb, a);
   return hipGetLastError();
 }
 
@@ -540,12 +589,13 @@ template <int EPI>
 hipError_t launch_dgrad_cfg(int id, const void* X, int ldx, const int32_t* x_index, int x_rows,
                             const void* W, long long w_estride, int ldw, int K, void* C, int ldc,
                             const int32_t* c_index, int c_rows, const void* tile_ws, int N, int E,
-                            int n_ntiles, const SwigluBwd& sb, hipStream_t s) {
+                            int n_ntiles, const SwigluBwd& sb, hipStream_t s,
+                            const DgradAux& aux) {
 #define MOE_DG(ID, BM, BN, WM, WN, ST)                                                        \
   case ID:                                                                                 \
     return launch_dgrad_t<BM, BN, WM, WN, ST, EPI>(X, ldx, x_index, x_rows, W, w_estride, ldw, \
                                                    K, C, ldc, c_index, c_rows, tile_ws, N, E,  \
-                                                   n_ntiles, sb, s);
+                                                   n_ntiles, sb, s, aux);
   switch (id) {
     MOE_DG(0, 128, 128, 2, 2, 4)
     MOE_DG(1, 64, 128, 2, 2, 4)
@@ -605,25 +655,40 @@ int pick_dgrad1_cfg(int N, int E) {
 hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
                                     const void* down, int N, int H, int I, int E,
                                     const void* G, const float* w, const int32_t* sorted_slot,
-                                    void* dG, void* hw, const void* tile_ws, hipStream_t s) {
+                                    void* dG, void* hw, const void* tile_ws, hipStream_t s,
+                                    const DgradShared* sh) {
   if (N <= 0) return hipSuccess;
   const SwigluBwd sb{(const bf16_t*)G, 2 * I, I, w, sorted_slot, (bf16_t*)dG, (bf16_t*)hw, I};
   const int cfg = dgrad_id(id, I);
   const int bn = cfg == 3 ? 256 : 128;
+  DgradAux aux{};
+  if (sh) {
+    // dout rows in order against the shared down projection, weight 1
+    if (sh->Is % bn != 0) return hipErrorInvalidValue;
+    aux = DgradAux{(const bf16_t*)dout, H, (const bf16_t*)sh->down, H, H, nullptr, 0, sh->rows,
+                   sh->Is / bn, 0,
+                   SwigluBwd{(const bf16_t*)sh->G, 2 * sh->Is, sh->Is, nullptr, nullptr,
+                             (bf16_t*)sh->dG, (bf16_t*)sh->hw, sh->Is}};
+  }
   return launch_dgrad_cfg<DG_SWIGLU_BWD>(cfg, dout, H, sorted_token, T, down, (long long)I * H, H,
-                                         H, nullptr, 0, nullptr, 0, tile_ws, N, E, I / bn, sb, s);
+                                         H, nullptr, 0, nullptr, 0, tile_ws, N, E, I / bn, sb, s,
+                                         aux);
 }
 
 hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int N, int H, int I,
                                 int E, const int32_t* out_index, void* dX, const void* tile_ws,
-                                hipStream_t s) {
+                                hipStream_t s, const DgradShared* sh) {
   if (N <= 0) return hipSuccess;
   const SwigluBwd none{};
   const int cfg = dgrad_id(id, H);
   const int bn = cfg == 3 ? 256 : 128;
+  DgradAux aux{};
+  if (sh)
+    aux = DgradAux{(const bf16_t*)sh->dG, 2 * sh->Is, (const bf16_t*)sh->gate_up, 2 * sh->Is,
+                   2 * sh->Is, (bf16_t*)sh->dx, H, sh->rows, H / bn, 0, none};
   return launch_dgrad_cfg<DG_PLAIN>(cfg, dG, 2 * I, nullptr, N, gate_up, (long long)H * 2 * I,
                                     2 * I, 2 * I, dX, H, out_index, N, tile_ws, N, E, H / bn,
-                                    none, s);
+                                    none, s, aux);
 }
 
 // Output tile of the wgrad config chosen for an M x N gradient.

@@ -114,15 +114,31 @@ hipError_t launch_down(bool bf16, const GemmTileCfg& c, const void* h,
 int pick_dgrad_cfg(int N, int E);
 int pick_dgrad1_cfg(int N, int E);
 int dgrad_bm(int id);
+// The shared expert's dgrads, folded into the routed dgrad launches as a
+// dense problem of `rows` token rows (weight 1): dout . down^T with the
+// SwiGLU backward into dG [rows, 2 Is] and hw [rows, Is], then
+// dG . gate_up^T into dx [rows, H].
+struct DgradShared {
+  const void* gate_up;
+  const void* down;
+  const void* G;
+  void* dG;
+  void* hw;
+  void* dx;
+  int rows, Is;
+};
+// The first dgrad's config must use 128-column tiles (pick_dgrad1_cfg)
+// so that any Is multiple of 128 fits.
 // w == NULL: every row's weight is 1 (a shared expert); sorted_slot NULL:
 // row p's weight is w[p].
 hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
                                     const void* down, int N, int H, int I, int E,
                                     const void* G, const float* w, const int32_t* sorted_slot,
-                                    void* dG, void* hw, const void* tile_ws, hipStream_t s);
+                                    void* dG, void* hw, const void* tile_ws, hipStream_t s,
+                                    const DgradShared* sh = nullptr);
 hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int N, int H, int I,
                                 int E, const int32_t* out_index, void* dX, const void* tile_ws,
-                                hipStream_t s);
+                                hipStream_t s, const DgradShared* sh = nullptr);
 // A dense problem folded into a wgrad launch (the shared expert): C [M, N]
 // = A^T B over `rows` rows; its jobs run first.
 struct WgradAux {

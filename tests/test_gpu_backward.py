@@ -212,3 +212,20 @@ def test_backward_unsupported_is_reported(moe):
     x, wr, gu, dn = (t.to(DEV) for t in (wl.hidden_states, wl.router_weight, wl.gate_up, wl.down))
     with pytest.raises(moe.MoEError):
         moe.layer_forward_train(x, wr, gu, dn, 2, True)
+
+
+def test_backward_zero_tokens(moe):
+    say("backward: T = 0 gives exact zero weight gradients")
+    wl = workloads.make_layer("bwd_empty", T=8, H=256, I=128, E=8, top_k=2, seed=16)
+    x, wr, gu, dn = (t.to(DEV) for t in (wl.hidden_states, wl.router_weight, wl.gate_up, wl.down))
+    x0 = x[:0].contiguous()
+    sh = _shared_layout(*workloads.shared_expert_weights(256, 128, wl.dtype))
+    sh = tuple(t.to(DEV) for t in sh)
+    _, saved = moe.layer_forward_train(x0, wr, gu, dn, 2, True, shared=sh)
+    dout = torch.empty(0, wl.H, dtype=wl.dtype, device=DEV)
+    g = moe.layer_backward(x0, wr, gu, dn, 2, True, saved, dout, shared=sh)
+    torch.cuda.synchronize()
+    assert g["dx"].shape == (0, wl.H)
+    for name in ("d_router_weight", "d_router_bias", "d_gate_up", "d_down", "d_shared_gate_up",
+                 "d_shared_down"):
+        assert not g[name].cpu().any(), name

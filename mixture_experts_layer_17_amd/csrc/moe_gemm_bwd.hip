@@ -11,9 +11,10 @@
 //           d gate_up[e] = X_e^T . dG_e        H x 2I,    K = rows of e
 //
 // dgrad: the weight is used as stored ([n][k], k contiguous), so both
-// operands are row tiles of 64 bytes of k per block, XOR-swizzled like the
-// forward's activation tile and read with ds_read_b128; no transposed copy of
-// any weight exists.  The first dgrad's epilogue is the SwiGLU backward.
+// operands are row tiles of KB k per block (KB = 64: every row copy is one
+// whole 128-byte line), XOR-swizzled like the forward's activation tile and
+// read with ds_read_b128; no transposed copy of any weight exists.  The
+// first dgrad's epilogue is the SwiGLU backward.
 //
 // wgrad: K runs over the expert's rows, so both operands arrive as k-rows
 // with their output dimension contiguous, the layout of the forward's weight
@@ -36,17 +37,18 @@ using namespace lds;
 
 // The K loop shared by both kernels: a ring of STAGES LDS slots filled by
 // issue(slot, block); wait_blocks(n) leaves n blocks of this wave's copies
-// in flight.  The fragments of the next 16-k step are read while the MFMAs
-// of the current one run (read_b for the whole step, then each m-tile's
-// read_a right after its MFMAs are issued); sched_barrier keeps that
-// interleave.  One barrier per block sits between its two k-steps: it
-// publishes the next block and retires the one just read, whose slot is
-// refilled at once.
-template <int TM, int TN, int STAGES, class Issue, class Wait, class ReadA, class ReadB>
+// in flight.  A block holds KS k-steps of 16.  The fragments of the next
+// k-step are read while the MFMAs of the current one run (read_b for the
+// whole step, then each m-tile's read_a right after its MFMAs are issued);
+// sched_barrier keeps that interleave.  One barrier per block sits before
+// its last k-step: it publishes the next block and retires the one just
+// read, whose slot is refilled at once.
+template <int TM, int TN, int STAGES, int KS, class Issue, class Wait, class ReadA, class ReadB>
 __device__ __forceinline__ void pipelined_k_loop(int KT, unsigned char* smem, int stage_bytes,
                                                  Issue&& issue, Wait&& wait_blocks,
                                                  ReadA&& read_a, ReadB&& read_b,
                                                  f32x16_v (&acc)[TM][TN]) {
+  static_assert(KS >= 2, "k-steps per block");
 #pragma unroll
   for (int p = 0; p < STAGES; ++p)
     if (p < KT) issue(smem + p * stage_bytes, p);
@@ -54,25 +56,31 @@ __device__ __forceinline__ void pipelined_k_loop(int KT, unsigned char* smem, in
   wait_blocks(min(STAGES, KT) - 1);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  bf16x8_v b0[TN], b1[TN], af[TM];
-  auto mma_roll = [&](const bf16x8_v (&bf)[TN], const unsigned char* nbase, int nkk) {
+  bf16x8_v bf[2][TN], af[TM];   // k-step s of a block multiplies bf[s & 1]
+  auto mma_roll = [&](const bf16x8_v (&b)[TN], const unsigned char* nbase, int nkk) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], af[i], acc[i][j], 0, 0, 0);
       af[i] = read_a(nbase, nkk, i);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto read_bs = [&](const unsigned char* base, int kk, bf16x8_v (&b)[TN]) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b0[j] = read_b(smem, 0, j);
+    for (int j = 0; j < TN; ++j) b[j] = read_b(base, kk, j);
+  };
+  read_bs(smem, 0, bf[0]);
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[i] = read_a(smem, 0, i);
+  // k-steps 0 .. KS - 2 of block 0, each reading the next
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b1[j] = read_b(smem, 1, j);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_roll(b0, smem, 1);
+  for (int st = 0; st + 1 < KS; ++st) {
+    read_bs(smem, st + 1, bf[(st + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_roll(bf[st & 1], smem, st + 1);
+  }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (KT > 1) wait_blocks(min(STAGES - 2, KT - 2));
   __builtin_amdgcn_s_barrier();
@@ -83,14 +91,17 @@ __device__ __forceinline__ void pipelined_k_loop(int KT, unsigned char* smem, in
     slot = (slot + 1 == STAGES) ? 0 : slot + 1;
     unsigned char* nxt = smem + slot * stage_bytes;
     if (kb + STAGES < KT) issue(cur, kb + STAGES);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b0[j] = read_b(nxt, 0, j);
+    // last k-step of block kb, reading block kb + 1's first
+    read_bs(nxt, 0, bf[KS & 1]);
     __builtin_amdgcn_sched_barrier(0);
-    mma_roll(b1, nxt, 0);   // second k-step of block kb, first of kb + 1 read
+    mma_roll(bf[(KS - 1) & 1], nxt, 0);
+    // k-steps 0 .. KS - 2 of block kb + 1, each reading the next
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b1[j] = read_b(nxt, 1, j);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_roll(b0, nxt, 1);   // first k-step of block kb + 1, its second read
+    for (int st = 0; st + 1 < KS; ++st) {
+      read_bs(nxt, st + 1, bf[(KS + st + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_roll(bf[(KS + st) & 1], nxt, st + 1);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (kb + 2 < KT) wait_blocks(min(STAGES - 2, KT - 3 - kb));
     __builtin_amdgcn_s_barrier();
@@ -100,23 +111,38 @@ __device__ __forceinline__ void pipelined_k_loop(int KT, unsigned char* smem, in
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[j], af[i], acc[i][j], 0, 0, 0);
+      acc[i][j] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[(KS - 1) & 1][j], af[i], acc[i][j], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- dgrad
 
 enum { DG_PLAIN = 0, DG_SWIGLU_BWD = 1 };
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+// Row chunk swizzle of a dgrad stage: rows of KB k hold KB / 8 chunks of 16
+// bytes.  Four chunks take the measured f(row); eight (whole 128-byte lines)
+// take (row >> 1) & 7, so the 16 rows one 16-lane phase of a ds_read_b128
+// reads fall on 16 distinct 16-byte bank groups.
+template <int KB>
+__device__ __forceinline__ int dswz(int row) {
+  if constexpr (KB == 32) return fswz(row);
+  else return (row >> 1) & 7;
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int KB>
 struct dcfg {
+  static_assert(KB == 32 || KB == 64, "k per block");
   static constexpr int NW = WM * WN;
   static constexpr int THREADS = NW * 64;
   static constexpr int TM = BM / 32 / WM;            // 32-row m-tiles per wave
   static constexpr int CW = BN / WN;                 // output columns per wave
   static constexpr int TN = CW / 32;                 // 32-column n-tiles per wave
-  static constexpr int STAGE_BYTES = (BM + BN) * 64; // A rows then B rows, 64 B each
+  static constexpr int KS = KB / 16;                 // MFMA k-steps per block
+  static constexpr int CH = KB / 8;                  // 16-byte chunks per row
+  static constexpr int ROWB = KB * 2;                // bytes per stage row
+  static constexpr int STAGE_BYTES = (BM + BN) * ROWB;   // A rows then B rows
   static constexpr int RING = STAGES * STAGE_BYTES;
-  static constexpr int INST = STAGE_BYTES / 1024;    // wave copies per stage (16 rows)
+  static constexpr int INST = STAGE_BYTES / 1024;    // wave copies per stage
   static constexpr int PER = INST / NW;
   static constexpr int OBF = CW * 4 + 16;            // fp32 staging row stride
   static constexpr int OBP = CW * 2 + 8;             // bf16 staging row stride
@@ -151,14 +177,14 @@ struct DgradAux {
   SwigluBwd sb;
 };
 
-template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
+template <int BM, int BN, int WM, int WN, int STAGES, int KB, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
     const bf16_t* __restrict__ gX, int g_ldx, const int32_t* __restrict__ g_x_index, int g_x_rows,
     const bf16_t* __restrict__ gW, long long g_w_estride, int g_ldw, int g_K,
     bf16_t* __restrict__ gC, int g_ldc, const int32_t* __restrict__ g_c_index, int g_c_rows,
     const int4* __restrict__ tiles, const int32_t* __restrict__ tiles_count, int g_n_ntiles,
     SwigluBwd g_sb, DgradAux aux) {
-  using G = dcfg<BM, BN, WM, WN, STAGES>;
+  using G = dcfg<BM, BN, WM, WN, STAGES, KB>;
   extern __shared__ __align__(16) unsigned char smem[];
 
   // each XCD takes an equal share of the dense jobs first, then of the
@@ -213,14 +239,15 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
   const bf16_t* We = W + (long long)e * w_estride;
 
   // copy assignments: stage row r < BM is activation row r of the tile, row
-  // BM + c is weight row n0 + c; lane q of a copy moves chunk (q & 3) ^ f(r)
+  // BM + c is weight row n0 + c; lane q of a copy moves chunk
+  // (q % CH) ^ swizzle(r)
   const bf16_t* src[G::PER];
 #pragma unroll
   for (int u = 0; u < G::PER; ++u) {
     const int inst = wave + u * G::NW;
     const int q = inst * 64 + lane;
-    const int r = q >> 2;
-    const int c = (q & 3) ^ fswz(r);
+    const int r = q / G::CH;
+    const int c = (q % G::CH) ^ dswz<KB>(r);
     if (r < BM) {
       int s = row0 + min(r, rows - 1);
       if (x_index) s = x_index[s];
@@ -235,10 +262,10 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
 #pragma unroll
     for (int u = 0; u < G::PER; ++u) {
       copy16_to_lds(src[u], base + (wave + u * G::NW) * 1024);
-      src[u] += BK;
+      src[u] += KB;
     }
   };
-  const int KT = K / BK;
+  const int KT = K / KB;
   auto wait_blocks = [&](int nb) {
     static_assert(STAGES <= 4 && (STAGES - 1) * G::PER < 64, "wait table");
     switch (nb) {
@@ -249,16 +276,16 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
     }
   };
 
-  // fragment offsets: lane l reads row 32 t + l % 32, k chunk 2 kk + l / 32
+  // fragment offsets: lane l reads row 32 t + l % 32, k chunk 2 kk + l / 32;
+  // the swizzle depends on l % 32 only (tiles start at multiples of 32), so
+  // m- and n-tiles are constant offsets from the wave's first
   const int l32 = lane & 31, hl = lane >> 5;
-  int a_off[G::TM][2], b_off[G::TN][2];
+  int a_off[G::KS], b_off[G::KS];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int ch = 16 * ((2 * kk + hl) ^ fswz(l32));
-#pragma unroll
-    for (int i = 0; i < G::TM; ++i) a_off[i][kk] = (32 * (wm + WM * i) + l32) * 64 + ch;
-#pragma unroll
-    for (int j = 0; j < G::TN; ++j) b_off[j][kk] = (BM + wn * G::CW + 32 * j + l32) * 64 + ch;
+  for (int kk = 0; kk < G::KS; ++kk) {
+    const int ch = 16 * ((2 * kk + hl) ^ dswz<KB>(l32));
+    a_off[kk] = (32 * wm + l32) * G::ROWB + ch;
+    b_off[kk] = (BM + wn * G::CW + l32) * G::ROWB + ch;
   }
 
   f32x16_v acc[G::TM][G::TN];
@@ -270,13 +297,15 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   auto read_a = [&](const unsigned char* base, int kk, int i) {
-    return __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(base + a_off[i][kk]));
+    return __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(
+                                            base + a_off[kk] + 32 * WM * G::ROWB * i));
   };
   auto read_b = [&](const unsigned char* base, int kk, int j) {
-    return __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(base + b_off[j][kk]));
+    return __builtin_bit_cast(bf16x8_v,
+                              *reinterpret_cast<const u32x4*>(base + b_off[kk] + 32 * G::ROWB * j));
   };
-  pipelined_k_loop<G::TM, G::TN, STAGES>(KT, smem, G::STAGE_BYTES, issue, wait_blocks, read_a,
-                                         read_b, acc);
+  pipelined_k_loop<G::TM, G::TN, STAGES, G::KS>(KT, smem, G::STAGE_BYTES, issue, wait_blocks,
+                                                read_a, read_b, acc);
 
   // ---- epilogue.  acc[i][j][q] = C[row 32 (wm + WM i) + l % 32]
   //                                 [col wn CW + 32 j + 8 (q / 4) + 4 hl + q % 4]
@@ -524,7 +553,7 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
   auto read_b = [&](const unsigned char* base, int kk, int j) {
     return read_tr(base + b_off[j] + 16 * kk * G::B_ROWB, G::B_ROWB);
   };
-  pipelined_k_loop<G::TM, G::TN, STAGES>(KT, smem, G::STAGE_BYTES, issue, wait_blocks, read_a,
+  pipelined_k_loop<G::TM, G::TN, STAGES, 2>(KT, smem, G::STAGE_BYTES, issue, wait_blocks, read_a,
                                          read_b, acc);
 
   // ---- epilogue: acc[i][j][q] = C[m0 + (BM / WM) wm + 32 i + l % 32]
@@ -560,15 +589,16 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
+template <int BM, int BN, int WM, int WN, int STAGES, int KB, int EPI>
 hipError_t launch_dgrad_t(const void* X, int ldx, const int32_t* x_index, int x_rows,
                           const void* W, long long w_estride, int ldw, int K, void* C, int ldc,
                           const int32_t* c_index, int c_rows, const void* tile_ws, int N, int E,
                           int n_ntiles, const SwigluBwd& sb, hipStream_t s,
                           const DgradAux& aux) {
-  using G = dcfg<BM, BN, WM, WN, STAGES>;
+  using G = dcfg<BM, BN, WM, WN, STAGES, KB>;
+  if (K % KB != 0) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)dgrad_kernel<BM, BN, WM, WN, STAGES, EPI>,
+      (const void*)dgrad_kernel<BM, BN, WM, WN, STAGES, KB, EPI>,
       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   if (attr != hipSuccess) return attr;
   DgradAux a = aux;
@@ -577,7 +607,7 @@ hipError_t launch_dgrad_t(const void* X, int ldx, const int32_t* x_index, int x_
   const long long g_per = (max_tiles * n_ntiles + NUM_XCD - 1) / NUM_XCD;
   const long long d_per = ((long long)a.jobs + NUM_XCD - 1) / NUM_XCD;
   const int grid = (int)std::max<long long>((g_per + d_per) * NUM_XCD, NUM_XCD);
-  hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, STAGES, EPI>), dim3(grid), dim3(G::THREADS),
+  hipLaunchKernelGGL((dgrad_kernel<BM, BN, WM, WN, STAGES, KB, EPI>), dim3(grid), dim3(G::THREADS),
                      G::LDS, s, (const bf16_t*)X, ldx, x_index, x_rows, (const bf16_t*)W,
                      w_estride, ldw, K, (bf16_t*)C, ldc, c_index, c_rows,
                      (const int4*)((const char*)tile_ws + 256), (const int32_t*)tile_ws, n_ntiles,
@@ -591,27 +621,30 @@ hipError_t launch_dgrad_cfg(int id, const void* X, int ldx, const int32_t* x_ind
                             const int32_t* c_index, int c_rows, const void* tile_ws, int N, int E,
                             int n_ntiles, const SwigluBwd& sb, hipStream_t s,
                             const DgradAux& aux) {
-#define MOE_DG(ID, BM, BN, WM, WN, ST)                                                        \
-  case ID:                                                                                 \
-    return launch_dgrad_t<BM, BN, WM, WN, ST, EPI>(X, ldx, x_index, x_rows, W, w_estride, ldw, \
-                                                   K, C, ldc, c_index, c_rows, tile_ws, N, E,  \
-                                                   n_ntiles, sb, s, aux);
+#define MOE_DG(ID, BM, BN, WM, WN, ST, KB)                                                  \
+  case ID:                                                                               \
+    return launch_dgrad_t<BM, BN, WM, WN, ST, KB, EPI>(X, ldx, x_index, x_rows, W, w_estride, \
+                                                       ldw, K, C, ldc, c_index, c_rows, tile_ws, \
+                                                       N, E, n_ntiles, sb, s, aux);
   switch (id) {
-    MOE_DG(0, 128, 128, 2, 2, 4)
-    MOE_DG(1, 64, 128, 2, 2, 4)
-    MOE_DG(2, 32, 128, 1, 2, 4)
-    MOE_DG(3, 256, 256, 4, 2, 4)
-    MOE_DG(4, 256, 128, 2, 2, 4)
+    MOE_DG(0, 128, 128, 2, 2, 4, 32)
+    MOE_DG(1, 64, 128, 2, 2, 4, 32)
+    MOE_DG(2, 32, 128, 1, 2, 4, 32)
+    MOE_DG(3, 256, 256, 2, 4, 2, 64)
+    MOE_DG(4, 256, 128, 4, 2, 3, 64)
     default: return hipErrorInvalidValue;
   }
 #undef MOE_DG
 }
 
 // Row-tile classes (the tile list's height) and, within the 256-row class,
-// the 256-column config when the output width allows it.  Wave layouts and
-// stage counts were chosen by timing at the prefill shape (4 x 2 waves for
-// the 256 x 256 dgrad, 3 stages for the 256 x 256 wgrad: 5-10 % over the
-// alternatives).
+// the 256-column config when the output width allows it.  The 256-row
+// configs take 64 k per block, so every row copy of both operands is one
+// whole 128-byte line: at the prefill shape that measured 323 against
+// 356 us for the second dgrad and, as 256 x 128 tiles on 4 x 2 waves, 253
+// against 270 us for the first (which keeps 128-column tiles: I / 256
+// column tiles leave the grid short of work-groups).  The shorter tiles
+// measured slower with 64 k and keep 32.
 constexpr int kDgradBM[] = {128, 64, 32, 256};
 
 int dgrad_id(int cls, int n_cols) { return cls == 3 ? (n_cols % 256 == 0 ? 3 : 4) : cls; }
@@ -645,12 +678,9 @@ int pick_dgrad_cfg(int N, int E) {
 
 int dgrad_bm(int id) { return kDgradBM[id]; }
 
-// The first dgrad has only I / BN column tiles per row tile, so with tall
-// row tiles the grid is short of work-groups; it keeps 128-row tiles.
-int pick_dgrad1_cfg(int N, int E) {
-  const int c = pick_dgrad_cfg(N, E);
-  return c == 3 ? 0 : c;
-}
+// The first dgrad uses the same row classes (its configs differ only in
+// the 256-row class, see launch_dgrad_down_swiglu).
+int pick_dgrad1_cfg(int N, int E) { return pick_dgrad_cfg(N, E); }
 
 hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
                                     const void* down, int N, int H, int I, int E,
@@ -659,8 +689,9 @@ hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32
                                     const DgradShared* sh) {
   if (N <= 0) return hipSuccess;
   const SwigluBwd sb{(const bf16_t*)G, 2 * I, I, w, sorted_slot, (bf16_t*)dG, (bf16_t*)hw, I};
-  const int cfg = dgrad_id(id, I);
-  const int bn = cfg == 3 ? 256 : 128;
+  // 256-row tiles: always 128 columns wide
+  const int cfg = id == 3 ? 4 : id;
+  const int bn = 128;
   DgradAux aux{};
   if (sh) {
     // dout rows in order against the shared down projection, weight 1

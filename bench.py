@@ -73,7 +73,7 @@ def parse():
     return ap.parse_args()
 
 
-BWD_STAGES = ("routing_grads", "dgrad_down_swiglu", "dgrad_gate_up_dx", "wgrad_down",
+BWD_STAGES = ("permute", "dgrad_down_swiglu_dw", "dgrad_gate_up_dx", "wgrad_down",
               "wgrad_gate_up", "router_wgrad")
 
 
@@ -86,16 +86,20 @@ def algorithmic_backward(wl, counts, Is=0):
     N = T * k
     hit = int((counts > 0).sum())
     f = {
-        "routing_grads": 2.0 * N * H,
-        "dgrad_down_swiglu": 2.0 * N * H * I,
+        "permute": 0.0,
+        # dout . down^T, then <., h> for the routing weights' gradient
+        "dgrad_down_swiglu_dw": 2.0 * N * H * I + 2.0 * N * I,
         "dgrad_gate_up_dx": 2.0 * N * 2 * I * H,
         "wgrad_down": 2.0 * N * I * H,
         "wgrad_gate_up": 2.0 * N * H * 2 * I,
         "router_wgrad": 2.0 * N * H if wl.norm_topk_prob else 2.0 * T * E * H,
     }
     b = {
-        "routing_grads": N * H * es + T * H * es + T * E * 4 + 3 * N * 4,
-        "dgrad_down_swiglu": hit * I * H * es + T * H * es + 2 * N * 2 * I * es + N * I * es,
+        # ids in; counts, offsets and the three index maps out
+        "permute": N * 4 + 3 * N * 4,
+        # down, dout and G in; dG and hw out; logits in, dL out
+        "dgrad_down_swiglu_dw": hit * I * H * es + T * H * es + 2 * N * 2 * I * es + N * I * es
+        + 2 * T * E * 4,
         "dgrad_gate_up_dx": hit * H * 2 * I * es + N * 2 * I * es + 2 * N * H * es + T * H * es,
         "wgrad_down": N * I * es + T * H * es + E * I * H * es,
         "wgrad_gate_up": N * 2 * I * es + T * H * es + E * H * 2 * I * es,

@@ -381,7 +381,8 @@ int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
  *                      of every routed row, rows in the expert-major order of
  *                      moe_permute (stable in the flat slot index), gate in
  *                      columns [0, I), up in [I, 2I);
- *   expert_out         [T*k, H] dt: each slot's expert output, row t*k + j;
+ *   expert_out         [T*k, H] dt: each slot's expert output, row t*k + j
+ *                      (the combine's input; the backward does not read it);
  *   shared_gate_up_out [T, 2Is] dt: the shared expert's pre-activations
  *                      (only with a shared expert; Is a multiple of 128).
  * router_logits, topk_ids and topk_weights are required (the backward reads
@@ -409,6 +410,8 @@ int moe_layer_forward_train(const void* hidden_states, const void* router_weight
  * moe_layer_backward — from dout [T, H] dt and the training forward's
  * router_logits, topk_ids, topk_weights and saved activations:
  *   d_topk_weights[t, j] = <dout[t], y[t, j]>            float32 [T, k], or NULL
+ *       (evaluated as <dout[t] down[e]^T, h[t, j]>, the first dgrad's
+ *       product against the recomputed h, so y is not re-read)
  *   dL (router logits): the routing weights' Jacobian applied to d_w —
  *       softmax, renormalised:  w (d_w - <d_w, w>) on the selection, else 0
  *       softmax, plain:         p (route_scale g - <d_w, w>), p = softmax,
@@ -429,11 +432,11 @@ int moe_layer_forward_train(const void* hidden_states, const void* router_weight
  * overwrite their buffers (no accumulation).  Workspace:
  * moe_workspace_size(MOE_OP_LAYER_BACKWARD, T, H, I, E, top_k, Is, T*top_k, dt).
  * stage_events: NULL, or 7 caller-created events recorded before the
- * permutation, before the first dgrad GEMM (after d_topk_weights and dL),
- * before the second dgrad GEMM, before the first wgrad GEMM (after the shared
- * expert's dgrads and dx), before the second wgrad GEMM, before the router's
- * weight gradient (then the shared expert's wgrads), and at the end (NULL
- * entries are skipped).
+ * permutation, before the first dgrad GEMM, before the second dgrad GEMM
+ * (after d_topk_weights and dL), before the first wgrad GEMM (after the
+ * shared expert's dgrads and dx), before the second wgrad GEMM, before the
+ * router's weight gradient (then the shared expert's wgrads), and at the end
+ * (NULL entries are skipped).  saved->expert_out may be NULL here.
  */
 typedef struct moe_layer_grads {
   void* dx;

@@ -158,7 +158,7 @@ int router_variant(const moe_router_config* c, int E, int k, RouterVariant* out,
 struct BwdWs {
   int32_t *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
   void *perm, *tiles, *tiles1;
-  float *dw, *dL, *dl_perm;
+  float *dw, *dw_parts, *dL, *dl_perm;
   void *dG, *hw, *dX, *x_perm, *dout_perm, *zero, *rw_part;
   void *dG_s, *hw_s, *dx_s;   // shared expert (Is > 0)
   int32_t* offs_s;
@@ -183,6 +183,7 @@ BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt, int Is
   w.tiles = take(tile_list_bytes((int)N, E, dgrad_bm(pick_dgrad_cfg((int)N, E))));
   w.tiles1 = take(tile_list_bytes((int)N, E, dgrad_bm(pick_dgrad1_cfg((int)N, E))));
   w.dw = (float*)take(N * 4);
+  w.dw_parts = (float*)take(N * (size_t)std::max(1, dgrad1_weight_parts(I)) * 4);
   w.dL = (float*)take((size_t)T * E * 4);
   w.dl_perm = (float*)take(N * 4);
   w.rw_part = take(router_weight_grad_ws(E, H));
@@ -568,14 +569,14 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   if (!saved || !grads) return MOE_ERR_NULL;
   const moe_layer_grads& g = *grads;
   if (T > 0 && (!x || !wr || !gate_up || !down || !logits || !ids || !weights ||
-                !saved->gate_up_out || !saved->expert_out || !dout || !g.dx ||
-                !g.d_router_weight || !g.d_gate_up || !g.d_down))
+                !saved->gate_up_out || !dout || !g.dx || !g.d_router_weight || !g.d_gate_up ||
+                !g.d_down))
     return MOE_ERR_NULL;
   if (T > 0 && shared && (!shared->gate_up || !shared->down || !saved->shared_gate_up_out ||
                           !g.d_shared_gate_up || !g.d_shared_down))
     return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(wr) || !aligned16(gate_up) || !aligned16(down) ||
-      !aligned16(saved->gate_up_out) || !aligned16(saved->expert_out) || !aligned16(dout) ||
+      !aligned16(saved->gate_up_out) || !aligned16(dout) ||
       !aligned16(g.dx) || !aligned16(g.d_router_weight) || !aligned16(g.d_gate_up) ||
       !aligned16(g.d_down))
     return MOE_ERR_ALIGN;
@@ -618,22 +619,25 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
     e = launch_fill_u32(w.offs_s, 1, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(w.offs_s + 1, 1, (uint32_t)T, s);
   }
-  // d_weights = <dout, y>, then the softmax / router gradient
-  if (e == hipSuccess) e = launch_weight_grad(bf16, dout, saved->expert_out, N, k, H, dw, s);
-  if (e == hipSuccess)
-    e = launch_router_grad(logits, ids, weights, dw, w.slot_pos, T, E, k, norm, sigmoid, scale,
-                           w.dL, w.dl_perm, s);
   mark(1);
   // dgrad: SwiGLU backward in the first GEMM's epilogue, then dX in slot
   // order.  The shared expert (weight 1 on every token) runs inside the same
   // launches (the first one's 128-column tiles fit any Is multiple of 128).
+  // The first epilogue also leaves d_weights = <dout, y> = <dout . down^T, h>
+  // in column-slice partials, which are added up before the softmax /
+  // router gradient.
   const bool dfold = shared != nullptr;
   const DgradShared dsh{shared ? shared->gate_up : nullptr, shared ? shared->down : nullptr,
                         saved->shared_gate_up_out, w.dG_s, w.hw_s, w.dx_s, T, Is};
   if (e == hipSuccess)
     e = launch_dgrad_down_swiglu(id1, dout, T, w.sorted_token, down, N, H, I, E,
                                  saved->gate_up_out, weights, w.sorted_slot, w.dG, w.hw, w.tiles1,
-                                 s, dfold ? &dsh : nullptr);
+                                 s, dfold ? &dsh : nullptr, w.dw_parts);
+  if (e == hipSuccess)
+    e = launch_weight_grad(w.dw_parts, dgrad1_weight_parts(I), w.slot_pos, N, dw, s);
+  if (e == hipSuccess)
+    e = launch_router_grad(logits, ids, weights, dw, w.slot_pos, T, E, k, norm, sigmoid, scale,
+                           w.dL, w.dl_perm, s);
   mark(2);
   if (e == hipSuccess)
     e = launch_dgrad_gate_up(id, w.dG, gate_up, N, H, I, E, w.sorted_slot, w.dX, w.tiles, s,

@@ -71,27 +71,19 @@ __device__ __forceinline__ void store8(T* p, const float (&f)[8]) {
   }
 }
 
-// d_weights[i] = <dout[i / k], y[i]>: one wave per flat slot, each lane a
-// strided set of 8-column chunks, then a fixed butterfly sum.
-template <typename T>
-__global__ __launch_bounds__(256) void weight_grad_kernel(const T* __restrict__ dout,
-                                                          const T* __restrict__ y, int N, int k,
-                                                          int H, float* __restrict__ dw) {
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+// d_weights[i] = <dout[i / k], y[i]> = <dout[i / k] . down[e]^T, h[i]>: the
+// first dgrad's epilogue leaves the inner products of its column slices of
+// that second form (P per expert-major row); one thread per flat slot adds
+// them in slice order.
+__global__ __launch_bounds__(256) void weight_grad_kernel(const float* __restrict__ parts, int P,
+                                                          const int32_t* __restrict__ slot_pos,
+                                                          int N, float* __restrict__ dw) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
-  const T* d = dout + (size_t)(i / k) * H;
-  const T* r = y + (size_t)i * H;
+  const float* p = parts + (size_t)min(max(slot_pos[i], 0), N - 1) * P;
   float s = 0.f;
-  for (int c = 8 * lane; c < H; c += 512) {
-    float a[8], b[8];
-    load8(d + c, a);
-    load8(r + c, b);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) s = fmaf(a[x], b[x], s);
-  }
-  s = wave_sum(s);
-  if (lane == 0) dw[i] = s;
+  for (int c = 0; c < P; ++c) s += p[c];
+  dw[i] = s;
 }
 
 // dL[t, :] from the routing-weight gradient: one wave per token.
@@ -272,16 +264,10 @@ int grid_for_total(long long total) {
 
 }  // namespace
 
-hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N, int k, int H,
+hipError_t launch_weight_grad(const float* parts, int P, const int32_t* slot_pos, int N,
                               float* dw, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  const int grid = (N + 3) / 4;
-  if (bf16)
-    weight_grad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)dout, (const bf16_t*)y, N, k,
-                                                    H, dw);
-  else
-    weight_grad_kernel<float><<<grid, 256, 0, s>>>((const float*)dout, (const float*)y, N, k, H,
-                                                   dw);
+  weight_grad_kernel<<<(N + 255) / 256, 256, 0, s>>>(parts, P, slot_pos, N, dw);
   return hipGetLastError();
 }
 

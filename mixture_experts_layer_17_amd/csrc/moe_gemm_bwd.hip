@@ -162,7 +162,27 @@ struct SwigluBwd {
   bf16_t* dG;             // [N, 2I]
   bf16_t* hw;             // [N, I]  w * silu(g) * u
   int ldh;
+  float* dw_part;         // [N, I / 64] <z, silu(g) u> per 64-column slice, or NULL
+  int dw_ld;              // I / 64
 };
+
+// Column slice of the first dgrad's epilogue (CW of its configs): one
+// partial routing-weight gradient per expert-major row and slice.
+constexpr int kDgrad1Slice = 64;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Sum over each 16-lane row (pairs, quads, half-rows, rows): every lane of
+// the row ends with the same value, in a fixed order.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141>(v);   // row_half_mirror
+  v += dpp_f32<0x140>(v);   // row_mirror
+  return v;
+}
 
 // A dense problem folded into a dgrad launch (the shared expert): `rows`
 // rows of X read in order against one weight, outputs in row order, with its
@@ -343,12 +363,15 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
       }
     }
   } else {
+    static_assert(G::CW == kDgrad1Slice, "one partial per slice of the first dgrad");
     // SwiGLU backward.  z = dout . down^T for row p, column n of I:
     //   h = silu(g) u,  dh = w z,  du = dh silu(g),  dg = dh u silu'(g),
     //   hw = w h   (the first operand of the down-projection's wgrad)
     constexpr int LPR = G::CW * 4 / 16;        // lanes per staged fp32 row
     constexpr int RPI = 64 / LPR;
+    static_assert(LPR == 16, "a staged row is one 16-lane DPP row");
     unsigned char* stg = smem + wave * 32 * G::OBF;
+    float hzs[G::TM][32 / RPI];   // this lane's part of <z, h> per staged row
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
 #pragma unroll
@@ -364,6 +387,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
         const int r = rr * RPI + lane / LPR;
         const int m = 32 * (wm + WM * i) + r;
         const float4 z = *reinterpret_cast<const float4*>(stg + r * G::OBF + 16 * (lane % LPR));
+        float hz = 0.f;   // <z, silu(g) u> over this lane's 4 columns
         if (m < rows) {
           const int p = row0 + m;
           const int n = n0 + wn * G::CW + 4 * (lane % LPR);
@@ -386,6 +410,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
               o_du[hh] = dh * a;
               o_dg[hh] = dh * u * (s * (1.0f + g * (1.0f - s)));
               o_h[hh] = wt * (a * u);
+              hz = fmaf(zz[2 * c + hh], a * u, hz);
             }
             dg[c] = (uint32_t)f32_to_bf16_bits(o_dg[0]) | ((uint32_t)f32_to_bf16_bits(o_dg[1]) << 16);
             du[c] = (uint32_t)f32_to_bf16_bits(o_du[0]) | ((uint32_t)f32_to_bf16_bits(o_du[1]) << 16);
@@ -396,7 +421,22 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
               make_uint2(du[0], du[1]);
           *reinterpret_cast<uint2*>(sb.hw + (long long)p * sb.ldh + n) = make_uint2(hv[0], hv[1]);
         }
+        hzs[i][rr] = hz;
       }
+    }
+    if (sb.dw_part) {
+      // after every row is written (so the loop above keeps its loads in
+      // flight): the 16 lanes of a staged row add their parts, the first
+      // stores the slice's partial
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 32 / RPI; ++rr) {
+          const float v = row16_sum(hzs[i][rr]);
+          const int m = 32 * (wm + WM * i) + rr * RPI + lane / LPR;
+          if (m < rows && lane % LPR == 0)
+            sb.dw_part[(long long)(row0 + m) * sb.dw_ld + (n0 + wn * G::CW) / kDgrad1Slice] = v;
+        }
     }
   }
 }
@@ -682,13 +722,16 @@ int dgrad_bm(int id) { return kDgradBM[id]; }
 // the 256-row class, see launch_dgrad_down_swiglu).
 int pick_dgrad1_cfg(int N, int E) { return pick_dgrad_cfg(N, E); }
 
+int dgrad1_weight_parts(int I) { return I / kDgrad1Slice; }
+
 hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
                                     const void* down, int N, int H, int I, int E,
                                     const void* G, const float* w, const int32_t* sorted_slot,
                                     void* dG, void* hw, const void* tile_ws, hipStream_t s,
-                                    const DgradShared* sh) {
+                                    const DgradShared* sh, float* dw_parts) {
   if (N <= 0) return hipSuccess;
-  const SwigluBwd sb{(const bf16_t*)G, 2 * I, I, w, sorted_slot, (bf16_t*)dG, (bf16_t*)hw, I};
+  const SwigluBwd sb{(const bf16_t*)G, 2 * I,       I,  w, sorted_slot, (bf16_t*)dG,
+                     (bf16_t*)hw,      I,           dw_parts, dgrad1_weight_parts(I)};
   // 256-row tiles: always 128 columns wide
   const int cfg = id == 3 ? 4 : id;
   const int bn = 128;
@@ -699,7 +742,7 @@ hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32
     aux = DgradAux{(const bf16_t*)dout, H, (const bf16_t*)sh->down, H, H, nullptr, 0, sh->rows,
                    sh->Is / bn, 0,
                    SwigluBwd{(const bf16_t*)sh->G, 2 * sh->Is, sh->Is, nullptr, nullptr,
-                             (bf16_t*)sh->dG, (bf16_t*)sh->hw, sh->Is}};
+                             (bf16_t*)sh->dG, (bf16_t*)sh->hw, sh->Is, nullptr, 0}};
   }
   return launch_dgrad_cfg<DG_SWIGLU_BWD>(cfg, dout, H, sorted_token, T, down, (long long)I * H, H,
                                          H, nullptr, 0, nullptr, 0, tile_ws, N, E, I / bn, sb, s,

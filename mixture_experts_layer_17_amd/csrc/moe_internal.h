@@ -131,11 +131,15 @@ struct DgradShared {
 // so that any Is multiple of 128 fits.
 // w == NULL: every row's weight is 1 (a shared expert); sorted_slot NULL:
 // row p's weight is w[p].
+// dw_parts (optional, [N, dgrad1_weight_parts(I)] float): for each
+// expert-major row p the inner products <dout . down^T, h> over the
+// epilogue's column slices, which launch_weight_grad adds up.
+int dgrad1_weight_parts(int I);
 hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32_t* sorted_token,
                                     const void* down, int N, int H, int I, int E,
                                     const void* G, const float* w, const int32_t* sorted_slot,
                                     void* dG, void* hw, const void* tile_ws, hipStream_t s,
-                                    const DgradShared* sh = nullptr);
+                                    const DgradShared* sh = nullptr, float* dw_parts = nullptr);
 hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int N, int H, int I,
                                 int E, const int32_t* out_index, void* dX, const void* tile_ws,
                                 hipStream_t s, const DgradShared* sh = nullptr);
@@ -156,7 +160,9 @@ bool wgrad_can_fold(int M, int N, int Ma, int Na);
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const void* zero_row,
                         const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s,
                         const WgradAux* aux = nullptr);
-hipError_t launch_weight_grad(bool bf16, const void* dout, const void* y, int N, int k, int H,
+// d_weights [N] (flat slot order) from the first dgrad's P partial inner
+// products per expert-major row (dgrad1_weight_parts).
+hipError_t launch_weight_grad(const float* parts, int P, const int32_t* slot_pos, int N,
                               float* dw, hipStream_t s);
 // dL [T, E] for softmax or sigmoid scores times `scale`; when dL is zero
 // off the selection (renormalised or sigmoid) also dl_perm [N] (dL of each

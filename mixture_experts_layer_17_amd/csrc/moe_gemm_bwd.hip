@@ -37,21 +37,25 @@ using namespace lds;
 
 // The K loop shared by both kernels: a ring of STAGES LDS slots filled by
 // issue(slot, block); wait_blocks(n) leaves n blocks of this wave's copies
-// in flight.  A block holds KS k-steps of 16.  The fragments of the next
+// in flight (PRE: the caller has issued the first blocks itself).  A block
+// holds KS k-steps of 16.  The fragments of the next
 // k-step are read while the MFMAs of the current one run (read_b for the
 // whole step, then each m-tile's read_a right after its MFMAs are issued);
 // sched_barrier keeps that interleave.  One barrier per block sits before
 // its last k-step: it publishes the next block and retires the one just
 // read, whose slot is refilled at once.
-template <int TM, int TN, int STAGES, int KS, class Issue, class Wait, class ReadA, class ReadB>
+template <int TM, int TN, int STAGES, int KS, bool PRE = false, class Issue, class Wait,
+          class ReadA, class ReadB>
 __device__ __forceinline__ void pipelined_k_loop(int KT, unsigned char* smem, int stage_bytes,
                                                  Issue&& issue, Wait&& wait_blocks,
                                                  ReadA&& read_a, ReadB&& read_b,
                                                  f32x16_v (&acc)[TM][TN]) {
   static_assert(KS >= 2, "k-steps per block");
+  if constexpr (!PRE) {
 #pragma unroll
-  for (int p = 0; p < STAGES; ++p)
-    if (p < KT) issue(smem + p * stage_bytes, p);
+    for (int p = 0; p < STAGES; ++p)
+      if (p < KT) issue(smem + p * stage_bytes, p);
+  }
   if (KT <= 0) return;
   wait_blocks(min(STAGES, KT) - 1);
   __builtin_amdgcn_s_barrier();
@@ -468,7 +472,7 @@ struct wcfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, bool PERSIST = false>
 __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
     const bf16_t* __restrict__ gA, int g_lda, const bf16_t* __restrict__ gB, int g_ldb,
     const bf16_t* __restrict__ zero_row, const int32_t* __restrict__ offsets, int E, int M,
@@ -476,41 +480,62 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
   using G = wcfg<BM, BN, WM, WN, STAGES>;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  // ---- job (expert, m-tile, n-tile); consecutive jobs share an expert's rows
-  // Each XCD first takes an equal share of the dense problem's jobs (all
-  // of its rows each: the long ones go first), then of the grouped jobs.
+  // ---- jobs (expert, m-tile, n-tile); consecutive jobs share an expert's
+  // rows.  Each XCD takes an equal share of the dense problem's jobs (all of
+  // its rows each: the long ones go first), then of the grouped jobs.
+  // PERSIST: one work-group per CU walks its XCD's share with a stride; the
+  // next job's first block is copied into slot 0 while the current job's
+  // epilogue stages through the other slots, so the K loop of every job but
+  // the first starts on a landed block (measured 9 % faster at the prefill
+  // shape: the jobs are short, K being an expert's rows).
   const int m_tiles = M / BM, n_tiles = N / BN;
   const int g_jobs = E * m_tiles * n_tiles;
   const int d_per = (aux.jobs + NUM_XCD - 1) / NUM_XCD;
   const int g_per = (g_jobs + NUM_XCD - 1) / NUM_XCD;
   const int xcd = blockIdx.x % NUM_XCD;
-  const int local = blockIdx.x / NUM_XCD;
-  const bool dense = local < d_per;   // uniform over the work-group
-  int job;
-  if (dense) {
-    job = xcd * d_per + local;
-    if (job >= aux.jobs) return;
-  } else {
-    if (local - d_per >= g_per) return;
-    job = xcd * g_per + (local - d_per);
-    if (job >= g_jobs) return;
-  }
-  const int nt_of = dense ? aux.N / BN : n_tiles;
-  const int e = dense ? 0 : job / (m_tiles * n_tiles);
-  const int rem = dense ? job : job - e * m_tiles * n_tiles;
-  const int mt = rem / nt_of;
-  const int nt = rem - mt * nt_of;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int lo = dense ? 0 : offsets[e];
-  const int hi = dense ? aux.rows : max(offsets[e + 1], lo);
-  const int KT = (hi - lo + BK - 1) / BK;
-  const bf16_t* __restrict__ A = dense ? (const bf16_t*)aux.A : gA;
-  const int lda = dense ? aux.lda : g_lda;
-  const bf16_t* __restrict__ B = dense ? (const bf16_t*)aux.B : gB;
-  const int ldb = dense ? aux.ldb : g_ldb;
-  bf16_t* __restrict__ C = dense ? (bf16_t*)aux.C : gC;
-  const long long c_estride = dense ? 0 : g_c_estride;
-  const int ldc = dense ? aux.N : g_ldc;
+  const int lstride = PERSIST ? max(1, (int)(gridDim.x / NUM_XCD)) : (1 << 30);
+  // the first share index >= loc that holds a job, or -1 (uniform)
+  auto next_job = [&](int loc) {
+    while (loc < d_per + g_per) {
+      if (loc < d_per) {
+        if (xcd * d_per + loc < aux.jobs) return loc;
+      } else {
+        // grouped jobs of a share are contiguous: past the end, none follow
+        return xcd * g_per + (loc - d_per) < g_jobs ? loc : -1;
+      }
+      loc += lstride;
+    }
+    return -1;
+  };
+  struct Job {
+    int e, m0, n0, lo, hi, lda, ldb, ldc;   // rows [lo, hi) of expert e
+    const bf16_t* A;
+    const bf16_t* B;
+    bf16_t* C;
+    long long c_estride;
+  };
+  auto make_job = [&](int loc) {
+    Job J;
+    const bool dense = loc < d_per;
+    const int job = dense ? xcd * d_per + loc : xcd * g_per + (loc - d_per);
+    const int nt_of = dense ? aux.N / BN : n_tiles;
+    J.e = dense ? 0 : job / (m_tiles * n_tiles);
+    const int rem = dense ? job : job - J.e * m_tiles * n_tiles;
+    const int mt = rem / nt_of;
+    const int nt = rem - mt * nt_of;
+    J.m0 = mt * BM;
+    J.n0 = nt * BN;
+    J.lo = dense ? 0 : offsets[J.e];
+    J.hi = dense ? aux.rows : max(offsets[J.e + 1], J.lo);
+    J.A = dense ? (const bf16_t*)aux.A : gA;
+    J.lda = dense ? aux.lda : g_lda;
+    J.B = dense ? (const bf16_t*)aux.B : gB;
+    J.ldb = dense ? aux.ldb : g_ldb;
+    J.C = dense ? (bf16_t*)aux.C : gC;
+    J.c_estride = dense ? 0 : g_c_estride;
+    J.ldc = dense ? aux.N : g_ldc;
+    return J;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -521,7 +546,7 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
   // copy u of this wave moves 1 KB = 1024 / ROWB k-rows of the A or B tile;
   // lane q takes 16-byte piece p of k-row r, whose 32-byte segment is
   // swizzled by h(r)
-  int c_col[G::PER], c_row[G::PER], c_lds[G::PER];
+  int c_col0[G::PER], c_row[G::PER], c_lds[G::PER];
   bool c_isa[G::PER];
 #pragma unroll
   for (int u = 0; u < G::PER; ++u) {
@@ -535,18 +560,21 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
     const int seg = (p >> 1) ^ hswz(r);
     c_isa[u] = isa;
     c_row[u] = r;
-    c_col[u] = 16 * seg + 8 * (p & 1) + (isa ? m0 : n0);
+    c_col0[u] = 16 * seg + 8 * (p & 1);
     c_lds[u] = (isa ? 0 : G::A_BYTES) + local_inst * 1024;
   }
-  // source of copy u for K-block kb: expert-major row lo + 32 kb + r, or
-  // the zero row past the expert's end
+  // source of copy u for K-block kb of job I (the job whose blocks are
+  // being issued): expert-major row lo + 32 kb + r, or the zero row past
+  // the expert's end
+  Job I;
   auto issue = [&](unsigned char* base, int kb) {
 #pragma unroll
     for (int u = 0; u < G::PER; ++u) {
-      const int rg = lo + kb * BK + c_row[u];
-      const bf16_t* g = rg < hi ? (c_isa[u] ? A + (long long)rg * lda : B + (long long)rg * ldb)
-                                : zr;
-      copy16_to_lds(g + c_col[u], base + c_lds[u]);
+      const int rg = I.lo + kb * BK + c_row[u];
+      const bf16_t* g = rg < I.hi ? (c_isa[u] ? I.A + (long long)rg * I.lda + I.m0
+                                              : I.B + (long long)rg * I.ldb + I.n0)
+                                  : zr;
+      copy16_to_lds(g + c_col0[u], base + c_lds[u]);
     }
   };
   auto wait_blocks = [&](int nb) {
@@ -578,54 +606,85 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
     const i16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * rowb));
     return __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-
-  f32x16_v acc[G::TM][G::TN];
-#pragma unroll
-  for (int i = 0; i < G::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < G::TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
   auto read_a = [&](const unsigned char* base, int kk, int i) {
     return read_tr(base + a_off[i] + 16 * kk * G::A_ROWB, G::A_ROWB);
   };
   auto read_b = [&](const unsigned char* base, int kk, int j) {
     return read_tr(base + b_off[j] + 16 * kk * G::B_ROWB, G::B_ROWB);
   };
-  pipelined_k_loop<G::TM, G::TN, STAGES, 2>(KT, smem, G::STAGE_BYTES, issue, wait_blocks, read_a,
-                                         read_b, acc);
-
-  // ---- epilogue: acc[i][j][q] = C[m0 + (BM / WM) wm + 32 i + l % 32]
-  //                                [n0 + CW wn + 32 j + 8 (q / 4) + 4 hl + q % 4]
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
   const int l32 = lane & 31, hl = lane >> 5;
   constexpr int LPR = G::CW * 2 / 16;
   constexpr int RPI = 64 / LPR;
-  unsigned char* stg = smem + wave * 32 * G::OBP;
-  bf16_t* Ce = C + (long long)e * c_estride;
+  // PERSIST stages the output through slots 1 .. STAGES - 1 (slot 0 holds
+  // the next job's first block)
+  static_assert(!PERSIST || 32 * G::OBP * G::NW <= (STAGES - 1) * G::STAGE_BYTES, "staging");
+
+  int loc = next_job((int)(blockIdx.x / NUM_XCD));
+  if (loc < 0) return;
+  Job J = make_job(loc);   // the job being multiplied and stored
+  I = J;
+  int KT = (J.hi - J.lo + BK - 1) / BK;
 #pragma unroll
-  for (int i = 0; i < G::TM; ++i) {
+  for (int p = 0; p < STAGES; ++p)
+    if (p < KT) issue(smem + p * G::STAGE_BYTES, p);
+  f32x16_v acc[G::TM][G::TN];
+  for (;;) {
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j)
+    for (int i = 0; i < G::TM; ++i)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x16_v& v = acc[i][j];
-        const uint2 d = make_uint2(
-            (uint32_t)f32_to_bf16_bits(v[4 * a]) | ((uint32_t)f32_to_bf16_bits(v[4 * a + 1]) << 16),
-            (uint32_t)f32_to_bf16_bits(v[4 * a + 2]) | ((uint32_t)f32_to_bf16_bits(v[4 * a + 3]) << 16));
-        *reinterpret_cast<uint2*>(stg + l32 * G::OBP + 2 * (32 * j + 8 * a + 4 * hl)) = d;
+      for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    // the loop's first wait also covers anything issued before block 1,
+    // such as the previous job's output stores
+    pipelined_k_loop<G::TM, G::TN, STAGES, 2, true>(KT, smem, G::STAGE_BYTES, issue, wait_blocks,
+                                                     read_a, read_b, acc);
+    // ---- epilogue: acc[i][j][q] = C[m0 + (BM / WM) wm + 32 i + l % 32]
+    //                                 [n0 + CW wn + 32 j + 8 (q / 4) + 4 hl + q % 4]
+    __builtin_amdgcn_s_barrier();                 // every wave is done with the ring
+    asm volatile("" ::: "memory");
+    int nloc = -1, nKT = 0;
+    if constexpr (PERSIST) {
+      nloc = next_job(loc + lstride);
+      if (nloc >= 0) {
+        I = make_job(nloc);
+        nKT = (I.hi - I.lo + BK - 1) / BK;
+        if (nKT > 0) issue(smem, 0);
       }
-#pragma unroll
-    for (int rr = 0; rr < 32 / RPI; ++rr) {
-      const int r = rr * RPI + lane / LPR;
-      const int m = m0 + (BM / WM) * wm + 32 * i + r;
-      const uint2 x0 = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR));
-      const uint2 x1 = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR) + 8);
-      *reinterpret_cast<u32x4*>(Ce + (long long)m * ldc + n0 + wn * G::CW + 8 * (lane % LPR)) =
-          u32x4{x0.x, x0.y, x1.x, x1.y};
     }
+    unsigned char* stg = smem + (PERSIST ? G::STAGE_BYTES : 0) + wave * 32 * G::OBP;
+    bf16_t* Ce = J.C + (long long)J.e * J.c_estride;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x16_v& v = acc[i][j];
+          const uint2 d = make_uint2(
+              (uint32_t)f32_to_bf16_bits(v[4 * a]) | ((uint32_t)f32_to_bf16_bits(v[4 * a + 1]) << 16),
+              (uint32_t)f32_to_bf16_bits(v[4 * a + 2]) | ((uint32_t)f32_to_bf16_bits(v[4 * a + 3]) << 16));
+          *reinterpret_cast<uint2*>(stg + l32 * G::OBP + 2 * (32 * j + 8 * a + 4 * hl)) = d;
+        }
+#pragma unroll
+      for (int rr = 0; rr < 32 / RPI; ++rr) {
+        const int r = rr * RPI + lane / LPR;
+        const int m = J.m0 + (BM / WM) * wm + 32 * i + r;
+        const uint2 x0 = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR));
+        const uint2 x1 = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR) + 8);
+        *reinterpret_cast<u32x4*>(Ce + (long long)m * J.ldc + J.n0 + wn * G::CW + 8 * (lane % LPR)) =
+            u32x4{x0.x, x0.y, x1.x, x1.y};
+      }
+    }
+    if (nloc < 0) break;
+    __builtin_amdgcn_s_barrier();                 // the staged rows are read
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int p = 1; p < STAGES; ++p)
+      if (p < nKT) issue(smem + p * G::STAGE_BYTES, p);
+    J = I;
+    KT = nKT;
+    loc = nloc;
   }
 }
 
@@ -689,13 +748,13 @@ constexpr int kDgradBM[] = {128, 64, 32, 256};
 
 int dgrad_id(int cls, int n_cols) { return cls == 3 ? (n_cols % 256 == 0 ? 3 : 4) : cls; }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, bool PERSIST = false>
 hipError_t launch_wgrad_t(const void* A, int lda, const void* B, int ldb, const void* zero_row,
                           const int32_t* offsets, int E, int M, int N, void* C,
                           long long c_estride, int ldc, hipStream_t s, const WgradAux& aux) {
   using G = wcfg<BM, BN, WM, WN, STAGES>;
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)wgrad_kernel<BM, BN, WM, WN, STAGES>,
+      (const void*)wgrad_kernel<BM, BN, WM, WN, STAGES, PERSIST>,
       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   if (attr != hipSuccess) return attr;
   WgradAux a = aux;
@@ -703,7 +762,10 @@ hipError_t launch_wgrad_t(const void* A, int lda, const void* B, int ldb, const 
   const long long g_per = ((long long)E * (M / BM) * (N / BN) + NUM_XCD - 1) / NUM_XCD;
   const long long d_per = ((long long)a.jobs + NUM_XCD - 1) / NUM_XCD;
   const int grid = (int)std::max<long long>((g_per + d_per) * NUM_XCD, NUM_XCD);
-  hipLaunchKernelGGL((wgrad_kernel<BM, BN, WM, WN, STAGES>), dim3(grid), dim3(G::THREADS), G::LDS,
+  // PERSIST: one work-group per CU (the ring needs all of a CU's LDS); a
+  // multiple of NUM_XCD so that every XCD's share has the same walkers
+  const int g = PERSIST ? std::min(grid, NUM_CU) : grid;
+  hipLaunchKernelGGL((wgrad_kernel<BM, BN, WM, WN, STAGES, PERSIST>), dim3(g), dim3(G::THREADS), G::LDS,
                      s, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, (const bf16_t*)zero_row,
                      offsets, E, M, N, (bf16_t*)C, c_estride, ldc, a);
   return hipGetLastError();
@@ -791,8 +853,8 @@ hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const vo
   int bm, bn;
   wgrad_tile(M, N, &bm, &bn);
   if (bm == 256)
-    return launch_wgrad_t<256, 256, 2, 4, 3>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
-                                             (long long)M * N, N, s, a);
+    return launch_wgrad_t<256, 256, 2, 4, 3, true>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
+                                                   (long long)M * N, N, s, a);
   if (bn == 256)
     return launch_wgrad_t<128, 256, 2, 2, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
                                              (long long)M * N, N, s, a);

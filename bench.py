@@ -390,7 +390,7 @@ def bench_backward(args, wl):
         roof = {"bound": "mfma", "achieved": round(flops[dom] / t_dom / 1e12, 2),
                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = load_traffic(dom, wl.name)
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = int(bytes_[dom])
     roof["algorithmic_flops"] = int(flops[dom])

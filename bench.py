@@ -518,9 +518,12 @@ def load_traffic(kernel: str, workload: str):
         return None
     with open(p) as fh:
         t = json.load(fh)
-    src = os.path.join(ROOT, t["source"])
-    if not os.path.exists(src) or source_sha(src) != t.get("source_sha256"):
-        return None
+    # every source the measured kernels are built from must be unchanged
+    shas = t.get("sources") or {t["source"]: t.get("source_sha256")}
+    for rel, sha in shas.items():
+        src = os.path.join(ROOT, rel)
+        if not os.path.exists(src) or source_sha(src) != sha:
+            return None
     return t.get("traffic_bytes")
 
 

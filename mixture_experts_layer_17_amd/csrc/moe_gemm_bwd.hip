@@ -852,6 +852,13 @@ hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const vo
   if (a.rows > 0 && !wgrad_can_fold(M, N, a.M, a.N)) return hipErrorInvalidValue;
   int bm, bn;
   wgrad_tile(M, N, &bm, &bn);
+  // The persistent walk gives every work-group the same number of jobs; a
+  // folded dense problem (its jobs reduce all T rows, many times a grouped
+  // job's K) would leave the work-groups that draw one far behind, so with
+  // one the hardware's dynamic dispatch of one job per work-group is kept.
+  if (bm == 256 && a.rows > 0)
+    return launch_wgrad_t<256, 256, 2, 4, 3, false>(A, lda, B, ldb, zero_row, offsets, E, M, N,
+                                                    C, (long long)M * N, N, s, a);
   if (bm == 256)
     return launch_wgrad_t<256, 256, 2, 4, 3, true>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
                                                    (long long)M * N, N, s, a);

@@ -731,22 +731,34 @@ hipError_t launch_dgrad_cfg(int id, const void* X, int ldx, const int32_t* x_ind
     MOE_DG(2, 32, 128, 1, 2, 4, 32)
     MOE_DG(3, 256, 256, 2, 4, 2, 64)
     MOE_DG(4, 256, 128, 4, 2, 3, 64)
+    MOE_DG(5, 320, 256, 2, 4, 2, 64)
+    MOE_DG(6, 320, 128, 2, 2, 2, 64)
     default: return hipErrorInvalidValue;
   }
 #undef MOE_DG
 }
 
-// Row-tile classes (the tile list's height) and, within the 256-row class,
-// the 256-column config when the output width allows it.  The 256-row
-// configs take 64 k per block, so every row copy of both operands is one
-// whole 128-byte line: at the prefill shape that measured 323 against
-// 356 us for the second dgrad and, as 256 x 128 tiles on 4 x 2 waves, 253
-// against 270 us for the first (which keeps 128-column tiles: I / 256
-// column tiles leave the grid short of work-groups).  The shorter tiles
-// measured slower with 64 k and keep 32.
-constexpr int kDgradBM[] = {128, 64, 32, 256};
+// Row-tile classes (the tile list's height: 128, 64, 32, 256, 320 rows)
+// and, within the 256- and 320-row classes, the 256-column config when the
+// output width allows it.  The tall configs take 64 k per block, so every
+// row copy of both operands is one whole 128-byte line: at the prefill shape
+// that measured 323 against 356 us for the second dgrad and, as 256 x 128
+// tiles on 4 x 2 waves, 253 against 270 us for the first.  With groups of
+// 160 rows and more the second dgrad takes 320-row tiles, which hold a
+// whole expert up to 320 rows (280 against 344 us with the 256-row tiles,
+// which split the larger groups and read their weights twice); the first
+// keeps 256 x 128 (equal to 320 x 256 there, and 128-column tiles fit any
+// shared expert).  The shorter tiles measured slower with 64 k and keep 32.
+constexpr int kDgradBM[] = {128, 64, 32, 256, 320};
 
-int dgrad_id(int cls, int n_cols) { return cls == 3 ? (n_cols % 256 == 0 ? 3 : 4) : cls; }
+int dgrad_id(int cls, int n_cols) {
+  if (cls == 3) return n_cols % 256 == 0 ? 3 : 4;
+  if (cls == 4) return n_cols % 256 == 0 ? 5 : 6;
+  return cls;
+}
+
+// The config's output columns per tile.
+int dgrad_bn(int cfg) { return (cfg == 3 || cfg == 5) ? 256 : 128; }
 
 template <int BM, int BN, int WM, int WN, int STAGES, bool PERSIST = false>
 hipError_t launch_wgrad_t(const void* A, int lda, const void* B, int ldb, const void* zero_row,
@@ -775,14 +787,17 @@ hipError_t launch_wgrad_t(const void* A, int lda, const void* B, int ldb, const 
 
 int pick_dgrad_cfg(int N, int E) {
   const double mean_rows = E > 0 ? (double)N / E : 0.0;
-  return mean_rows >= 160.0 ? 3 : mean_rows >= 96.0 ? 0 : mean_rows >= 40.0 ? 1 : 2;
+  return mean_rows >= 160.0 ? 4 : mean_rows >= 96.0 ? 0 : mean_rows >= 40.0 ? 1 : 2;
 }
 
 int dgrad_bm(int id) { return kDgradBM[id]; }
 
-// The first dgrad uses the same row classes (its configs differ only in
-// the 256-row class, see launch_dgrad_down_swiglu).
-int pick_dgrad1_cfg(int N, int E) { return pick_dgrad_cfg(N, E); }
+// The first dgrad takes the 256-row class where the second takes 320 rows
+// (see launch_dgrad_down_swiglu), else the same class.
+int pick_dgrad1_cfg(int N, int E) {
+  const int c = pick_dgrad_cfg(N, E);
+  return c == 4 ? 3 : c;
+}
 
 int dgrad1_weight_parts(int I) { return I / kDgrad1Slice; }
 
@@ -794,8 +809,8 @@ hipError_t launch_dgrad_down_swiglu(int id, const void* dout, int T, const int32
   if (N <= 0) return hipSuccess;
   const SwigluBwd sb{(const bf16_t*)G, 2 * I,       I,  w, sorted_slot, (bf16_t*)dG,
                      (bf16_t*)hw,      I,           dw_parts, dgrad1_weight_parts(I)};
-  // 256-row tiles: always 128 columns wide
-  const int cfg = id == 3 ? 4 : id;
+  // the tall classes: always 128 columns wide
+  const int cfg = id == 3 ? 4 : id == 4 ? 6 : id;
   const int bn = 128;
   DgradAux aux{};
   if (sh) {
@@ -817,7 +832,7 @@ hipError_t launch_dgrad_gate_up(int id, const void* dG, const void* gate_up, int
   if (N <= 0) return hipSuccess;
   const SwigluBwd none{};
   const int cfg = dgrad_id(id, H);
-  const int bn = cfg == 3 ? 256 : 128;
+  const int bn = dgrad_bn(cfg);
   DgradAux aux{};
   if (sh)
     aux = DgradAux{(const bf16_t*)sh->dG, 2 * sh->Is, (const bf16_t*)sh->gate_up, 2 * sh->Is,

@@ -664,8 +664,8 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
                      fold ? &aux_gu : nullptr);
   mark(5);
   if (e == hipSuccess)
-    e = launch_router_weight_grad(bf16, x, w.x_perm, w.dL, w.dl_perm, w.offsets, T, E, H, sparse,
-                                  g.d_router_weight, g.d_router_bias, w.rw_part, s);
+    e = launch_router_weight_grad(bf16, x, w.sorted_token, w.dL, w.dl_perm, w.offsets, T, E, H,
+                                  sparse, g.d_router_weight, g.d_router_bias, w.rw_part, s);
   if (e == hipSuccess && shared && !fold)
     e = launch_wgrad(w.hw_s, Is, dout, H, w.zero, w.offs_s, 1, Is, H, g.d_shared_down, s);
   if (e == hipSuccess && shared && !fold)

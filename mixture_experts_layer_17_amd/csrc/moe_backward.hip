@@ -193,13 +193,15 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
 // passes: `splits` work-groups per expert each sum one contiguous share of
 // its rows into a partial, then the partials are added in order.  With
 // renormalised weights dL[t, e] is nonzero only where token t chose e, so
-// the rows are the expert's rows of the permutation (x_perm, dl_perm, both
-// expert-major); otherwise every token's x row with dL[t, e].
+// the rows are the expert's rows of the permutation (dl_perm expert-major,
+// x read through the permutation's row index, so the 16.8 MB of x serve all
+// k selections from the caches instead of an expert-major copy k times its
+// size); otherwise every token's x row with dL[t, e].
 template <typename T>
 __global__ __launch_bounds__(256) void router_weight_grad_part_kernel(
-    const T* __restrict__ rows_x, const float* __restrict__ g, const int32_t* __restrict__ offsets,
-    int T_, int E, int H, int sparse, int splits, float* __restrict__ part,
-    float* __restrict__ part_b) {
+    const T* __restrict__ rows_x, const int32_t* __restrict__ row_index,
+    const float* __restrict__ g, const int32_t* __restrict__ offsets, int T_, int E, int H,
+    int sparse, int splits, float* __restrict__ part, float* __restrict__ part_b) {
   const int e = blockIdx.x / splits, r = blockIdx.x - (blockIdx.x / splits) * splits;
   const int lo0 = sparse ? offsets[e] : 0;
   const int hi0 = sparse ? max(offsets[e + 1], lo0) : T_;
@@ -216,7 +218,8 @@ __global__ __launch_bounds__(256) void router_weight_grad_part_kernel(
       for (int u = 0; u < U; ++u) {
         const int p = min(p0 + u, hi - 1);
         gv[u] = p0 + u < hi ? (sparse ? g[p] : g[(size_t)p * E + e]) : 0.f;
-        load8(rows_x + (size_t)p * H + c, v[u]);
+        const int row = row_index ? min(max(row_index[p], 0), T_ - 1) : p;
+        load8(rows_x + (size_t)row * H + c, v[u]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -299,21 +302,21 @@ size_t router_weight_grad_ws(int E, int H) {
   return (size_t)kRouterSplits * E * (H + 1) * sizeof(float);
 }
 
-hipError_t launch_router_weight_grad(bool bf16, const void* x, const void* x_perm,
+hipError_t launch_router_weight_grad(bool bf16, const void* x, const int32_t* sorted_token,
                                      const float* dL, const float* dl_perm,
                                      const int32_t* offsets, int T, int E, int H, int sparse,
                                      float* dwr, float* dbias, void* ws, hipStream_t s) {
   float* part = (float*)ws;
   float* part_b = part + (size_t)kRouterSplits * E * H;
-  const void* rows = sparse ? x_perm : x;
+  const int32_t* idx = sparse ? sorted_token : nullptr;
   const float* g = sparse ? dl_perm : dL;
   const int grid = E * kRouterSplits;
   if (bf16)
     router_weight_grad_part_kernel<bf16_t><<<grid, 256, 0, s>>>(
-        (const bf16_t*)rows, g, offsets, T, E, H, sparse, kRouterSplits, part, part_b);
+        (const bf16_t*)x, idx, g, offsets, T, E, H, sparse, kRouterSplits, part, part_b);
   else
     router_weight_grad_part_kernel<float><<<grid, 256, 0, s>>>(
-        (const float*)rows, g, offsets, T, E, H, sparse, kRouterSplits, part, part_b);
+        (const float*)x, idx, g, offsets, T, E, H, sparse, kRouterSplits, part, part_b);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   router_weight_grad_sum_kernel<<<grid_for_total((long long)E * H), 256, 0, s>>>(

@@ -178,9 +178,10 @@ hipError_t launch_input_grad(bool bf16, const void* dX, const float* dL, const i
                              const void* wr, int T, int k, int E, int H, const void* add,
                              void* dx, hipStream_t s);
 // Router weight and bias gradients; ws holds router_weight_grad_ws(E, H)
-// bytes of partial sums.  sparse: rows from x_perm / dl_perm (expert-major).
+// bytes of partial sums.  sparse: the expert-major rows x[sorted_token[p]]
+// with dl_perm[p].
 size_t router_weight_grad_ws(int E, int H);
-hipError_t launch_router_weight_grad(bool bf16, const void* x, const void* x_perm,
+hipError_t launch_router_weight_grad(bool bf16, const void* x, const int32_t* sorted_token,
                                      const float* dL, const float* dl_perm,
                                      const int32_t* offsets, int T, int E, int H, int sparse,
                                      float* dwr, float* dbias, void* ws, hipStream_t s);

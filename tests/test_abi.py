@@ -116,3 +116,45 @@ def test_shared_expert_validation_and_workspace(lib):
         None, None, None, None, fake, ws(_lib.MOE_OP_LAYER, 4, 128, 64, 8, 2, 0, 8, 1), None,
         None)
     assert small(_lib.SharedExpert(fake, fake, 64)) == -4   # room for the routed part only
+
+
+def test_training_validation_and_workspace(lib):
+    ws = lambda *a: lib.moe_workspace_size(*a)
+    plain = ws(_lib.MOE_OP_LAYER_BACKWARD, 4096, 2048, 768, 128, 8, 0, 32768, 1)
+    shared = ws(_lib.MOE_OP_LAYER_BACKWARD, 4096, 2048, 768, 128, 8, 768, 32768, 1)
+    # dG [N, 2I], w h [N, I], dX [N, H] and the two expert-major copies [N, H]
+    assert plain >= 32768 * (2 * 768 + 768 + 3 * 2048) * 2
+    # the shared expert adds dG_s [T, 2Is], h_s [T, Is] and dx_s [T, H]
+    assert shared - plain >= 4096 * (3 * 768 + 2048) * 2
+    assert ws(_lib.MOE_OP_LAYER_BACKWARD, 64, 2048, 0, 128, 8, 0, 512, 1) == SIZE_MAX   # I = 0
+    fake = 4096  # never dereferenced: every call below fails validation
+    saved = _lib.TrainSaved(fake, fake, None)
+    big = 1 << 34
+    train = lambda T, I, dt, sv, wsb=big: lib.moe_layer_forward_train(
+        fake, fake, None, fake, fake, T, 256, I, 8, 2, 1, dt, None, None, fake, fake, fake, fake,
+        None, ctypes.addressof(sv) if sv is not None else None, fake, wsb, None, None)
+    assert train(16, 128, 0, saved) == -5          # float32 training is not built
+    assert train(16, 192, 1, saved) == -5          # I % 128
+    assert train(16, 128, 1, None) == -1           # no saved-activation buffers
+    assert train(16, 128, 1, _lib.TrainSaved(None, fake, None)) == -1
+    assert train(16, 128, 1, _lib.TrainSaved(fake + 2, fake, None)) == -7
+    grads = _lib.LayerGrads(fake, fake, None, fake, fake, None, None, None)
+    bwd = lambda T, I, dt, sv, g, wsb=big, sh=None: lib.moe_layer_backward(
+        fake, fake, fake, fake, T, 256, I, 8, 2, 1, dt, None,
+        ctypes.addressof(sh) if sh is not None else None, fake, fake, fake,
+        ctypes.addressof(sv) if sv is not None else None, fake,
+        ctypes.addressof(g) if g is not None else None, fake, wsb, None, None)
+    assert bwd(16, 128, 0, saved, grads) == -5
+    assert bwd(16, 192, 1, saved, grads) == -5
+    assert bwd(16, 128, 1, None, grads) == -1
+    assert bwd(16, 128, 1, saved, None) == -1
+    assert bwd(16, 128, 1, saved, _lib.LayerGrads(None, fake, None, fake, fake, None, None,
+                                                  None)) == -1
+    assert bwd(16, 128, 1, saved, _lib.LayerGrads(fake, fake, None, fake + 4, fake, None, None,
+                                                  None)) == -7
+    assert bwd(16, 128, 1, saved, grads, wsb=16) == -4
+    assert bwd(-1, 128, 1, saved, grads) == -2
+    # a shared expert needs its saved pre-activations and gradient buffers
+    sh = _lib.SharedExpert(fake, fake, 128)
+    assert bwd(16, 128, 1, saved, grads, sh=sh) == -1
+    assert bwd(16, 128, 1, saved, grads, sh=_lib.SharedExpert(fake, fake, 64)) == -5

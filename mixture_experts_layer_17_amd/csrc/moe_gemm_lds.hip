@@ -149,7 +149,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int g = lane >> 4, r16 = lane & 15;
   const int n0 = SWIGLU ? nt * (BN / 2) : nt * BN;
   const bf16_t* We = W + (long long)e * w_estride;
 

@@ -1,4 +1,5 @@
-"""CPU oracle for the Mixture-of-Experts layer forward.
+"""CPU oracle for the Mixture-of-Experts layer: the forward, its router
+variants and shared expert, and the layer backward.
 
 TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, obviously correct
 statement of what the layer computes.  Only the test suite, the package's

@@ -162,6 +162,7 @@ struct BwdWs {
   void *dG, *hw, *dX, *x_perm, *dout_perm, *zero, *rw_part;
   void *dG_s, *hw_s, *dx_s;   // shared expert (Is > 0)
   int32_t* offs_s;
+  unsigned* counters;         // 2 x kWgradCounters, zeroed with the zero row
   size_t zero_bytes, total;
 };
 
@@ -198,8 +199,11 @@ BwdWs bwd_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt, int Is
     w.dx_s = take((size_t)T * H * esize(dt));
     w.offs_s = (int32_t*)take(2 * sizeof(int32_t));
   }
-  w.zero_bytes = al((size_t)std::max(std::max(H, 2 * I), 2 * Is) * esize(dt));
+  // one zero row, then the two wgrad launches' job counters (zeroed with it)
+  const size_t row_bytes = al((size_t)std::max(std::max(H, 2 * I), 2 * Is) * esize(dt));
+  w.zero_bytes = row_bytes + al(2 * kWgradCounters * sizeof(unsigned));
   w.zero = take(w.zero_bytes);
+  w.counters = base ? (unsigned*)((char*)w.zero + row_bytes) : nullptr;
   w.total = off;
   return w;
 }
@@ -657,11 +661,11 @@ int moe_layer_backward(const void* x, const void* wr, const void* gate_up, const
   const WgradAux aux_gu{x, H, w.dG_s, 2 * Is, T, H, 2 * Is, g.d_shared_gate_up, 0};
   if (e == hipSuccess)
     e = launch_wgrad(w.hw, I, w.dout_perm, H, w.zero, w.offsets, E, I, H, g.d_down, s,
-                     fold ? &aux_dn : nullptr);
+                     fold ? &aux_dn : nullptr, w.counters);
   mark(4);
   if (e == hipSuccess)
     e = launch_wgrad(w.x_perm, H, w.dG, 2 * I, w.zero, w.offsets, E, H, 2 * I, g.d_gate_up, s,
-                     fold ? &aux_gu : nullptr);
+                     fold ? &aux_gu : nullptr, w.counters + kWgradCounters);
   mark(5);
   if (e == hipSuccess)
     e = launch_router_weight_grad(bf16, x, w.sorted_token, w.dL, w.dl_perm, w.offsets, T, E, H,

@@ -476,18 +476,22 @@ template <int BM, int BN, int WM, int WN, int STAGES, bool PERSIST = false>
 __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
     const bf16_t* __restrict__ gA, int g_lda, const bf16_t* __restrict__ gB, int g_ldb,
     const bf16_t* __restrict__ zero_row, const int32_t* __restrict__ offsets, int E, int M,
-    int N, bf16_t* __restrict__ gC, long long g_c_estride, int g_ldc, WgradAux aux) {
+    int N, bf16_t* __restrict__ gC, long long g_c_estride, int g_ldc, WgradAux aux,
+    unsigned* __restrict__ job_counters) {
   using G = wcfg<BM, BN, WM, WN, STAGES>;
   extern __shared__ __align__(16) unsigned char smem[];
 
   // ---- jobs (expert, m-tile, n-tile); consecutive jobs share an expert's
   // rows.  Each XCD takes an equal share of the dense problem's jobs (all of
   // its rows each: the long ones go first), then of the grouped jobs.
-  // PERSIST: one work-group per CU walks its XCD's share with a stride; the
-  // next job's first block is copied into slot 0 while the current job's
-  // epilogue stages through the other slots, so the K loop of every job but
-  // the first starts on a landed block (measured 9 % faster at the prefill
-  // shape: the jobs are short, K being an expert's rows).
+  // PERSIST: one work-group per CU takes the jobs of its XCD's share one at
+  // a time from that XCD's counter in job_counters (zero at launch; one
+  // vector atomic per job, issued a job ahead), so the CUs of an XCD stay
+  // balanced even when a share mixes long dense jobs with short grouped
+  // ones; the next job's first block is copied into slot 0 while the
+  // current job's epilogue stages through the other slots, so the K loop of
+  // every job but the first starts on a landed block (measured 9 % faster at
+  // the prefill shape: the jobs are short, K being an expert's rows).
   const int m_tiles = M / BM, n_tiles = N / BN;
   const int g_jobs = E * m_tiles * n_tiles;
   const int d_per = (aux.jobs + NUM_XCD - 1) / NUM_XCD;
@@ -514,10 +518,17 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
     bf16_t* C;
     long long c_estride;
   };
+  // PERSIST: the XCD's share without holes, dense jobs first
+  const int d_lo = min(xcd * d_per, aux.jobs);
+  const int d_cnt = max(0, min(d_per, aux.jobs - d_lo));
+  const int g_lo = min(xcd * g_per, g_jobs);
+  const int g_cnt = max(0, min(g_per, g_jobs - g_lo));
+  const int share = d_cnt + g_cnt;
   auto make_job = [&](int loc) {
     Job J;
-    const bool dense = loc < d_per;
-    const int job = dense ? xcd * d_per + loc : xcd * g_per + (loc - d_per);
+    const bool dense = PERSIST ? loc < d_cnt : loc < d_per;
+    const int job = PERSIST ? (dense ? d_lo + loc : g_lo + (loc - d_cnt))
+                            : (dense ? xcd * d_per + loc : xcd * g_per + (loc - d_per));
     const int nt_of = dense ? aux.N / BN : n_tiles;
     J.e = dense ? 0 : job / (m_tiles * n_tiles);
     const int rem = dense ? job : job - J.e * m_tiles * n_tiles;
@@ -619,8 +630,23 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
   // the next job's first block)
   static_assert(!PERSIST || 32 * G::OBP * G::NW <= (STAGES - 1) * G::STAGE_BYTES, "staging");
 
-  int loc = next_job((int)(blockIdx.x / NUM_XCD));
-  if (loc < 0) return;
+  // PERSIST: thread 0 takes share indices from the XCD's counter; the one
+  // for the next job is taken while this one runs and published through
+  // LDS at its epilogue
+  unsigned* const ctr = PERSIST ? job_counters + xcd : nullptr;
+  int* const s_loc = reinterpret_cast<int*>(smem + G::LDS);
+  int pref = 0;
+  int loc;
+  if constexpr (PERSIST) {
+    if (tid == 0) s_loc[0] = (int)atomicAdd(ctr, 1u);
+    __syncthreads();
+    loc = s_loc[0];
+    if (loc >= share) return;
+    if (tid == 0) pref = (int)atomicAdd(ctr, 1u);
+  } else {
+    loc = next_job((int)(blockIdx.x / NUM_XCD));
+    if (loc < 0) return;
+  }
   Job J = make_job(loc);   // the job being multiplied and stored
   I = J;
   int KT = (J.hi - J.lo + BK - 1) / BK;
@@ -641,16 +667,21 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
                                                      read_a, read_b, acc);
     // ---- epilogue: acc[i][j][q] = C[m0 + (BM / WM) wm + 32 i + l % 32]
     //                                 [n0 + CW wn + 32 j + 8 (q / 4) + 4 hl + q % 4]
-    __builtin_amdgcn_s_barrier();                 // every wave is done with the ring
-    asm volatile("" ::: "memory");
     int nloc = -1, nKT = 0;
     if constexpr (PERSIST) {
-      nloc = next_job(loc + lstride);
+      if (tid == 0) s_loc[0] = pref;
+      __syncthreads();                            // the ring is free; the index is visible
+      nloc = s_loc[0];
+      if (nloc >= share) nloc = -1;
       if (nloc >= 0) {
+        if (tid == 0) pref = (int)atomicAdd(ctr, 1u);
         I = make_job(nloc);
         nKT = (I.hi - I.lo + BK - 1) / BK;
         if (nKT > 0) issue(smem, 0);
       }
+    } else {
+      __builtin_amdgcn_s_barrier();               // every wave is done with the ring
+      asm volatile("" ::: "memory");
     }
     unsigned char* stg = smem + (PERSIST ? G::STAGE_BYTES : 0) + wave * 32 * G::OBP;
     bf16_t* Ce = J.C + (long long)J.e * J.c_estride;
@@ -763,11 +794,16 @@ int dgrad_bn(int cfg) { return (cfg == 3 || cfg == 5) ? 256 : 128; }
 template <int BM, int BN, int WM, int WN, int STAGES, bool PERSIST = false>
 hipError_t launch_wgrad_t(const void* A, int lda, const void* B, int ldb, const void* zero_row,
                           const int32_t* offsets, int E, int M, int N, void* C,
-                          long long c_estride, int ldc, hipStream_t s, const WgradAux& aux) {
+                          long long c_estride, int ldc, hipStream_t s, const WgradAux& aux,
+                          unsigned* job_counters = nullptr) {
   using G = wcfg<BM, BN, WM, WN, STAGES>;
+  // PERSIST: 16 more bytes publish the next job's share index
+  constexpr int LDS = G::LDS + (PERSIST ? 16 : 0);
+  static_assert(LDS <= 160 * 1024, "LDS");
+  if (PERSIST && !job_counters) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)wgrad_kernel<BM, BN, WM, WN, STAGES, PERSIST>,
-      hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+      hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (attr != hipSuccess) return attr;
   WgradAux a = aux;
   a.jobs = a.rows > 0 ? (a.M / BM) * (a.N / BN) : 0;
@@ -777,9 +813,9 @@ hipError_t launch_wgrad_t(const void* A, int lda, const void* B, int ldb, const 
   // PERSIST: one work-group per CU (the ring needs all of a CU's LDS); a
   // multiple of NUM_XCD so that every XCD's share has the same walkers
   const int g = PERSIST ? std::min(grid, NUM_CU) : grid;
-  hipLaunchKernelGGL((wgrad_kernel<BM, BN, WM, WN, STAGES, PERSIST>), dim3(g), dim3(G::THREADS), G::LDS,
+  hipLaunchKernelGGL((wgrad_kernel<BM, BN, WM, WN, STAGES, PERSIST>), dim3(g), dim3(G::THREADS), LDS,
                      s, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, (const bf16_t*)zero_row,
-                     offsets, E, M, N, (bf16_t*)C, c_estride, ldc, a);
+                     offsets, E, M, N, (bf16_t*)C, c_estride, ldc, a, job_counters);
   return hipGetLastError();
 }
 
@@ -861,22 +897,18 @@ bool wgrad_can_fold(int M, int N, int Ma, int Na) {
 
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const void* zero_row,
                         const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s,
-                        const WgradAux* aux) {
+                        const WgradAux* aux, unsigned* job_counters) {
   const WgradAux none{nullptr, 0, nullptr, 0, 0, 0, 0, nullptr, 0};
   const WgradAux& a = aux ? *aux : none;
   if (a.rows > 0 && !wgrad_can_fold(M, N, a.M, a.N)) return hipErrorInvalidValue;
   int bm, bn;
   wgrad_tile(M, N, &bm, &bn);
-  // The persistent walk gives every work-group the same number of jobs; a
-  // folded dense problem (its jobs reduce all T rows, many times a grouped
-  // job's K) would leave the work-groups that draw one far behind, so with
-  // one the hardware's dynamic dispatch of one job per work-group is kept.
-  if (bm == 256 && a.rows > 0)
+  if (bm == 256 && job_counters)
+    return launch_wgrad_t<256, 256, 2, 4, 3, true>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
+                                                   (long long)M * N, N, s, a, job_counters);
+  if (bm == 256)
     return launch_wgrad_t<256, 256, 2, 4, 3, false>(A, lda, B, ldb, zero_row, offsets, E, M, N,
                                                     C, (long long)M * N, N, s, a);
-  if (bm == 256)
-    return launch_wgrad_t<256, 256, 2, 4, 3, true>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
-                                                   (long long)M * N, N, s, a);
   if (bn == 256)
     return launch_wgrad_t<128, 256, 2, 2, 4>(A, lda, B, ldb, zero_row, offsets, E, M, N, C,
                                              (long long)M * N, N, s, a);

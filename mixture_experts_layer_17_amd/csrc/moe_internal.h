@@ -157,9 +157,12 @@ struct WgradAux {
 bool wgrad_can_fold(int M, int N, int Ma, int Na);
 // C[e] = A_e^T B_e over the expert-major rows [offsets[e], offsets[e + 1]);
 // `aux` (when wgrad_can_fold) adds a dense problem to the same launch.
+// job_counters (optional): kWgradCounters unsigned zeros, used up by the
+// launch; with them the 256 x 256 tiles run the persistent kernel.
+constexpr int kWgradCounters = 8;
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const void* zero_row,
                         const int32_t* offsets, int E, int M, int N, void* C, hipStream_t s,
-                        const WgradAux* aux = nullptr);
+                        const WgradAux* aux = nullptr, unsigned* job_counters = nullptr);
 // d_weights [N] (flat slot order) from the first dgrad's P partial inner
 // products per expert-major row (dgrad1_weight_parts).
 hipError_t launch_weight_grad(const float* parts, int P, const int32_t* slot_pos, int N,

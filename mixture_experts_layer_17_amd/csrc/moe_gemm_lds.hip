@@ -15,7 +15,9 @@
 //     its LDS slot, which realises an XOR swizzle of the 4 chunks of a row
 //     by f(row) = (row ^ (row >> 2)) & 3.  Reads are ds_read_b128.
 //   * weights: 32 rows (k) x BN columns in their natural [k][n] layout
-//     (n contiguous), loaded the same way with 32-byte segments of a row
+//     (n contiguous), loaded the same way (WNT: with the non-temporal
+//     hint, for launches whose experts mostly fit one row tile, so that no
+//     other job re-reads a weight tile) with 32-byte segments of a row
 //     XOR-swizzled by h(row) = ((row & 3) << 1) | ((row >> 3) & 1).  The MFMA
 //     operand needs 8 consecutive k of one column per lane; two
 //     ds_read_b64_tr_b16 deliver that: within each 16-lane group, lane s
@@ -85,7 +87,7 @@ struct lcfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU, int KB>
+template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU, int KB, bool WNT>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     const bf16_t* __restrict__ gX, int g_ldx, const int32_t* __restrict__ g_x_index,
     int g_x_rows, const bf16_t* __restrict__ gW, long long g_w_estride, int g_ldw, int g_K,
@@ -197,7 +199,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     }
 #pragma unroll
     for (int u = 0; u < G::B_PER; ++u) {
-      copy16_to_lds(b_src[u], base + b_lds[u]);
+      if constexpr (WNT) copy16_to_lds_nt(b_src[u], base + b_lds[u]);
+      else copy16_to_lds(b_src[u], base + b_lds[u]);
       b_src[u] += (long long)KB * ldw;
     }
   };
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU, int KB>
+template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU, int KB, bool WNT>
 hipError_t launch_lds(const void* X, int ldx, const int32_t* x_index, int x_rows, const void* W,
                       long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
                       const int32_t* c_index, int c_rows, const int4* tiles,
@@ -497,10 +500,10 @@ hipError_t launch_lds(const void* X, int ldx, const int32_t* x_index, int x_rows
                       const DenseAux& aux, void* g_save) {
   using G = lcfg<BM, BN, WM, WN, STAGES, SWIGLU, KB>;
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU, KB>,
+      (const void*)gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU, KB, WNT>,
       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU, KB>), dim3(grid),
+  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, WM, WN, STAGES, SWIGLU, KB, WNT>), dim3(grid),
                      dim3(G::THREADS), G::LDS, s, (const bf16_t*)X, ldx, x_index, x_rows,
                      (const bf16_t*)W, w_estride, ldw, K, up_off, (bf16_t*)C, ldc, c_index,
                      c_rows, tiles, tiles_count, n_ntiles, aux, (bf16_t*)g_save);
@@ -519,30 +522,43 @@ struct LdsCfg { int BM, BN; };
 //     activation row copy is one whole 128-byte line (measured 2-4 % faster
 //     than 14 at the prefill shape; for the shorter tiles 64 k per block was
 //     slower)
+// The configs the grouped picker returns (11, 12, 13, 15) also come with
+// non-temporal weight copies (WNT), taken when the mean rows per expert fit
+// one row tile.
 constexpr LdsCfg kLds[] = {{256, 256}, {128, 256}, {64, 256}, {32, 256}, {320, 256},
                            {320, 256}};
 
-hipError_t launch_lds_cfg(bool swiglu, int id, const void* X, int ldx, const int32_t* x_index,
-                          int x_rows, const void* W, long long w_estride, int ldw, int K,
-                          int up_off, void* C, int ldc, const int32_t* c_index, int c_rows,
+hipError_t launch_lds_cfg(bool swiglu, int id, bool wnt, const void* X, int ldx,
+                          const int32_t* x_index, int x_rows, const void* W,
+                          long long w_estride, int ldw, int K, int up_off, void* C, int ldc,
+                          const int32_t* c_index, int c_rows,
                           const int4* tiles, const int32_t* tiles_count, int n_ntiles, int grid,
                           hipStream_t s, const DenseAux& aux, void* g_save) {
 #define MOE_ARGS X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C, ldc, c_index, c_rows, \
                  tiles, tiles_count, n_ntiles, grid, s, aux, g_save
-#define MOE_CASE(ID, BM, BN, WM, WN, ST, KB)                                \
-  case ID:                                                                \
-    return swiglu ? launch_lds<BM, BN, WM, WN, ST, true, KB>(MOE_ARGS)    \
-                  : launch_lds<BM, BN, WM, WN, ST, false, KB>(MOE_ARGS);
+#define MOE_LAUNCH(BM, BN, WM, WN, ST, KB, NT)                                  \
+  (swiglu ? launch_lds<BM, BN, WM, WN, ST, true, KB, NT>(MOE_ARGS)            \
+          : launch_lds<BM, BN, WM, WN, ST, false, KB, NT>(MOE_ARGS))
+// configs the grouped picker returns come in both cache-hint variants
+#define MOE_CASE2(ID, BM, BN, WM, WN, ST, KB)                                   \
+  case ID:                                                                    \
+    return wnt ? MOE_LAUNCH(BM, BN, WM, WN, ST, KB, true)                     \
+               : MOE_LAUNCH(BM, BN, WM, WN, ST, KB, false);
+#define MOE_CASE1(ID, BM, BN, WM, WN, ST, KB)                                   \
+  case ID:                                                                    \
+    return MOE_LAUNCH(BM, BN, WM, WN, ST, KB, false);
   switch (id) {
-    MOE_CASE(10, 256, 256, 2, 2, 4, 32)
-    MOE_CASE(11, 128, 256, 2, 2, 4, 32)
-    MOE_CASE(12, 64, 256, 1, 4, 4, 32)
-    MOE_CASE(13, 32, 256, 1, 4, 4, 32)
-    MOE_CASE(14, 320, 256, 2, 4, 4, 32)
-    MOE_CASE(15, 320, 256, 2, 4, 2, 64)
+    MOE_CASE1(10, 256, 256, 2, 2, 4, 32)
+    MOE_CASE2(11, 128, 256, 2, 2, 4, 32)
+    MOE_CASE2(12, 64, 256, 1, 4, 4, 32)
+    MOE_CASE2(13, 32, 256, 1, 4, 4, 32)
+    MOE_CASE1(14, 320, 256, 2, 4, 4, 32)
+    MOE_CASE2(15, 320, 256, 2, 4, 2, 64)
     default: return hipErrorInvalidValue;
   }
-#undef MOE_CASE
+#undef MOE_CASE1
+#undef MOE_CASE2
+#undef MOE_LAUNCH
 #undef MOE_ARGS
 }
 
@@ -563,7 +579,10 @@ GemmTileCfg pick_lds_cfg(int N, int E, int cols, bool swiglu) {
   else if (mean_rows >= 64.0) id = 11;
   else if (mean_rows >= 24.0) id = 12;
   else id = 13;
-  return GemmTileCfg{kLds[id - 10].BM, kLds[id - 10].BN, id};
+  // mean rows within one row tile: each weight tile is read by about one
+  // job, so its copies take the non-temporal hint (copy16_to_lds_nt)
+  const int wnt = mean_rows <= kLds[id - 10].BM ? 1 : 0;
+  return GemmTileCfg{kLds[id - 10].BM, kLds[id - 10].BN, id, wnt};
 }
 
 GemmTileCfg pick_lds_dense_cfg(int rows, int cols, bool swiglu) {
@@ -610,7 +629,7 @@ hipError_t launch_lds_gemm(bool swiglu, const GemmTileCfg& c, const void* X, int
   const long long g_per = (max_tiles * n_ntiles + NUM_XCD - 1) / NUM_XCD;
   const long long d_per = ((long long)a.jobs + NUM_XCD - 1) / NUM_XCD;
   const int grid = (int)std::max<long long>((g_per + d_per) * NUM_XCD, NUM_XCD);
-  return launch_lds_cfg(swiglu, c.id, X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C,
+  return launch_lds_cfg(swiglu, c.id, c.wnt != 0, X, ldx, x_index, x_rows, W, w_estride, ldw, K, up_off, C,
                         ldc, c_index, c_rows, tiles, count, n_ntiles, grid, s, a, g_save);
 }
 

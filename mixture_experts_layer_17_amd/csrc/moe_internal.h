@@ -12,6 +12,7 @@ struct GemmTileCfg {
   int BM;        // rows per tile
   int BN;        // B columns per tile (SwiGLU: gate half + up half)
   int id;        // which compiled instance
+  int wnt = 0;   // LDS configs: weight copies with the non-temporal hint
 };
 
 // Router: logits, top-k ids/weights, optional counts (counts must be zeroed

@@ -37,8 +37,8 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&f)[8]) {
-  const chunk8<T> c = load_chunk<T>(p);
+__device__ __forceinline__ void load8(const T* p, float (&f)[8], bool stream = false) {
+  const chunk8<T> c = stream ? load_chunk_stream<T>(p) : load_chunk<T>(p);
   if constexpr (sizeof(T) == 2) {
     const uint32_t* d = reinterpret_cast<const uint32_t*>(&c.v);
 #pragma unroll
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       float v[8];
-      load8(dX + ((size_t)t * k + j) * H + c, v);
+      load8(dX + ((size_t)t * k + j) * H + c, v, true);   // read once
 #pragma unroll
       for (int x = 0; x < 8; ++x) acc[x] += v[x];
     }

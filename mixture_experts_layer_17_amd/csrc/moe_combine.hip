@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
       const int src = slot_pos ? slot_pos[i] : i;
       if (src < 0 || src >= N) continue;
       const float wt = w ? w[i] : 1.0f;
-      const chunk8<T> v = load_chunk<T>(y + (size_t)src * H + 8 * c);
+      const chunk8<T> v = load_chunk_stream<T>(y + (size_t)src * H + 8 * c);
       if constexpr (sizeof(T) == 2) {
         const uint32_t* d = reinterpret_cast<const uint32_t*>(&v.v);
 #pragma unroll

@@ -69,6 +69,20 @@ __device__ __forceinline__ chunk8<float> load_chunk<float>(const float* p) {
   return c;
 }
 
+// The same load with the non-temporal hint, for rows read once (the expert
+// outputs the combine sums, the per-slot input gradients).
+template <typename T>
+__device__ __forceinline__ chunk8<T> load_chunk_stream(const T* p) {
+  chunk8<T> c;
+  if constexpr (sizeof(T) == 2) {
+    c.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  } else {
+    c.lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    c.hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
+  }
+  return c;
+}
+
 template <typename T>
 __device__ __forceinline__ chunk8<T> zero_chunk() {
   chunk8<T> c;

@@ -703,8 +703,10 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
         const int m = J.m0 + (BM / WM) * wm + 32 * i + r;
         const uint2 x0 = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR));
         const uint2 x1 = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR) + 8);
-        *reinterpret_cast<u32x4*>(Ce + (long long)m * J.ldc + J.n0 + wn * G::CW + 8 * (lane % LPR)) =
-            u32x4{x0.x, x0.y, x1.x, x1.y};
+        // the weight gradients are not read again here: non-temporal stores
+        __builtin_nontemporal_store(
+            u32x4{x0.x, x0.y, x1.x, x1.y},
+            reinterpret_cast<u32x4*>(Ce + (long long)m * J.ldc + J.n0 + wn * G::CW + 8 * (lane % LPR)));
       }
     }
     if (nloc < 0) break;

@@ -360,9 +360,10 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
         const uint2 hi = *reinterpret_cast<const uint2*>(stg + r * G::OBP + 16 * (lane % LPR) + 8);
         if (m < rows) {
           const int dst = c_index ? c_index[row0 + m] : row0 + m;
-          if (dst >= 0 && dst < c_rows)
-            *reinterpret_cast<u32x4*>(C + (long long)dst * ldc + n0 + wn * G::CW +
-                                      8 * (lane % LPR)) = u32x4{lo.x, lo.y, hi.x, hi.y};
+          if (dst >= 0 && dst < c_rows)   // read once, by the input gradient
+            __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y},
+                                        reinterpret_cast<u32x4*>(C + (long long)dst * ldc + n0 +
+                                                                 wn * G::CW + 8 * (lane % LPR)));
         }
       }
     }

@@ -452,6 +452,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
         const uint2 lo = *reinterpret_cast<const uint2*>(stg + r * OBP + 16 * (lane % LPR));
         const uint2 hi = *reinterpret_cast<const uint2*>(stg + r * OBP + 16 * (lane % LPR) + 8);
         const int dst = dsts[i][rr];
+        // plain stores: h is re-read by every n-tile of the second GEMM and
+        // the second GEMM's rows by the combine right after (non-temporal
+        // stores here slowed the combine by 15 %)
         if (dst >= 0 && dst < c_rows)
           *reinterpret_cast<u32x4*>(C + (long long)dst * ldc + n0 + wn * G::CW + 8 * (lane % LPR)) =
               u32x4{lo.x, lo.y, hi.x, hi.y};
@@ -480,10 +483,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
               const uint2 hi =
                   *reinterpret_cast<const uint2*>(stg + r * OBP + 16 * (lane % LPR) + 8);
               const int dst = dsts[i][rr];
-              if (dst >= 0 && dst < c_rows)
-                *reinterpret_cast<u32x4*>(gs + (long long)dst * (2 * up_off) + half * up_off +
-                                          n0 + wn * G::CW + 8 * (lane % LPR)) =
-                    u32x4{lo.x, lo.y, hi.x, hi.y};
+              if (dst >= 0 && dst < c_rows)   // read by the backward only
+                __builtin_nontemporal_store(
+                    u32x4{lo.x, lo.y, hi.x, hi.y},
+                    reinterpret_cast<u32x4*>(gs + (long long)dst * (2 * up_off) + half * up_off +
+                                             n0 + wn * G::CW + 8 * (lane % LPR)));
             }
           }
         }

@@ -89,6 +89,8 @@ def test_layer_tiny_fp32(moe):
     dict(T=70, H=256, I=128, E=1, top_k=1),       # one expert
     dict(T=200, H=256, I=128, E=32, top_k=8),     # ~50 rows per expert
     dict(T=150, H=512, I=192, E=8, top_k=2),      # K-blocks not a multiple of the stages
+    dict(T=800, H=256, I=128, E=4, top_k=2),      # ~400 rows per expert: 320-row tiles, plain weight copies
+    dict(T=300, H=256, I=128, E=4, top_k=2),      # ~150 rows per expert: 128-row tiles, plain weight copies
 ])
 def test_layer_small_bf16(moe, shape):
     wl = workloads.make_layer(f"small_{shape['T']}", norm_topk_prob=True, seed=1, **shape)

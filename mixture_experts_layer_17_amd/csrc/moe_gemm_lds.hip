@@ -520,12 +520,12 @@ struct LdsCfg { int BM, BN; };
 // 11: 128 x 256, 2 x 2 waves,  64 x 128
 // 12:  64 x 256, 1 x 4 waves,  64 x  64
 // 13:  32 x 256, 1 x 4 waves,  32 x  64   (decode)
-// 14: 320 x 256, 2 x 4 waves, 160 x  64   (2 waves per SIMD; one tile per
-//     expert when groups hold up to 320 rows)
-// 15: the 320 x 256 tile with 64 k per block in two stages, so every
-//     activation row copy is one whole 128-byte line (measured 2-4 % faster
-//     than 14 at the prefill shape; for the shorter tiles 64 k per block was
-//     slower)
+// 14: (retired) the 320 x 256 tile below with 32 k per block in four
+//     stages, measured 2-4 % slower than 15 at the prefill shape
+// 15: 320 x 256, 2 x 4 waves, 160 x  64   (2 waves per SIMD; one tile per
+//     expert when groups hold up to 320 rows), 64 k per block in two
+//     stages, so every activation row copy is one whole 128-byte line (for
+//     the shorter tiles 64 k per block was slower)
 // The configs the grouped picker returns (11, 12, 13, 15) also come with
 // non-temporal weight copies (WNT), taken when the mean rows per expert fit
 // one row tile.
@@ -556,7 +556,6 @@ hipError_t launch_lds_cfg(bool swiglu, int id, bool wnt, const void* X, int ldx,
     MOE_CASE2(11, 128, 256, 2, 2, 4, 32)
     MOE_CASE2(12, 64, 256, 1, 4, 4, 32)
     MOE_CASE2(13, 32, 256, 1, 4, 4, 32)
-    MOE_CASE1(14, 320, 256, 2, 4, 4, 32)
     MOE_CASE2(15, 320, 256, 2, 4, 2, 64)
     default: return hipErrorInvalidValue;
   }
@@ -568,7 +567,7 @@ hipError_t launch_lds_cfg(bool swiglu, int id, bool wnt, const void* X, int ldx,
 
 }  // namespace
 
-bool lds_cfg_id(int id) { return id >= 10 && id <= 15; }
+bool lds_cfg_id(int id) { return id >= 10 && id <= 15 && id != 14; }
 
 GemmTileCfg pick_lds_cfg(int N, int E, int cols, bool swiglu) {
   // weight columns per tile: 256 (SwiGLU: 128 gate + 128 up)

@@ -71,6 +71,23 @@ __device__ __forceinline__ void store8(T* p, const float (&f)[8]) {
   }
 }
 
+// p[0] + p[stride] + ... + p[(n - 1) stride], added in that order, with the
+// loads issued 8 at a time (a plain loop waited for each load in turn).
+__device__ __forceinline__ float sum_in_order(const float* __restrict__ p, long long stride,
+                                              int n) {
+  constexpr int U = 8;
+  float s = 0.f;
+  for (int b = 0; b < n; b += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = b + u < n ? p[(long long)(b + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (b + u < n) s += v[u];
+  }
+  return s;
+}
+
 // d_weights[i] = <dout[i / k], y[i]> = <dout[i / k] . down[e]^T, h[i]>: the
 // first dgrad's epilogue leaves the inner products of its column slices of
 // that second form (P per expert-major row); one thread per flat slot adds
@@ -81,9 +98,7 @@ __global__ __launch_bounds__(256) void weight_grad_kernel(const float* __restric
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
   const float* p = parts + (size_t)min(max(slot_pos[i], 0), N - 1) * P;
-  float s = 0.f;
-  for (int c = 0; c < P; ++c) s += p[c];
-  dw[i] = s;
+  dw[i] = sum_in_order(p, 1, P);
 }
 
 // dL[t, :] from the routing-weight gradient: one wave per token.
@@ -153,31 +168,42 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
     const int t = (int)(q / per_row);
     const int c = 8 * (int)(q - (long long)t * per_row);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      float v[8];
-      load8(dX + ((size_t)t * k + j) * H + c, v, true);   // read once
+    // rows in batches of U loaded together (a plain loop waited for each
+    // load in turn), added in the same order as one at a time
+    constexpr int U = 8;
+    for (int jb = 0; jb < k; jb += U) {
+      float v[U][8];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) acc[x] += v[x];
+      for (int u = 0; u < U; ++u)
+        if (jb + u < k) load8(dX + ((size_t)t * k + jb + u) * H + c, v[u], true);   // read once
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (jb + u < k)
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[x] += v[u][x];
     }
     const float* l = dL + (size_t)t * E;
-    if (ids) {
-      // dL is zero off the token's selection: its k router rows, slot order
-      for (int j = 0; j < k; ++j) {
-        const int e = min(max(ids[(size_t)t * k + j], 0), E - 1);
-        const float g = l[e];
-        float v[8];
-        load8(wr + (size_t)e * H + c, v);
+    // dL is zero off the token's selection when ids is set: then its k
+    // router rows in slot order, else all E rows
+    const int nr = ids ? k : E;
+    for (int jb = 0; jb < nr; jb += U) {
+      int ex[U];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
+      for (int u = 0; u < U; ++u) {
+        const int j = min(jb + u, nr - 1);
+        ex[u] = ids ? min(max(ids[(size_t)t * k + j], 0), E - 1) : j;
       }
-    } else {
-      for (int e = 0; e < E; ++e) {
-        const float g = l[e];
-        float v[8];
-        load8(wr + (size_t)e * H + c, v);
+      float g[U], v[U][8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
+      for (int u = 0; u < U; ++u) {
+        g[u] = l[ex[u]];
+        load8(wr + (size_t)ex[u] * H + c, v[u]);
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (jb + u < nr)
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[x] = fmaf(g[u], v[u][x], acc[x]);
     }
     if (add) {
       float v[8];
@@ -241,9 +267,7 @@ __global__ __launch_bounds__(256) void router_weight_grad_sum_kernel(
   const long long total = (long long)E * H;
   for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total;
        q += (long long)gridDim.x * 256) {
-    float a = 0.f;
-    for (int r = 0; r < splits; ++r) a += part[(size_t)r * total + q];
-    dwr[q] = a;
+    dwr[q] = sum_in_order(part + q, total, splits);
   }
   if (dbias && blockIdx.x == 0)
     for (int e = threadIdx.x; e < E; e += 256) {

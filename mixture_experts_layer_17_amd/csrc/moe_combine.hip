@@ -31,26 +31,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
     const int t = (int)(q / per_row);
     const int c = (int)(q - (long long)t * per_row);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int i = t * k + j;
-      const int src = slot_pos ? slot_pos[i] : i;
-      if (src < 0 || src >= N) continue;
-      const float wt = w ? w[i] : 1.0f;
-      const chunk8<T> v = load_chunk_stream<T>(y + (size_t)src * H + 8 * c);
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t* d = reinterpret_cast<const uint32_t*>(&v.v);
+    // slots in batches of U: their positions and weights, then their rows,
+    // are loaded together (a plain loop waited for each load in turn); the
+    // products are added in slot order as before
+    constexpr int U = 8;
+    for (int jb = 0; jb < k; jb += U) {
+      int src[U];
+      float wt[U];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          acc[2 * x] = fmaf(wt, bf16_bits_to_f32(d[x] & 0xffffu), acc[2 * x]);
-          acc[2 * x + 1] = fmaf(wt, bf16_bits_to_f32(d[x] >> 16), acc[2 * x + 1]);
-        }
-      } else {
-        const float* f0 = reinterpret_cast<const float*>(&v.lo);
-        const float* f1 = reinterpret_cast<const float*>(&v.hi);
+      for (int u = 0; u < U; ++u) {
+        const int i = t * k + jb + u;
+        const bool on = jb + u < k;
+        const int sp = on ? (slot_pos ? slot_pos[i] : i) : -1;
+        src[u] = (sp >= 0 && sp < N) ? sp : -1;
+        wt[u] = (on && w) ? w[i] : 1.0f;
+      }
+      chunk8<T> v[U];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          acc[x] = fmaf(wt, f0[x], acc[x]);
-          acc[4 + x] = fmaf(wt, f1[x], acc[4 + x]);
+      for (int u = 0; u < U; ++u)
+        v[u] = src[u] >= 0 ? load_chunk_stream<T>(y + (size_t)src[u] * H + 8 * c) : zero_chunk<T>();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (src[u] < 0) continue;
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t* d = reinterpret_cast<const uint32_t*>(&v[u].v);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            acc[2 * x] = fmaf(wt[u], bf16_bits_to_f32(d[x] & 0xffffu), acc[2 * x]);
+            acc[2 * x + 1] = fmaf(wt[u], bf16_bits_to_f32(d[x] >> 16), acc[2 * x + 1]);
+          }
+        } else {
+          const float* f0 = reinterpret_cast<const float*>(&v[u].lo);
+          const float* f1 = reinterpret_cast<const float*>(&v[u].hi);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            acc[x] = fmaf(wt[u], f0[x], acc[x]);
+            acc[4 + x] = fmaf(wt[u], f1[x], acc[4 + x]);
+          }
         }
       }
     }

@@ -113,11 +113,18 @@ __global__ __launch_bounds__(1024) void permute_place_kernel(
   const int per = (nchunk + 3) / 4;
   const int c0 = part * per, c1 = min(nchunk, c0 + per);
   int tot = 0, bef = 0;
+  // loads in batches of 8 in flight (a plain loop waited for each in turn)
+  constexpr int U = 8;
   if (e < E)
-    for (int cc = c0; cc < c1; ++cc) {
-      const int v = hist[(size_t)cc * E + e];
-      tot += v;
-      bef += cc < c ? v : 0;
+    for (int cb = c0; cb < c1; cb += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = cb + u < c1 ? hist[(size_t)(cb + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        tot += v[u];
+        bef += cb + u < c ? v[u] : 0;
+      }
     }
   s_tot_p[part][e] = tot;
   s_bef_p[part][e] = bef;

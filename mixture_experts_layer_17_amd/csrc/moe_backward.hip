@@ -168,42 +168,34 @@ __global__ __launch_bounds__(256) void input_grad_kernel(const T* __restrict__ d
     const int t = (int)(q / per_row);
     const int c = 8 * (int)(q - (long long)t * per_row);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // rows in batches of U loaded together (a plain loop waited for each
-    // load in turn), added in the same order as one at a time
-    constexpr int U = 8;
-    for (int jb = 0; jb < k; jb += U) {
-      float v[U][8];
+    // one row at a time: the latency hides behind the other resident waves
+    // (holding 8 rows per thread in flight lowered the occupancy and
+    // measured 15 % slower)
+    for (int j = 0; j < k; ++j) {
+      float v[8];
+      load8(dX + ((size_t)t * k + j) * H + c, v, true);   // read once
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (jb + u < k) load8(dX + ((size_t)t * k + jb + u) * H + c, v[u], true);   // read once
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (jb + u < k)
-#pragma unroll
-          for (int x = 0; x < 8; ++x) acc[x] += v[u][x];
+      for (int x = 0; x < 8; ++x) acc[x] += v[x];
     }
     const float* l = dL + (size_t)t * E;
-    // dL is zero off the token's selection when ids is set: then its k
-    // router rows in slot order, else all E rows
-    const int nr = ids ? k : E;
-    for (int jb = 0; jb < nr; jb += U) {
-      int ex[U];
+    if (ids) {
+      // dL is zero off the token's selection: its k router rows, slot order
+      for (int j = 0; j < k; ++j) {
+        const int e = min(max(ids[(size_t)t * k + j], 0), E - 1);
+        const float g = l[e];
+        float v[8];
+        load8(wr + (size_t)e * H + c, v);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = min(jb + u, nr - 1);
-        ex[u] = ids ? min(max(ids[(size_t)t * k + j], 0), E - 1) : j;
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
       }
-      float g[U], v[U][8];
+    } else {
+      for (int e = 0; e < E; ++e) {
+        const float g = l[e];
+        float v[8];
+        load8(wr + (size_t)e * H + c, v);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        g[u] = l[ex[u]];
-        load8(wr + (size_t)ex[u] * H + c, v[u]);
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(g, v[x], acc[x]);
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (jb + u < nr)
-#pragma unroll
-          for (int x = 0; x < 8; ++x) acc[x] = fmaf(g[u], v[u][x], acc[x]);
     }
     if (add) {
       float v[8];

@@ -390,7 +390,8 @@ def bench_backward(args, wl):
         roof = {"bound": "mfma", "achieved": round(flops[dom] / t_dom / 1e12, 2),
                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = load_traffic(dom, wl.name)
+    # the counters were taken for the layer without a shared expert
+    roof["traffic"] = load_traffic(dom, wl.name) if Is == 0 else None
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = int(bytes_[dom])
     roof["algorithmic_flops"] = int(flops[dom])
@@ -719,7 +720,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops[dom] / t_dom / 1e12, 2),
                 "peak": peak_f / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = load_traffic(dom, wl.name)
+    # the counters were taken for the softmax router without a shared expert
+    plain = Is == 0 and args.router == "softmax"
+    roof["traffic"] = load_traffic(dom, wl.name) if plain else None
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = int(bytes_[dom])
     roof["algorithmic_flops"] = int(flops[dom])

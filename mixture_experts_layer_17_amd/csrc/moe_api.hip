@@ -469,9 +469,13 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
       launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr, s, var);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(1);
-  // the permutation's scan pass also writes both GEMMs' tile lists
+  // the permutation's scan pass also writes both GEMMs' tile lists (one
+  // list when their row tiles have the same height)
+  const bool one_list = cu.BM == cd.BM;
+  void* const tiles_down = one_list ? w.tiles_up : w.tiles_down;
   e = launch_permute_topk(ids, T, k, E, counts, w.offsets, w.sorted_token, w.sorted_slot,
-                          w.slot_pos, w.perm, s, w.tiles_up, cu.BM, w.tiles_down, cd.BM);
+                          w.slot_pos, w.perm, s, w.tiles_up, cu.BM,
+                          one_list ? nullptr : w.tiles_down, cd.BM);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(2);
   // The shared expert (MindSpore moe.py, MoE.forward) sees every token and
@@ -497,7 +501,7 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
   // token's k rows contiguously.
   if (N > 0) {
     e = launch_down(bf16, cd, w.h, w.offsets, w.sorted_slot, N, H, I, E, down, y,
-                    w.tiles_down, true, s, fused ? &aux_down : nullptr);
+                    tiles_down, true, s, fused ? &aux_down : nullptr);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   mark(4);

@@ -6,11 +6,22 @@ synthetic input already resident in HBM, on torch's current stream.  The
 library records caller-supplied HIP events between its stages, so each
 stage's average duration is measured live over the timed steps.
 
-Prints one JSON line.  Default workload: the Qwen3-30B-A3B-shaped prefill
-layer, T = 4096 tokens, H = 2048, I = 768, E = 128, top_k = 8, bf16.
+Prints one JSON line.  Headline workload: the Qwen3-30B-A3B-shaped prefill
+layer, T = 4096 tokens, H = 2048, I = 768, E = 128, top_k = 8, bf16.  With
+no --workload the same line also carries, under "workloads", the decode
+layer (T = 64; its layer_hbm_frac is the decode HBM figure), the skewed
+batch (T = 16384, Zipf(1.2) popularity), the tiny float32 layer and one
+expert-parallel rank's share, each timed the same way.
+
+Byte counts: a kernel's algorithmic bytes are what the method must move
+(hit experts' weights once, the hidden states it reads, the router's and
+the layer's outputs); this implementation's intermediates (h, the per-slot
+expert outputs, index maps) are reported separately as bytes moved.
 
 Other modes:
-  --workload NAME        another named workload (decode, skewed, tiny)
+  --workload NAME        one named workload alone (prefill, decode, skewed,
+                         tiny_fp32, ep_rank_235b)
+  --no-extra             the prefill headline alone
   --copy-calibration     only run a plain 1 GiB device copy (for scaling the
                          rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
   --router sigmoid-groups  a sigmoid, node-limited, biased router variant
@@ -59,7 +70,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_30b_a3b_prefill")
+    ap.add_argument("--workload", default=None,
+                    help="time one named workload alone (default: the prefill headline, "
+                         "with the decode, skewed, tiny and EP-rank workloads beside it)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time the prefill headline alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--router", default="softmax", choices=["softmax", "sigmoid-groups"],
@@ -163,7 +178,7 @@ def cpu_baseline_backward(wl, dout, budget_s=12.0):
                       f"{runs} run(s), {el:.1f} s, float64 NumPy"}
 
 
-def bench_ep_rank(args, wl):
+def bench_ep_rank(args, wl, cpu=True):
     """One expert-parallel rank: rows received rank-major from R source
     ranks (built untimed with the library's router and torch indexing), then
     the timed span moe_permute (rank-major reshuffle) -> moe_grouped_swiglu
@@ -265,7 +280,7 @@ def bench_ep_rank(args, wl):
                     "warm_min": round(float(np.min(steps)), 4)},
         "wall_s_timed": round(t_wall, 3),
     }
-    if not args.no_cpu_baseline:
+    if cpu and not args.no_cpu_baseline:
         from oracle import moe_oracle as O
         n0 = int(C[0].sum())
         xs = x_rm[:n0].float().cpu().numpy()
@@ -277,7 +292,7 @@ def bench_ep_rank(args, wl):
                                   os.cpu_count(), "kind": "oracle",
                                   "sample": f"source rank 0's {n0} received rows, one run, "
                                             f"{el:.1f} s, float64 NumPy"}
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def bench_backward(args, wl):
@@ -420,8 +435,15 @@ def bench_backward(args, wl):
 
 def algorithmic(wl, counts, Is=0, fused=False):
     """Per-kernel algorithmic FLOPs and HBM bytes for one layer pass.
-    Weights count once per expert that received rows; gathered rows count
-    once per token; intermediates count once written and once read."""
+
+    Bytes count what the method itself must move: each hit expert's weights
+    once, the router weight, the hidden states each kernel has to read, the
+    router's outputs and the layer output.  The intermediates of this
+    implementation (h between the GEMMs, the per-slot expert outputs Y
+    between the second GEMM and the combine, the index maps) are not
+    algorithmic; they are returned separately as ``moved`` (bytes each
+    kernel actually reads and writes, intermediates included).  The layer's
+    algorithmic bytes count the hidden states once."""
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.top_k
     es = 2 if wl.dtype.itemsize == 2 else 4
     N = T * k
@@ -435,25 +457,37 @@ def algorithmic(wl, counts, Is=0, fused=False):
     }
     b = {
         "route": T * H * es + E * H * es + T * E * 4 + T * k * 8,
-        "permute": N * 4 * 5,
-        "gate_up_swiglu": hit * H * 2 * I * es + T * H * es + N * I * es,
-        "down": hit * I * H * es + N * I * es + N * H * es,
-        "combine": N * H * es + N * 4 + T * H * es,
+        "permute": 0,
+        "gate_up_swiglu": hit * H * 2 * I * es + T * H * es,
+        "down": hit * I * H * es,
+        "combine": T * H * es,
     }
+    moved = {
+        "route": b["route"],
+        "permute": N * 4 * 5,
+        "gate_up_swiglu": b["gate_up_swiglu"] + N * I * es,
+        "down": b["down"] + N * I * es + N * H * es,
+        "combine": b["combine"] + N * H * es + N * 4,
+    }
+    layer_b = hit * 3 * H * I * es + E * H * es + 2 * T * H * es + T * E * 4 + T * k * 8
     if Is and fused:
-        # the shared expert inside the grouped launches: its weights once, x
-        # read once more, h written and read, its output written and then
-        # read by the combine
+        # the shared expert inside the grouped launches: its weights once; x
+        # is read once more, its h and output are intermediates
         f["gate_up_swiglu"] += 2.0 * T * H * 2 * Is
-        b["gate_up_swiglu"] += H * 2 * Is * es + T * H * es + T * Is * es
+        b["gate_up_swiglu"] += H * 2 * Is * es
+        moved["gate_up_swiglu"] += H * 2 * Is * es + T * H * es + T * Is * es
         f["down"] += 2.0 * T * Is * H
-        b["down"] += Is * H * es + T * Is * es + T * H * es
-        b["combine"] += T * H * es
+        b["down"] += Is * H * es
+        moved["down"] += Is * H * es + T * Is * es + T * H * es
+        moved["combine"] += T * H * es
     elif Is:
         # on its own, in the last stage with the combine
         f["combine"] += 2.0 * T * H * 2 * Is + 2.0 * T * Is * H
-        b["combine"] += 3 * H * Is * es + T * H * es + 2 * T * Is * es + 2 * T * H * es
-    return f, b, hit
+        b["combine"] += 3 * H * Is * es
+        moved["combine"] += 3 * H * Is * es + T * H * es + 2 * T * Is * es + 2 * T * H * es
+    if Is:
+        layer_b += 3 * H * Is * es
+    return f, b, moved, layer_b, hit
 
 
 def copy_calibration():
@@ -550,17 +584,9 @@ def graph_replay(torch, step, s, steps):
         return {"error": str(err)[:200]}
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", args.gpus))
-    if args.gpus > 1 or world > 1:
-        print("bench.py measures one GPU only: the MoE layer forward here has no multi-GPU "
-              "path (no collectives); run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
+def run_forward(args, wl, router="softmax", Is=0, context=True):
+    """Times moe_layer_forward_ex on one workload; returns the measured
+    fields of the JSON line (no CPU baseline)."""
     import numpy as np
     import torch
 
@@ -568,13 +594,6 @@ def main():
     import workloads
     from mixture_experts_layer_17_amd import _lib
 
-    wl = workloads.make(args.workload)
-    if not hasattr(wl, "T"):
-        bench_ep_rank(args, wl)
-        return
-    if args.backward:
-        bench_backward(args, wl)
-        return
     dev = torch.device("cuda:0")
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.top_k
     N = T * k
@@ -592,18 +611,16 @@ def main():
     L = moe.lib
 
     cfg = None
-    if args.router == "sigmoid-groups":
+    if router == "sigmoid-groups":
         g = torch.Generator().manual_seed(1)
         ebias = (torch.randn(E, generator=g) * 0.05).to(dev)
         cfg = moe.router_config("sigmoid", 2.5, ebias, 8, 4)
     cfg_p = ctypes.addressof(cfg) if cfg is not None else None
-    Is = args.shared_I
-    sh_w = sh_p = None
+    sh_p = None
     fused = False
     kernels = KERNELS
     if Is:
-        sh_w = workloads.shared_expert_weights(H, Is, wl.dtype)
-        w1, w2, w3 = sh_w
+        w1, w2, w3 = workloads.shared_expert_weights(H, Is, wl.dtype)
         sgu = torch.cat([w1.t(), w3.t()], dim=1).contiguous().to(dev)
         sdn = w2.t().contiguous().to(dev)
         sh = moe.shared_expert(sgu, sdn)
@@ -671,12 +688,12 @@ def main():
         per_kernel_ms[kname] = float(np.mean(acc))
 
     def step_times(arrs):
-        out = []
+        out_ = []
         for arr in arrs:
             if hip.hipEventElapsedTime(ctypes.byref(f), arr[0], arr[nst - 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
-            out.append(f.value)
-        return out
+            out_.append(f.value)
+        return out_
 
     warm = step_times(ev_arrays)
     # cold: a 512 MB scratch write before each step evicts L2 and the MALL;
@@ -692,12 +709,13 @@ def main():
         for j in range(nst):
             hip.hipEventDestroy(arr[j])
     graph = graph_replay(torch, step, s, args.steps)
-    context = dense_gemm_context(wl) if wl.dtype == torch.bfloat16 else None
+    ctx = dense_gemm_context(wl) if (context and bf16) else None
 
     c_np = counts.cpu().numpy()
-    flops, bytes_, hit = algorithmic(wl, c_np, Is, fused)
+    flops, bytes_, moved, layer_bytes, hit = algorithmic(wl, c_np, Is, fused)
     flops = dict(zip(kernels, flops.values()))
     bytes_ = dict(zip(kernels, bytes_.values()))
+    moved = dict(zip(kernels, moved.values()))
     peak_f = PEAK_BF16_FLOPS if bf16 else PEAK_F32_FLOPS
     kern = {}
     for kname in kernels:
@@ -706,6 +724,7 @@ def main():
             "avg_us": round(per_kernel_ms[kname] * 1e3, 2),
             "tflops": round(flops[kname] / t_s / 1e12, 2),
             "gbps": round(bytes_[kname] / t_s / 1e9, 1),
+            "gbps_moved": round(moved[kname] / t_s / 1e9, 1),
             "mfma_frac": round(flops[kname] / t_s / peak_f, 4),
             "hbm_frac": round(bytes_[kname] / t_s / PEAK_HBM, 4),
         }
@@ -721,11 +740,12 @@ def main():
                 "peak": peak_f / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     # the counters were taken for the softmax router without a shared expert
-    plain = Is == 0 and args.router == "softmax"
+    plain = Is == 0 and router == "softmax"
     roof["traffic"] = load_traffic(dom, wl.name) if plain else None
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = int(bytes_[dom])
     roof["algorithmic_flops"] = int(flops[dom])
+    roof["bytes_moved"] = int(moved[dom])
 
     layer_flops = sum(flops.values())
     # the headline step time is the graph replay's (the same kernels on the
@@ -734,24 +754,19 @@ def main():
     eager_ms = ms_per_step
     if "ms_per_step" in graph:
         ms_per_step = graph["ms_per_step"]
-    result = {
-        "metric": METRIC,
-        "value": round(N / (ms_per_step * 1e-3), 1),
-        "unit": "routed tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    t_layer = ms_per_step * 1e-3
+    return {
+        "value": round(N / t_layer, 1),
         "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
-        "data": "synthetic: seeded Gaussian inputs and random-init weights of the named layer shape",
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "top_k": k,
                    "norm_topk_prob": wl.norm_topk_prob, "routed_rows": N,
-                   "experts_hit": hit, "router": args.router, "shared_I": Is},
-        "layer_tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
-        "layer_mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / peak_f, 4),
+                   "experts_hit": hit, "router": router, "shared_I": Is},
+        "layer_tflops": round(layer_flops / t_layer / 1e12, 2),
+        "layer_mfma_frac": round(layer_flops / t_layer / peak_f, 4),
+        "layer_algorithmic_bytes": int(layer_bytes),
+        "layer_hbm_gbps": round(layer_bytes / t_layer / 1e9, 1),
+        "layer_hbm_frac": round(layer_bytes / t_layer / PEAK_HBM, 4),
         "roofline": roof,
         "kernels": kern,
         "step_ms": {"warm_median": round(float(np.median(warm)), 4),
@@ -761,13 +776,79 @@ def main():
         "timing": "hip_graph_replay" if "ms_per_step" in graph else "eager_stream",
         "eager_ms_per_step": round(eager_ms, 4),
         "graph": graph,
-        "context": context,
+        "context": ctx,
         "wall_s_timed": round(t_wall, 3),
-        "host": platform.node(),
     }
+
+
+def compact(r: dict) -> dict:
+    """The fields of a secondary workload kept in the headline line."""
+    keep = ("value", "unit", "ms_per_step", "eager_ms_per_step", "dtype", "layer_tflops",
+            "layer_mfma_frac", "layer_hbm_gbps", "layer_hbm_frac", "roofline", "step_ms")
+    c = {k_: r[k_] for k_ in keep if k_ in r}
+    c["config"] = r["config"]
+    c["kernels_us"] = {n: v["avg_us"] for n, v in r["kernels"].items()}
+    return c
+
+
+# Secondary workloads timed next to the headline when bench.py runs with no
+# --workload: the decode layer (graded on its HBM fraction), the skewed
+# batch, the tiny float32 layer and one expert-parallel rank's share.
+EXTRA_WORKLOADS = ("qwen3_30b_a3b_decode", "qwen3_30b_a3b_skewed", "tiny_fp32", "ep_rank_235b")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", args.gpus))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU only: the MoE layer forward here has no multi-GPU "
+              "path (no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    import mixture_experts_layer_17_amd  # noqa: F401  (fails loudly without libmoe.so)
+    import workloads
+
+    name = args.workload or "qwen3_30b_a3b_prefill"
+    wl = workloads.make(name)
+    if not hasattr(wl, "T"):
+        print(json.dumps(bench_ep_rank(args, wl)), flush=True)
+        return
+    if args.backward:
+        bench_backward(args, wl)
+        return
+    r = run_forward(args, wl, args.router, args.shared_I)
+    result = {"metric": METRIC, "value": r["value"], "unit": "routed tokens/s", "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": r["dtype"],
+              "data": "synthetic: seeded Gaussian inputs and random-init weights of the named "
+                      "layer shape"}
+    result.update({k_: v for k_, v in r.items() if k_ not in result})
+    result["host"] = platform.node()
+    del wl
+    if args.workload is None and not args.no_extra:
+        extra = {}
+        for xname in EXTRA_WORKLOADS:
+            xw = workloads.make(xname)
+            if hasattr(xw, "T"):
+                xr = run_forward(args, xw, context=False)
+                xr["unit"] = "routed tokens/s"
+            else:
+                xr = bench_ep_rank(args, xw, cpu=False)
+            extra[xname] = compact(xr)
+            del xw
+            torch.cuda.empty_cache()
+        result["workloads"] = extra
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(
-            wl, shared=tuple(t.float().numpy() for t in sh_w) if sh_w is not None else None)
+        sh_w = (tuple(t.float().numpy() for t in workloads.shared_expert_weights(
+            r["config"]["H"], args.shared_I, workloads.make(name).dtype))
+            if args.shared_I else None)
+        result["cpu_baseline"] = cpu_baseline(workloads.make(name), shared=sh_w)
     print(json.dumps(result), flush=True)
 
 

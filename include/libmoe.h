@@ -361,6 +361,38 @@ int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
                          hipStream_t stream);
 
 /*
+ * moe_layer_workspace_offset — where the layer forward keeps its own
+ * permutation and expert outputs inside its workspace, for callers that
+ * inspect them after the call (the layer's stream must have reached the end
+ * of the call).  These are the values moe_permute would return for the
+ * call's topk_ids (MindSpore moe.py, MoE.permutation) and the second grouped
+ * GEMM's outputs before the combine (Qwen3-Omni issue #115,
+ * SpeedupMoeExperts.forward, expert_out before it is weighted):
+ *   MOE_LAYER_WS_OFFSETS       int32 [E + 1] expert_offsets
+ *   MOE_LAYER_WS_SORTED_TOKEN  int32 [T*k]   sorted_token_ids
+ *   MOE_LAYER_WS_SORTED_SLOT   int32 [T*k]   sorted_slot_ids
+ *   MOE_LAYER_WS_SLOT_POS      int32 [T*k]   slot_pos
+ *   MOE_LAYER_WS_EXPERT_OUT    dt [T*k, H]   expert outputs, row t*k + j
+ *                                            (not written by the training
+ *                                            forward, which puts them in
+ *                                            moe_train_saved.expert_out)
+ * Arguments as moe_workspace_size(MOE_OP_LAYER, T, H, I, E, top_k, shared_I,
+ * T*top_k, dt).  Returns the byte offset from the start of the workspace
+ * (256-byte aligned), or (size_t)-1 for an unknown piece or invalid sizes.
+ * Pure host computation; enqueues nothing.
+ */
+enum {
+  MOE_LAYER_WS_OFFSETS = 0,
+  MOE_LAYER_WS_SORTED_TOKEN = 1,
+  MOE_LAYER_WS_SORTED_SLOT = 2,
+  MOE_LAYER_WS_SLOT_POS = 3,
+  MOE_LAYER_WS_EXPERT_OUT = 4
+};
+
+size_t moe_layer_workspace_offset(int piece, int T, int H, int I, int E, int top_k,
+                                  int shared_I, moe_dtype dt);
+
+/*
  * Training: the layer forward that keeps what its backward needs, and the
  * backward.  The pages train this layer through autograd (Qwen3-Omni issue
  * #115, SpeedupMoeExperts' per-expert training loop and

@@ -88,7 +88,7 @@ def router_config(score_func: str = "sigmoid", route_scale: float = 1.0,
     optional float32 [E] accumulator of selections."""
     funcs = {"softmax": _lib.MOE_SCORE_SOFTMAX, "sigmoid": _lib.MOE_SCORE_SIGMOID}
     if score_func not in funcs:
-        raise ValueError("score_func must be 'sigmoid' or 'softmax'")
+        raise ValueError(f"unknown score function {score_func!r}: use sigmoid or softmax")
     _chk(expert_bias, "expert_bias", torch.float32)
     _chk(tokens_per_expert, "tokens_per_expert", torch.float32)
     cfg = _lib.RouterConfig(funcs[score_func], float(route_scale),
@@ -279,6 +279,27 @@ class LayerBuffers:
                                     dt)
         self.workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
         self.ws_bytes = nb
+        self._dims = (T, H, I, E, top_k, shared_I, dt, dtype)
+
+    def internals(self) -> dict:
+        """Views of what the last layer_forward on these buffers left in the
+        workspace (moe_layer_workspace_offset): expert offsets, the
+        permutation and the expert outputs in flat slot order."""
+        T, H, I, E, k, Is, dt, dtype = self._dims
+        N = T * k
+
+        def view(piece, n, elt):
+            off = lib.moe_layer_workspace_offset(piece, T, H, I, E, k, Is, dt)
+            if off == ctypes_size_max():
+                raise ValueError("invalid sizes for workspace views")
+            nbytes = n * torch.empty(0, dtype=elt).element_size()
+            return self.workspace[off:off + nbytes].view(elt)
+
+        return dict(offsets=view(_lib.MOE_LAYER_WS_OFFSETS, E + 1, torch.int32),
+                    sorted_token=view(_lib.MOE_LAYER_WS_SORTED_TOKEN, N, torch.int32),
+                    sorted_slot=view(_lib.MOE_LAYER_WS_SORTED_SLOT, N, torch.int32),
+                    slot_pos=view(_lib.MOE_LAYER_WS_SLOT_POS, N, torch.int32),
+                    expert_out=view(_lib.MOE_LAYER_WS_EXPERT_OUT, N * H, dtype).view(N, H))
 
 
 def shared_expert(gate_up: torch.Tensor, down: torch.Tensor) -> "_lib.SharedExpert":

@@ -23,6 +23,12 @@ MOE_OP_LAYER = 5
 MOE_OP_SHARED = 6
 MOE_OP_LAYER_BACKWARD = 7
 
+MOE_LAYER_WS_OFFSETS = 0
+MOE_LAYER_WS_SORTED_TOKEN = 1
+MOE_LAYER_WS_SORTED_SLOT = 2
+MOE_LAYER_WS_SLOT_POS = 3
+MOE_LAYER_WS_EXPERT_OUT = 4
+
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 
@@ -66,6 +72,7 @@ class RouterConfig(ctypes.Structure):
 # name -> (restype, argtypes); must match include/libmoe.h
 SIGNATURES = {
     "moe_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "moe_layer_workspace_offset": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "moe_status_string": (ctypes.c_char_p, [_i]),
     "moe_version": (_i, []),
     "moe_route": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]),

@@ -13,7 +13,7 @@ namespace {
 
 constexpr int kMaxE = 256;
 constexpr int kMaxRankMajorBlocks = 4096;
-constexpr int kVersion = 1;
+constexpr int kVersion = 2;
 
 size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -42,6 +42,8 @@ struct LayerWs {
   float *weights, *logits;
   void *perm, *h, *y, *tiles_up, *tiles_down;
   void *h_s, *y_s, *tiles_s_up, *tiles_s_down;  // shared expert (Is > 0)
+  // byte offsets of the pieces moe_layer_workspace_offset reports
+  size_t at_offsets, at_sorted_token, at_sorted_slot, at_slot_pos, at_y;
   size_t total;
 };
 
@@ -96,12 +98,17 @@ LayerWs layer_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt, in
   w.weights = (float*)take(N * 4);
   w.logits = (float*)take((size_t)T * E * 4);
   w.counts = (int32_t*)take((size_t)E * 4);
+  w.at_offsets = off;
   w.offsets = (int32_t*)take((size_t)(E + 1) * 4);
+  w.at_sorted_token = off;
   w.sorted_token = (int32_t*)take(N * 4);
+  w.at_sorted_slot = off;
   w.sorted_slot = (int32_t*)take(N * 4);
+  w.at_slot_pos = off;
   w.slot_pos = (int32_t*)take(N * 4);
   w.perm = take(permute_ws_bytes((int)N, E, 0));
   w.h = take(N * (size_t)I * esize(dt));
+  w.at_y = off;
   w.y = take(N * (size_t)H * esize(dt));
   const GemmTileCfg cu = pick_gate_up_cfg(bf16, (int)N, H, I, E);
   const GemmTileCfg cd = pick_down_cfg(bf16, (int)N, H, I, E);
@@ -267,6 +274,23 @@ size_t moe_workspace_size(int op, int T, int H, int I, int E, int top_k, int R, 
     case MOE_OP_SHARED:
       if (check_dims(H, I, 1, 1) != MOE_OK || I == 0 || T < 0 || !rows_ok(T)) return bad;
       return shared_ws(nullptr, T, H, I, dt, false).total;
+    default: return bad;
+  }
+}
+
+size_t moe_layer_workspace_offset(int piece, int T, int H, int I, int E, int top_k,
+                                  int shared_I, moe_dtype dt) {
+  const size_t bad = (size_t)-1;
+  if (!dtype_ok(dt) || check_dims(H, I, E, top_k) != MOE_OK || I == 0 || T < 0 ||
+      !rows_ok((long long)T * top_k) || shared_I < 0 || shared_I % 64 != 0)
+    return bad;
+  const LayerWs w = layer_ws(nullptr, T, H, I, E, top_k, dt, shared_I);
+  switch (piece) {
+    case MOE_LAYER_WS_OFFSETS: return w.at_offsets;
+    case MOE_LAYER_WS_SORTED_TOKEN: return w.at_sorted_token;
+    case MOE_LAYER_WS_SORTED_SLOT: return w.at_sorted_slot;
+    case MOE_LAYER_WS_SLOT_POS: return w.at_slot_pos;
+    case MOE_LAYER_WS_EXPERT_OUT: return w.at_y;
     default: return bad;
   }
 }

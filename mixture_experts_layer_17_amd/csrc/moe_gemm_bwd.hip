@@ -633,15 +633,20 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
 
   // PERSIST: thread 0 takes share indices from the XCD's counter; the one
   // for the next job is taken while this one runs and published through
-  // LDS at its epilogue
+  // LDS at its epilogue.  Publications alternate between two LDS words: a
+  // job without rows passes no barrier in its K loop, so the word read
+  // after one publication's barrier is written again only after the next
+  // publication's barrier, which every wave reaches after its read.
   unsigned* const ctr = PERSIST ? job_counters + xcd : nullptr;
   int* const s_loc = reinterpret_cast<int*>(smem + G::LDS);
+  int pub = 0;   // LDS word of the next publication
   int pref = 0;
   int loc;
   if constexpr (PERSIST) {
     if (tid == 0) s_loc[0] = (int)atomicAdd(ctr, 1u);
     __syncthreads();
     loc = s_loc[0];
+    pub = 1;
     if (loc >= share) return;
     if (tid == 0) pref = (int)atomicAdd(ctr, 1u);
   } else {
@@ -670,9 +675,10 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
     //                                 [n0 + CW wn + 32 j + 8 (q / 4) + 4 hl + q % 4]
     int nloc = -1, nKT = 0;
     if constexpr (PERSIST) {
-      if (tid == 0) s_loc[0] = pref;
+      if (tid == 0) s_loc[pub] = pref;
       __syncthreads();                            // the ring is free; the index is visible
-      nloc = s_loc[0];
+      nloc = s_loc[pub];
+      pub ^= 1;
       if (nloc >= share) nloc = -1;
       if (nloc >= 0) {
         if (tid == 0) pref = (int)atomicAdd(ctr, 1u);

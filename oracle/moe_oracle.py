@@ -9,8 +9,8 @@ and its binding never do, and this module never imports them.
 Precision.  Every floating-point step runs in float64 (NumPy).  The one place
 the pages fix a precision that decides an integer is the router: the gate
 output is taken in float32 before the softmax and the top-k (MindSpore
-hyper-parallel ``moe.py``, ``TokenChoiceTopKRouter.forward``: the gate is
-evaluated "in float32 for numerical stability"; Qwen3-Omni issue #115,
+hyper-parallel ``moe.py``, ``TokenChoiceTopKRouter.forward`` runs the gate
+on float32 inputs so that the scores are stable; Qwen3-Omni issue #115,
 ``SpeedupMoeSparseMoeBlock.forward``: ``softmax(..., dtype=float)``).  So the
 router logits are rounded once to float32 and the top-k decision is taken on
 those float32 values; everything after that is float64 again.
@@ -137,7 +137,7 @@ def router_scores(logits32, score_func: str = "sigmoid", route_scale: float = 1.
         p = np.exp(L - L.max(axis=1, keepdims=True))
         s = p / p.sum(axis=1, keepdims=True)
     else:
-        raise ValueError("score_func must be 'sigmoid' or 'softmax'")
+        raise ValueError(f"unknown score function {score_func!r}: use sigmoid or softmax")
     return s * float(route_scale)
 
 
@@ -468,7 +468,7 @@ def routing_weight_jacobian(logits32, ids, norm_topk_prob: bool, score_func: str
         s = route_scale * sg
         ds = (route_scale * sg * (1.0 - sg))[:, :, None] * eye[None]
     else:
-        raise ValueError("score_func must be 'sigmoid' or 'softmax'")
+        raise ValueError(f"unknown score function {score_func!r}: use sigmoid or softmax")
     dsel = np.take_along_axis(ds, ii[:, :, None], axis=1)                  # [T, k, E]
     if not norm_topk_prob:
         return dsel

@@ -158,3 +158,25 @@ def test_training_validation_and_workspace(lib):
     sh = _lib.SharedExpert(fake, fake, 128)
     assert bwd(16, 128, 1, saved, grads, sh=sh) == -1
     assert bwd(16, 128, 1, saved, grads, sh=_lib.SharedExpert(fake, fake, 64)) == -5
+
+
+def test_layer_workspace_offsets(lib):
+    """The layer's permutation and expert outputs sit inside its workspace,
+    256-byte aligned, in disjoint pieces large enough for their contents."""
+    for (T, H, I, E, k, Is, dt) in ((4096, 2048, 768, 128, 8, 0, 1), (64, 128, 64, 8, 2, 0, 0),
+                                    (37, 256, 128, 32, 4, 256, 1)):
+        N = T * k
+        total = lib.moe_workspace_size(_lib.MOE_OP_LAYER, T, H, I, E, k, Is, N, dt)
+        es = 2 if dt == 1 else 4
+        sizes = {_lib.MOE_LAYER_WS_OFFSETS: 4 * (E + 1), _lib.MOE_LAYER_WS_SORTED_TOKEN: 4 * N,
+                 _lib.MOE_LAYER_WS_SORTED_SLOT: 4 * N, _lib.MOE_LAYER_WS_SLOT_POS: 4 * N,
+                 _lib.MOE_LAYER_WS_EXPERT_OUT: es * N * H}
+        spans = []
+        for piece, nbytes in sizes.items():
+            off = lib.moe_layer_workspace_offset(piece, T, H, I, E, k, Is, dt)
+            assert off != SIZE_MAX and off % 256 == 0 and off + nbytes <= total
+            spans.append((off, off + nbytes))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])), "pieces overlap"
+    assert lib.moe_layer_workspace_offset(5, 64, 128, 64, 8, 2, 0, 1) == SIZE_MAX
+    assert lib.moe_layer_workspace_offset(0, 64, 100, 64, 8, 2, 0, 1) == SIZE_MAX   # H % 128

@@ -40,9 +40,15 @@ def shared_layout(w1, w2, w3):
     return torch.cat([w1.t(), w3.t()], dim=1).contiguous(), w2.t().contiguous()
 
 
-def run_layer(moe, wl, check_counts=True, shared=None):
-    """Full layer on the GPU vs the oracle's per-expert loop.  ``shared`` =
-    (w1, w2, w3): a shared expert in nn.Linear layout."""
+def run_layer(moe, wl, shared=None):
+    """Full layer on the GPU vs the oracle's per-expert loop, by the routing
+    protocol: logits within tolerance; the GPU's ids equal the oracle's
+    selection on the GPU's float32 logits on every token (and the oracle's
+    own ids on every decided token); the layer's counts, offsets and
+    permutation bit for bit against the oracle's of the GPU's ids; expert
+    outputs, routing weights and the layer output against the oracle's layer
+    run on the GPU's ids, on every token.  ``shared`` = (w1, w2, w3): a
+    shared expert in nn.Linear layout."""
     say(f"layer {wl.name} T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.top_k} {wl.dtype}"
         + (f" shared Is={shared[0].shape[0]}" if shared is not None else ""))
     x = wl.hidden_states.to(DEV)
@@ -51,27 +57,34 @@ def run_layer(moe, wl, check_counts=True, shared=None):
     dn = wl.down.to(DEV)
     b = wl.router_bias.to(DEV) if wl.router_bias is not None else None
     sh = tuple(t.to(DEV) for t in shared_layout(*shared)) if shared is not None else None
+    Is = shared[0].shape[0] if shared is not None else 0
+    buf = moe.LayerBuffers(wl.T, wl.H, wl.I, wl.E, wl.top_k, wl.dtype, x.device, Is)
     out, logits, ids, w, counts = moe.layer_forward(x, wr, gu, dn, wl.top_k, wl.norm_topk_prob,
-                                                    router_bias=b, shared=sh)
+                                                    router_bias=b, shared=sh, buffers=buf)
     torch.cuda.synchronize()
+    internals = {n: t.cpu() for n, t in buf.internals().items()}
     out, logits, ids, w, counts = (t.cpu() for t in (out, logits, ids, w, counts))
+    xs, wrs = _np32(wl.hidden_states), _np32(wl.router_weight)
     bias_np = wl.router_bias.numpy() if wl.router_bias is not None else None
-    ref = O.moe_layer_forward(_np32(wl.hidden_states), _np32(wl.router_weight), bias_np,
-                              _np32(wl.gate_up), _np32(wl.down), wl.top_k, wl.norm_topk_prob,
+    # the oracle's own routing, then its whole layer on the GPU's routing
+    ref_L, own_ids, _ = O.route(xs, wrs, bias_np, wl.top_k, wl.norm_topk_prob)
+    U.assert_close(logits, ref_L, wl.dtype, "router logits")
+    decided, same = U.routing_check(logits.numpy(), ids.numpy(), ref_L, own_ids, wl.top_k)
+    ref = O.moe_layer_forward(xs, wrs, bias_np, _np32(wl.gate_up), _np32(wl.down), wl.top_k,
+                              wl.norm_topk_prob, ids=ids.numpy(),
                               shared=tuple(_np32(t) for t in shared) if shared is not None
                               else None)
-    U.assert_close(logits, ref["logits"], wl.dtype, "router logits")
-    decided, same = U.routing_check(logits.numpy(), ids.numpy(), ref["logits"], ref["ids"],
-                                    wl.top_k)
-    U.weights_check(w, ref["weights"], logits, ref["logits"], same)
-    if same.all() and check_counts:
-        assert np.array_equal(counts.numpy(), ref["counts"]), "counts"
-    else:
-        assert np.array_equal(counts.numpy(), np.bincount(ids.numpy().ravel(), minlength=wl.E))
-    U.assert_close(out, ref["out"], wl.dtype, "layer output", rows=same)
-    print(f"  tokens routed as the oracle: {same.sum()}/{wl.T}, undecided {(~decided).sum()}",
-          flush=True)
-    return dict(out=out, logits=logits, ids=ids, w=w, counts=counts, ref=ref, same=same)
+    every = np.ones(wl.T, dtype=bool)
+    U.weights_check(w, ref["weights"], logits, ref_L, every)
+    U.permutation_check(counts.numpy(), {n: t.numpy() for n, t in internals.items()
+                                         if n != "expert_out"}, ids.numpy(), wl.E)
+    U.assert_close(internals["expert_out"], O.unpermute(ref["y"], ref["slot_pos"]), wl.dtype,
+                   "expert outputs (flat slot order)")
+    U.assert_close(out, ref["out"], wl.dtype, "layer output")
+    print(f"  tokens the oracle routes the same from its own logits: {same.sum()}/{wl.T}, "
+          f"undecided {(~decided).sum()}", flush=True)
+    return dict(out=out, logits=logits, ids=ids, w=w, counts=counts, ref=ref, same=same,
+                own_ids=own_ids, ref_logits=ref_L)
 
 
 # ----------------------------------------------------------------- layers
@@ -122,9 +135,9 @@ def test_integer_logits_route_bit_exact(moe):
     are frequent, and routing must match bit for bit on every token."""
     wl = workloads.integer_grid_layer(T=4096, H=2048, I=128, E=128, top_k=8)
     r = run_layer(moe, wl)
-    assert np.array_equal(r["logits"].numpy(), r["ref"]["logits"])
+    assert np.array_equal(r["logits"].numpy(), r["ref_logits"])
     assert r["same"].all()
-    assert np.array_equal(r["ids"].numpy(), r["ref"]["ids"])
+    assert np.array_equal(r["ids"].numpy(), r["own_ids"])
 
 
 def test_all_ties_zero_router(moe):

@@ -40,7 +40,8 @@
  *     multiple of 64 (the router alone needs only H a multiple of 64);
  *     routed rows N <= 2^30; rank-major mode R * E <= 4096.
  *   - Calls are stateless and may be made from several host threads on
- *     different streams.
+ *     different streams (moe_layer_forward_noalloc excepted: its calls on
+ *     one GPU share a static scratch buffer; see there).
  */
 #ifndef LIBMOE_H
 #define LIBMOE_H
@@ -63,7 +64,9 @@ enum {
   MOE_ERR_WORKSPACE = -4,   /* workspace missing or smaller than moe_workspace_size() */
   MOE_ERR_UNSUPPORTED = -5, /* valid request this build does not handle */
   MOE_ERR_HIP = -6,         /* a HIP launch failed */
-  MOE_ERR_ALIGN = -7        /* a pointer is not 16-byte aligned */
+  MOE_ERR_ALIGN = -7,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_SCRATCH = -8      /* moe_layer_forward_noalloc: the request needs more
+                               than MOE_STATIC_SCRATCH_BYTES of workspace */
 };
 
 /* Workspace queries: `op` names the entry point. */
@@ -359,6 +362,40 @@ int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
                          int32_t* num_tokens_per_expert, void* workspace,
                          size_t workspace_bytes, hipEvent_t* stage_events,
                          hipStream_t stream);
+
+/*
+ * moe_layer_forward_noalloc — moe_layer_forward_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace argument and
+ * calls no allocating routine (hipMalloc, hipFree or any library that
+ * allocates); its workspace is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  Arguments, outputs and results are those of
+ * moe_layer_forward_ex (bit-identical for the same inputs).  The caller still
+ * passes (and owns) every input and output.
+ *   - The array of the CURRENT device is used: the stream must belong to the
+ *     device that is current when the call is made.
+ *   - A request whose moe_workspace_size(MOE_OP_LAYER, ...) exceeds
+ *     MOE_STATIC_SCRATCH_BYTES returns MOE_ERR_SCRATCH and enqueues nothing
+ *     (at the Qwen3-30B-A3B expert shape, H = 2048, I = 768, top-8, that is
+ *     above about 1,400 tokens).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents.  Calls that overlap on one GPU (on several streams,
+ *     or from several host threads without ordering) race on it; serialise
+ *     them on one stream.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress); a failure there returns MOE_ERR_HIP.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+
+int moe_layer_forward_noalloc(const void* hidden_states, const void* router_weight,
+                              const float* router_bias, const void* gate_up,
+                              const void* down, int T, int H, int I, int E, int top_k,
+                              int norm_topk_prob, moe_dtype dt, const moe_router_config* cfg,
+                              const moe_shared_expert* shared, void* out, float* router_logits,
+                              int32_t* topk_ids, float* topk_weights,
+                              int32_t* num_tokens_per_expert, hipEvent_t* stage_events,
+                              hipStream_t stream);
 
 /*
  * moe_layer_workspace_offset — where the layer forward keeps its own

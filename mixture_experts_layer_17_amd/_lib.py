@@ -29,12 +29,14 @@ MOE_LAYER_WS_SORTED_SLOT = 2
 MOE_LAYER_WS_SLOT_POS = 3
 MOE_LAYER_WS_EXPERT_OUT = 4
 
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
+
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_UNSUPPORTED", -6: "MOE_ERR_HIP",
-          -7: "MOE_ERR_ALIGN"}
+          -7: "MOE_ERR_ALIGN", -8: "MOE_ERR_SCRATCH"}
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -93,6 +95,8 @@ SIGNATURES = {
                                   _p, _p, _p, _p, _sz, _p, _p]),
     "moe_layer_forward_train": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p,
                                      _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_layer_forward_noalloc": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p,
+                                       _p, _p, _p, _p, _p, _p, _p]),
     "moe_layer_backward": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
                                 _p, _p, _p, _p, _sz, _p, _p]),
 }

@@ -4,6 +4,7 @@
 
 #include "../../include/libmoe.h"
 #include <cmath>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -231,6 +232,9 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported request";
     case MOE_ERR_HIP: return "HIP launch failed";
     case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_ERR_SCRATCH:
+      return "request needs more than the library's static scratch buffer "
+             "(MOE_STATIC_SCRATCH_BYTES); use the workspace entry point";
     default: return "unknown status";
   }
 }
@@ -722,6 +726,64 @@ int moe_layer_forward(const void* x, const void* wr, const float* bias, const vo
                       hipStream_t s) {
   return moe_layer_forward_cfg(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, nullptr, out,
                                logits, ids, weights, counts, ws, ws_bytes, stage_events, s);
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing --------------------------------
+//
+// Its workspace is one file-scope device array of MOE_STATIC_SCRATCH_BYTES.
+// Each GPU the library runs on holds its own copy (at its own address) until
+// the process ends.  Host code never uses the array's name as a device
+// address: the address is looked up once per device, with that device
+// current, and kept in scratch_ptr[].
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_noalloc(const void* x, const void* wr, const float* bias,
+                              const void* gate_up, const void* down, int T, int H, int I, int E,
+                              int k, int norm, moe_dtype dt, const moe_router_config* cfg,
+                              const moe_shared_expert* shared, void* out, float* logits,
+                              int32_t* ids, float* weights, int32_t* counts,
+                              hipEvent_t* stage_events, hipStream_t s) {
+  // sizes first: invalid ones fall through to the full validation below,
+  // valid ones that do not fit the array are refused before anything runs
+  const int Is = shared ? shared->intermediate_size : 0;
+  const long long N = (long long)T * k;
+  const size_t need = (N >= 0 && N <= (1ll << 30))
+                          ? moe_workspace_size(MOE_OP_LAYER, T, H, I, E, k, Is, (int)N, dt)
+                          : (size_t)-1;
+  if (need != (size_t)-1 && need > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int st = current_scratch(&ws);
+  if (st != MOE_OK) return st;
+  return layer_forward_impl(x, wr, bias, gate_up, down, T, H, I, E, k, norm, dt, cfg, shared,
+                            out, logits, ids, weights, counts, nullptr, nullptr, nullptr, ws,
+                            (size_t)MOE_STATIC_SCRATCH_BYTES, stage_events, s);
 }
 
 }  // extern "C"

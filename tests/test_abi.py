@@ -180,3 +180,17 @@ def test_layer_workspace_offsets(lib):
         assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])), "pieces overlap"
     assert lib.moe_layer_workspace_offset(5, 64, 128, 64, 8, 2, 0, 1) == SIZE_MAX
     assert lib.moe_layer_workspace_offset(0, 64, 100, 64, 8, 2, 0, 1) == SIZE_MAX   # H % 128
+
+
+def test_noalloc_refuses_requests_above_the_static_scratch(lib):
+    """moe_layer_forward_noalloc checks the workspace the request needs
+    against its static array before anything else runs (fake pointers are
+    never dereferenced): the prefill shape is refused, and invalid sizes get
+    the ordinary validation errors."""
+    fake = 4096
+    args = lambda T, H=2048: (fake, fake, None, fake, fake, T, H, 768, 128, 8, 1, 1, None, None,
+                              fake, fake, fake, fake, fake, None, None)
+    need = lib.moe_workspace_size(_lib.MOE_OP_LAYER, 4096, 2048, 768, 128, 8, 0, 32768, 1)
+    assert need > _lib.MOE_STATIC_SCRATCH_BYTES
+    assert lib.moe_layer_forward_noalloc(*args(4096)) == -8
+    assert lib.moe_status_string(-8) != b"unknown status"

@@ -38,6 +38,7 @@
 #include "moe_internal.h"
 #include "moe_lds.h"
 
+
 namespace moe {
 namespace {
 
@@ -53,6 +54,17 @@ __device__ __forceinline__ int aswz(int row) {
   else return (row >> 1) & 7;
 }
 
+// f(integral_constant<int, i>) for i = I .. N - 1, unrolled at compile time.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// STAGES ring slots for the activation tiles, then STAGES for the weight
+// tiles.
 template <int BM, int BN, int WM, int WN, int STAGES, bool SWIGLU, int KB = BK>
 struct lcfg {
   static_assert(KB == 32 || KB == 64, "k per block");
@@ -68,8 +80,8 @@ struct lcfg {
   static constexpr int TN = SWIGLU ? 2 * TNO : TNO;  // weight tiles per wave
   static constexpr int A_BYTES = BM * KB * 2;        // per stage
   static constexpr int B_BYTES = KB * BN * 2;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int RING = STAGES * STAGE_BYTES;
+  static constexpr int B_RING = STAGES * A_BYTES;     // weight slots follow the activation slots
+  static constexpr int RING = STAGES * (A_BYTES + B_BYTES);
   // 1 KB that absorbs the surplus activation copies of waves with a short
   // share, so every wave issues the same number of copies per block
   static constexpr int DUMP = (BM * KB * 2 / 1024) % NW ? 1024 : 0;
@@ -187,21 +199,47 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     else
       col = n0 + col;
     b_src[u] = We + (long long)row * ldw + col;
-    b_lds[u] = G::A_BYTES + inst * 1024;
+    b_lds[u] = inst * 1024;
   }
 
-  auto issue = [&](unsigned char* base) {
+  // Copies of the next activation block into activation slot `as` and of
+  // the next weight block into weight slot `bs`.
+  auto issue_a = [&](int as) {
+    unsigned char* const base = smem + as * G::A_BYTES;
 #pragma unroll
     for (int u = 0; u < G::A_PER; ++u) {
       // a copy past the A block re-reads row chunk 0 into the dump area
       copy16_to_lds(a_src[u], a_on[u] ? base + a_lds[u] : smem + G::RING);
       a_src[u] += KB;
     }
+  };
+  auto issue_b = [&](int bs) {
+    unsigned char* const base = smem + G::B_RING + bs * G::B_BYTES;
 #pragma unroll
     for (int u = 0; u < G::B_PER; ++u) {
       if constexpr (WNT) copy16_to_lds_nt(b_src[u], base + b_lds[u]);
       else copy16_to_lds(b_src[u], base + b_lds[u]);
       b_src[u] += (long long)KB * ldw;
+    }
+  };
+  // The same copies one at a time, for the main loop, which spreads them
+  // between its MFMAs: copy c (compile-time) of a block into activation
+  // slot `as` and weight slot `bs`.  The weight copies go first: they come
+  // from HBM, the activation rows mostly from the caches.
+  constexpr int PER = G::A_PER + G::B_PER;   // copies per block, every wave
+  auto issue_one = [&](auto c_c, int as, int bs, bool on) {
+    constexpr int c = decltype(c_c)::value;
+    if (!on) return;
+    if constexpr (c < G::B_PER) {
+      unsigned char* const base = smem + G::B_RING + bs * G::B_BYTES;
+      if constexpr (WNT) copy16_to_lds_nt(b_src[c], base + b_lds[c]);
+      else copy16_to_lds(b_src[c], base + b_lds[c]);
+      b_src[c] += (long long)KB * ldw;
+    } else {
+      constexpr int u = c - G::B_PER;
+      unsigned char* const base = smem + as * G::A_BYTES;
+      copy16_to_lds(a_src[u], a_on[u] ? base + a_lds[u] : smem + G::RING);
+      a_src[u] += KB;
     }
   };
 
@@ -237,7 +275,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     else
       cb = wn * G::CW + 32 * j;
     const int col = cb + 16 * (gq & 1) + 4 * (s16 & 3);
-    wb_off[j] = G::A_BYTES + wrow * G::ROWB + 32 * ((col >> 4) ^ wsw) + 2 * (col & 15);
+    wb_off[j] = wrow * G::ROWB + 32 * ((col >> 4) ^ wsw) + 2 * (col & 15);
   }
 
   f32x16_v acc[G::TM][G::TN];
@@ -264,7 +302,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
                               *reinterpret_cast<const u32x4*>(base + xa_off[kk] + XI * i));
   };
   const int KT = K / KB;
-  constexpr int PER = G::A_PER + G::B_PER;   // copies per block, every wave
   // Wait until at most `nb` of this wave's most recent blocks are in flight.
   auto wait_blocks = [&](int nb) {
     static_assert(STAGES <= 8 && (STAGES - 1) * PER < 64, "wait table");
@@ -281,11 +318,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
       default: wait_vmcnt<(M < 7 ? M : 7) * PER>(); break;
     }
   };
-
+  // The copy stream, in issue order: the prologue gives block p its
+  // activation copies then its weight copies, p = 0 .. STAGES - 1; the
+  // loop's iteration kb then issues block kb + STAGES.  Blocks are waited
+  // for whole, so the order inside a block does not matter.
   // prologue: every slot gets a block
 #pragma unroll
-  for (int p = 0; p < STAGES; ++p)
-    if (p < KT) issue(smem + p * G::STAGE_BYTES);
+  for (int p = 0; p < STAGES; ++p) {
+    if (p < KT) {
+      issue_a(p);
+      issue_b(p);
+    }
+  }
 
   // block 0 landed (blocks 1 .. min(STAGES, KT) - 1 may stay in flight)
   wait_blocks(min(STAGES, KT) - 1);
@@ -303,17 +347,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     // are issued its activation register is refilled with the fragment of
     // the next k-step (`nbase`, `nkk`), so the LDS read runs under the
     // remaining MFMAs and one register set serves both k-steps.
-    auto mma_roll = [&](const bf16x8_v (&wf)[G::TN], const unsigned char* nbase, int nkk) {
-#pragma unroll
-      for (int i = 0; i < TA; ++i) {
+    //
+    // Inside the loop, step STEP (0 .. KS - 1) of an iteration also issues
+    // that iteration's copies of the next blocks, one per MFMA group over
+    // its first groups (m-tile i of step STEP is group STEP * TA + i),
+    // instead of all at the top: the load unit takes a CU's copies only as
+    // fast as it drains them (about 16 clocks per 1 KB copy), so issuing a
+    // block's copies together held the later waves of the work-group at
+    // the top of each iteration (timestamps: 1,640 clocks per iteration for
+    // waves 4-7 against 570 for waves 0-3) while their MFMAs waited.
+    // Packing the copies into the first 2-5 groups, or spreading them over
+    // the whole iteration, measured slower.  STEP < 0: none.
+    constexpr int GROUPS = TA * KS;
+    constexpr int GP = GROUPS < PER ? GROUPS : PER;   // groups that issue copies
+    auto mma_roll = [&](auto step_c, const bf16x8_v (&wf)[G::TN], const unsigned char* nbase,
+                        int nkk, int as, int bs, bool on) {
+      constexpr int STEP = decltype(step_c)::value;
+      static_for<0, TA>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
 #pragma unroll
         for (int j = 0; j < G::TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
         xf[i] = read_x(nbase, nkk, i);
+        if constexpr (STEP >= 0) {
+          constexpr int g = STEP * TA + i;
+          if constexpr (g < GP)
+            static_for<g * PER / GP, (g + 1) * PER / GP>(
+                [&](auto c_c) { issue_one(c_c, as, bs, on); });
+        }
         // keep this order: the scheduler would otherwise gather the reads
         // next to their first use and expose their latency
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     };
     // Block b's k-steps 0 .. KS - 2 are multiplied before the barrier that
     // publishes block b + 1, its last k-step after it.  Between the two,
@@ -321,15 +386,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     // barrier also retires slot b, which is refilled with block b + STAGES
     // right after it.  The loop body starts after a barrier, where no LDS
     // read is pending, so the wait-count state at the loop head is exact.
-    read_w(smem, 0, wf[0]);
+    const unsigned char* const b0 = smem + G::B_RING;
+    read_w(b0, 0, wf[0]);
 #pragma unroll
     for (int i = 0; i < TA; ++i) xf[i] = read_x(smem, 0, i);
-#pragma unroll
-    for (int st = 0; st + 1 < KS; ++st) {
-      read_w(smem, st + 1, wf[(st + 1) & 1]);
+    static_for<0, KS - 1>([&](auto st_c) {
+      constexpr int st = decltype(st_c)::value;
+      read_w(b0, st + 1, wf[(st + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      mma_roll(wf[st & 1], smem, st + 1);
-    }
+      mma_roll(std::integral_constant<int, -1>{}, wf[st & 1], smem, st + 1, 0, 0, false);
+    });
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (KT > 1) wait_blocks(min(STAGES - 2, KT - 2));
     __builtin_amdgcn_s_barrier();
@@ -337,21 +403,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
 
     int slot = 0;                                      // kb % STAGES
     for (int kb = 0; kb + 1 < KT; ++kb) {
-      unsigned char* cur = smem + slot * G::STAGE_BYTES;
+      const int cur = slot;
       slot = (slot + 1 == STAGES) ? 0 : slot + 1;
-      unsigned char* nxt = smem + slot * G::STAGE_BYTES;
-      if (kb + STAGES < KT) issue(cur);
+      const unsigned char* const an = smem + slot * G::A_BYTES;
+      const unsigned char* const bn = smem + G::B_RING + slot * G::B_BYTES;
+      // block kb + STAGES goes into the slot of block kb, retired by the
+      // barrier that ended the previous iteration
+      const bool on = kb + STAGES < KT;
       // last k-step of block kb, reading block kb + 1's first
-      read_w(nxt, 0, wf[KS & 1]);
+      read_w(bn, 0, wf[KS & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      mma_roll(wf[(KS - 1) & 1], nxt, 0);
+      mma_roll(std::integral_constant<int, 0>{}, wf[(KS - 1) & 1], an, 0, cur, cur, on);
       // k-steps 0 .. KS - 2 of block kb + 1, each reading the next
-#pragma unroll
-      for (int st = 0; st + 1 < KS; ++st) {
-        read_w(nxt, st + 1, wf[(KS + st + 1) & 1]);
+      static_for<0, KS - 1>([&](auto st_c) {
+        constexpr int st = decltype(st_c)::value;
+        read_w(bn, st + 1, wf[(KS + st + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        mma_roll(wf[(KS + st) & 1], nxt, st + 1);
-      }
+        mma_roll(std::integral_constant<int, st + 1>{}, wf[(KS + st) & 1], an, st + 1, cur, cur,
+                 on);
+      });
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (kb + 2 < KT) wait_blocks(min(STAGES - 2, KT - 3 - kb));
       __builtin_amdgcn_s_barrier();
@@ -371,7 +441,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     for (int kb = 0; kb + 1 < KT; ++kb) {
-      if (kb + STAGES < KT) issue(smem + (kb % STAGES) * G::STAGE_BYTES);
+      if (kb + STAGES < KT) {
+        issue_b(kb % STAGES);
+        issue_a(kb % STAGES);
+      }
       if (kb + 2 < KT) wait_blocks(min(STAGES - 2, KT - 3 - kb));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -529,6 +602,10 @@ struct LdsCfg { int BM, BN; };
 // The configs the grouped picker returns (11, 12, 13, 15) also come with
 // non-temporal weight copies (WNT), taken when the mean rows per expert fit
 // one row tile.
+// (a 256 x 256 tile with two activation slots and three weight slots,
+// copying the weights two blocks ahead in exactly the 160 KB of LDS,
+// measured 15-20 % slower than 15 at the prefill shape and 1-3 % at the
+// skewed one: the copies' latency was not what held the loop back)
 constexpr LdsCfg kLds[] = {{256, 256}, {128, 256}, {64, 256}, {32, 256}, {320, 256},
                            {320, 256}};
 
@@ -551,6 +628,7 @@ hipError_t launch_lds_cfg(bool swiglu, int id, bool wnt, const void* X, int ldx,
 #define MOE_CASE1(ID, BM, BN, WM, WN, ST, KB)                                   \
   case ID:                                                                    \
     return MOE_LAUNCH(BM, BN, WM, WN, ST, KB, false);
+
   switch (id) {
     MOE_CASE1(10, 256, 256, 2, 2, 4, 32)
     MOE_CASE2(11, 128, 256, 2, 2, 4, 32)

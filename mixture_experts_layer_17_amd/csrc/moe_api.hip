@@ -42,6 +42,8 @@ struct LayerWs {
   int32_t *ids, *counts, *offsets, *sorted_token, *sorted_slot, *slot_pos;
   float *weights, *logits;
   void *perm, *h, *y, *tiles_up, *tiles_down;
+  float* route_parts;                           // the router's partial logits
+  size_t route_parts_bytes;
   void *h_s, *y_s, *tiles_s_up, *tiles_s_down;  // shared expert (Is > 0)
   // byte offsets of the pieces moe_layer_workspace_offset reports
   size_t at_offsets, at_sorted_token, at_sorted_slot, at_slot_pos, at_y;
@@ -115,6 +117,8 @@ LayerWs layer_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt, in
   const GemmTileCfg cd = pick_down_cfg(bf16, (int)N, H, I, E);
   w.tiles_up = take(tile_list_bytes((int)N, E, cu.BM));
   w.tiles_down = take(tile_list_bytes((int)N, E, cd.BM));
+  w.route_parts_bytes = route_ws_bytes(T, H, E, bf16);
+  w.route_parts = (float*)take(w.route_parts_bytes);
   if (Is > 0) {
     const SharedWs sw = shared_ws(nullptr, T, H, Is, dt, true);
     const SharedWs sp = shared_ws(base ? base + off : nullptr, T, H, Is, dt, true);
@@ -493,8 +497,8 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
   };
   mark(0);
   // the histogram comes from the permutation pass, so the router skips it
-  hipError_t e =
-      launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr, s, var);
+  hipError_t e = launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr,
+                              s, var, w.route_parts, w.route_parts_bytes);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(1);
   // the permutation's scan pass also writes both GEMMs' tile lists (one

@@ -31,10 +31,14 @@ struct RouterVariant {
   float* tpe;
 };
 
+// `parts` (optional, route_ws_bytes of it): float32 partial logits, which
+// let large batches take the split-K router.
 hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* bias,
                         int T, int H, int E, int k, int norm, float* logits,
                         int32_t* ids, float* w, int32_t* counts, hipStream_t s,
-                        const RouterVariant* var = nullptr);
+                        const RouterVariant* var = nullptr, float* parts = nullptr,
+                        size_t parts_bytes = 0);
+size_t route_ws_bytes(int T, int H, int E, bool bf16);
 hipError_t launch_update_expert_bias(float* bias, float* tpe, int E, float lr, int nrec,
                                      hipStream_t s);
 

@@ -479,6 +479,170 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(
                           E, k, norm, ids_out, w_out, counts);
 }
 
+// ---- Large-batch path with a workspace.  The kernel above streams all of
+// Wr through LDS once per 16 tokens (at 4096 tokens about 150 MB of copies
+// for 2 MB of logits).  Here a work-group takes 64 tokens and every expert
+// over one slice of K, so Wr is streamed once per 64 tokens, and the slices
+// keep enough work-groups for every CU; each writes float32 partial logits
+// parts[slice][t][e], and route_select_kernel adds the slices in order.
+constexpr int RP_TOK = 64;
+constexpr int RP_NS = 4;          // ring stages (3 or 2 with 512 work-groups: slower)
+constexpr int RP_TARGET = 256;    // work-groups the slices aim for
+
+template <typename T, int NT>
+struct rpcfg {
+  static constexpr int KB = 128 / (int)sizeof(T);   // K elements per block (128-byte rows)
+  static constexpr int ROWS = RP_TOK + NT * 16;      // x rows, then Wr rows
+  static constexpr int STAGE = ROWS * 128;
+  static constexpr int Q = ROWS / 8;                 // copy instructions per block (8 rows each)
+  static constexpr int NS0 = (160 * 1024) / STAGE;
+  static constexpr int NS = NS0 > RP_NS ? RP_NS : NS0;
+  static constexpr int LDS = NS * STAGE;
+  static_assert(NS >= 2, "ring");
+  static_assert(ROWS % 8 == 0, "whole copy instructions");
+};
+
+template <typename T, int NT>
+__global__ __launch_bounds__(RT_WAVES * 64) void route_part_kernel(
+    const T* __restrict__ x, const T* __restrict__ wr, int T_, int H, int E, int kslice,
+    float* __restrict__ parts) {
+  using C = rpcfg<T, NT>;
+  constexpr int NS = C::NS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * RP_TOK;
+  const int sl = blockIdx.y;
+  const int g = lane >> 4, r = lane & 15;
+
+  // copies: instruction q of a block covers LDS rows 8q .. 8q + 7, one
+  // 16-byte chunk per lane; waves take q = wave, wave + 8, ...
+  constexpr int CPW = (C::Q + RT_WAVES - 1) / RT_WAVES;
+  const int cnt = (C::Q - wave + RT_WAVES - 1) / RT_WAVES;
+  constexpr int EL = 16 / (int)sizeof(T);
+  const T* src[CPW];
+  int dst[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int q = min(wave + RT_WAVES * u, C::Q - 1);
+    const int row = 8 * q + (lane >> 3);
+    const int chunk = (lane & 7) ^ rt_swz(row);
+    const T* rowp = row < RP_TOK ? x + (size_t)min(t0 + row, T_ - 1) * H
+                                 : wr + (size_t)min(row - RP_TOK, E - 1) * H;
+    src[u] = rowp + (size_t)sl * kslice + EL * chunk;
+    dst[u] = q * 1024;
+  }
+  const int nblk = kslice / C::KB;
+  auto issue = [&](int blk) {
+    unsigned char* base = smem + (blk % NS) * C::STAGE;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u)
+      if (u < cnt) rt_copy16(src[u] + (size_t)blk * C::KB, base + dst[u]);
+  };
+  auto wait_block = [&](int b) {
+    const int after = min(b == 0 ? NS - 1 : NS - 2, nblk - 1 - b);
+    if (after == NS - 1) {
+      if (cnt == CPW) rt_wait_vmcnt<(NS - 1) * CPW>();
+      else rt_wait_vmcnt<(NS - 1) * (CPW - 1)>();
+    } else if (after == NS - 2) {
+      if (cnt == CPW) rt_wait_vmcnt<(NS - 2) * CPW>();
+      else rt_wait_vmcnt<(NS - 2) * (CPW - 1)>();
+    } else {
+      rt_wait_vmcnt<0>();
+    }
+  };
+
+  // operands as in route_kernel: lane (g, r) takes chunks 2 g and 2 g + 1 of
+  // row r of each 16-token group and of each of its expert tiles (tiles
+  // wave, wave + 8, ...)
+  constexpr int TPW = (NT + RT_WAVES - 1) / RT_WAVES;
+  constexpr int TG = RP_TOK / 16;
+  const int c0 = 16 * ((2 * g) ^ rt_swz(r));
+  const int c1 = 16 * ((2 * g + 1) ^ rt_swz(r));
+  f32x4_v acc[TPW][TG];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) acc[j][tg] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  auto rd = [&](const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p); };
+  auto compute = [&](const unsigned char* base) {
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+      const int j = wave + RT_WAVES * jj;
+      if (j < NT) {
+        const unsigned char* wrw = base + (RP_TOK + 16 * j + r) * 128;
+        const u32x4 wa = rd(wrw + c0), wb = rd(wrw + c1);
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          const unsigned char* xr = base + (16 * tg + r) * 128;
+          const u32x4 xa = rd(xr + c0), xb = rd(xr + c1);
+          if constexpr (sizeof(T) == 2) {
+            acc[jj][tg] = mfma_16x16x32(chunk8<bf16_t>{xa}, chunk8<bf16_t>{wa}, acc[jj][tg]);
+            acc[jj][tg] = mfma_16x16x32(chunk8<bf16_t>{xb}, chunk8<bf16_t>{wb}, acc[jj][tg]);
+          } else {
+            acc[jj][tg] =
+                mfma_16x16x32(chunk8<float>{xa, xb}, chunk8<float>{wa, wb}, acc[jj][tg]);
+          }
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int p = 0; p < NS; ++p)
+    if (p < nblk) issue(p);
+  for (int b = 0; b < nblk; ++b) {
+    wait_block(b);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (b >= 1 && b - 1 + NS < nblk) issue(b - 1 + NS);
+    compute(smem + (b % NS) * C::STAGE);
+  }
+
+  // acc[jj][tg][q] = partial L[token 16 tg + 4 g + q][expert 16 j + r]
+  float* const out = parts + (size_t)sl * T_ * E;
+#pragma unroll
+  for (int jj = 0; jj < TPW; ++jj) {
+    const int j = wave + RT_WAVES * jj;
+    const int e = 16 * j + r;
+    if (j < NT && e < E) {
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = t0 + 16 * tg + 4 * g + q;
+          if (t < T_) out[(size_t)t * E + e] = acc[jj][tg][q];
+        }
+    }
+  }
+}
+
+// Slices of K for the partial-logits path: the fewest (1, 2, 4 or 8, each
+// a whole number of 128-byte blocks) that give 256 work-groups.
+int route_slices(int T, int H, bool bf16) {
+  const int kb = bf16 ? 64 : 32;
+  const int blocks = H / kb;
+  const int tiles = (T + RP_TOK - 1) / RP_TOK;
+  int S = 1;
+  while (S < 8 && tiles * S < RP_TARGET && blocks % (2 * S) == 0) S *= 2;
+  return S;
+}
+
+template <typename V, int NT>
+hipError_t launch_route_part(const void* x, const void* wr, int T, int H, int E, int S,
+                             float* parts, hipStream_t s) {
+  using C = rpcfg<V, NT>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)route_part_kernel<V, NT>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((T + RP_TOK - 1) / RP_TOK, S);
+  route_part_kernel<V, NT><<<grid, RT_WAVES * 64, C::LDS, s>>>((const V*)x, (const V*)wr, T, H, E,
+                                                               H / S, parts);
+  return hipGetLastError();
+}
+
 // ---- Small-batch path.  With few tokens the kernel above runs on few CUs,
 // each streaming all of Wr; here the logits are spread over (16-token tile,
 // 16-expert tile) workgroups first, then one workgroup per 16 tokens selects.
@@ -542,10 +706,13 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   }
 }
 
-// Selection for 16 tokens from their logits in global memory.
+// Selection for 16 tokens from logits in global memory: the sum of S
+// partial slices parts[s][t][e] (s = 0 .. S - 1, added in that order), plus
+// the bias when there is one; written to logits_out when it is not null.
 template <int NT, bool VAR>
 __global__ __launch_bounds__(RT_WAVES * 64) void route_select_kernel(
-    const float* __restrict__ logits, int T_, int E, int k, int norm,
+    const float* __restrict__ parts, int S, const float* __restrict__ bias,
+    float* __restrict__ logits_out, int T_, int E, int k, int norm,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
     RouterVariant var) {
   constexpr int LDE = NT * 16 + 4;
@@ -555,9 +722,34 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_select_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * RT_TOK;
-  for (int idx = threadIdx.x; idx < RT_TOK * E; idx += RT_WAVES * 64) {
-    const int tr = idx / E, e = idx - tr * E;
-    s_log[tr * LDE + e] = logits[(size_t)min(t0 + tr, T_ - 1) * E + e];
+  // every load of a thread is issued before the first sum (a runtime loop
+  // over the slices would wait for each load in turn)
+  const size_t slice = (size_t)T_ * E;
+  constexpr int PER = (RT_TOK * NT * 16 + RT_WAVES * 64 - 1) / (RT_WAVES * 64);
+  constexpr int SMAX = 8;
+  float pv[PER][SMAX];
+  size_t at[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = threadIdx.x + RT_WAVES * 64 * i;
+    const int tr = min(idx / E, RT_TOK - 1), e = idx - (idx / E) * E;
+    at[i] = (size_t)min(t0 + tr, T_ - 1) * E + min(e, E - 1);
+#pragma unroll
+    for (int sl = 0; sl < SMAX; ++sl) pv[i][sl] = sl < S ? parts[sl * slice + at[i]] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = threadIdx.x + RT_WAVES * 64 * i;
+    if (idx < RT_TOK * E) {
+      const int tr = idx / E, e = idx - tr * E;
+      float v = pv[i][0];
+#pragma unroll
+      for (int sl = 1; sl < SMAX; ++sl)
+        if (sl < S) v += pv[i][sl];
+      if (bias) v += bias[e];
+      s_log[tr * LDE + e] = v;
+      if (logits_out && t0 + tr < T_) logits_out[at[i]] = v;
+    }
   }
   __syncthreads();
   if constexpr (VAR)
@@ -597,10 +789,16 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
+size_t route_ws_bytes(int T, int H, int E, bool bf16) {
+  const int tiles = (T + RT_TOK - 1) / RT_TOK;
+  if (T <= 0 || tiles <= RT_SPLIT_MAX_TILES || H % 64 != 0) return 0;
+  return (size_t)route_slices(T, H, bf16) * T * E * sizeof(float);
+}
+
 hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* bias,
                         int T, int H, int E, int k, int norm, float* logits,
                         int32_t* ids, float* w, int32_t* counts, hipStream_t s,
-                        const RouterVariant* var) {
+                        const RouterVariant* var, float* parts, size_t parts_bytes) {
   if (counts) {
     hipError_t e = launch_fill_i32(counts, E, 0, s);
     if (e != hipSuccess) return e;
@@ -610,7 +808,13 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
   const bool isvar = var != nullptr;
   const int nt = (E + 15) / 16;
   const int tiles = (T + RT_TOK - 1) / RT_TOK;
-  // Small batches (and a logits buffer to pass through) take the split path.
+  // Small batches (and a logits buffer to pass through) take the split path;
+  // large ones with a workspace the partial-logits path; both then select
+  // with route_select_kernel.
+  const float* sel_src = nullptr;
+  const float* sel_bias = nullptr;
+  float* sel_out = nullptr;
+  int sel_S = 1;
   if (logits && tiles <= RT_SPLIT_MAX_TILES && H % 64 == 0) {
     const dim3 g1(tiles, nt);
     if (bf16)
@@ -619,6 +823,26 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
     else
       route_logits_kernel<float><<<g1, 256, 0, s>>>((const float*)x, (const float*)wr, bias, T, H,
                                                     E, logits);
+    sel_src = logits;   // bias already added
+  } else if (parts && parts_bytes >= route_ws_bytes(T, H, E, bf16) &&
+             route_ws_bytes(T, H, E, bf16) > 0) {
+    sel_S = route_slices(T, H, bf16);
+    hipError_t e;
+#define MOE_PART(NT)                                                                          \
+  e = bf16 ? launch_route_part<bf16_t, NT>(x, wr, T, H, E, sel_S, parts, s)                   \
+           : launch_route_part<float, NT>(x, wr, T, H, E, sel_S, parts, s)
+    if (nt <= 1) MOE_PART(1);
+    else if (nt <= 2) MOE_PART(2);
+    else if (nt <= 4) MOE_PART(4);
+    else if (nt <= 8) MOE_PART(8);
+    else MOE_PART(16);
+#undef MOE_PART
+    if (e != hipSuccess) return e;
+    sel_src = parts;
+    sel_bias = bias;
+    sel_out = logits;
+  }
+  if (sel_src) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t sel_bytes = (size_t)RT_TOK * k * sizeof(uint64_t) +
@@ -626,13 +850,11 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
 #define MOE_SELECT(NT)                                                                          \
   do {                                                                                          \
     if (isvar)                                                                                  \
-      route_select_kernel<NT, true><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(logits, T, E, k,   \
-                                                                            norm, ids, w,      \
-                                                                            counts, v);        \
+      route_select_kernel<NT, true><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(                  \
+          sel_src, sel_S, sel_bias, sel_out, T, E, k, norm, ids, w, counts, v);                 \
     else                                                                                        \
-      route_select_kernel<NT, false><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(logits, T, E, k,  \
-                                                                             norm, ids, w,     \
-                                                                             counts, v);       \
+      route_select_kernel<NT, false><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(                 \
+          sel_src, sel_S, sel_bias, sel_out, T, E, k, norm, ids, w, counts, v);                 \
   } while (0)
     if (nt <= 1) MOE_SELECT(1);
     else if (nt <= 2) MOE_SELECT(2);

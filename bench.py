@@ -562,15 +562,15 @@ def load_traffic(kernel: str, workload: str):
     return t.get("traffic_bytes")
 
 
-def graph_replay(torch, step, s, steps):
+def graph_replay(torch, step, s, steps, warmup):
     """The same layer call captured once in a HIP graph (as a serving loop
-    would run it) and replayed `steps` times: the per-step time without the
-    host's launch gaps.  Context next to the eager stream timing above."""
+    would run it), replayed `warmup` times untimed, then `steps` times: the
+    per-step time without the host's launch gaps."""
     try:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(stream=torch.cuda.current_stream().cuda_stream)
-        for _ in range(3):
+        for _ in range(max(warmup, 1)):
             g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -708,7 +708,7 @@ def run_forward(args, wl, router="softmax", Is=0, context=True):
     for arr in ev_arrays:
         for j in range(nst):
             hip.hipEventDestroy(arr[j])
-    graph = graph_replay(torch, step, s, args.steps)
+    graph = graph_replay(torch, step, s, args.steps, args.warmup)
     ctx = dense_gemm_context(wl) if (context and bf16) else None
 
     c_np = counts.cpu().numpy()

@@ -202,12 +202,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     b_lds[u] = inst * 1024;
   }
 
+  // A wave's last activation copy is left out when all its rows lie past
+  // the tile's end (or it only fills the dump area): such rows feed only
+  // outputs that are never stored, so their LDS rows may stay stale.  The
+  // choice is per wave, and so are the vmcnt counts it changes.
+  constexpr int AL = G::A_PER - 1;
+  const int skl = __builtin_amdgcn_readfirstlane(
+      (!a_on[AL] || (wave + AL * G::NW) * (64 / G::CH) >= rows) ? 1 : 0);
+
   // Copies of the next activation block into activation slot `as` and of
   // the next weight block into weight slot `bs`.
   auto issue_a = [&](int as) {
     unsigned char* const base = smem + as * G::A_BYTES;
 #pragma unroll
     for (int u = 0; u < G::A_PER; ++u) {
+      if (u == AL && skl) break;
       // a copy past the A block re-reads row chunk 0 into the dump area
       copy16_to_lds(a_src[u], a_on[u] ? base + a_lds[u] : smem + G::RING);
       a_src[u] += KB;
@@ -303,19 +312,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   };
   const int KT = K / KB;
   // Wait until at most `nb` of this wave's most recent blocks are in flight.
-  auto wait_blocks = [&](int nb) {
-    static_assert(STAGES <= 8 && (STAGES - 1) * PER < 64, "wait table");
+  auto wait_blocks = [&](auto px_c, int nb) {
+    constexpr int PB = decltype(px_c)::value;   // this wave's loads per block
+    static_assert(STAGES <= 8 && (STAGES - 1) * PB < 64, "wait table");
     // nb never exceeds STAGES - 1; larger cases clamp to it
     constexpr int M = STAGES - 1;
     switch (nb) {
       case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<(M < 1 ? M : 1) * PER>(); break;
-      case 2: wait_vmcnt<(M < 2 ? M : 2) * PER>(); break;
-      case 3: wait_vmcnt<(M < 3 ? M : 3) * PER>(); break;
-      case 4: wait_vmcnt<(M < 4 ? M : 4) * PER>(); break;
-      case 5: wait_vmcnt<(M < 5 ? M : 5) * PER>(); break;
-      case 6: wait_vmcnt<(M < 6 ? M : 6) * PER>(); break;
-      default: wait_vmcnt<(M < 7 ? M : 7) * PER>(); break;
+      case 1: wait_vmcnt<(M < 1 ? M : 1) * PB>(); break;
+      case 2: wait_vmcnt<(M < 2 ? M : 2) * PB>(); break;
+      case 3: wait_vmcnt<(M < 3 ? M : 3) * PB>(); break;
+      case 4: wait_vmcnt<(M < 4 ? M : 4) * PB>(); break;
+      case 5: wait_vmcnt<(M < 5 ? M : 5) * PB>(); break;
+      case 6: wait_vmcnt<(M < 6 ? M : 6) * PB>(); break;
+      default: wait_vmcnt<(M < 7 ? M : 7) * PB>(); break;
     }
   };
   // The copy stream, in issue order: the prologue gives block p its
@@ -332,16 +342,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
   }
 
   // block 0 landed (blocks 1 .. min(STAGES, KT) - 1 may stay in flight)
-  wait_blocks(min(STAGES, KT) - 1);
+  if (skl) wait_blocks(std::integral_constant<int, PER - 1>{}, min(STAGES, KT) - 1);
+  else wait_blocks(std::integral_constant<int, PER>{}, min(STAGES, KT) - 1);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
   // The main loop, specialised on the number of this wave's m-tiles that
   // hold rows (TA), so it is straight-line code: m-tiles past TA are neither
   // read nor multiplied.
-  auto main_loop = [&](auto ta_c) {
+  auto main_loop = [&](auto ta_c, auto sk_c) {
     constexpr int TA = decltype(ta_c)::value;
     constexpr int KS = G::KS;
+    constexpr int PX = PER - decltype(sk_c)::value;   // copies per block, this wave
+    const auto px_c = std::integral_constant<int, PX>{};
     bf16x8_v wf[2][G::TN], xf[TA];   // k-step s of a block uses wf[s & 1]
     // MFMAs of one k-step, m-tile by m-tile; right after m-tile i's MFMAs
     // are issued its activation register is refilled with the fragment of
@@ -359,7 +372,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
     // Packing the copies into the first 2-5 groups, or spreading them over
     // the whole iteration, measured slower.  STEP < 0: none.
     constexpr int GROUPS = TA * KS;
-    constexpr int GP = GROUPS < PER ? GROUPS : PER;   // groups that issue copies
+    constexpr int GP = GROUPS < PX ? GROUPS : PX;     // groups that issue copies
     auto mma_roll = [&](auto step_c, const bf16x8_v (&wf)[G::TN], const unsigned char* nbase,
                         int nkk, int as, int bs, bool on) {
       constexpr int STEP = decltype(step_c)::value;
@@ -372,7 +385,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
         if constexpr (STEP >= 0) {
           constexpr int g = STEP * TA + i;
           if constexpr (g < GP)
-            static_for<g * PER / GP, (g + 1) * PER / GP>(
+            static_for<g * PX / GP, (g + 1) * PX / GP>(
                 [&](auto c_c) { issue_one(c_c, as, bs, on); });
         }
         // keep this order: the scheduler would otherwise gather the reads
@@ -397,7 +410,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
       mma_roll(std::integral_constant<int, -1>{}, wf[st & 1], smem, st + 1, 0, 0, false);
     });
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (KT > 1) wait_blocks(min(STAGES - 2, KT - 2));
+    if (KT > 1) wait_blocks(px_c, min(STAGES - 2, KT - 2));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
                  on);
       });
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (kb + 2 < KT) wait_blocks(min(STAGES - 2, KT - 3 - kb));
+      if (kb + 2 < KT) wait_blocks(px_c, min(STAGES - 2, KT - 3 - kb));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
@@ -436,8 +449,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[(KS - 1) & 1][j], xf[i], acc[i][j], 0, 0, 0);
   };
   // Waves without rows issue the same copies and join the same barriers.
-  auto empty_loop = [&]() {
-    if (KT > 1) wait_blocks(min(STAGES - 2, KT - 2));
+  auto empty_loop = [&](auto sk_c) {
+    const auto px_c = std::integral_constant<int, PER - decltype(sk_c)::value>{};
+    if (KT > 1) wait_blocks(px_c, min(STAGES - 2, KT - 2));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     for (int kb = 0; kb + 1 < KT; ++kb) {
@@ -445,23 +459,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_lds_kernel(
         issue_b(kb % STAGES);
         issue_a(kb % STAGES);
       }
-      if (kb + 2 < KT) wait_blocks(min(STAGES - 2, KT - 3 - kb));
+      if (kb + 2 < KT) wait_blocks(px_c, min(STAGES - 2, KT - 3 - kb));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
   };
   static_assert(G::TM <= 8, "m-tiles per wave");
-  switch (tm_on) {
-    case 0: empty_loop(); break;
-    case 1: main_loop(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (G::TM >= 2) main_loop(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr (G::TM >= 3) main_loop(std::integral_constant<int, 3>{}); break;
-    case 4: if constexpr (G::TM >= 4) main_loop(std::integral_constant<int, 4>{}); break;
-    case 5: if constexpr (G::TM >= 5) main_loop(std::integral_constant<int, 5>{}); break;
-    case 6: if constexpr (G::TM >= 6) main_loop(std::integral_constant<int, 6>{}); break;
-    case 7: if constexpr (G::TM >= 7) main_loop(std::integral_constant<int, 7>{}); break;
-    default: if constexpr (G::TM >= 8) main_loop(std::integral_constant<int, 8>{}); break;
-  }
+  auto run = [&](auto sk_c) {
+    switch (tm_on) {
+      case 0: empty_loop(sk_c); break;
+      case 1: main_loop(std::integral_constant<int, 1>{}, sk_c); break;
+      case 2: if constexpr (G::TM >= 2) main_loop(std::integral_constant<int, 2>{}, sk_c); break;
+      case 3: if constexpr (G::TM >= 3) main_loop(std::integral_constant<int, 3>{}, sk_c); break;
+      case 4: if constexpr (G::TM >= 4) main_loop(std::integral_constant<int, 4>{}, sk_c); break;
+      case 5: if constexpr (G::TM >= 5) main_loop(std::integral_constant<int, 5>{}, sk_c); break;
+      case 6: if constexpr (G::TM >= 6) main_loop(std::integral_constant<int, 6>{}, sk_c); break;
+      case 7: if constexpr (G::TM >= 7) main_loop(std::integral_constant<int, 7>{}, sk_c); break;
+      default: if constexpr (G::TM >= 8) main_loop(std::integral_constant<int, 8>{}, sk_c); break;
+    }
+  };
+  if (skl) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
 
   // ---- epilogue.  acc[i][j][q] = C[row m][col cb_j + 8 (q / 4) + 4 hl + q % 4]
   // with m = 32 * mtile + l % 32.  Results go through LDS so that global

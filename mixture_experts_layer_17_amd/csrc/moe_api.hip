@@ -109,7 +109,7 @@ LayerWs layer_ws(char* base, int T, int H, int I, int E, int k, moe_dtype dt, in
   w.sorted_slot = (int32_t*)take(N * 4);
   w.at_slot_pos = off;
   w.slot_pos = (int32_t*)take(N * 4);
-  w.perm = take(permute_ws_bytes((int)N, E, 0));
+  w.perm = take(permute_fold_ws_bytes(T, k, E));   // with the router-folded first pass
   w.h = take(N * (size_t)I * esize(dt));
   w.at_y = off;
   w.y = take(N * (size_t)H * esize(dt));
@@ -496,9 +496,14 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
     if (stage_events && stage_events[i]) (void)hipEventRecord(stage_events[i], s);
   };
   mark(0);
-  // the histogram comes from the permutation pass, so the router skips it
+  // the histogram comes from the permutation pass, so the router skips it.
+  // On the split-K router path its selection kernel also runs the
+  // permutation's first pass (ranks and block histograms).
+  const bool fold_on = route_can_fold(T, H, E, k, bf16) && w.route_parts_bytes > 0;
+  const PermuteFold fold = fold_on ? permute_fold_scratch(w.perm, T, k, E) : PermuteFold{};
   hipError_t e = launch_route(bf16, x, wr, bias, T, H, E, k, norm, logits, ids, weights, nullptr,
-                              s, var, w.route_parts, w.route_parts_bytes);
+                              s, var, w.route_parts, w.route_parts_bytes,
+                              fold_on ? &fold : nullptr);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(1);
   // the permutation's scan pass also writes both GEMMs' tile lists (one
@@ -507,7 +512,7 @@ int layer_forward_impl(const void* x, const void* wr, const float* bias, const v
   void* const tiles_down = one_list ? w.tiles_up : w.tiles_down;
   e = launch_permute_topk(ids, T, k, E, counts, w.offsets, w.sorted_token, w.sorted_slot,
                           w.slot_pos, w.perm, s, w.tiles_up, cu.BM,
-                          one_list ? nullptr : w.tiles_down, cd.BM);
+                          one_list ? nullptr : w.tiles_down, cd.BM, fold_on ? &fold : nullptr);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(2);
   // The shared expert (MindSpore moe.py, MoE.forward) sees every token and

@@ -31,14 +31,28 @@ struct RouterVariant {
   float* tpe;
 };
 
+// The permutation's first pass folded into the router's selection kernel
+// (large batches on the split-K path): each 16-token block writes its
+// slots' ranks among equal experts (`rank`, [N]) and its expert histogram
+// (`sub`, [ceil(T / 16)][E]) and adds that histogram into the 1024-slot
+// chunk histograms (`hist`, [ceil(N / 1024)][E], cleared by the router's
+// first kernel).
+struct PermuteFold {
+  int32_t* hist;
+  int32_t* sub;
+  int32_t* rank;
+};
+
 // `parts` (optional, route_ws_bytes of it): float32 partial logits, which
-// let large batches take the split-K router.
+// let large batches take the split-K router.  `fold` (only where
+// route_can_fold holds): also run the permutation's first pass.
 hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* bias,
                         int T, int H, int E, int k, int norm, float* logits,
                         int32_t* ids, float* w, int32_t* counts, hipStream_t s,
                         const RouterVariant* var = nullptr, float* parts = nullptr,
-                        size_t parts_bytes = 0);
+                        size_t parts_bytes = 0, const PermuteFold* fold = nullptr);
 size_t route_ws_bytes(int T, int H, int E, bool bf16);
+bool route_can_fold(int T, int H, int E, int k, bool bf16);
 hipError_t launch_update_expert_bias(float* bias, float* tpe, int E, float lr, int nrec,
                                      hipStream_t s);
 
@@ -46,13 +60,19 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 
 // Token-choice permutation.  ws layout is given by permute_ws_bytes().
 size_t permute_ws_bytes(int N, int E, int R);
+// The folded first pass's scratch: the two-pass permutation's histogram and
+// ranks (same place in a permute workspace), then the block histograms.
+size_t permute_fold_ws_bytes(int T, int k, int E);
+PermuteFold permute_fold_scratch(void* ws, int T, int k, int E);
 // Optionally also writes the GEMMs' tile lists (tile_ws_a / tile_ws_b for
-// row-tile heights BM_a / BM_b; NULL to skip).
+// row-tile heights BM_a / BM_b; NULL to skip).  With `fold` the first pass
+// already ran inside the router (launch_route with the same fold).
 hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E,
                                int32_t* counts, int32_t* offsets, int32_t* sorted_token,
                                int32_t* sorted_slot, int32_t* slot_pos, void* ws,
                                hipStream_t s, void* tile_ws_a = nullptr, int BM_a = 0,
-                               void* tile_ws_b = nullptr, int BM_b = 0);
+                               void* tile_ws_b = nullptr, int BM_b = 0,
+                               const PermuteFold* fold = nullptr);
 hipError_t launch_permute_rank_major(const int32_t* counts_rm, int R, int N, int E,
                                      int32_t* counts, int32_t* offsets,
                                      int32_t* sorted_token, int32_t* sorted_slot,

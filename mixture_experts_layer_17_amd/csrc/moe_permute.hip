@@ -29,6 +29,7 @@ constexpr int PM_CHUNK = 1024;            // slots per chunk
 constexpr int PM_SEG = 64;                // slots per wave step
 constexpr int PM_NSEG = PM_CHUNK / PM_SEG;
 constexpr int PM_MAXE = 256;
+constexpr int PM_MAXSUB = 8;              // router blocks per chunk when folded
 constexpr int PM_MAX_RE = 4096;           // rank-major: max R * E
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -99,8 +100,10 @@ __global__ __launch_bounds__(1024) void permute_place_kernel(
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int4* __restrict__ tiles_a, int32_t* __restrict__ count_a, int BM_a,
-    int4* __restrict__ tiles_b, int32_t* __restrict__ count_b, int BM_b) {
+    int4* __restrict__ tiles_b, int32_t* __restrict__ count_b, int BM_b,
+    const int32_t* __restrict__ sub /*[nsub][E] or NULL*/, int sub_slots) {
   __shared__ int s_tot_p[4][PM_MAXE];
+  __shared__ int s_sub[PM_MAXSUB][PM_MAXE];
   __shared__ int s_bef_p[4][PM_MAXE];
   __shared__ int s_tot[PM_MAXE];
   __shared__ int s_off[PM_MAXE + 1];
@@ -126,6 +129,25 @@ __global__ __launch_bounds__(1024) void permute_place_kernel(
         bef += cb + u < c ? v[u] : 0;
       }
     }
+  // Folded first pass: ranks count within the router's blocks of sub_slots
+  // slots, so a slot's base also takes its expert's slots in the earlier
+  // blocks of this chunk (an exclusive scan of their histograms).
+  if (sub && part == 1 && e < E) {
+    const int spc = PM_CHUNK / sub_slots;
+    const int nsub = (N + sub_slots - 1) / sub_slots;
+    int v[PM_MAXSUB];
+#pragma unroll
+    for (int q = 0; q < PM_MAXSUB; ++q) {
+      const int b = c * spc + q;
+      v[q] = (q < spc && b < nsub) ? sub[(size_t)b * E + e] : 0;
+    }
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < PM_MAXSUB; ++q) {
+      s_sub[q][e] = run;
+      run += v[q];
+    }
+  }
   s_tot_p[part][e] = tot;
   s_bef_p[part][e] = bef;
   __syncthreads();
@@ -143,6 +165,7 @@ __global__ __launch_bounds__(1024) void permute_place_kernel(
     int pos = -1;
     if (ei >= 0 && ei < E && rk >= 0) {
       pos = s_base[ei] + rk;
+      if (sub) pos += s_sub[threadIdx.x / sub_slots][ei];
       if (pos >= N) pos = -1;
     }
     if (pos >= 0) {
@@ -337,10 +360,26 @@ size_t permute_ws_bytes(int N, int E, int R) {
   return align256(nchunk * E * sizeof(int32_t)) + align256((size_t)N * sizeof(int32_t));
 }
 
+size_t permute_fold_ws_bytes(int T, int k, int E) {
+  const size_t nsub = (size_t)(T + 15) / 16;
+  return permute_ws_bytes(T * k, E, 0) + align256(nsub * E * sizeof(int32_t));
+}
+
+PermuteFold permute_fold_scratch(void* ws, int T, int k, int E) {
+  const int N = T * k;
+  const size_t nchunk = (size_t)(N + PM_CHUNK - 1) / PM_CHUNK;
+  char* const b = (char*)ws;
+  PermuteFold f;
+  f.hist = (int32_t*)b;
+  f.rank = (int32_t*)(b + align256(nchunk * E * sizeof(int32_t)));
+  f.sub = (int32_t*)(b + permute_ws_bytes(N, E, 0));
+  return f;
+}
+
 hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E, int32_t* counts,
                                int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot,
                                int32_t* slot_pos, void* ws, hipStream_t s, void* tile_ws_a,
-                               int BM_a, void* tile_ws_b, int BM_b) {
+                               int BM_a, void* tile_ws_b, int BM_b, const PermuteFold* fold) {
   const int N = T * k;
   if (N <= 0) {
     hipError_t e = launch_fill_i32(counts, E, 0, s);
@@ -349,19 +388,25 @@ hipError_t launch_permute_topk(const int32_t* ids, int T, int k, int E, int32_t*
   }
   const int nchunk = (N + PM_CHUNK - 1) / PM_CHUNK;
   auto tl = [](void* w) { return w ? (int4*)((char*)w + 256) : (int4*)nullptr; };
+  // the router's blocks of 16 tokens must tile the chunks exactly
+  if (fold && (nchunk == 1 || PM_CHUNK % (16 * k) != 0 || PM_CHUNK / (16 * k) > PM_MAXSUB ||
+               E > PM_MAXE))
+    return hipErrorInvalidValue;
   if (nchunk == 1) {
     permute_single_kernel<<<1, 1024, 0, s>>>(ids, N, E, k, sorted_token, sorted_slot, slot_pos,
                                              counts, offsets, tl(tile_ws_a), (int32_t*)tile_ws_a,
                                              BM_a, tl(tile_ws_b), (int32_t*)tile_ws_b, BM_b);
     return hipGetLastError();
   }
-  int32_t* hist = (int32_t*)ws;
-  int32_t* rank = (int32_t*)((char*)ws + align256((size_t)nchunk * E * sizeof(int32_t)));
-  permute_chunk_kernel<<<nchunk, 256, 0, s>>>(ids, N, E, hist, rank);
+  int32_t* hist = fold ? fold->hist : (int32_t*)ws;
+  int32_t* rank = fold ? fold->rank
+                       : (int32_t*)((char*)ws + align256((size_t)nchunk * E * sizeof(int32_t)));
+  if (!fold) permute_chunk_kernel<<<nchunk, 256, 0, s>>>(ids, N, E, hist, rank);
   permute_place_kernel<<<nchunk, 1024, 0, s>>>(ids, rank, hist, nchunk, N, E, k, sorted_token,
                                                sorted_slot, slot_pos, counts, offsets,
                                                tl(tile_ws_a), (int32_t*)tile_ws_a, BM_a,
-                                               tl(tile_ws_b), (int32_t*)tile_ws_b, BM_b);
+                                               tl(tile_ws_b), (int32_t*)tile_ws_b, BM_b,
+                                               fold ? fold->sub : nullptr, 16 * k);
   return hipGetLastError();
 }
 

@@ -505,10 +505,17 @@ struct rpcfg {
 template <typename T, int NT>
 __global__ __launch_bounds__(RT_WAVES * 64) void route_part_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, int T_, int H, int E, int kslice,
-    float* __restrict__ parts) {
+    float* __restrict__ parts, int32_t* __restrict__ clear, int clear_n) {
   using C = rpcfg<T, NT>;
   constexpr int NS = C::NS;
   extern __shared__ __align__(16) unsigned char smem[];
+  // the folded permutation's chunk histograms start from zero
+  if (clear) {
+    const int nthr = gridDim.x * gridDim.y * blockDim.x;
+    for (int i = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < clear_n;
+         i += nthr)
+      clear[i] = 0;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * RP_TOK;
@@ -631,7 +638,7 @@ int route_slices(int T, int H, bool bf16) {
 
 template <typename V, int NT>
 hipError_t launch_route_part(const void* x, const void* wr, int T, int H, int E, int S,
-                             float* parts, hipStream_t s) {
+                             float* parts, int32_t* clear, int clear_n, hipStream_t s) {
   using C = rpcfg<V, NT>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)route_part_kernel<V, NT>,
@@ -639,7 +646,7 @@ hipError_t launch_route_part(const void* x, const void* wr, int T, int H, int E,
   if (attr != hipSuccess) return attr;
   const dim3 grid((T + RP_TOK - 1) / RP_TOK, S);
   route_part_kernel<V, NT><<<grid, RT_WAVES * 64, C::LDS, s>>>((const V*)x, (const V*)wr, T, H, E,
-                                                               H / S, parts);
+                                                               H / S, parts, clear, clear_n);
   return hipGetLastError();
 }
 
@@ -706,6 +713,54 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   }
 }
 
+// The permutation's first pass for the block's RT_TOK * k slots (MindSpore
+// moe.py, MoE.permutation: a stable sort of the flat slots by expert): each
+// 64-slot wave segment ranks its slots among equal experts with ballots on
+// the id bits, the segments' histograms are scanned per expert, and the
+// block writes each slot's rank within the block, its histogram, and adds
+// the histogram into its 1024-slot chunk's (integer adds: any order gives
+// the same sums).  k is 8, 16 or 32 (route_can_fold), so the block is 2, 4
+// or 8 whole segments and lies inside one chunk.
+__device__ __forceinline__ void fold_block(const uint64_t* keys, int t0, int wave, int lane,
+                                           int T_, int E, int k, const PermuteFold& f) {
+  __shared__ int s_seg[RT_WAVES][256];
+  for (int i = threadIdx.x; i < RT_WAVES * 256; i += RT_WAVES * 64) (&s_seg[0][0])[i] = 0;
+  __syncthreads();   // also: every token's keys are in LDS
+  const int nseg = RT_TOK * k / 64;
+  const int sl = wave * 64 + lane;
+  int e = -1;
+  if (wave < nseg && t0 + sl / k < T_) e = key_expert(keys[sl]);
+  const bool valid = e >= 0 && e < E;
+  int my_rank = 0;
+  if (wave < nseg) {   // uniform over the wave
+    unsigned long long match = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const unsigned long long bb = __ballot(bit);
+      match &= bit ? bb : ~bb;
+    }
+    const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    my_rank = valid ? __popcll(match & below) : 0;
+    // the lowest lane of each equal-expert group records its size
+    if (valid && (match & below) == 0ull) s_seg[wave][e] = __popcll(match);
+  }
+  __syncthreads();
+  if (threadIdx.x < E) {
+    const int x = threadIdx.x;
+    int run = 0;
+    for (int w = 0; w < nseg; ++w) {
+      const int v = s_seg[w][x];
+      s_seg[w][x] = run;
+      run += v;
+    }
+    f.sub[(size_t)blockIdx.x * E + x] = run;
+    if (run > 0) atomicAdd(&f.hist[(size_t)(t0 * k / 1024) * E + x], run);
+  }
+  __syncthreads();
+  if (valid) f.rank[(size_t)t0 * k + sl] = s_seg[wave][e] + my_rank;
+}
+
 // Selection for 16 tokens from logits in global memory: the sum of S
 // partial slices parts[s][t][e] (s = 0 .. S - 1, added in that order), plus
 // the bias when there is one; written to logits_out when it is not null.
@@ -714,7 +769,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_select_kernel(
     const float* __restrict__ parts, int S, const float* __restrict__ bias,
     float* __restrict__ logits_out, int T_, int E, int k, int norm,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
-    RouterVariant var) {
+    RouterVariant var, PermuteFold fold) {
   constexpr int LDE = NT * 16 + 4;
   constexpr int CPL = (NT * 16 + 31) / 32;
   __shared__ float s_log[RT_TOK * LDE];
@@ -759,6 +814,8 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_select_kernel(
   else
     select_tokens<CPL>(s_log, LDE, reinterpret_cast<uint64_t*>(s_sel), t0, wave, lane, T_, E, k,
                        norm, ids_out, w_out, counts);
+  if (fold.hist) fold_block(reinterpret_cast<const uint64_t*>(s_sel), t0, wave, lane, T_, E, k,
+                            fold);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
@@ -789,6 +846,10 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool route_can_fold(int T, int H, int E, int k, bool bf16) {
+  return route_ws_bytes(T, H, E, bf16) > 0 && (k == 8 || k == 16 || k == 32) && E <= 256;
+}
+
 size_t route_ws_bytes(int T, int H, int E, bool bf16) {
   const int tiles = (T + RT_TOK - 1) / RT_TOK;
   if (T <= 0 || tiles <= RT_SPLIT_MAX_TILES || H % 64 != 0) return 0;
@@ -798,7 +859,12 @@ size_t route_ws_bytes(int T, int H, int E, bool bf16) {
 hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* bias,
                         int T, int H, int E, int k, int norm, float* logits,
                         int32_t* ids, float* w, int32_t* counts, hipStream_t s,
-                        const RouterVariant* var, float* parts, size_t parts_bytes) {
+                        const RouterVariant* var, float* parts, size_t parts_bytes,
+                        const PermuteFold* fold) {
+  // the fold rides on the partial-logits path only
+  if (fold && (!parts || parts_bytes < route_ws_bytes(T, H, E, bf16) ||
+               !route_can_fold(T, H, E, k, bf16) || !fold->hist || !fold->sub || !fold->rank))
+    return hipErrorInvalidValue;
   if (counts) {
     hipError_t e = launch_fill_i32(counts, E, 0, s);
     if (e != hipSuccess) return e;
@@ -828,9 +894,11 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
              route_ws_bytes(T, H, E, bf16) > 0) {
     sel_S = route_slices(T, H, bf16);
     hipError_t e;
+    int32_t* const clear = fold ? fold->hist : nullptr;
+    const int clear_n = fold ? (T * k + 1023) / 1024 * E : 0;
 #define MOE_PART(NT)                                                                          \
-  e = bf16 ? launch_route_part<bf16_t, NT>(x, wr, T, H, E, sel_S, parts, s)                   \
-           : launch_route_part<float, NT>(x, wr, T, H, E, sel_S, parts, s)
+  e = bf16 ? launch_route_part<bf16_t, NT>(x, wr, T, H, E, sel_S, parts, clear, clear_n, s)   \
+           : launch_route_part<float, NT>(x, wr, T, H, E, sel_S, parts, clear, clear_n, s)
     if (nt <= 1) MOE_PART(1);
     else if (nt <= 2) MOE_PART(2);
     else if (nt <= 4) MOE_PART(4);
@@ -842,6 +910,7 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
     sel_bias = bias;
     sel_out = logits;
   }
+  const PermuteFold pf = fold ? *fold : PermuteFold{nullptr, nullptr, nullptr};
   if (sel_src) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -851,10 +920,10 @@ hipError_t launch_route(bool bf16, const void* x, const void* wr, const float* b
   do {                                                                                          \
     if (isvar)                                                                                  \
       route_select_kernel<NT, true><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(                  \
-          sel_src, sel_S, sel_bias, sel_out, T, E, k, norm, ids, w, counts, v);                 \
+          sel_src, sel_S, sel_bias, sel_out, T, E, k, norm, ids, w, counts, v, pf);             \
     else                                                                                        \
       route_select_kernel<NT, false><<<tiles, RT_WAVES * 64, sel_bytes, s>>>(                 \
-          sel_src, sel_S, sel_bias, sel_out, T, E, k, norm, ids, w, counts, v);                 \
+          sel_src, sel_S, sel_bias, sel_out, T, E, k, norm, ids, w, counts, v, pf);             \
   } while (0)
     if (nt <= 1) MOE_SELECT(1);
     else if (nt <= 2) MOE_SELECT(2);

@@ -110,6 +110,21 @@ def test_layer_small_bf16(moe, shape):
     run_layer(moe, wl)
 
 
+# Batches on the split-K router path (T > 512), where top_k of 8, 16 or 32
+# folds the permutation's first pass into the selection kernel: a ragged last
+# block of 16 tokens, 256- and 512-slot blocks, and float32.
+@pytest.mark.parametrize("shape", [
+    dict(T=777, H=256, I=128, E=32, top_k=8, dtype=torch.bfloat16),
+    dict(T=700, H=256, I=128, E=64, top_k=16, dtype=torch.bfloat16),
+    dict(T=600, H=128, I=64, E=40, top_k=32, dtype=torch.bfloat16),
+    dict(T=900, H=256, I=64, E=16, top_k=8, dtype=torch.float32),
+])
+def test_layer_router_folded_permutation(moe, shape):
+    wl = workloads.make_layer(f"fold_{shape['T']}_{shape['top_k']}", norm_topk_prob=True, seed=3,
+                              **shape)
+    run_layer(moe, wl)
+
+
 def test_layer_no_renorm(moe):
     wl = workloads.make_layer("no_renorm", T=96, H=256, I=128, E=16, top_k=4,
                               norm_topk_prob=False, seed=2)

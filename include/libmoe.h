@@ -378,7 +378,7 @@ int moe_layer_forward_ex(const void* hidden_states, const void* router_weight,
  *   - A request whose moe_workspace_size(MOE_OP_LAYER, ...) exceeds
  *     MOE_STATIC_SCRATCH_BYTES returns MOE_ERR_SCRATCH and enqueues nothing
  *     (at the Qwen3-30B-A3B expert shape, H = 2048, I = 768, top-8, that is
- *     above 1,345 tokens; 1,209 with a 768-wide shared expert).
+ *     above 1,344 tokens; 1,208 with a 768-wide shared expert).
  *   - Every call on one GPU shares that GPU's array, which keeps the last
  *     call's contents.  Calls that overlap on one GPU (on several streams,
  *     or from several host threads without ordering) race on it; serialise

@@ -53,9 +53,14 @@ def _noalloc(moe, x, wr, gu, dn, k, norm, shared=None):
     return out, logits, ids, w, counts
 
 
+# (workload, token counts of the two calls): decode-sized calls take the
+# small-batch router; 1024 and 600 tokens the split-K router with the
+# permutation's first pass folded into it, near the array's limit
 @pytest.mark.parametrize("shared_I", [0, 768])
-def test_noalloc_matches_workspace_entry_point(moe, shared_I):
-    wl = workloads.make("qwen3_30b_a3b_decode")
+@pytest.mark.parametrize("name,Ts", [("qwen3_30b_a3b_decode", (64, 16)),
+                                     ("qwen3_30b_a3b_prefill", (1024, 600))])
+def test_noalloc_matches_workspace_entry_point(moe, name, Ts, shared_I):
+    wl = workloads.make(name)
     x_all, wr, gu, dn = (t.to(DEV) for t in (wl.hidden_states, wl.router_weight, wl.gate_up,
                                              wl.down))
     shared = None
@@ -63,7 +68,7 @@ def test_noalloc_matches_workspace_entry_point(moe, shared_I):
         w1, w2, w3 = workloads.shared_expert_weights(wl.H, shared_I, wl.dtype)
         shared = (torch.cat([w1.t(), w3.t()], dim=1).contiguous().to(DEV),
                   w2.t().contiguous().to(DEV))
-    for T in (64, 16):   # the second call is smaller
+    for T in Ts:   # the second call is smaller
         say(f"noalloc layer T={T} H={wl.H} I={wl.I} E={wl.E} k={wl.top_k} shared_I={shared_I}")
         x = x_all[:T].contiguous()
         got = _noalloc(moe, x, wr, gu, dn, wl.top_k, wl.norm_topk_prob, shared)

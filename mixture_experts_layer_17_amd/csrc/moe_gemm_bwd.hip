@@ -148,6 +148,10 @@ struct dcfg {
   static constexpr int RING = STAGES * STAGE_BYTES;
   static constexpr int INST = STAGE_BYTES / 1024;    // wave copies per stage
   static constexpr int PER = INST / NW;
+  static constexpr int A_INST = BM * ROWB / 1024;    // of which activation rows
+  // activation copies come first in each wave's list (u < A_PER); the last
+  // of them may be left out (below) when they split evenly over the waves
+  static constexpr int A_PER = A_INST % NW == 0 ? A_INST / NW : 0;
   static constexpr int OBF = CW * 4 + 16;            // fp32 staging row stride
   static constexpr int OBP = CW * 2 + 8;             // bf16 staging row stride
   static constexpr int STG = 32 * OBF * NW;
@@ -281,24 +285,17 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
       src[u] = We + (long long)(n0 + r - BM) * ldw + 8 * c;
     }
   }
-  // called once per block, in block order
-  auto issue = [&](unsigned char* base, int) {
-#pragma unroll
-    for (int u = 0; u < G::PER; ++u) {
-      copy16_to_lds(src[u], base + (wave + u * G::NW) * 1024);
-      src[u] += KB;
-    }
-  };
+  // A wave's last activation copy is left out when all its rows lie past
+  // the tile's end: those rows feed only outputs that are never stored.
+  // The choice is per wave, and so are the vmcnt counts it changes.  Only
+  // where the accumulators take at most half of a wave's registers: with
+  // both copy counts in one kernel the 320 x 256 tile spilled 10 registers
+  // and its launch ran 8 % slower.
+  constexpr int UA = G::A_PER - 1;
+  constexpr bool SKIP_OK = G::A_PER > 0 && G::TM * G::TN * 16 <= 128;
+  const int skl = __builtin_amdgcn_readfirstlane(
+      (SKIP_OK && (wave + UA * G::NW) * (64 / G::CH) >= rows) ? 1 : 0);
   const int KT = K / KB;
-  auto wait_blocks = [&](int nb) {
-    static_assert(STAGES <= 4 && (STAGES - 1) * G::PER < 64, "wait table");
-    switch (nb) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<G::PER>(); break;
-      case 2: wait_vmcnt<2 * G::PER>(); break;
-      default: wait_vmcnt<3 * G::PER>(); break;
-    }
-  };
 
   // fragment offsets: lane l reads row 32 t + l % 32, k chunk 2 kk + l / 32;
   // the swizzle depends on l % 32 only (tiles start at multiples of 32), so
@@ -328,8 +325,36 @@ __global__ __launch_bounds__(WM * WN * 64) void dgrad_kernel(
     return __builtin_bit_cast(bf16x8_v,
                               *reinterpret_cast<const u32x4*>(base + b_off[kk] + 32 * G::ROWB * j));
   };
-  pipelined_k_loop<G::TM, G::TN, STAGES, G::KS>(KT, smem, G::STAGE_BYTES, issue, wait_blocks,
-                                                read_a, read_b, acc);
+  auto run = [&](auto sk_c) {
+    constexpr int SK = decltype(sk_c)::value;
+    constexpr int PX = G::PER - SK;               // this wave's copies per block
+    // called once per block, in block order
+    auto issue = [&](unsigned char* base, int) {
+#pragma unroll
+      for (int u = 0; u < G::PER; ++u) {
+        if (SK && u == UA) continue;
+        copy16_to_lds(src[u], base + (wave + u * G::NW) * 1024);
+        src[u] += KB;
+      }
+    };
+    auto wait_blocks = [&](int nb) {
+      static_assert(STAGES <= 4 && (STAGES - 1) * PX < 64, "wait table");
+      switch (nb) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<PX>(); break;
+        case 2: wait_vmcnt<2 * PX>(); break;
+        default: wait_vmcnt<3 * PX>(); break;
+      }
+    };
+    pipelined_k_loop<G::TM, G::TN, STAGES, G::KS>(KT, smem, G::STAGE_BYTES, issue, wait_blocks,
+                                                  read_a, read_b, acc);
+  };
+  if constexpr (SKIP_OK) {
+    if (skl) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 0>{});
+  } else {
+    run(std::integral_constant<int, 0>{});
+  }
 
   // ---- epilogue.  acc[i][j][q] = C[row 32 (wm + WM i) + l % 32]
   //                                 [col wn CW + 32 j + 8 (q / 4) + 4 hl + q % 4]
